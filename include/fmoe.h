@@ -1,0 +1,183 @@
+/*
+ * fmoe.h -- C-ABI of the MI355X (gfx950) quantized MoE expert-block library.
+ *
+ * The library computes the per-token Mixture-of-Experts expert block described on the
+ * Flash-MoE pages:
+ *   [aibit]  aibit.im, "397B MoE sur MacBook : 4,4 t/s Moteur Flash-MoE"
+ *   [hada]   tr.news.hada.io topic 27758, "Flash-MoE - Dizustunde 397 milyar parametreli
+ *            modeli calistirma"
+ *   [radar]  openclawradar.com, "Autoresearch pousse Qwen3.5-397B a 20,34 tok/s sur M5 Max
+ *            via le streaming SSD"
+ * i.e. an fp32 router over the experts, top-k selection with softmax weights, affine
+ * group-quantized (4-bit or 2-bit codes with a bf16 scale and bias per group of 64
+ * weights) gate/up matvecs with a fused SwiGLU, the down matvec, and the weighted
+ * combine plus residual, with an RMS norm between layers.
+ *
+ * Conventions shared by every entry point
+ *  - Every data pointer is a DEVICE pointer owned by the caller (e.g. a torch tensor's
+ *    data_ptr()). Descriptor structs (fmoe_qmat, fmoe_expert, fmoe_layer) live in host
+ *    memory and are read only during the call. The library never allocates or frees
+ *    caller memory; scratch memory comes from a caller workspace sized by
+ *    fmoe_workspace_bytes().
+ *  - Work is enqueued asynchronously on `stream` (a hipStream_t; 0 = the null stream).
+ *    Buffers must stay alive until the stream reaches that point.
+ *  - Every entry point returns FMOE_OK (0) or a negative fmoe_status. All arguments are
+ *    validated before anything is enqueued: on an error nothing was enqueued. A failed
+ *    launch returns FMOE_ERR_HIP. No C++ exception crosses this interface.
+ *  - Entry points keep no mutable global state and may be called from several threads;
+ *    two calls that share a workspace must not overlap on the device.
+ *  - Alignment: codes, sb, activation and output pointers must be 16-byte aligned.
+ *
+ * Quantized matrix layout (the library's packed layout, produced by fmoe_pack)
+ *  - codes: row-major, rows x (cols*bits/8) bytes. 4-bit: byte j of a row holds column
+ *    2j in bits 0-3 and column 2j+1 in bits 4-7. 2-bit: byte j holds column 4j+t in bits
+ *    2t..2t+1. (This equals the canonical layout, so fmoe_pack copies codes unchanged.)
+ *  - sb: uint32 [rows][cols/group]; bits 0-15 = bf16 scale s, bits 16-31 = bf16 bias b
+ *    of the group. Weight (r, c) is q*s + b with s, b of group floor(c/group)
+ *    ([aibit] "Techniques de rupture" item 2 and [hada] "FMA optimize dequant cekirdegi":
+ *    the affine nibble*scale+bias form).
+ *  - group must be 64 and cols a multiple of 64.
+ *
+ * Expert blob (one expert, fixed size fmoe_expert_bytes()):
+ *    [gate codes][up codes][down codes][gate sb][up sb][down sb]
+ *  gate/up are inter x hidden, down is hidden x inter. At hidden 4096, inter 1024 a
+ *  4-bit blob is 7,077,888 bytes (the pages' "about 6.75 MB per expert", [aibit]
+ *  "Techniques de rupture" item 1 and [hada] "SSD Expert Streaming"); 2-bit: 3,932,160.
+ */
+#ifndef FMOE_H
+#define FMOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* fmoe_stream_t; /* same type as hipStream_t */
+
+enum fmoe_status {
+  FMOE_OK = 0,
+  FMOE_ERR_NULL = -1,      /* a required pointer is NULL */
+  FMOE_ERR_SHAPE = -2,     /* sizes out of range, not a multiple of 64, or inconsistent */
+  FMOE_ERR_BITS = -3,      /* bits not in {2, 4} */
+  FMOE_ERR_GROUP = -4,     /* group != 64 */
+  FMOE_ERR_K = -5,         /* k not in 1..min(16, n_experts) */
+  FMOE_ERR_ALIGN = -6,     /* a pointer or stride is not 16-byte (stride: 256-byte) aligned */
+  FMOE_ERR_WORKSPACE = -7, /* workspace NULL or smaller than fmoe_workspace_bytes() */
+  FMOE_ERR_HIP = -8,       /* a HIP call or kernel launch failed */
+  FMOE_ERR_INTERNAL = -9,  /* unexpected internal condition */
+  FMOE_ERR_DEVICE = -10,   /* the current device is not gfx950 */
+  FMOE_ERR_OVERLAP = -11   /* an output buffer overlaps an input buffer */
+};
+
+/* Flags of fmoe_moe_layer. */
+#define FMOE_PRENORM 1u /* v = rmsnorm(h) feeds router and experts (between layers) */
+
+/* Operation ids of fmoe_workspace_bytes. */
+enum fmoe_op { FMOE_OP_EXPERT_FFN = 1, FMOE_OP_MOE_LAYER = 2 };
+
+typedef struct fmoe_qmat {
+  const void* codes;  /* packed codes, see layout above */
+  const uint32_t* sb; /* packed (scale, bias) pairs */
+  int rows, cols, bits, group;
+} fmoe_qmat;
+
+typedef struct fmoe_expert {
+  fmoe_qmat gate, up, down; /* gate/up: inter x hidden; down: hidden x inter */
+} fmoe_expert;
+
+typedef struct fmoe_layer {
+  const float* router;  /* fp32 [n_experts][hidden], row-major */
+  const void* experts;  /* n_experts expert blobs, blob e at experts + e * expert_stride */
+  size_t expert_stride; /* bytes; >= fmoe_expert_bytes(), multiple of 256 */
+  int n_experts, hidden, inter, bits, group;
+} fmoe_layer;
+
+/* Human-readable text of a status code (static storage). */
+const char* fmoe_status_string(int status);
+
+/* Library version string, e.g. "fmoe 0.1 gfx950". */
+const char* fmoe_version(void);
+
+/* Bytes of a packed matrix's codes and of its sb array; 0 if the shape is invalid. */
+size_t fmoe_codes_bytes(int rows, int cols, int bits);
+size_t fmoe_sb_bytes(int rows, int cols, int group);
+
+/* Bytes of one expert blob (layout above); 0 if the shape is invalid. */
+size_t fmoe_expert_bytes(int hidden, int inter, int bits, int group);
+
+/* Views of the three matrices of the expert blob at `blob` (no device access). */
+int fmoe_expert_view(const void* blob, int hidden, int inter, int bits, int group, fmoe_expert* out);
+
+/* Canonical -> packed. codes_canon: uint8 [rows][cols*bits/8] (the canonical layout,
+ * identical to the packed one); scale, bias: bf16 bit patterns [rows][cols/group].
+ * Writes codes_out (skipped when codes_out == codes_canon) and sb_out. Device pointers. */
+int fmoe_pack(const uint8_t* codes_canon, const uint16_t* scale, const uint16_t* bias, int rows, int cols,
+              int bits, int group, void* codes_out, uint32_t* sb_out, fmoe_stream_t stream);
+
+/* Workspace bytes needed by an operation (0 when none is needed). For FMOE_OP_MOE_LAYER
+ * pass the largest n_tokens, hidden, inter, n_experts and k that the calls will use. */
+size_t fmoe_workspace_bytes(int op, int n_tokens, int hidden, int inter, int n_experts, int k);
+
+/*
+ * y[v][r] = sum_c (q[r][c] * s[r][c/64] + b[r][c/64]) * x[v][c]  for v < n_vec.
+ * The dequantized matvec of [aibit] "Techniques de rupture" item 4 (4-bit and 2-bit
+ * dequant matvec), computed per group as s * sum(q*x) + b * sum(x) in fp32.
+ * x: fp32 [n_vec][cols]; y: fp32 [n_vec][rows]; 1 <= n_vec <= 64; cols <= 8192 (4-bit)
+ * or 16384 (2-bit). y must not overlap x.
+ */
+int fmoe_dequant_matvec(const fmoe_qmat* W, const float* x, float* y, int n_vec, fmoe_stream_t stream);
+
+/*
+ * Router + top-k for n_tokens tokens ([aibit] "Techniques de rupture" items 1 and 3,
+ * [hada] "Model mimarisi": k of n_experts experts per token; the pages route on the
+ * CPU, here it runs on the device):
+ *   logits[t][e] = sum_i router[e][i] * x[t][i]                  (fp32)
+ *   idx[t][0..k) = the k largest logits, descending; equal logits -> lower index first;
+ *                  NaN ranks last
+ *   w[t][j]      = exp(l_j - l_0) / sum_{j'<k} exp(l_j' - l_0)    (softmax over the k)
+ * router: fp32 [n_experts][hidden]; x: fp32 [n_tokens][hidden]; idx: int32
+ * [n_tokens][k]; w: fp32 [n_tokens][k]; logits: fp32 [n_tokens][n_experts] or NULL.
+ * Limits: 1 <= n_experts <= 4096, hidden multiple of 64 and <= 16384, 1 <= k <= 16.
+ */
+int fmoe_route_topk(const float* router, const float* x, int n_tokens, int n_experts, int hidden, int k,
+                    int32_t* idx, float* w, float* logits, fmoe_stream_t stream);
+
+/*
+ * One expert's SwiGLU FFN for one token ([aibit] "Techniques de rupture" item 4: fused
+ * SwiGLU, dequant matvecs):  y = Wd (silu(Wg x) * (Wu x)),  silu(z) = z / (1 + e^-z).
+ * x: fp32 [hidden]; y: fp32 [hidden]; ws: >= fmoe_workspace_bytes(FMOE_OP_EXPERT_FFN,
+ * 1, hidden, inter, 1, 1) bytes. All three matrices share bits and group; hidden <=
+ * 8192, inter <= 8192 (4-bit limits of fmoe_dequant_matvec).
+ */
+int fmoe_expert_ffn(const fmoe_expert* e, const float* x, float* y, void* ws, size_t ws_bytes,
+                    fmoe_stream_t stream);
+
+/*
+ * MoE layers. For each layer l in order ([aibit] "Techniques de rupture" item 3 and
+ * [hada] "Deferred GPU Expert Compute": route, run the selected experts, then combine
+ * with the residual and normalize for the next layer):
+ *   v   = (flags & FMOE_PRENORM) ? h / sqrt(mean(h^2) + eps) : h
+ *   idx, w = route(router_l, v, k)                  (as fmoe_route_topk)
+ *   h   = h + sum_j w_j * FFN_{idx_j}(v)            (as fmoe_expert_ffn)
+ * with h = x_in at the start; h_out receives the final h.
+ * x_in, h_out: fp32 [n_tokens][hidden], must not overlap. idx_out (nullable): int32
+ * [n_tokens][n_layers][k]; w_out (nullable): fp32 [n_tokens][n_layers][k].
+ * n_tokens == 1 runs the single-token decode path (one persistent kernel for all
+ * layers). n_tokens > 1 runs the batched path: tokens are grouped by expert and each
+ * expert's gate/up/down run as bf16 matrix-core GEMMs with fp32 accumulation (weights
+ * dequantized to fp32 then rounded to bf16; inputs and the SwiGLU output rounded to
+ * bf16); routing and the combine stay fp32.
+ * All layers must share n_experts, hidden, inter, bits and group. Limits: hidden ==
+ * 4096 or a multiple of 256 up to 8192 ... see fmoe_workspace_bytes; n_tokens <= 4096;
+ * n_layers <= 4096.
+ */
+int fmoe_moe_layer(const fmoe_layer* layers, int n_layers, const float* x_in, float* h_out, int n_tokens, int k,
+                   float eps, unsigned flags, int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes,
+                   fmoe_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif

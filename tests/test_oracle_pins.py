@@ -1,0 +1,417 @@
+"""Pins of the CPU oracle against facts fixed by the pages and by mathematics.
+
+The oracle (oracle/oracle.c) is the parity reference for the HIP library, so it is
+checked here against things other than itself:
+  * hand-set tensors with hand-computed outputs (tests/golden/*.json, cited there);
+  * exact integer arithmetic (Python ints) on integer-valued data, which also pins the
+    pages' FMA rewrite identity (n*s+b)*x == fma(n, s*x, b*x) and the per-group
+    factorisation s*sum(n*x) + b*sum(x) used by the GPU kernels;
+  * brute force over every element of small matrices (code layout);
+  * numpy/scipy/torch library routines as independent steps (dense matmul, sorting,
+    softmax, expit, bf16 rounding);
+  * invariants: linearity, sum of weights = 1, scale invariance, zero experts.
+A plausible slip anywhere in the oracle (a dropped term, a wrong sign or index, a
+transposed operand, a wrong nibble order) fails at least one test below.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+import synth
+
+
+# ------------------------------------------------------------------ helpers (independent decoders)
+def dense_decode(codes, scale, bias, rows, cols, bits, group):
+    """Dense fp64 weights from the canonical layout, vectorized numpy (independent of oracle.c)."""
+    codes = np.asarray(codes, dtype=np.uint8).reshape(rows, cols * bits // 8)
+    if bits == 4:
+        q = np.empty((rows, cols), dtype=np.int64)
+        q[:, 0::2] = codes & 0x0F
+        q[:, 1::2] = codes >> 4
+    else:
+        q = np.empty((rows, cols), dtype=np.int64)
+        for t in range(4):
+            q[:, t::4] = (codes >> (2 * t)) & 0x03
+    s = synth.bf16_to_f32(scale).astype(np.float64).reshape(rows, cols // group)
+    b = synth.bf16_to_f32(bias).astype(np.float64).reshape(rows, cols // group)
+    return q * np.repeat(s, group, axis=1) + np.repeat(b, group, axis=1)
+
+
+def random_matrix(rng, rows, cols, bits, group=64):
+    codes = rng.integers(0, 256, size=(rows, cols * bits // 8), dtype=np.uint8)
+    scale = synth.bf16_bits(rng.uniform(0.001, 0.02, size=(rows, cols // group)).astype(np.float32))
+    bias = synth.bf16_bits(rng.uniform(-0.1, 0.1, size=(rows, cols // group)).astype(np.float32))
+    return codes, scale, bias
+
+
+def bf16_of(values):
+    return synth.bf16_bits(np.asarray(values, dtype=np.float32))
+
+
+# ------------------------------------------------------------------ O1/O2 dequant matvec
+def _x_of(kind, cols):
+    if kind == "ones":
+        return np.ones(cols)
+    if kind == "alternating":
+        return np.array([1.0 if c % 2 == 0 else -1.0 for c in range(cols)])
+    raise ValueError(kind)
+
+
+def test_golden_dequant_tiny(golden_dir):
+    """Hand-set tensors with hand-computed outputs (tests/golden/dequant_tiny.json)."""
+    d = json.load(open(os.path.join(golden_dir, "dequant_tiny.json")))
+    for case in d["cases"]:
+        rows, cols, bits, group = case["rows"], case["cols"], case["bits"], case["group"]
+        codes = np.frombuffer(bytes.fromhex("".join(case["codes_hex"])), dtype=np.uint8).reshape(rows, -1)
+        scale, bias = bf16_of(case["scale"]), bf16_of(case["bias"])
+        for xc in case["x_cases"]:
+            y = oracle.matvec(codes, scale, bias, rows, cols, bits, group, _x_of(xc["x"], cols))
+            assert y.tolist() == xc["y"], (case["name"], xc["x"])
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_code_layout_bruteforce(bits):
+    """oracle_code reads element (r, c) exactly where the canonical layout puts it."""
+    rng = np.random.default_rng(1)
+    rows, cols = 3, 128
+    codes = rng.integers(0, 256, size=(rows, cols * bits // 8), dtype=np.uint8)
+    per = 8 // bits
+    for r in range(rows):
+        for c in range(cols):
+            byte = int(codes[r, c // per])
+            want = (byte >> (bits * (c % per))) & ((1 << bits) - 1)
+            assert oracle.code(codes, cols, bits, r, c) == want
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_integer_exact_and_fma_identity(bits):
+    """Integer-valued s, b, x: oracle == exact integer sum; == per-group factorisation;
+    == the FMA rewrite sum fma(n, s*x, b*x), in fp32 and fp64 (all exact on such data)."""
+    rng = np.random.default_rng(2)
+    rows, cols, group = 4, 192, 64
+    codes = rng.integers(0, 256, size=(rows, cols * bits // 8), dtype=np.uint8)
+    s_int = rng.integers(1, 9, size=(rows, cols // group))
+    b_int = rng.integers(-8, 9, size=(rows, cols // group))
+    x_int = rng.integers(-5, 6, size=cols)
+    y = oracle.matvec(codes, bf16_of(s_int), bf16_of(b_int), rows, cols, bits, group, x_int.astype(np.float64))
+    per = 8 // bits
+    for r in range(rows):
+        exact = 0
+        fact = 0
+        for g in range(cols // group):
+            sum_nx = 0
+            sum_x = 0
+            for c in range(g * group, (g + 1) * group):
+                n = (int(codes[r, c // per]) >> (bits * (c % per))) & ((1 << bits) - 1)
+                exact += (n * int(s_int[r, g]) + int(b_int[r, g])) * int(x_int[c])
+                sum_nx += n * int(x_int[c])
+                sum_x += int(x_int[c])
+            fact += int(s_int[r, g]) * sum_nx + int(b_int[r, g]) * sum_x
+        assert exact == fact
+        assert y[r] == float(exact)
+        for dt in (np.float32, np.float64):
+            acc_plain = dt(0)
+            acc_fma = dt(0)
+            for c in range(cols):
+                g = c // group
+                n = dt((int(codes[r, c // per]) >> (bits * (c % per))) & ((1 << bits) - 1))
+                s, b, x = dt(s_int[r, g]), dt(b_int[r, g]), dt(x_int[c])
+                acc_plain = dt(acc_plain + (n * s + b) * x)
+                acc_fma = dt(acc_fma + (n * (s * x) + (b * x)))
+            assert acc_plain == acc_fma == dt(exact)
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_onehot_returns_dequantized_column(bits):
+    rng = np.random.default_rng(3)
+    rows, cols, group = 5, 128, 64
+    codes, scale, bias = random_matrix(rng, rows, cols, bits)
+    W = dense_decode(codes, scale, bias, rows, cols, bits, group)
+    for c in (0, 1, 2, 3, 63, 64, 127):
+        x = np.zeros(cols)
+        x[c] = 1.0
+        y = oracle.matvec(codes, scale, bias, rows, cols, bits, group, x)
+        assert np.array_equal(y, W[:, c])
+        for r in range(rows):
+            assert oracle.weight(codes, scale, bias, cols, bits, group, r, c) == W[r, c]
+
+
+def test_zero_codes_and_zero_affine():
+    rng = np.random.default_rng(4)
+    rows, cols, group = 3, 256, 64
+    _, scale, bias = random_matrix(rng, rows, cols, 4)
+    x = rng.standard_normal(cols)
+    zero_codes = np.zeros((rows, cols // 2), dtype=np.uint8)
+    y = oracle.matvec(zero_codes, scale, bias, rows, cols, 4, group, x)
+    b = synth.bf16_to_f32(bias).astype(np.float64)
+    X = x.reshape(cols // group, group).sum(axis=1)
+    assert np.allclose(y, (b * X[None, :]).sum(axis=1), rtol=1e-14, atol=1e-15)
+    codes = rng.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    zeros = np.zeros((rows, cols // group), dtype=np.uint16)
+    assert np.all(oracle.matvec(codes, zeros, zeros, rows, cols, 4, group, x) == 0.0)
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_dense_matmul_and_linearity(bits):
+    rng = np.random.default_rng(5)
+    rows, cols, group = 96, 320, 64
+    codes, scale, bias = random_matrix(rng, rows, cols, bits)
+    W = dense_decode(codes, scale, bias, rows, cols, bits, group)
+    x, z = rng.standard_normal(cols), rng.standard_normal(cols)
+    yx = oracle.matvec(codes, scale, bias, rows, cols, bits, group, x)
+    yz = oracle.matvec(codes, scale, bias, rows, cols, bits, group, z)
+    assert np.allclose(yx, W @ x, rtol=1e-13, atol=1e-13)
+    a, b = 0.75, -2.5
+    ylin = oracle.matvec(codes, scale, bias, rows, cols, bits, group, a * x + b * z)
+    ref = a * yx + b * yz
+    assert np.max(np.abs(ylin - ref)) <= 1e-13 * np.max(np.abs(ref))
+
+
+# ------------------------------------------------------------------ O3 routing
+def test_golden_route_tiny(golden_dir):
+    d = json.load(open(os.path.join(golden_dir, "route_tiny.json")))
+    R = np.array(d["router"], dtype=np.float32)
+    e05 = math.exp(-0.5)
+    e2 = math.exp(-2.0)
+    closed = [[1 / (2 + e05), 1 / (2 + e05), e05 / (2 + e05)], [1 / (1 + e2), e2 / (1 + e2)]]
+    for case, wc in zip(d["cases"], closed):
+        idx, w, logits, margin = oracle.route(R, case["v"], case["k"])
+        assert idx.tolist() == case["idx"]
+        assert logits.tolist() == case["logits"]
+        assert np.allclose(w, wc, rtol=1e-15, atol=0)
+        assert margin == case["margin"]
+
+
+def test_route_bruteforce_sort_with_ties_and_nan():
+    """Selection equals a full library sort by (logit desc, index asc), NaN last."""
+    rng = np.random.default_rng(6)
+    for trial in range(200):
+        E, H = int(rng.integers(2, 12)), 1
+        k = int(rng.integers(1, min(E, 16) + 1))
+        col = rng.integers(-3, 4, size=E).astype(np.float32)  # many ties
+        if trial % 5 == 0:
+            col[rng.integers(0, E)] = np.nan
+        R = col.reshape(E, H)
+        idx, w, logits, margin = oracle.route(R, [1.0], k)
+        key = [(1 if math.isnan(v) else 0, -v if not math.isnan(v) else 0.0, e) for e, v in enumerate(col.tolist())]
+        want = [e for (_, _, e) in sorted(key)][:k]
+        assert idx.tolist() == want
+        sel = np.array([col[e] for e in want], dtype=np.float64)
+        if not np.isnan(sel).any():
+            assert np.allclose(w, scipy.special.softmax(sel), rtol=1e-14, atol=1e-300)
+            assert abs(1.0 - w.sum()) <= 1e-15
+
+
+def test_route_invariants():
+    rng = np.random.default_rng(7)
+    E, H = 64, 32
+    R = (0.02 * rng.standard_normal((E, H))).astype(np.float32)
+    v = rng.standard_normal(H)
+    idx, w, logits, margin = oracle.route(R, v, 4)
+    assert abs(1.0 - w.sum()) <= 1e-15
+    assert np.all(np.diff(logits[idx]) <= 0)
+    # logits are the plain product (library matmul)
+    assert np.allclose(logits, R.astype(np.float64) @ v, rtol=1e-14, atol=1e-15)
+    # k = 1 gives weight 1
+    i1, w1, _, _ = oracle.route(R, v, 1)
+    assert i1[0] == idx[0] and w1[0] == 1.0
+    # positive scaling of v keeps the selection, margin scales with it
+    i2, w2, _, m2 = oracle.route(R, 3.0 * v, 4)
+    assert i2.tolist() == idx.tolist()
+    assert m2 == pytest.approx(3.0 * margin, rel=1e-12)
+    # margin is the smallest gap among the first k+1 ordered logits
+    order = sorted(range(E), key=lambda e: (-logits[e], e))
+    gaps = [logits[order[j]] - logits[order[j + 1]] for j in range(4)]
+    assert margin == pytest.approx(min(gaps), rel=1e-14)
+
+
+def test_route_planted():
+    """A router with planted rows returns the planted experts in the planted order."""
+    E, H = 512, 64
+    rng = np.random.default_rng(8)
+    R = (0.02 * rng.standard_normal((E, H))).astype(np.float32)
+    v = np.zeros(H)
+    v[0] = 1.0
+    planted = [17, 300, 5, 511]
+    R[:, 0] = 0.0
+    for rank, e in enumerate(planted):
+        R[e, 0] = 4.0 - rank
+    idx, w, _, margin = oracle.route(R, v, 4)
+    assert idx.tolist() == planted
+    assert margin == pytest.approx(1.0)
+
+
+# ------------------------------------------------------------------ SwiGLU / RMSNorm
+def test_swiglu_special_values():
+    assert oracle.swiglu(0.0, 5.0) == 0.0
+    assert oracle.swiglu(3.0, 0.0) == 0.0
+    assert oracle.swiglu(50.0, 2.0) == pytest.approx(100.0, rel=1e-15)
+    v = oracle.swiglu(-1000.0, 1.0)
+    assert v == 0.0 and math.copysign(1.0, v) == -1.0 and not math.isnan(v)
+    rng = np.random.default_rng(9)
+    for g, u in rng.standard_normal((100, 2)) * 6:
+        assert oracle.swiglu(g, u) == pytest.approx(g * scipy.special.expit(g) * u, rel=1e-14, abs=1e-300)
+
+
+def test_rmsnorm_closed_forms():
+    rng = np.random.default_rng(10)
+    h = rng.standard_normal(4096) * 7.0
+    eps = 1e-6
+    v = oracle.rmsnorm(h, eps)
+    m = np.mean(h * h)
+    assert np.sqrt(np.mean(v * v)) == pytest.approx(math.sqrt(m / (m + eps)), rel=1e-13)
+    # scaling h by alpha > 0 changes v only through eps: v2 = v * sqrt(m + eps) / sqrt(m + eps / alpha^2)
+    v2 = oracle.rmsnorm(1e3 * h, eps)
+    assert np.allclose(v2, v * math.sqrt(m + eps) / math.sqrt(m + eps * 1e-6), rtol=1e-14)
+    c = oracle.rmsnorm(np.full(16, 2.0), 0.0)
+    assert np.allclose(c, 1.0, rtol=1e-15)
+
+
+# ------------------------------------------------------------------ O4 expert FFN, O5 layer, O6 stack
+def _expert(rng, H, I, bits):
+    return [random_matrix(rng, I, H, bits), random_matrix(rng, I, H, bits), random_matrix(rng, H, I, bits)]
+
+
+@pytest.mark.parametrize("bits", [4, 2])
+def test_expert_ffn_dense(bits):
+    rng = np.random.default_rng(11)
+    H, I = 256, 128
+    mats = _expert(rng, H, I, bits)
+    x = rng.standard_normal(H)
+    y, a = oracle.expert_ffn(mats, H, I, bits, 64, x)
+    Wg = dense_decode(*mats[0], I, H, bits, 64)
+    Wu = dense_decode(*mats[1], I, H, bits, 64)
+    Wd = dense_decode(*mats[2], H, I, bits, 64)
+    g, u = Wg @ x, Wu @ x
+    a_ref = g * scipy.special.expit(g) * u
+    assert np.allclose(a, a_ref, rtol=1e-12, atol=1e-14)
+    assert np.allclose(y, Wd @ a_ref, rtol=1e-12, atol=1e-12)
+
+
+def _tiny_model(rng, L, E, H, I, bits):
+    experts = [[_expert(rng, H, I, bits) for _ in range(E)] for _ in range(L)]
+    routers = [(0.02 * rng.standard_normal((E, H))).astype(np.float32) for _ in range(L)]
+    return experts, routers
+
+
+def test_layer_zero_experts_is_identity():
+    rng = np.random.default_rng(12)
+    E, H, I = 8, 128, 64
+    zero = [(np.zeros((r, c // 2), np.uint8), np.zeros((r, c // 64), np.uint16), np.zeros((r, c // 64), np.uint16))
+            for (r, c) in ((I, H), (I, H), (H, I))]
+    prov = oracle.ArrayProvider([[zero] * E])
+    R = (0.02 * rng.standard_normal((E, H))).astype(np.float32)
+    h = rng.standard_normal(H)
+    for prenorm in (0, 1):
+        out, idx, w, m = oracle.moe_layer(prov, 0, R, h, I, 2, 4, 64, prenorm, 1e-6)
+        assert np.array_equal(out, h)
+
+
+def test_layer_identical_experts_and_planted_weights():
+    """All experts equal -> out = h + FFN(v) (weights sum to 1); planted order is respected."""
+    rng = np.random.default_rng(13)
+    E, H, I, k = 8, 128, 64, 3
+    ex = _expert(rng, H, I, 4)
+    prov = oracle.ArrayProvider([[ex] * E])
+    R = (0.02 * rng.standard_normal((E, H))).astype(np.float32)
+    h = rng.standard_normal(H)
+    out, idx, w, m = oracle.moe_layer(prov, 0, R, h, I, k, 4, 64, 0, 1e-6)
+    y, _ = oracle.expert_ffn(ex, H, I, 4, 64, h)
+    assert np.allclose(out, h + y, rtol=1e-12, atol=1e-12)
+    # distinct experts: out = h + sum_j w_j FFN_j(v), with v = rmsnorm(h) under pre-norm
+    experts, routers = _tiny_model(rng, 1, E, H, I, 4)
+    prov2 = oracle.ArrayProvider(experts)
+    out2, idx2, w2, _ = oracle.moe_layer(prov2, 0, routers[0], h, I, k, 4, 64, 1, 1e-6)
+    v = h / np.sqrt(np.mean(h * h) + 1e-6)
+    i_ref, w_ref, _, _ = oracle.route(routers[0], v, k)
+    assert idx2.tolist() == i_ref.tolist()
+    ref = h.copy()
+    for j in range(k):
+        yj, _ = oracle.expert_ffn(experts[0][idx2[j]], H, I, 4, 64, v)
+        ref += w_ref[j] * yj
+    assert np.allclose(out2, ref, rtol=1e-13, atol=1e-13)
+
+
+def test_stack_equals_repeated_layers():
+    rng = np.random.default_rng(14)
+    L, E, H, I, k = 3, 8, 128, 64, 2
+    experts, routers = _tiny_model(rng, L, E, H, I, 4)
+    prov = oracle.ArrayProvider(experts)
+    x = rng.standard_normal(H).astype(np.float32)
+    res = oracle.stack(prov, routers, x, I, k, 4, 64, 1e-6)
+    h = x.astype(np.float64)
+    for l in range(L):
+        h, idx, w, m = oracle.moe_layer(prov, l, routers[l], h, I, k, 4, 64, 1, 1e-6)
+        assert idx.tolist() == res["idx"][l].tolist()
+        assert np.allclose(res["h_all"][l], h, rtol=0, atol=0)
+        assert res["margins"][l] == m
+    assert np.array_equal(res["out"], h)
+    assert res["layers_done"] == L
+
+
+def test_stack_stop_margin():
+    rng = np.random.default_rng(15)
+    L, E, H, I, k = 4, 8, 128, 64, 2
+    experts, routers = _tiny_model(rng, L, E, H, I, 4)
+    prov = oracle.ArrayProvider(experts)
+    x = rng.standard_normal(H).astype(np.float32)
+    full = oracle.stack(prov, routers, x, I, k, 4, 64, 1e-6)
+    thr = float(np.max(full["margins"])) * 1.0001
+    part = oracle.stack(prov, routers, x, I, k, 4, 64, 1e-6, stop_margin=thr)
+    first_bad = int(np.argmax(full["margins"] < thr))
+    assert part["layers_done"] == first_bad + 1
+
+
+# ------------------------------------------------------------------ O7 batched bf16 contract
+def test_round_bf16_matches_torch():
+    rng = np.random.default_rng(16)
+    vals = np.concatenate([rng.standard_normal(2000) * 10.0 ** rng.integers(-8, 8, 2000),
+                           [1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -9, 1.0 + 2.0 ** -9, -0.0, 0.0, 1e-40]])
+    for v in vals:
+        want = float(torch.tensor(np.float32(v)).to(torch.bfloat16).float())
+        assert oracle.round_bf16(float(np.float32(v))) == want
+    assert oracle.round_bf16(1.0 + 2.0 ** -8) == 1.0  # tie -> even
+    assert oracle.round_bf16(1.0 + 3 * 2.0 ** -9) == 1.0 + 2.0 ** -7
+
+
+def test_layer_bf16_contract():
+    rng = np.random.default_rng(17)
+    E, H, I, k, T = 8, 128, 64, 2, 5
+    experts, routers = _tiny_model(rng, 1, E, H, I, 4)
+    prov = oracle.ArrayProvider(experts)
+    X = rng.standard_normal((T, H)).astype(np.float32)
+    res = oracle.layer_bf16(prov, 0, routers[0], X, I, k, 4, 64, want_stages=True)
+    tb = lambda a: torch.tensor(np.asarray(a, dtype=np.float32)).to(torch.bfloat16).double().numpy()
+    for t in range(T):
+        i_ref, w_ref, _, m_ref = oracle.route(routers[0], X[t].astype(np.float64), k)
+        assert res["idx"][t].tolist() == i_ref.tolist()
+        assert np.allclose(res["w"][t], w_ref, rtol=0, atol=0)
+        ref = X[t].astype(np.float64).copy()
+        for j in range(k):
+            mats = experts[0][i_ref[j]]
+            Wg16 = tb(dense_decode(*mats[0], I, H, 4, 64))
+            Wu16 = tb(dense_decode(*mats[1], I, H, 4, 64))
+            Wd16 = tb(dense_decode(*mats[2], H, I, 4, 64))
+            x16 = tb(X[t])
+            g, u = Wg16 @ x16, Wu16 @ x16
+            assert np.allclose(res["g"][t, j], g, rtol=1e-13, atol=1e-13)
+            assert np.allclose(res["u"][t, j], u, rtol=1e-13, atol=1e-13)
+            a16 = tb(g * scipy.special.expit(g) * u)
+            assert np.array_equal(res["a16"][t, j].astype(np.float64), a16)
+            ref += w_ref[j] * (Wd16 @ a16)
+        assert np.allclose(res["out"][t], ref, rtol=1e-12, atol=1e-12)
+    # teacher forcing with the oracle's own a16 changes nothing
+    forced = oracle.layer_bf16(prov, 0, routers[0], X, I, k, 4, 64, a16_force=res["a16"])
+    assert np.array_equal(forced["out"], res["out"])
+    # batch invariance: one token at a time gives the same rows
+    one = oracle.layer_bf16(prov, 0, routers[0], X[2:3], I, k, 4, 64)
+    assert np.array_equal(one["out"][0], res["out"][2])
+    # sanity band against the full-precision layer
+    full, _, _, _ = oracle.moe_layer(prov, 0, routers[0], X[2].astype(np.float64), I, k, 4, 64, 0, 1e-6)
+    assert np.linalg.norm(res["out"][2] - full) <= 1e-2 * np.linalg.norm(full)
