@@ -1,0 +1,17 @@
+// fmoe_batched.h -- the multi-token (batched) path of fmoe_moe_layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "fmoe.h"
+
+namespace fmoe {
+
+size_t batched_workspace_bytes(int n_tokens, int hidden, int inter, int n_experts, int k);
+int launch_batched(const fmoe_layer* layers, int n_layers, const float* x_in, float* h_out, int n_tokens, int k,
+                   float eps, unsigned flags, int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes,
+                   hipStream_t s);
+
+}  // namespace fmoe

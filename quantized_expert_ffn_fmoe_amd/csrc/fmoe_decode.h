@@ -1,0 +1,42 @@
+// fmoe_decode.h -- parameters of the persistent single-token decode kernel.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace fmoe {
+
+constexpr int kMaxLayersPerLaunch = 64;
+
+struct DecodeParams {
+  const float* router[kMaxLayersPerLaunch];
+  const uint8_t* experts[kMaxLayersPerLaunch];
+  size_t expert_stride;
+  int n_layers;   // layers in this launch
+  int layer0;     // global index of the first of them
+  int is_final;   // this launch ends with the last layer of the call
+  int n_experts, hidden, inter, k, bits;
+  int lpr_g, cpl_g, lpr_d, cpl_d;
+  int rows_per_wg, router_items;
+  float eps;
+  unsigned flags;
+  const float* x_in;
+  float* h_out;
+  int32_t* idx_out;  // [n_layers_total][k] or null (single token)
+  float* w_out;
+  // workspace
+  float* h;            // [hidden]
+  float* a;            // [k][inter]
+  uint64_t* logits;    // [n_experts], tagged
+  uint32_t* flags_arr; // [G]
+  uint32_t* err;       // [1]
+};
+
+int decode_geometry(int hidden, int inter, int bits, int* lpr_g, int* cpl_g, int* lpr_d, int* cpl_d);
+size_t decode_smem_bytes(int hidden, int inter, int n_experts, int k, int G, int rows_per_wg);
+int decode_grid(int* G_out);
+int launch_decode(const DecodeParams& p, int G, hipStream_t s);
+int launch_clear(uint32_t* p, size_t n_words, hipStream_t s);
+
+}  // namespace fmoe

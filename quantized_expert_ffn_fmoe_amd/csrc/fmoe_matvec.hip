@@ -1,0 +1,205 @@
+// fmoe_matvec.hip -- standalone dequantized matvec, packing, and router/top-k kernels.
+//
+// Dequantized matvec: the 4-bit / 2-bit "dequant matvec" kernel of the Flash-MoE pages
+// (aibit.im "Techniques de rupture" item 4), redesigned for gfx950: a 64-lane wave
+// covers LPR lanes per row (LPR = a power of two, up to 64) and 64/LPR rows at a time;
+// each lane reads CPL 16-byte chunks of its row(s) (16-byte coalesced loads) and keeps
+// the matching activation values in registers for every row it visits.
+#include "fmoe_device.h"
+#include "fmoe_internal.h"
+
+namespace fmoe {
+
+template <int BITS, int CPL>
+__global__ void __launch_bounds__(256) matvec_kernel(const uint8_t* __restrict__ codes,
+                                                     const uint32_t* __restrict__ sb, const float* __restrict__ x,
+                                                     float* __restrict__ y, int rows, int cols, int lpr) {
+  using C = Chunk<BITS>;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int rpw = kWave / lpr;
+  const int sub = lane & (lpr - 1);
+  const int rsel = lane / lpr;
+  const int n_chunks = cols / C::kCodes;
+  const int ngroups = cols / 64;
+  const size_t row_bytes = (size_t)cols * BITS / 8;
+  const float* xv = x + (size_t)blockIdx.y * cols;
+  float* yv = y + (size_t)blockIdx.y * rows;
+
+  XChunk<BITS> xc[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    int c = sub + lpr * j;
+    if (c < n_chunks) load_xchunk<BITS>(xc[j], xv + (size_t)c * C::kCodes);
+  }
+  const int waves_total = gridDim.x * (blockDim.x >> 6);
+  for (int rb = (blockIdx.x * (blockDim.x >> 6) + wave) * rpw; rb < rows; rb += waves_total * rpw) {
+    const int r = rb + rsel;
+    float acc = 0.f;
+    if (r < rows) {
+      const uint4* rowp = reinterpret_cast<const uint4*>(codes + (size_t)r * row_bytes);
+      const uint32_t* sbp = sb + (size_t)r * ngroups;
+      uint4 w[CPL];
+      uint32_t s[CPL];
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        int c = sub + lpr * j;
+        if (c < n_chunks) {
+          w[j] = rowp[c];
+          s[j] = sbp[c / C::kPerGroup];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        int c = sub + lpr * j;
+        if (c < n_chunks) acc += chunk_dot<BITS>(w[j], s[j], xc[j]);
+      }
+    }
+    acc = group_sum(acc, lpr);
+    if (r < rows && sub == 0) yv[r] = acc;
+  }
+}
+
+__global__ void pack_kernel(const uint8_t* __restrict__ codes_in, const uint16_t* __restrict__ scale,
+                            const uint16_t* __restrict__ bias, uint8_t* __restrict__ codes_out,
+                            uint32_t* __restrict__ sb_out, size_t n_code16, size_t n_groups) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n_groups; i += stride)
+    sb_out[i] = (uint32_t)scale[i] | ((uint32_t)bias[i] << 16);
+  if (codes_out != codes_in) {
+    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n_code16; i += stride)
+      reinterpret_cast<uint4*>(codes_out)[i] = reinterpret_cast<const uint4*>(codes_in)[i];
+  }
+}
+
+// Router logits for a tile of up to 8 tokens: logits[t][e] = sum_i R[e][i] x[t][i] (fp32).
+// One wave per expert row; the row is streamed once per token tile in 16-byte loads.
+constexpr int kRouteTile = 8;
+__global__ void __launch_bounds__(256) router_kernel(const float* __restrict__ R, const float* __restrict__ x,
+                                                     float* __restrict__ logits, int n_tokens, int n_experts,
+                                                     int hidden) {
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6);
+  const int t0 = blockIdx.y * kRouteTile;
+  if (e >= n_experts) return;
+  const int nt = min(kRouteTile, n_tokens - t0);
+  float acc[kRouteTile];
+#pragma unroll
+  for (int t = 0; t < kRouteTile; ++t) acc[t] = 0.f;
+  const float4* row = reinterpret_cast<const float4*>(R + (size_t)e * hidden);
+  for (int c = lane; c < hidden / 4; c += kWave) {
+    float4 r = row[c];
+#pragma unroll
+    for (int t = 0; t < kRouteTile; ++t) {
+      if (t < nt) {
+        float4 v = reinterpret_cast<const float4*>(x + (size_t)(t0 + t) * hidden)[c];
+        acc[t] = fmaf(r.x, v.x, acc[t]);
+        acc[t] = fmaf(r.y, v.y, acc[t]);
+        acc[t] = fmaf(r.z, v.z, acc[t]);
+        acc[t] = fmaf(r.w, v.w, acc[t]);
+      }
+    }
+  }
+#pragma unroll
+  for (int t = 0; t < kRouteTile; ++t) {
+    float s = wave_sum(acc[t]);
+    if (lane == 0 && t < nt) logits[(size_t)(t0 + t) * n_experts + e] = s;
+  }
+}
+
+// One wave per token: k rounds of a wave-wide argmax (larger logit first, lower index on
+// equal logits, NaN last), then the softmax over the k selected logits.
+__global__ void __launch_bounds__(64) topk_kernel(const float* __restrict__ logits, int n_tokens, int n_experts,
+                                                  int k, int32_t* __restrict__ idx, float* __restrict__ w) {
+  const int t = blockIdx.x;
+  const int lane = threadIdx.x;
+  const float* l = logits + (size_t)t * n_experts;
+  __shared__ float sel_l[16];
+  __shared__ int sel_i[16];
+  uint64_t taken = 0;  // bit j: element lane + 64 j already selected
+  for (int r = 0; r < k; ++r) {
+    float best = 0.f;
+    int bi = -1;
+    for (int j = 0, e = lane; e < n_experts; ++j, e += kWave) {
+      if ((taken >> j) & 1ull) continue;
+      float v = l[e];
+      if (bi < 0 || ranks_before(v, e, best, bi)) {
+        best = v;
+        bi = e;
+      }
+    }
+    // wave argmax under the same order (bi < 0 = nothing left in this lane)
+    for (int m = 32; m >= 1; m >>= 1) {
+      float ov = __shfl_xor(best, m, kWave);
+      int oi = __shfl_xor(bi, m, kWave);
+      if (oi >= 0 && (bi < 0 || ranks_before(ov, oi, best, bi))) {
+        best = ov;
+        bi = oi;
+      }
+    }
+    if (bi >= 0 && (bi % kWave) == lane) taken |= 1ull << (bi / kWave);
+    if (lane == 0) {
+      sel_l[r] = best;
+      sel_i[r] = bi;
+    }
+  }
+  __syncthreads();
+  if (lane < k) {
+    float l0 = sel_l[0];
+    float denom = 0.f;
+    for (int j = 0; j < k; ++j) denom += expf(sel_l[j] - l0);
+    idx[(size_t)t * k + lane] = sel_i[lane];
+    w[(size_t)t * k + lane] = expf(sel_l[lane] - l0) / denom;
+  }
+}
+
+// ------------------------------------------------------------------ host launchers
+int launch_matvec(const QMat& W, const float* x, float* y, int n_vec, hipStream_t s) {
+  const int n_chunks = W.cols * W.bits / 128;
+  int lpr = 1;
+  while (lpr < n_chunks && lpr < 64) lpr <<= 1;
+  const int cpl = (n_chunks + lpr - 1) / lpr;
+  const int rpw = 64 / lpr;
+  const int waves_needed = (W.rows + rpw - 1) / rpw;
+  int blocks = (waves_needed + 3) / 4;
+  if (blocks > 2048) blocks = 2048;
+  dim3 grid(blocks, n_vec);
+  const uint8_t* codes = static_cast<const uint8_t*>(W.codes);
+#define FMOE_MV(B, C) hipLaunchKernelGGL((matvec_kernel<B, C>), grid, dim3(256), 0, s, codes, W.sb, x, y, W.rows, W.cols, lpr)
+  if (W.bits == 4) {
+    if (cpl == 1) FMOE_MV(4, 1);
+    else if (cpl == 2) FMOE_MV(4, 2);
+    else if (cpl <= 4) FMOE_MV(4, 4);
+    else return FMOE_ERR_SHAPE;
+  } else {
+    if (cpl == 1) FMOE_MV(2, 1);
+    else if (cpl == 2) FMOE_MV(2, 2);
+    else if (cpl <= 4) FMOE_MV(2, 4);
+    else return FMOE_ERR_SHAPE;
+  }
+#undef FMOE_MV
+  return hipGetLastError() == hipSuccess ? FMOE_OK : FMOE_ERR_HIP;
+}
+
+int launch_pack(const uint8_t* codes_in, const uint16_t* scale, const uint16_t* bias, int rows, int cols, int bits,
+                void* codes_out, uint32_t* sb_out, hipStream_t s) {
+  size_t n_code16 = (size_t)rows * cols * bits / 8 / 16;
+  size_t n_groups = (size_t)rows * (cols / 64);
+  size_t work = n_code16 > n_groups ? n_code16 : n_groups;
+  size_t blocks = (work + 255) / 256;
+  if (blocks > 65536) blocks = 65536;
+  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, codes_in, scale, bias,
+                     static_cast<uint8_t*>(codes_out), sb_out, n_code16, n_groups);
+  return hipGetLastError() == hipSuccess ? FMOE_OK : FMOE_ERR_HIP;
+}
+
+int launch_route(const float* R, const float* x, int n_tokens, int n_experts, int hidden, int k, int32_t* idx,
+                 float* w, float* logits, hipStream_t s) {
+  dim3 g1((n_experts + 3) / 4, (n_tokens + kRouteTile - 1) / kRouteTile);
+  hipLaunchKernelGGL(router_kernel, g1, dim3(256), 0, s, R, x, logits, n_tokens, n_experts, hidden);
+  if (hipGetLastError() != hipSuccess) return FMOE_ERR_HIP;
+  hipLaunchKernelGGL(topk_kernel, dim3(n_tokens), dim3(64), 0, s, logits, n_tokens, n_experts, k, idx, w);
+  return hipGetLastError() == hipSuccess ? FMOE_OK : FMOE_ERR_HIP;
+}
+
+}  // namespace fmoe

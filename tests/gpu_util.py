@@ -1,0 +1,97 @@
+"""Helpers for the GPU tests and the benchmark: put synthetic experts/routers on the device
+in the library's packed layout (through fmoe_pack), and compare against the oracle."""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+import quantized_expert_ffn_fmoe_amd as fm
+import synth
+
+
+def to_dev(a: np.ndarray, dev="cuda") -> torch.Tensor:
+    if a.dtype == np.uint16:
+        a = a.view(np.int16)
+    return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+
+def rel_l2(got, want) -> float:
+    got = np.asarray(got, dtype=np.float64)
+    want = np.asarray(want, dtype=np.float64)
+    den = np.linalg.norm(want)
+    return float(np.linalg.norm(got - want) / (den if den > 0 else 1.0))
+
+
+class DevMatrix:
+    """One packed quantized matrix on the device (keeps its buffers alive)."""
+
+    def __init__(self, codes, scale, bias, rows, cols, bits, dev="cuda"):
+        self.codes = torch.empty(fm.codes_bytes(rows, cols, bits), dtype=torch.uint8, device=dev)
+        self.sb = torch.empty(fm.sb_bytes(rows, cols) // 4, dtype=torch.int32, device=dev)
+        fm.pack(to_dev(codes, dev), to_dev(scale, dev), to_dev(bias, dev), rows, cols, bits, 64, self.codes, self.sb)
+        self.q = fm.qmat(self.codes, self.sb, rows, cols, bits)
+
+
+def fill_experts_cpu(blob: torch.Tensor, stride: int, layer: int, n_experts: int, H: int, I: int, bits: int,
+                     seed: int = 0) -> None:
+    """Experts 0..n_experts-1 of `layer` from the CPU generator, packed into blob."""
+    dev = blob.device
+    for e in range(n_experts):
+        view = fm.expert_view(blob.data_ptr() + e * stride, H, I, bits)
+        for m, q in enumerate((view.gate, view.up, view.down)):
+            rows, cols = (I, H) if m < 2 else (H, I)
+            codes, scale, bias = synth.matrix(seed, layer, e, m, rows, cols, bits)
+            fm.pack(to_dev(codes, dev), to_dev(scale, dev), to_dev(bias, dev), rows, cols, bits, 64, q.codes, q.sb)
+
+
+def fill_experts_gpu(blob: torch.Tensor, stride: int, layer: int, n_experts: int, H: int, I: int, bits: int,
+                     seed: int = 0, chunk: int = 128) -> None:
+    """Same as fill_experts_cpu but generated on the device (GPU fixture), in chunks of experts.
+    Codes are generated straight into the blob (the packed codes layout is the canonical one);
+    scales/biases go to a scratch buffer and are interleaved by fmoe_pack."""
+    dev = blob.device
+    cb = fm.codes_bytes(I, H, bits)
+    ngrp = I * H // 64
+    scale = torch.empty((chunk, ngrp), dtype=torch.int16, device=dev)
+    bias = torch.empty((chunk, ngrp), dtype=torch.int16, device=dev)
+    stream = torch.cuda.current_stream().cuda_stream
+    for e0 in range(0, n_experts, chunk):
+        ne = min(chunk, n_experts - e0)
+        base = blob.data_ptr() + e0 * stride
+        for m in range(3):
+            rows, cols = (I, H) if m < 2 else (H, I)
+            synth.gpu_matrix(seed, layer, e0, ne, m, rows, cols, bits, 64, base + m * cb, stride,
+                             scale.data_ptr(), bias.data_ptr(), ngrp * 2, stream)
+            for j in range(ne):
+                view = fm.expert_view(base + j * stride, H, I, bits)
+                q = (view.gate, view.up, view.down)[m]
+                fm.pack(q.codes, scale[j], bias[j], rows, cols, bits, 64, q.codes, q.sb)
+
+
+class DevStack:
+    """A stack of MoE layers on the device: routers (fp32) and packed expert blobs."""
+
+    def __init__(self, n_layers, E, H, I, bits, seed=0, dev="cuda", gpu_fill=False):
+        self.L, self.E, self.H, self.I, self.bits, self.seed = n_layers, E, H, I, bits, seed
+        eb = fm.expert_bytes(H, I, bits)
+        self.stride = (eb + 255) // 256 * 256
+        self.routers_np = []
+        self.routers = []
+        self.blobs = []
+        layers = []
+        for l in range(n_layers):
+            blob = torch.empty(E * self.stride, dtype=torch.uint8, device=dev)
+            if gpu_fill:
+                fill_experts_gpu(blob, self.stride, l, E, H, I, bits, seed)
+            else:
+                fill_experts_cpu(blob, self.stride, l, E, H, I, bits, seed)
+            R = synth.router(seed, l, E, H)
+            self.routers_np.append(R)
+            Rd = to_dev(R, dev)
+            self.routers.append(Rd)
+            self.blobs.append(blob)
+            layers.append(fm.Layer(Rd.data_ptr(), blob.data_ptr(), self.stride, E, H, I, bits, 64))
+        self.layers = fm.layers_array(layers)
+
+    def provider(self):
+        return synth.Provider(self.seed, self.H, self.I, self.bits)

@@ -1,0 +1,179 @@
+"""CPU checks of the C-ABI library: it loads, exports every symbol of include/fmoe.h,
+sizes the formats as the pages do, and rejects bad arguments before touching a device.
+No compute call is made here (no GPU in this environment)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import quantized_expert_ffn_fmoe_amd as fm
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+FAKE = 0x100000  # aligned stand-in address, never dereferenced (validation fails first)
+
+
+def header_functions():
+    text = open(os.path.join(ROOT, "include", "fmoe.h")).read()
+    return sorted(set(re.findall(r"\b(fmoe_[a-z_]+)\s*\(", text)))
+
+
+def test_exports_every_declared_function():
+    names = header_functions()
+    assert len(names) >= 12
+    L = fm.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    assert set(fm.EXPORTS) == set(names)
+
+
+def test_status_strings_and_version():
+    for code in range(0, -12, -1):
+        assert fm.status_string(code) and fm.status_string(code) != "unknown status"
+    assert fm.status_string(-99) == "unknown status"
+    assert "gfx950" in fm.version()
+
+
+def test_format_sizes_match_pages():
+    """About 6.75 MB per active expert at 4 bits (aibit.im 'Techniques de rupture' item 1;
+    tr.news.hada.io 'SSD Expert Streaming'), and a 2-bit expert set of about 120 GB
+    (aibit.im table of the first section; hada 'Performans sonuclari')."""
+    e4 = fm.expert_bytes(4096, 1024, 4)
+    e2 = fm.expert_bytes(4096, 1024, 2)
+    assert e4 == 7_077_888 == int(6.75 * 2 ** 20)
+    assert e2 == 3_932_160
+    assert abs(60 * 512 * e2 / 1e9 - 120.8) < 0.05
+    assert fm.codes_bytes(1024, 4096, 4) == 2_097_152
+    assert fm.sb_bytes(1024, 4096) == 262_144
+    assert fm.codes_bytes(1024, 4096, 3) == 0
+    assert fm.expert_bytes(4096, 1000, 4) == 0
+    assert fm.sb_bytes(10, 128, 32) == 0
+
+
+def test_expert_view_offsets():
+    H, I = 4096, 1024
+    e = fm.expert_view(FAKE, H, I, 4)
+    cb, sb = fm.codes_bytes(I, H, 4), fm.sb_bytes(I, H)
+    assert e.gate.codes == FAKE and e.up.codes == FAKE + cb and e.down.codes == FAKE + 2 * cb
+    assert e.gate.sb == FAKE + 3 * cb and e.up.sb == FAKE + 3 * cb + sb and e.down.sb == FAKE + 3 * cb + 2 * sb
+    assert (e.gate.rows, e.gate.cols, e.down.rows, e.down.cols) == (I, H, H, I)
+    with pytest.raises(fm.FmoeError) as ei:
+        fm.expert_view(FAKE, H, I, 3)
+    assert ei.value.status == fm.ERR_BITS
+
+
+def test_workspace_bytes():
+    assert fm.workspace_bytes(fm.OP_EXPERT_FFN, 1, 4096, 1024, 1, 1) >= 1024 * 4
+    d = fm.workspace_bytes(fm.OP_MOE_LAYER, 1, 4096, 1024, 512, 4)
+    assert d >= 4096 * 4 + 4 * 1024 * 4 + 512 * 8
+    assert fm.workspace_bytes(fm.OP_MOE_LAYER, 1, 4096, 1024, 512, 17) == 0
+    assert fm.workspace_bytes(99, 1, 4096, 1024, 512, 4) == 0
+
+
+def _raises(status, fn, *args, **kw):
+    with pytest.raises(fm.FmoeError) as ei:
+        fn(*args, **kw)
+    assert ei.value.status == status, (ei.value.status, status)
+
+
+def test_matvec_validation():
+    W = fm.qmat(FAKE, FAKE, 1024, 4096, 4)
+    _raises(fm.ERR_NULL, fm.dequant_matvec, fm.qmat(None, FAKE, 4, 64, 4), FAKE, FAKE, stream=0)
+    _raises(fm.ERR_NULL, fm.dequant_matvec, W, None, FAKE, stream=0)
+    _raises(fm.ERR_BITS, fm.dequant_matvec, fm.qmat(FAKE, FAKE, 4, 64, 3), FAKE, FAKE + 4096, stream=0)
+    _raises(fm.ERR_GROUP, fm.dequant_matvec, fm.qmat(FAKE, FAKE, 4, 64, 4, 32), FAKE, FAKE + 4096, stream=0)
+    _raises(fm.ERR_SHAPE, fm.dequant_matvec, fm.qmat(FAKE, FAKE, 4, 96, 4), FAKE, FAKE + 4096, stream=0)
+    _raises(fm.ERR_SHAPE, fm.dequant_matvec, fm.qmat(FAKE, FAKE, 0, 64, 4), FAKE, FAKE + 4096, stream=0)
+    _raises(fm.ERR_SHAPE, fm.dequant_matvec, fm.qmat(FAKE, FAKE, 4, 16384, 4), FAKE, FAKE + 1 << 20, stream=0)
+    _raises(fm.ERR_SHAPE, fm.dequant_matvec, W, FAKE, FAKE + (1 << 24), 0, stream=0)
+    _raises(fm.ERR_SHAPE, fm.dequant_matvec, W, FAKE, FAKE + (1 << 24), 65, stream=0)
+    _raises(fm.ERR_ALIGN, fm.dequant_matvec, fm.qmat(FAKE + 8, FAKE, 4, 64, 4), FAKE, FAKE + 4096, stream=0)
+    _raises(fm.ERR_ALIGN, fm.dequant_matvec, W, FAKE + 4, FAKE + (1 << 24), stream=0)
+    _raises(fm.ERR_OVERLAP, fm.dequant_matvec, W, FAKE, FAKE + 1024, stream=0)
+
+
+def test_route_validation():
+    args = dict(router=FAKE, x=FAKE + (1 << 24), n_tokens=1, n_experts=512, hidden=4096, k=4,
+                idx=FAKE + (2 << 24), w=FAKE + (3 << 24), logits=FAKE + (4 << 24), stream=0)
+
+    def call(**over):
+        a = dict(args)
+        a.update(over)
+        fm.route_topk(**a)
+
+    _raises(fm.ERR_NULL, call, logits=None)
+    _raises(fm.ERR_NULL, call, router=None)
+    _raises(fm.ERR_K, call, k=0)
+    _raises(fm.ERR_K, call, k=17)
+    _raises(fm.ERR_K, call, n_experts=3, k=4)
+    _raises(fm.ERR_SHAPE, call, hidden=100)
+    _raises(fm.ERR_SHAPE, call, n_experts=5000)
+    _raises(fm.ERR_SHAPE, call, n_tokens=0)
+    _raises(fm.ERR_ALIGN, call, x=FAKE + (1 << 24) + 4)
+    _raises(fm.ERR_OVERLAP, call, logits=FAKE + (1 << 24))
+
+
+def test_expert_ffn_validation():
+    e = fm.expert_view(FAKE, 4096, 1024, 4)
+    x, y, ws = FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30)
+    _raises(fm.ERR_WORKSPACE, fm.expert_ffn, e, x, y, None, 0, stream=0)
+    _raises(fm.ERR_WORKSPACE, fm.expert_ffn, e, x, y, ws, 100, stream=0)
+    bad = fm.expert_view(FAKE, 4096, 1024, 4)
+    bad.down.rows = 2048
+    _raises(fm.ERR_SHAPE, fm.expert_ffn, bad, x, y, ws, 1 << 20, stream=0)
+    mixed = fm.expert_view(FAKE, 4096, 1024, 4)
+    mixed.up.bits = 2
+    _raises(fm.ERR_BITS, fm.expert_ffn, mixed, x, y, ws, 1 << 20, stream=0)
+    _raises(fm.ERR_OVERLAP, fm.expert_ffn, e, x, x + 64, ws, 1 << 20, stream=0)
+
+
+def test_moe_layer_validation():
+    H, I, E, k = 4096, 1024, 512, 4
+    stride = fm.expert_bytes(H, I, 4)
+    L = fm.Layer(FAKE, 1 << 32, stride, E, H, I, 4, 64)
+    x, h, ws = FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30)
+    wsb = fm.workspace_bytes(fm.OP_MOE_LAYER, 1, H, I, E, k)
+
+    def call(layers=None, **over):
+        a = dict(x_in=x, h_out=h, n_tokens=1, k=k, eps=1e-6, flags=fm.PRENORM, idx_out=None, w_out=None, ws=ws,
+                 ws_bytes=wsb, stream=0)
+        a.update(over)
+        fm.moe_layer(layers if layers is not None else [L], **a)
+
+    _raises(fm.ERR_NULL, call, x_in=None)
+    _raises(fm.ERR_K, call, k=0)
+    _raises(fm.ERR_K, call, k=17)
+    _raises(fm.ERR_WORKSPACE, call, ws=None)
+    _raises(fm.ERR_WORKSPACE, call, ws_bytes=wsb - 1)
+    _raises(fm.ERR_ALIGN, call, ws=ws + 16)
+    _raises(fm.ERR_OVERLAP, call, h_out=x + 256)
+    _raises(fm.ERR_SHAPE, call, n_tokens=0)
+    _raises(fm.ERR_SHAPE, call, eps=float("nan"))
+    L2 = fm.Layer(FAKE, 1 << 32, stride, E, H, 512, 4, 64)
+    _raises(fm.ERR_SHAPE, call, layers=[L, L2])
+    L3 = fm.Layer(FAKE, 1 << 32, stride + 16, E, H, I, 4, 64)
+    _raises(fm.ERR_ALIGN, call, layers=[L3])
+    L4 = fm.Layer(FAKE, 1 << 32, stride - 256, E, H, I, 4, 64)
+    _raises(fm.ERR_SHAPE, call, layers=[L4])
+    L5 = fm.Layer(None, 1 << 32, stride, E, H, I, 4, 64)
+    _raises(fm.ERR_NULL, call, layers=[L5])
+    L6 = fm.Layer(FAKE, 1 << 32, stride, E, H, I, 3, 64)
+    _raises(fm.ERR_BITS, call, layers=[L6])
+    L7 = fm.Layer(FAKE, 1 << 32, stride, E, H, I, 4, 128)
+    _raises(fm.ERR_GROUP, call, layers=[L7])
+
+
+def test_pack_validation():
+    _raises(fm.ERR_NULL, fm.pack, None, FAKE, FAKE, 4, 64, 4, 64, FAKE, FAKE, stream=0)
+    _raises(fm.ERR_BITS, fm.pack, FAKE, FAKE, FAKE, 4, 64, 8, 64, FAKE, FAKE, stream=0)
+    _raises(fm.ERR_GROUP, fm.pack, FAKE, FAKE, FAKE, 4, 64, 4, 16, FAKE, FAKE, stream=0)
+    _raises(fm.ERR_ALIGN, fm.pack, FAKE + 2, FAKE, FAKE, 4, 64, 4, 64, FAKE + 4096, FAKE + 8192, stream=0)
+    _raises(fm.ERR_OVERLAP, fm.pack, FAKE, FAKE + (1 << 20), FAKE + (2 << 20), 4, 64, 4, 64, FAKE + 16, FAKE + (3 << 20),
+            stream=0)
+
+
+def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
+    monkeypatch.setattr(fm, "SO_PATH", str(tmp_path / "missing.so"))
+    monkeypatch.setattr(fm, "_lib", None)
+    with pytest.raises(RuntimeError, match="no non-HIP fallback"):
+        fm.lib()
