@@ -1,0 +1,254 @@
+#!/usr/bin/env python3
+"""Benchmark of the MoE expert-block decode on one MI355X.
+
+Workload (default, --config stack4): 60 layers x 512 experts, hidden 4096, expert
+intermediate 1024, 4-bit codes with bf16 scale/bias per group of 64 (about 217 GB resident
+in HBM), fp32 routers N(0, 0.02), top-4 softmax routing, SwiGLU, combine + residual, RMS
+norm (eps 1e-6) before every layer; 256 consecutive single-token decodes (each token one
+fmoe_moe_layer call through all 60 layers). Inputs are synthetic (seeded generator, token
+draws 0..255 ~ N(0,1)); the expert set is generated on the device.
+
+A step is one pass of the 256 tokens. Prints one JSON line: tokens/s, the decode kernel's
+achieved HBM bandwidth against the 8 TB/s peak (HIP events around every launch), a parity
+spot check of the full-size stack against stored oracle results, the measured inter-token
+expert reuse, and the CPU oracle's throughput on a small sample (cpu_baseline).
+
+Usage: python bench.py [--gpus 1] [--steps 5] [--warmup 1] [--config stack4|stack2]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+sys.path.insert(0, os.path.join(ROOT, "tests"))
+
+L_, E_, H_, I_, K_, EPS = 60, 512, 4096, 1024, 4, 1e-6
+PEAK_GBS = 8000.0
+METRIC = "MoE-block decode tokens/s (60 layers, 4-bit) + achieved HBM GB/s vs peak"
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def algorithmic_bytes_per_layer(bits: int) -> int:
+    import quantized_expert_ffn_fmoe_amd as fm
+    return E_ * H_ * 4 + K_ * fm.expert_bytes(H_, I_, bits)
+
+
+def decode_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in ("fmoe_decode.hip", "fmoe_device.h", "fmoe_decode.h"):
+        h.update(open(os.path.join(ROOT, "quantized_expert_ffn_fmoe_amd", "csrc", f), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def build_stack(bits: int, dev):
+    import torch
+
+    import quantized_expert_ffn_fmoe_amd as fm
+    import synth
+    from gpu_util import fill_experts_gpu, to_dev
+
+    eb = fm.expert_bytes(H_, I_, bits)
+    stride = (eb + 255) // 256 * 256
+    blobs, routers, layers = [], [], []
+    t0 = time.time()
+    for l in range(L_):
+        blob = torch.empty(E_ * stride, dtype=torch.uint8, device=dev)
+        fill_experts_gpu(blob, stride, l, E_, H_, I_, bits, seed=0)
+        R = to_dev(synth.router(0, l, E_, H_), dev)
+        blobs.append(blob)
+        routers.append(R)
+        layers.append(fm.Layer(R.data_ptr(), blob.data_ptr(), stride, E_, H_, I_, bits, 64))
+        if l % 10 == 9:
+            torch.cuda.synchronize()
+            log(f"filled layer {l + 1}/{L_} ({time.time() - t0:.0f}s, {(l + 1) * E_ * stride / 1e9:.1f} GB)")
+    torch.cuda.synchronize()
+    return blobs, routers, fm.layers_array(layers), E_ * stride * L_
+
+
+def cpu_baseline(bits: int, n_tokens: int = 2):
+    """The oracle, as it stands, on the host: n_tokens draws through all 60 layers.
+    Expert generation (done on demand inside the oracle's provider) is timed separately
+    and subtracted."""
+    import oracle
+    import synth
+
+    routers = [synth.router(0, l, E_, H_) for l in range(L_)]
+    prov = synth.Provider(0, H_, I_, bits)
+    t_total = 0.0
+    t_gen = 0.0
+    for d in range(n_tokens):
+        x = synth.token(0, d, H_)
+        t0 = time.perf_counter()
+        r = oracle.stack(prov, routers, x, I_, K_, bits, 64, EPS, keep_all=False)
+        t_total += time.perf_counter() - t0
+        t0 = time.perf_counter()
+        for l in range(L_):
+            for e in r["idx"][l]:
+                synth.expert(0, l, int(e), H_, I_, bits)
+        t_gen += time.perf_counter() - t0
+    t_oracle = max(t_total - t_gen, 1e-9)
+    threads = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": round(n_tokens / t_oracle, 6), "unit": "tokens/s", "cores": threads, "kind": "oracle",
+            "sample": f"{n_tokens} tokens (draws 0-{n_tokens - 1}) through all {L_} layers, fp64 plain loops, "
+                      f"OpenMP over rows; on-demand expert generation ({t_gen:.1f}s) subtracted from {t_total:.1f}s",
+            "seconds": round(t_oracle, 3)}
+
+
+def parity_check(layers, bits, dev, ws, wsb):
+    import torch
+
+    import quantized_expert_ffn_fmoe_amd as fm
+    import synth
+
+    path = os.path.join(ROOT, "tests", "golden", f"stack_full_{bits}bit.npz")
+    if not os.path.exists(path):
+        return None
+    g = np.load(path, allow_pickle=False)
+    worst, exact = 0.0, True
+    for i, d in enumerate(g["draw"]):
+        x = torch.from_numpy(synth.token(0, int(d), H_)).to(dev)
+        h = torch.empty(H_, dtype=torch.float32, device=dev)
+        idx = torch.empty((L_, K_), dtype=torch.int32, device=dev)
+        fm.moe_layer(layers, x, h, 1, K_, EPS, fm.PRENORM, idx, None, ws, wsb)
+        torch.cuda.synchronize()
+        exact &= bool(np.array_equal(idx.cpu().numpy(), g["idx"][i]))
+        ref = g["out"][i]
+        rel = float(np.linalg.norm(h.cpu().numpy().astype(np.float64) - ref) / np.linalg.norm(ref))
+        worst = max(worst, rel)
+    return {"tokens": int(len(g["draw"])), "draws": [int(d) for d in g["draw"]], "experts_bit_exact": exact,
+            "max_rel_l2": worst, "tolerance": 1e-5, "pass": bool(exact and worst <= 1e-5)}
+
+
+def traffic_from_profiles(kernel_tag: str):
+    """HBM bytes per launch from committed rocprofv3 PMC summaries, if they were taken on the
+    current decode kernel source (else None)."""
+    path = os.path.join(ROOT, "profiles", f"{kernel_tag}_traffic.json")
+    if not os.path.exists(path):
+        return None
+    d = json.load(open(path))
+    if d.get("source_hash") != decode_source_hash():
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=1)
+    ap.add_argument("--config", choices=["stack4", "stack2"], default="stack4")
+    ap.add_argument("--tokens", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-parity", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only: the whole expert stack fits in one "
+                                   "MI355X's HBM and the path has no multi-GPU mode (see DESIGN.md on sharding)",
+                          "n_gpus": args.gpus}))
+        return 2
+    if int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print(json.dumps({"error": "launched with WORLD_SIZE > 1; one GPU only"}))
+        return 2
+
+    import torch
+
+    import quantized_expert_ffn_fmoe_amd as fm
+    import synth
+
+    bits = 4 if args.config == "stack4" else 2
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    log(f"building {L_}-layer {bits}-bit stack on {torch.cuda.get_device_name(dev)}")
+    blobs, routers, layers, resident = build_stack(bits, dev)
+    T = args.tokens
+    X = torch.from_numpy(np.stack([synth.token(0, d, H_) for d in range(T)])).to(dev)
+    Hout = torch.empty((T, H_), dtype=torch.float32, device=dev)
+    idx = torch.empty((T, L_, K_), dtype=torch.int32, device=dev)
+    wsb = fm.workspace_bytes(fm.OP_MOE_LAYER, 1, H_, I_, E_, K_)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    s_handle = stream.cuda_stream
+    n_ev = args.steps * T
+    ev0 = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    ev1 = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+
+    def step(timed_step: int):
+        for t in range(T):
+            if timed_step >= 0:
+                ev0[timed_step * T + t].record(stream)
+            fm.moe_layer(layers, X[t], Hout[t], 1, K_, EPS, fm.PRENORM, idx[t], None, ws, wsb, s_handle)
+            if timed_step >= 0:
+                ev1[timed_step * T + t].record(stream)
+
+    log(f"warmup {args.warmup} step(s) of {T} tokens")
+    for _ in range(args.warmup):
+        step(-1)
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} step(s)")
+    t0 = time.perf_counter()
+    for s_i in range(args.steps):
+        step(s_i)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    kernel_ms = [ev0[i].elapsed_time(ev1[i]) for i in range(n_ev)]
+    tok_s = args.steps * T / elapsed
+    ms_step = elapsed * 1e3 / args.steps
+    per_launch = L_ * algorithmic_bytes_per_layer(bits)
+    avg_kernel_s = float(np.mean(kernel_ms)) * 1e-3
+    achieved = per_launch / avg_kernel_s / 1e9
+    ids = idx.cpu().numpy()
+    reuse = float(np.mean([len(set(ids[t, l]) & set(ids[t - 1, l])) / K_ for t in range(1, T) for l in range(L_)]))
+    reuse_l0 = float(np.mean([len(set(ids[t, 0]) & set(ids[t - 1, 0])) / K_ for t in range(1, T)]))
+    log(f"{tok_s:.1f} tok/s, kernel avg {avg_kernel_s * 1e6:.1f} us, {achieved:.0f} GB/s")
+    parity = None if args.no_parity else parity_check(layers, bits, dev, ws, wsb)
+    if parity is not None:
+        log(f"parity: {parity}")
+    cpu = None
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a sample")
+        cpu = cpu_baseline(bits)
+    kernel_tag = f"decode_stack{bits}"
+    traffic = traffic_from_profiles(kernel_tag)
+    out = {
+        "metric": METRIC if bits == 4 else METRIC.replace("4-bit", "2-bit"),
+        "value": round(tok_s, 2),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{L_}-layer x {E_}-expert {bits}-bit MoE expert-block decode stack, "
+                               f"{T} consecutive single tokens per step",
+                   "layers": L_, "experts": E_, "hidden": H_, "inter": I_, "top_k": K_, "bits": bits, "group": 64,
+                   "tokens_per_step": T, "resident_expert_bytes": int(resident)},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / PEAK_GBS, 4),
+                     "traffic": traffic, "kernel": "fmoe::decode_kernel (one launch = one token, 60 layers)",
+                     "algorithmic_bytes_per_launch": per_launch, "avg_launch_us": round(avg_kernel_s * 1e6, 2)},
+        "cpu_baseline": cpu,
+        "parity": parity,
+        "wall_gbps": round(per_launch * tok_s / 1e9, 1),
+        "inter_token_expert_reuse": {"all_layers": round(reuse, 4), "layer0": round(reuse_l0, 4)},
+    }
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -117,7 +117,11 @@ int fmoe_pack(const uint8_t* codes_canon, const uint16_t* scale, const uint16_t*
               int bits, int group, void* codes_out, uint32_t* sb_out, fmoe_stream_t stream);
 
 /* Workspace bytes needed by an operation (0 when none is needed). For FMOE_OP_MOE_LAYER
- * pass the largest n_tokens, hidden, inter, n_experts and k that the calls will use. */
+ * pass the largest n_tokens, hidden, inter, n_experts and k that the calls will use.
+ * A FMOE_OP_MOE_LAYER workspace must be zero-filled before its first use; each call
+ * leaves it ready for the next one (it holds the synchronization state of the decode
+ * kernel). After a call whose device-side wait gave up (outputs set to NaN), zero it
+ * again. */
 size_t fmoe_workspace_bytes(int op, int n_tokens, int hidden, int inter, int n_experts, int k);
 
 /*

@@ -10,7 +10,6 @@ using namespace fmoe;
 
 namespace {
 
-constexpr int kMaxGrid = 1024;  // flags reserved in the workspace (>= compute units)
 
 bool aligned(const void* p, size_t a) { return ((uintptr_t)p % a) == 0; }
 
@@ -49,7 +48,6 @@ struct DecodeWs {
   float* h;
   float* a;
   uint32_t* err;
-  size_t clear_words;  // flags + logits + err are cleared at every call
   size_t bytes;
 };
 
@@ -60,16 +58,15 @@ DecodeWs carve_decode(void* ws, int hidden, int inter, int n_experts, int k) {
   char* b = static_cast<char*>(ws);
   size_t off = 0;
   d.flags = reinterpret_cast<uint32_t*>(b + off);
-  off += up256((size_t)kMaxGrid * 4);
+  off += up256((size_t)kRep * kMaxGrid * 4);
   d.logits = reinterpret_cast<uint64_t*>(b + off);
-  off += up256((size_t)n_experts * 8);
+  off += up256((size_t)kRep * n_experts * 8);
   d.err = reinterpret_cast<uint32_t*>(b + off);
   off += 256;
-  d.clear_words = off / 4;
   d.h = reinterpret_cast<float*>(b + off);
-  off += up256((size_t)hidden * 4);
+  off += up256((size_t)kRep * hidden * 4);
   d.a = reinterpret_cast<float*>(b + off);
-  off += up256((size_t)k * inter * 4);
+  off += up256((size_t)kRep * k * inter * 4);
   d.bytes = off;
   return d;
 }
@@ -255,9 +252,8 @@ int fmoe_moe_layer(const fmoe_layer* layers, int n_layers, const float* x_in, fl
   if ((rc = decode_grid(&G))) return rc;
   if (G > kMaxGrid) G = kMaxGrid;
   const int rows_per_wg = (H + G - 1) / G;
-  if (decode_smem_bytes(H, I, E, k, G, rows_per_wg) > 64 * 1024) return FMOE_ERR_SHAPE;
+  if (decode_smem_bytes(H, I, E, k, G, rows_per_wg, bits) > 64 * 1024) return FMOE_ERR_SHAPE;
   DecodeWs d = carve_decode(ws, H, I, E, k);
-  if ((rc = launch_clear(d.flags, d.clear_words, s))) return rc;
   DecodeParams p;
   memset(&p, 0, sizeof(p));
   p.n_experts = E;

@@ -8,6 +8,8 @@
 namespace fmoe {
 
 constexpr int kMaxLayersPerLaunch = 64;
+constexpr int kMaxGrid = 1024;  // workgroups of the persistent kernel (>= compute units)
+constexpr int kRep = 8;         // replicas of every exchanged item (flags, logits, h, a)
 
 struct DecodeParams {
   const float* router[kMaxLayersPerLaunch];
@@ -26,17 +28,16 @@ struct DecodeParams {
   int32_t* idx_out;  // [n_layers_total][k] or null (single token)
   float* w_out;
   // workspace
-  float* h;            // [hidden]
-  float* a;            // [k][inter]
-  uint64_t* logits;    // [n_experts], tagged
-  uint32_t* flags_arr; // [G]
+  float* h;            // [kRep][hidden]
+  float* a;            // [kRep][k][inter]
+  uint64_t* logits;    // [kRep][n_experts], tagged
+  uint32_t* flags_arr; // [kRep][kMaxGrid], zero-filled before the first call on a workspace
   uint32_t* err;       // [1]
 };
 
 int decode_geometry(int hidden, int inter, int bits, int* lpr_g, int* cpl_g, int* lpr_d, int* cpl_d);
-size_t decode_smem_bytes(int hidden, int inter, int n_experts, int k, int G, int rows_per_wg);
+size_t decode_smem_bytes(int hidden, int inter, int n_experts, int k, int G, int rows_per_wg, int bits);
 int decode_grid(int* G_out);
 int launch_decode(const DecodeParams& p, int G, hipStream_t s);
-int launch_clear(uint32_t* p, size_t n_words, hipStream_t s);
 
 }  // namespace fmoe

@@ -131,23 +131,73 @@ __device__ __forceinline__ float chunk_dot(const uint4& w, uint32_t sb, const XC
   return fmaf(bf16_lo(sb), qx, bf16_hi(sb) * xc.sum);
 }
 
+// Cross-lane data movement with DPP (no LDS round trip). Controls (GFX9 encoding):
+// quad_perm [1,0,3,2] = 0xB1, quad_perm [2,3,0,1] = 0x4E, row_half_mirror = 0x141,
+// row_mirror = 0x140.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
+}
+__device__ __forceinline__ float readlane_f(float v, int l) {
+  return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), l));
+}
+
 // Sum over groups of `width` consecutive lanes (width a power of two <= 64); every lane
-// of the group gets the total.
+// of the group gets the group's total.
 __device__ __forceinline__ float group_sum(float v, int width) {
-  for (int m = width >> 1; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
+  if (width >= 2) v += dpp_f<0xB1>(v);
+  if (width >= 4) v += dpp_f<0x4E>(v);
+  if (width >= 8) v += dpp_f<0x141>(v);
+  if (width >= 16) v += dpp_f<0x140>(v);
+  if (width >= 32) {
+    const float r0 = readlane_f(v, 0), r1 = readlane_f(v, 16), r2 = readlane_f(v, 32), r3 = readlane_f(v, 48);
+    if (width == 32) v = (threadIdx.x & 32) ? (r2 + r3) : (r0 + r1);
+    else v = (r0 + r1) + (r2 + r3);
+  }
   return v;
 }
 
-__device__ __forceinline__ float wave_sum(float v) {
+__device__ __forceinline__ float wave_sum(float v) { return group_sum(v, 64); }
+
+// Maximum of a 64-bit key over the wave, returned in every lane.
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
+  uint32_t hi = (uint32_t)(k >> 32), lo = (uint32_t)k;
+#define FMOE_MAXSTEP(CTRL)                                             \
+  {                                                                    \
+    uint32_t oh = dpp_u<CTRL>(hi), ol = dpp_u<CTRL>(lo);               \
+    bool take = (oh > hi) || (oh == hi && ol > lo);                    \
+    hi = take ? oh : hi;                                               \
+    lo = take ? ol : lo;                                               \
+  }
+  FMOE_MAXSTEP(0xB1) FMOE_MAXSTEP(0x4E) FMOE_MAXSTEP(0x141) FMOE_MAXSTEP(0x140)
+#undef FMOE_MAXSTEP
+  uint64_t best = 0;
 #pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v += __shfl_xor(v, m, kWave);
-  return v;
+  for (int r = 0; r < 4; ++r) {
+    uint64_t c = ((uint64_t)(uint32_t)__builtin_amdgcn_readlane((int)hi, 16 * r) << 32) |
+                 (uint32_t)__builtin_amdgcn_readlane((int)lo, 16 * r);
+    best = c > best ? c : best;
+  }
+  return best;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) v = fmaxf(v, __shfl_xor(v, m, kWave));
-  return v;
+// Rank key of a router logit: larger key = earlier in rank order (larger logit first,
+// lower index on equal logits, NaN after every number). Keys of different experts are
+// distinct and never 0.
+__device__ __forceinline__ uint64_t rank_key(float logit, int e) {
+  uint32_t b = logit == 0.f ? 0u : __float_as_uint(logit);  // -0 ranks as +0
+  uint32_t ord = (logit != logit) ? 0u : ((b & 0x80000000u) ? ~b : (b | 0x80000000u));
+  return ((uint64_t)ord << 32) | (uint32_t)(0xFFFFFFFFu - (uint32_t)e);
+}
+__device__ __forceinline__ int rank_key_index(uint64_t key) { return (int)(0xFFFFFFFFu - (uint32_t)key); }
+__device__ __forceinline__ float rank_key_logit(uint64_t key) {
+  uint32_t ord = (uint32_t)(key >> 32);
+  uint32_t b = (ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord;
+  return __uint_as_float(b);
 }
 
 // Rank order of the router: a before b when its logit is larger, or equal with a lower
@@ -158,6 +208,39 @@ __device__ __forceinline__ bool ranks_before(float la, int ia, float lb, int ib)
   if (na) return ia < ib;
   if (la != lb) return la > lb;
   return ia < ib;
+}
+
+// Top-k of n ranked keys held in LDS (one wave; keys are consumed). Round r takes the
+// wave-wide maximum key; its owner lane clears it and rescans its own keys. Lane 0 writes
+// isel[r] (expert index) and lsel[r] (logit); then lanes < k turn the logits into the
+// softmax over the selected experts, shifted by the largest: wsel[j] = e^(l_j - l_0) /
+// sum_j' e^(l_j' - l_0).
+__device__ __forceinline__ void wave_topk_keys(uint64_t* keys, int n, int k, int* isel, float* lsel,
+                                               float* wsel) {
+  const int lane = threadIdx.x & 63;
+  uint64_t best = 0;
+  for (int e = lane; e < n; e += 64) best = keys[e] > best ? keys[e] : best;
+  for (int r = 0; r < k; ++r) {
+    const uint64_t w = wave_max_u64(best);
+    if (lane == 0) {
+      isel[r] = rank_key_index(w);
+      lsel[r] = rank_key_logit(w);
+    }
+    if (best == w && w != 0) {
+      best = 0;
+      for (int e = lane; e < n; e += 64) {
+        uint64_t kv = keys[e];
+        if (kv == w) keys[e] = 0;
+        else best = kv > best ? kv : best;
+      }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  float ex = 0.f;
+  if (lane < k) ex = expf(lsel[lane] - lsel[0]);
+  const float denom = wave_sum(ex);
+  if (lane < k) wsel[lane] = ex / denom;
 }
 
 // silu(g) * u with silu(g) = g / (1 + exp(-g)); for very negative g, exp(-g) is +inf

@@ -107,49 +107,24 @@ __global__ void __launch_bounds__(256) router_kernel(const float* __restrict__ R
   }
 }
 
-// One wave per token: k rounds of a wave-wide argmax (larger logit first, lower index on
-// equal logits, NaN last), then the softmax over the k selected logits.
+// One wave per token: the logits become rank keys in LDS, then k rounds of a wave-wide
+// maximum select the experts (larger logit first, lower index on equal logits, NaN last)
+// and the softmax over the k selected logits gives their weights.
 __global__ void __launch_bounds__(64) topk_kernel(const float* __restrict__ logits, int n_tokens, int n_experts,
                                                   int k, int32_t* __restrict__ idx, float* __restrict__ w) {
   const int t = blockIdx.x;
   const int lane = threadIdx.x;
   const float* l = logits + (size_t)t * n_experts;
-  __shared__ float sel_l[16];
-  __shared__ int sel_i[16];
-  uint64_t taken = 0;  // bit j: element lane + 64 j already selected
-  for (int r = 0; r < k; ++r) {
-    float best = 0.f;
-    int bi = -1;
-    for (int j = 0, e = lane; e < n_experts; ++j, e += kWave) {
-      if ((taken >> j) & 1ull) continue;
-      float v = l[e];
-      if (bi < 0 || ranks_before(v, e, best, bi)) {
-        best = v;
-        bi = e;
-      }
-    }
-    // wave argmax under the same order (bi < 0 = nothing left in this lane)
-    for (int m = 32; m >= 1; m >>= 1) {
-      float ov = __shfl_xor(best, m, kWave);
-      int oi = __shfl_xor(bi, m, kWave);
-      if (oi >= 0 && (bi < 0 || ranks_before(ov, oi, best, bi))) {
-        best = ov;
-        bi = oi;
-      }
-    }
-    if (bi >= 0 && (bi % kWave) == lane) taken |= 1ull << (bi / kWave);
-    if (lane == 0) {
-      sel_l[r] = best;
-      sel_i[r] = bi;
-    }
-  }
+  __shared__ uint64_t keys[4096];
+  __shared__ float lsel[16], wsel[16];
+  __shared__ int isel[16];
+  for (int e = lane; e < n_experts; e += kWave) keys[e] = rank_key(l[e], e);
+  __syncthreads();
+  wave_topk_keys(keys, n_experts, k, isel, lsel, wsel);
   __syncthreads();
   if (lane < k) {
-    float l0 = sel_l[0];
-    float denom = 0.f;
-    for (int j = 0; j < k; ++j) denom += expf(sel_l[j] - l0);
-    idx[(size_t)t * k + lane] = sel_i[lane];
-    w[(size_t)t * k + lane] = expf(sel_l[lane] - l0) / denom;
+    idx[(size_t)t * k + lane] = isel[lane];
+    w[(size_t)t * k + lane] = wsel[lane];
   }
 }
 

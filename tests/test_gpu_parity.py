@@ -180,7 +180,7 @@ def _decode(stack, x, k, prenorm=True, eps=1e-6):
     idx = torch.empty((stack.L, k), dtype=torch.int32, device="cuda")
     w = torch.empty((stack.L, k), dtype=torch.float32, device="cuda")
     wsb = fm.workspace_bytes(fm.OP_MOE_LAYER, 1, H, stack.I, stack.E, k)
-    ws = torch.empty(wsb, dtype=torch.uint8, device="cuda")
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
     fm.moe_layer(stack.layers, xd, hd, 1, k, eps, fm.PRENORM if prenorm else 0, idx, w, ws, wsb)
     torch.cuda.synchronize()
     return hd.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
