@@ -7,15 +7,19 @@
 // device):
 //   1. v = h * inv_rms(h) (or v = h without pre-norm), staged in LDS by every workgroup;
 //   2. router: workgroup g owns experts g, g+G, ...; its waves dot 1024-column slices of
-//      those rows with v; the logits are published with a tag (value | epoch << 32);
+//      those rows (loaded during the previous layer) with v; the logits are published
+//      with a tag (value | epoch << 32);
 //   3. every workgroup polls the tagged logits, then selects the top-k and their softmax
-//      weights itself (no extra round trip);
-//   4. gate/up: (slot j, row i) items spread over all waves of all workgroups; each item
-//      reads gate row i and up row i of expert idx[j] and publishes a[j][i] = silu(g)*u;
-//      waves 1.. then issue the loads of their down-projection rows (prefetch);
+//      weights itself (no extra round trip); meanwhile the digit image of v (see
+//      fmoe_intdot.h) is built in LDS;
+//   4. gate/up: workgroup g owns a contiguous run of (slot j, row i) items (consecutive
+//      rows of one expert); each item reads gate row i and up row i of expert idx[j] and
+//      publishes a[j][i] = silu(g)*u; every wave then issues the loads of its share of
+//      the down-projection rows (prefetch);
 //   5. grid barrier (arrival flags);
 //   6. down + combine + residual: workgroup g owns a contiguous block of h rows and
-//      computes h[r] += sum_j w_j * (Wd_j[r] . a_j) for them (fixed slot order);
+//      computes h[r] += sum_j w_j * (Wd_j[r] . a_j) for them (fixed slot order); the
+//      next layer's router rows are loaded meanwhile;
 //   7. grid barrier, next layer.
 //
 // Exchange between workgroups. Everything shared (h, a, logits, flags) is written and
@@ -27,43 +31,40 @@
 // G / kRep workgroups at once (polling one line from all 256 workgroups serializes at the
 // memory side and costs microseconds per round).
 //
-// Wave roles. Wave 0 is the communication wave: it raises the flags, polls, selects the
-// top-k and combines; it never holds prefetch loads in flight, because a wave's loads
-// return in issue order and a poll behind a prefetch would wait for it. Waves 1.. do the
-// down-projection and may keep its loads in flight across the barrier.
+// Wave 0 raises the flags and polls. A wave's loads return in issue order, so its poll
+// completes only after its own prefetched down rows have arrived; those are needed right
+// after the barrier anyway.
 //
-// LDS layout. Activation vectors are stored with one padding word after every chunk of
-// kCodes values, so that the 64 lanes of a wave, each reading its own chunk, hit 64
-// different banks.
+// Shapes. The template parameters HC, IC, EC, KC fix hidden, inter, n_experts and k at
+// compile time (0 = read them from the parameters); the decode shape of the 60-layer
+// 512-expert stack gets its own instantiation so that every index is a constant.
+//
+// LDS layout. fp32 vectors are stored with one padding word after every chunk of kCodes
+// values, so that threads reading consecutive chunks hit different banks.
 #include "fmoe_decode.h"
 #include "fmoe_device.h"
 #include "fmoe_internal.h"
+#include "fmoe_intdot.h"
 
 namespace fmoe {
 
 constexpr int kDecodeThreads = 256;
 constexpr int kDecodeWaves = kDecodeThreads / 64;
-constexpr int kDownWaves = kDecodeWaves - 1;  // waves 1.. run the down projection
 constexpr unsigned kSpinLimit = 1u << 21;
+constexpr int kBatchN = 16;     // h / a values loaded together per thread
+constexpr int kBatchR = 2;      // router slices per wave loaded ahead
+constexpr int kKeysInRegs = 8;  // top-k from registers when n_experts <= 512
+
 // gate/up items and down row blocks whose loads are issued together (fewer when every
 // lane holds more chunks per row, to stay within the register file)
 template <int CPL> constexpr int batch_gu() { return CPL >= 4 ? 1 : 4; }
-template <int CPL> constexpr int batch_d() { return CPL >= 4 ? 2 : (CPL == 2 ? 6 : 12); }
-constexpr int kBatchN = 8;   // h values loaded together per thread
+template <int CPL> constexpr int batch_d() { return CPL >= 4 ? 2 : (CPL == 2 ? 4 : 8); }
 
-struct DecodeSmem {
-  float* v;        // [hidden], padded
-  uint64_t* key;   // [n_experts] rank keys
-  float* part;     // [router items per workgroup]
-  float* a;        // [k][inter], padded
-  float* y;        // [k][rows per workgroup]
-  float* red;      // [kDecodeWaves]
-  float* wsel;     // [16]
-  float* lsel;     // [16]
-  int* isel;       // [16]
-  int* fail;       // [1]
-  uint32_t* base;  // [1]
-};
+__host__ __device__ constexpr int lanes_per_row(int n_chunks) {
+  int l = 1;
+  while (l < n_chunks && l < 64) l <<= 1;
+  return l;
+}
 
 template <int CC>
 __device__ __forceinline__ int padded(int i) {
@@ -97,49 +98,50 @@ __device__ bool flag_arrive_and_wait(uint32_t* flags, int G, int rep, uint32_t e
   }
 }
 
-// Fill XChunk registers from a padded LDS vector (chunk index c).
-template <int BITS>
-__device__ __forceinline__ void load_xchunk_padded(XChunk<BITS>& xc, const float* vpad, int c) {
-  constexpr int CC = Chunk<BITS>::kCodes;
-  load_xchunk<BITS>(xc, vpad + c * (CC + 1));
-}
-
-template <int BITS, int CPL_G, int CPL_D>
+template <int BITS, int CPL_G, int CPL_D, int HC, int IC, int EC, int KC>
 __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) {
   constexpr int kBatchGU = batch_gu<CPL_G>();
   constexpr int kBatchD = batch_d<CPL_D>();
   using C = Chunk<BITS>;
   constexpr int CC = C::kCodes;
+  constexpr int NW = Digits<BITS>::kWords;
   extern __shared__ float smem_raw[];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = gridDim.x, g = blockIdx.x, rep = g % kRep;
-  const int H = p.hidden, I = p.inter, E = p.n_experts, K = p.k;
+  const int H = HC ? HC : p.hidden;
+  const int I = IC ? IC : p.inter;
+  const int E = EC ? EC : p.n_experts;
+  const int K = KC ? KC : p.k;
+  const int KI = K * I;
+  const int vec_len = H > KI ? H : KI;
+  const int max_chunks = vec_len / CC;
 
-  DecodeSmem sm;
-  {
-    uint64_t* q64 = reinterpret_cast<uint64_t*>(smem_raw);
-    sm.key = q64;
-    float* q = reinterpret_cast<float*>(q64 + E);
-    sm.v = q; q += H + H / CC;
-    sm.part = q; q += p.router_items;
-    sm.a = q; q += K * (I + I / CC);
-    sm.y = q; q += K * p.rows_per_wg;
-    sm.red = q; q += kDecodeWaves;
-    sm.wsel = q; q += 16;
-    sm.lsel = q; q += 16;
-    sm.isel = reinterpret_cast<int*>(q); q += 16;
-    sm.fail = reinterpret_cast<int*>(q); q += 1;
-    sm.base = reinterpret_cast<uint32_t*>(q);
-  }
+  // ---- LDS carve-up
+  uint64_t* key = reinterpret_cast<uint64_t*>(smem_raw);  // [E] rank keys (large E)
+  float* vec = reinterpret_cast<float*>(key + E);         // padded v, later padded a
+  DigitStore dig;
+  dig.words = reinterpret_cast<uint32_t*>(vec + vec_len + vec_len / CC);
+  dig.step = reinterpret_cast<float*>(dig.words + (size_t)NW * max_chunks);
+  dig.xsum = dig.step + max_chunks;
+  dig.n_chunks = H / CC;
+  float* part = dig.xsum + max_chunks;  // [router items]
+  float* ybuf = part + p.router_items;  // [k][rows per workgroup]
+  float* red = ybuf + K * p.rows_per_wg;
+  float* wsel = red + kDecodeWaves;
+  float* lsel = wsel + 16;
+  int* isel = reinterpret_cast<int*>(lsel + 16);
+  int* fail = isel + 16;
+  uint32_t* base = reinterpret_cast<uint32_t*>(fail + 1);
+
   if (tid == 0) {
-    *sm.fail = 0;
+    *fail = 0;
     // Every flag holds the same value F when a launch starts: 0 in a zero-filled
     // workspace, else the last epoch of the previous launch (all workgroups reach it).
     // This launch's epochs and logit tags are F + 1, F + 2, ...
-    *sm.base = ld_dev_u32(p.flags_arr + (size_t)rep * kMaxGrid + blockIdx.x);
+    *base = ld_dev_u32(p.flags_arr + (size_t)rep * kMaxGrid + blockIdx.x);
   }
   __syncthreads();
-  const uint32_t F = *sm.base;
+  const uint32_t F = *base;
 
   // geometry of the quantized rows
   const size_t cbH = (size_t)I * H * BITS / 8;  // bytes of gate (= up = down) codes
@@ -147,22 +149,45 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
   const int ngH = H / 64, ngI = I / 64;
   const size_t rowH = (size_t)H * BITS / 8, rowI = (size_t)I * BITS / 8;
   const int nchG = H / CC, nchD = I / CC;
-  const int lprG = p.lpr_g, rpwG = 64 / lprG, subG = lane & (lprG - 1), rselG = lane / lprG;
-  const int lprD = p.lpr_d, rpwD = 64 / lprD, subD = lane & (lprD - 1), rselD = lane / lprD;
-  const int r0 = g * p.rows_per_wg;
-  const int nr = max(0, min(H - r0, p.rows_per_wg));
+  const int lprG = HC ? lanes_per_row(HC / CC) : p.lpr_g, rpwG = 64 / lprG, subG = lane & (lprG - 1),
+            rselG = lane / lprG;
+  const int lprD = IC ? lanes_per_row(IC / CC) : p.lpr_d, rpwD = 64 / lprD, subD = lane & (lprD - 1),
+            rselD = lane / lprD;
+  const int rows_wg = p.rows_per_wg;
+  const int r0 = g * rows_wg;
+  const int nr = max(0, min(H - r0, rows_wg));
   const int n_rb = (nr + rpwD - 1) / rpwD;  // down row blocks per slot
-  const int n_dit = (K * n_rb + kDownWaves - 1) / kDownWaves;  // down items per wave (waves 1..)
+  // down items (j, rb) of this workgroup, a contiguous run per wave
+  const int d_items = K * n_rb;
+  const int d_per = (d_items + kDecodeWaves - 1) / kDecodeWaves;
+  const int d_lo = wave * d_per, d_hi = min(d_items, d_lo + d_per);
   const int S = (H + 1023) / 1024;  // router slices per row
   const int my_experts = (E - g + G - 1) / G;
-  const size_t KI = (size_t)K * I;
+  const int n_ritems = my_experts * S;
   const float* h_rep = p.h + (size_t)rep * H;
   const float* a_rep = p.a + (size_t)rep * KI;
   const uint64_t* logits_rep = p.logits + (size_t)rep * E;
 
+  // router slice `it` of layer `lr`: up to 4 float4 per lane
+  float4 rv[kBatchR][4];
+  auto router_load = [&](int lr, int it, int u) {
+    if (it < n_ritems && lr < p.n_layers) {
+      const int el = it / S, s = it % S;
+      const int e = g + el * G;
+      const int c0 = s * 256, c1 = min(H / 4, c0 + 256);
+      const float4* row = reinterpret_cast<const float4*>(p.router[lr] + (size_t)e * H);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int c = c0 + lane + 64 * q;
+        if (c < c1) rv[u][q] = row[c];
+      }
+    }
+  };
+#pragma unroll
+  for (int u = 0; u < kBatchR; ++u) router_load(0, wave + kDecodeWaves * u, u);
+
   for (int l = 0; l < p.n_layers; ++l) {
     const int lg = p.layer0 + l;
-    const float* R = p.router[l];
     const uint8_t* X = p.experts[l];
 
     // ---- 1. v = rmsnorm(h) or h, in LDS (padded); loads issued kBatchN at a time
@@ -177,120 +202,131 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
 #pragma unroll
       for (int u = 0; u < kBatchN; ++u) {
         const int i = i0 + u * kDecodeThreads;
-        if (i < H) sm.v[padded<CC>(i)] = hv[u];
+        if (i < H) vec[padded<CC>(i)] = hv[u];
         ss = fmaf(hv[u], hv[u], ss);
       }
     }
     ss = wave_sum(ss);
-    if (lane == 0) sm.red[wave] = ss;
+    if (lane == 0) red[wave] = ss;
     __syncthreads();
     float inv = 1.f;
     if (p.flags & FMOE_PRENORM) {
       float tot = 0.f;
-      for (int w2 = 0; w2 < kDecodeWaves; ++w2) tot += sm.red[w2];
+      for (int w2 = 0; w2 < kDecodeWaves; ++w2) tot += red[w2];
       inv = 1.0f / sqrtf(tot / (float)H + p.eps);
     }
-    for (int i = tid; i < H; i += kDecodeThreads) sm.v[padded<CC>(i)] *= inv;
+    for (int i = tid; i < H; i += kDecodeThreads) vec[padded<CC>(i)] *= inv;
     __syncthreads();
 
-    // ---- 2. router rows of this workgroup's experts, 1024-column slices per wave
-    for (int it = wave; it < my_experts * S; it += kDecodeWaves) {
-      const int el = it / S, s = it % S;
-      const int e = g + el * G;
-      const int c0 = s * 256, c1 = min(H / 4, c0 + 256);  // float4 columns of the slice
-      const float4* row = reinterpret_cast<const float4*>(R + (size_t)e * H);
-      float4 rv[4];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int c = c0 + lane + 64 * u;
-        if (c < c1) rv[u] = row[c];
-      }
+    // ---- 2. router: dot the loaded slices with v
+    for (int m = 0; wave + kDecodeWaves * m < n_ritems; ++m) {
+      const int it = wave + kDecodeWaves * m;
+      const int u = m < kBatchR ? m : kBatchR - 1;
+      if (m >= kBatchR) router_load(l, it, u);
+      const int s = it % S;
+      const int c0 = s * 256, c1 = min(H / 4, c0 + 256);
       float acc = 0.f;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int c = c0 + lane + 64 * u;
+      for (int q = 0; q < 4; ++q) {
+        const int c = c0 + lane + 64 * q;
         if (c < c1) {
           const int pi = padded<CC>(4 * c);  // 4 consecutive values never straddle a chunk
-          acc = fmaf(rv[u].x, sm.v[pi + 0], acc);
-          acc = fmaf(rv[u].y, sm.v[pi + 1], acc);
-          acc = fmaf(rv[u].z, sm.v[pi + 2], acc);
-          acc = fmaf(rv[u].w, sm.v[pi + 3], acc);
+          acc = fmaf(rv[u][q].x, vec[pi + 0], acc);
+          acc = fmaf(rv[u][q].y, vec[pi + 1], acc);
+          acc = fmaf(rv[u][q].z, vec[pi + 2], acc);
+          acc = fmaf(rv[u][q].w, vec[pi + 3], acc);
         }
       }
       acc = wave_sum(acc);
-      if (lane == 0) sm.part[it] = acc;
+      if (lane == 0) part[it] = acc;
     }
     __syncthreads();
     const uint64_t tag = (uint64_t)(F + (uint32_t)l + 1u) << 32;
 
-    // ---- 3. publish this workgroup's logits, gather all of them, top-k (wave 0)
+    // ---- 3. publish this workgroup's logits and gather all of them (wave 0); the
+    // other waves build the digit image of v meanwhile
     if (wave == 0) {
       for (int t = lane; t < my_experts * kRep; t += 64) {
         const int el = t / kRep, rr = t % kRep;
         float lsum = 0.f;
-        for (int s = 0; s < S; ++s) lsum += sm.part[el * S + s];
+        for (int s = 0; s < S; ++s) lsum += part[el * S + s];
         st_dev_u64(p.logits + (size_t)rr * E + g + el * G, tag | __float_as_uint(lsum));
       }
       unsigned spins = 0;
+      uint64_t kr[kKeysInRegs];  // E <= 64 * kKeysInRegs: keys stay in registers
       while (true) {
         bool ok = true;
-        for (int e = lane; e < E; e += 64) {
-          uint64_t t = ld_dev_u64(logits_rep + e);
-          if ((t & 0xffffffff00000000ull) == tag) sm.key[e] = rank_key(__uint_as_float((uint32_t)t), e);
-          else ok = false;
+        if (E <= 64 * kKeysInRegs) {
+#pragma unroll
+          for (int j = 0; j < kKeysInRegs; ++j) {
+            const int e = lane + 64 * j;
+            kr[j] = 0;
+            if (e < E) {
+              const uint64_t t = ld_dev_u64(logits_rep + e);
+              ok &= (t & 0xffffffff00000000ull) == tag;
+              kr[j] = rank_key(__uint_as_float((uint32_t)t), e);
+            }
+          }
+        } else {
+          for (int e = lane; e < E; e += 64) {
+            const uint64_t t = ld_dev_u64(logits_rep + e);
+            ok &= (t & 0xffffffff00000000ull) == tag;
+            key[e] = rank_key(__uint_as_float((uint32_t)t), e);
+          }
         }
         if (__all(ok)) break;
         if (spin_failed(++spins, p.err)) {
           if (lane == 0) {
             st_dev_u32(p.err, 1u);
-            *sm.fail = 1;
+            *fail = 1;
           }
           break;
         }
         __builtin_amdgcn_s_sleep(1);
       }
-      if (*sm.fail) {
+      if (*fail) {
         if (lane < K) {
-          sm.isel[lane] = 0;
-          sm.wsel[lane] = 0.f;
+          isel[lane] = 0;
+          wsel[lane] = 0.f;
         }
+      } else if (E <= 64 * kKeysInRegs) {
+        wave_topk_regs<kKeysInRegs>(kr, K, isel, lsel, wsel);
       } else {
-        wave_topk_keys(sm.key, E, K, sm.isel, sm.lsel, sm.wsel);
+        wave_topk_keys(key, E, K, isel, lsel, wsel);
       }
       if (g == 0 && lane < K) {
         size_t o = ((size_t)lg) * K + lane;
-        if (p.idx_out) p.idx_out[o] = sm.isel[lane];
-        if (p.w_out) p.w_out[o] = sm.wsel[lane];
+        if (p.idx_out) p.idx_out[o] = isel[lane];
+        if (p.w_out) p.w_out[o] = wsel[lane];
       }
+    } else {
+      build_digits<BITS>(dig, H, [&](int i) { return vec[padded<CC>(i)]; }, kDecodeThreads - 64, tid - 64);
     }
     __syncthreads();
-    if (*sm.fail) break;
+    if (*fail) break;
 
-    // ---- 4. gate/up + SwiGLU: items (j, i) in blocks of rpwG consecutive items; the
-    // loads of kBatchGU blocks are issued before any of them is used
+    // ---- 4. gate/up + SwiGLU: workgroup g owns a contiguous run of blocks (rpwG
+    // consecutive items each; consecutive rows of one expert, so few distinct pages),
+    // dealt to its waves in runs of kBatchGU blocks whose loads are issued together
     {
-      XChunk<BITS> xc[CPL_G];
-#pragma unroll
-      for (int q = 0; q < CPL_G; ++q) {
-        int c = subG + lprG * q;
-        if (c < nchG) load_xchunk_padded<BITS>(xc[q], sm.v, c);
-      }
-      const int n_items = K * I;
-      const int n_blocks = (n_items + rpwG - 1) / rpwG;
-      const int bstride = G * kDecodeWaves;
-      for (int b0 = g + G * wave; b0 < n_blocks; b0 += bstride * kBatchGU) {
+      DChunk<BITS> dc[CPL_G];
+      bool dc_loaded = false;  // the digits are read from LDS after the first loads are issued
+      const int n_blocks = (KI + rpwG - 1) / rpwG;
+      const int per_wg = (n_blocks + G - 1) / G;
+      const int blk_lo = g * per_wg, blk_hi = min(n_blocks, blk_lo + per_wg);
+      for (int b0 = blk_lo + wave * kBatchGU; b0 < blk_hi; b0 += kDecodeWaves * kBatchGU) {
         uint4 wg[kBatchGU][CPL_G], wu[kBatchGU][CPL_G];
         uint32_t sg[kBatchGU][CPL_G], su[kBatchGU][CPL_G];
 #pragma unroll
         for (int u = 0; u < kBatchGU; ++u) {
-          const int item = (b0 + u * bstride) * rpwG + rselG;
-          if (b0 + u * bstride < n_blocks && item < n_items) {
+          const int item = (b0 + u) * rpwG + rselG;
+          if (b0 + u < blk_hi && item < KI) {
             const int j = item / I, i = item % I;
-            const uint8_t* base = X + (size_t)sm.isel[j] * p.expert_stride;
-            const uint4* gp = reinterpret_cast<const uint4*>(base + (size_t)i * rowH);
-            const uint4* up = reinterpret_cast<const uint4*>(base + cbH + (size_t)i * rowH);
-            const uint32_t* gsb = reinterpret_cast<const uint32_t*>(base + 3 * cbH) + (size_t)i * ngH;
-            const uint32_t* usb = reinterpret_cast<const uint32_t*>(base + 3 * cbH + sbb) + (size_t)i * ngH;
+            const uint8_t* bp = X + (size_t)isel[j] * p.expert_stride;
+            const uint4* gp = reinterpret_cast<const uint4*>(bp + (size_t)i * rowH);
+            const uint4* up = reinterpret_cast<const uint4*>(bp + cbH + (size_t)i * rowH);
+            const uint32_t* gsb = reinterpret_cast<const uint32_t*>(bp + 3 * cbH) + (size_t)i * ngH;
+            const uint32_t* usb = reinterpret_cast<const uint32_t*>(bp + 3 * cbH + sbb) + (size_t)i * ngH;
 #pragma unroll
             for (int q = 0; q < CPL_G; ++q) {
               int c = subG + lprG * q;
@@ -303,19 +339,27 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
             }
           }
         }
+        if (!dc_loaded) {
+#pragma unroll
+          for (int q = 0; q < CPL_G; ++q) {
+            int c = subG + lprG * q;
+            if (c < nchG) load_dchunk<BITS>(dc[q], dig, c);
+          }
+          dc_loaded = true;
+        }
 #pragma unroll
         for (int u = 0; u < kBatchGU; ++u) {
-          if (b0 + u * bstride >= n_blocks) break;  // uniform over the wave
-          const int item = (b0 + u * bstride) * rpwG + rselG;
-          const bool valid = item < n_items;
+          if (b0 + u >= blk_hi) break;  // uniform over the wave
+          const int item = (b0 + u) * rpwG + rselG;
+          const bool valid = item < KI;
           float gs = 0.f, us = 0.f;
           if (valid) {
 #pragma unroll
             for (int q = 0; q < CPL_G; ++q) {
               int c = subG + lprG * q;
               if (c < nchG) {
-                gs += chunk_dot<BITS>(wg[u][q], sg[u][q], xc[q]);
-                us += chunk_dot<BITS>(wu[u][q], su[u][q], xc[q]);
+                gs += chunk_dot_int<BITS>(wg[u][q], sg[u][q], dc[q]);
+                us += chunk_dot_int<BITS>(wu[u][q], su[u][q], dc[q]);
               }
             }
           }
@@ -331,28 +375,26 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
     }
     wait_vmem();  // this wave's a-stores are at the coherence point
 
-    // ---- prefetch: waves 1.. issue the loads of their first kBatchD down items
+    // ---- prefetch: every wave issues the loads of its first kBatchD down items
     uint4 wd[kBatchD][CPL_D];
     uint32_t sd[kBatchD][CPL_D];
-    auto down_item = [&](int m, int& j, int& rl) {
-      const int t = (wave - 1) + kDownWaves * m;
-      j = t / max(n_rb, 1);
-      rl = (t % max(n_rb, 1)) * rpwD + rselD;
-      return wave > 0 && m < n_dit && j < K;
-    };
     auto down_load = [&](int m, int u) {
-      int j, rl;
-      if (down_item(m, j, rl) && rl < nr) {
-        const int r = r0 + rl;
-        const uint8_t* base = X + (size_t)sm.isel[j] * p.expert_stride;
-        const uint4* dp = reinterpret_cast<const uint4*>(base + 2 * cbH + (size_t)r * rowI);
-        const uint32_t* dsb = reinterpret_cast<const uint32_t*>(base + 3 * cbH + 2 * sbb) + (size_t)r * ngI;
+      const int t = d_lo + m;
+      if (t < d_hi) {
+        const int j = t / n_rb;
+        const int rl = (t % n_rb) * rpwD + rselD;
+        if (rl < nr) {
+          const int r = r0 + rl;
+          const uint8_t* bp = X + (size_t)isel[j] * p.expert_stride;
+          const uint4* dp = reinterpret_cast<const uint4*>(bp + 2 * cbH + (size_t)r * rowI);
+          const uint32_t* dsb = reinterpret_cast<const uint32_t*>(bp + 3 * cbH + 2 * sbb) + (size_t)r * ngI;
 #pragma unroll
-        for (int q = 0; q < CPL_D; ++q) {
-          int c = subD + lprD * q;
-          if (c < nchD) {
-            wd[u][q] = dp[c];
-            sd[u][q] = dsb[c / C::kPerGroup];
+          for (int q = 0; q < CPL_D; ++q) {
+            int c = subD + lprD * q;
+            if (c < nchD) {
+              wd[u][q] = dp[c];
+              sd[u][q] = dsb[c / C::kPerGroup];
+            }
           }
         }
       }
@@ -362,42 +404,50 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
 
     // ---- 5. all of a is published
     __syncthreads();
-    if (wave == 0) flag_arrive_and_wait(p.flags_arr, G, rep, F + 2u * l + 1u, p.err, sm.fail);
+    if (wave == 0) flag_arrive_and_wait(p.flags_arr, G, rep, F + 2u * l + 1u, p.err, fail);
     __syncthreads();
-    if (*sm.fail) break;
-    for (int i0 = tid; i0 < (int)KI; i0 += kDecodeThreads * kBatchN) {
+    if (*fail) break;
+    for (int i0 = tid; i0 < KI; i0 += kDecodeThreads * kBatchN) {
       float av[kBatchN];
 #pragma unroll
       for (int u = 0; u < kBatchN; ++u) {
         const int i = i0 + u * kDecodeThreads;
-        av[u] = i < (int)KI ? ld_dev(a_rep + i) : 0.f;
+        av[u] = i < KI ? ld_dev(a_rep + i) : 0.f;
       }
 #pragma unroll
       for (int u = 0; u < kBatchN; ++u) {
         const int i = i0 + u * kDecodeThreads;
-        if (i < (int)KI) sm.a[(i / I) * (I + I / CC) + padded<CC>(i % I)] = av[u];
+        if (i < KI) vec[padded<CC>(i)] = av[u];
       }
     }
+    // the next layer's router slices are read while the down projection runs
+#pragma unroll
+    for (int u = 0; u < kBatchR; ++u) router_load(l + 1, wave + kDecodeWaves * u, u);
+    __syncthreads();
+    dig.n_chunks = KI / CC;
+    build_digits<BITS>(dig, KI, [&](int i) { return vec[padded<CC>(i)]; }, kDecodeThreads, tid);
     __syncthreads();
 
-    // ---- 6. down (waves 1..), then combine + residual (wave 0)
-    if (wave > 0) {
+    // ---- 6. down (every wave), then combine + residual (wave 0)
+    {
       int cur_j = -1;
-      XChunk<BITS> xc[CPL_D];
-      for (int m0 = 0; m0 < n_dit; m0 += kBatchD) {
+      DChunk<BITS> dc[CPL_D];
+      for (int m0 = 0; d_lo + m0 < d_hi; m0 += kBatchD) {
         if (m0 > 0) {
 #pragma unroll
           for (int u = 0; u < kBatchD; ++u) down_load(m0 + u, u);
         }
 #pragma unroll
         for (int u = 0; u < kBatchD; ++u) {
-          int j, rl;
-          if (!down_item(m0 + u, j, rl)) continue;  // uniform over the wave
+          const int t = d_lo + m0 + u;
+          if (t >= d_hi) break;  // uniform over the wave
+          const int j = t / n_rb;
+          const int rl = (t % n_rb) * rpwD + rselD;
           if (j != cur_j) {
 #pragma unroll
             for (int q = 0; q < CPL_D; ++q) {
               int c = subD + lprD * q;
-              if (c < nchD) load_xchunk_padded<BITS>(xc[q], sm.a + j * (I + I / CC), c);
+              if (c < nchD) load_dchunk<BITS>(dc[q], dig, j * nchD + c);
             }
             cur_j = j;
           }
@@ -406,22 +456,23 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
 #pragma unroll
             for (int q = 0; q < CPL_D; ++q) {
               int c = subD + lprD * q;
-              if (c < nchD) acc += chunk_dot<BITS>(wd[u][q], sd[u][q], xc[q]);
+              if (c < nchD) acc += chunk_dot_int<BITS>(wd[u][q], sd[u][q], dc[q]);
             }
           }
           acc = group_sum(acc, lprD);
-          if (rl < nr && subD == 0) sm.y[j * p.rows_per_wg + rl] = acc;
+          if (rl < nr && subD == 0) ybuf[j * rows_wg + rl] = acc;
         }
       }
     }
     __syncthreads();
+    dig.n_chunks = H / CC;
     const bool last = (l == p.n_layers - 1) && p.is_final;
     if (wave == 0) {
       for (int rl = lane; rl < nr; rl += 64) {
         const int r = r0 + rl;
         float hv = (lg == 0) ? p.x_in[r] : ld_dev(h_rep + r);
         float c = 0.f;
-        for (int j = 0; j < K; ++j) c = fmaf(sm.wsel[j], sm.y[j * p.rows_per_wg + rl], c);
+        for (int j = 0; j < K; ++j) c = fmaf(wsel[j], ybuf[j * rows_wg + rl], c);
         float hn = hv + c;
 #pragma unroll
         for (int rr = 0; rr < kRep; ++rr) st_dev(p.h + (size_t)rr * H + r, hn);
@@ -432,12 +483,12 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
     // ---- 7. all of h is published
     if (l + 1 < p.n_layers) {
       __syncthreads();
-      if (wave == 0) flag_arrive_and_wait(p.flags_arr, G, rep, F + 2u * l + 2u, p.err, sm.fail);
+      if (wave == 0) flag_arrive_and_wait(p.flags_arr, G, rep, F + 2u * l + 2u, p.err, fail);
       __syncthreads();
-      if (*sm.fail) break;
+      if (*fail) break;
     }
   }
-  if (*sm.fail && p.is_final) {
+  if (*fail && p.is_final) {
     for (int r = r0 + tid; r < r0 + nr; r += kDecodeThreads) p.h_out[r] = __uint_as_float(0x7fc00000u);
   }
 }
@@ -459,11 +510,15 @@ int decode_geometry(int hidden, int inter, int bits, int* lpr_g, int* cpl_g, int
 
 size_t decode_smem_bytes(int hidden, int inter, int n_experts, int k, int G, int rows_per_wg, int bits) {
   const int cc = bits == 4 ? 32 : 64;
+  const int nw = bits == 4 ? Digits<4>::kWords : Digits<2>::kWords;
+  const size_t ki = (size_t)k * inter;
+  const size_t vec_len = (size_t)hidden > ki ? (size_t)hidden : ki;
+  const size_t max_chunks = vec_len / cc;
   int my_experts = (n_experts + G - 1) / G;
   int S = (hidden + 1023) / 1024;
-  size_t floats = (size_t)hidden + hidden / cc + (size_t)my_experts * S + (size_t)k * (inter + inter / cc) +
-                  (size_t)k * rows_per_wg + kDecodeWaves + 16 + 16 + 16 + 2;
-  return (size_t)n_experts * 8 + floats * 4;
+  size_t words = vec_len + vec_len / cc + (size_t)nw * max_chunks + 2 * max_chunks + (size_t)my_experts * S +
+                 (size_t)k * rows_per_wg + kDecodeWaves + 16 + 16 + 16 + 2;
+  return (size_t)n_experts * 8 + words * 4;
 }
 
 int decode_grid(int* G_out) {
@@ -475,9 +530,9 @@ int decode_grid(int* G_out) {
   return FMOE_OK;
 }
 
-template <int BITS, int CG, int CD>
+template <int BITS, int CG, int CD, int HC, int IC, int EC, int KC>
 static int launch_decode_t(const DecodeParams& p, int G, size_t smem, hipStream_t s) {
-  auto fn = decode_kernel<BITS, CG, CD>;
+  auto fn = decode_kernel<BITS, CG, CD, HC, IC, EC, KC>;
   int occ = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kDecodeThreads, smem) != hipSuccess) return FMOE_ERR_HIP;
   if (occ < 1) return FMOE_ERR_SHAPE;
@@ -492,8 +547,13 @@ static int launch_decode_t(const DecodeParams& p, int G, size_t smem, hipStream_
 int launch_decode(const DecodeParams& p, int G, hipStream_t s) {
   const size_t smem = decode_smem_bytes(p.hidden, p.inter, p.n_experts, p.k, G, p.rows_per_wg, p.bits);
   int cg = p.cpl_g, cd = p.cpl_d;
+  // the decode shape of the 512-expert stack: hidden 4096, inter 1024, top-4
+  if (p.hidden == 4096 && p.inter == 1024 && p.n_experts == 512 && p.k == 4) {
+    if (p.bits == 4) return launch_decode_t<4, 2, 1, 4096, 1024, 512, 4>(p, G, smem, s);
+    return launch_decode_t<2, 1, 1, 4096, 1024, 512, 4>(p, G, smem, s);
+  }
 #define FMOE_DEC(B, X, Y) \
-  if (p.bits == B && cg == X && cd == Y) return launch_decode_t<B, X, Y>(p, G, smem, s);
+  if (p.bits == B && cg == X && cd == Y) return launch_decode_t<B, X, Y, 0, 0, 0, 0>(p, G, smem, s);
   FMOE_DEC(4, 1, 1) FMOE_DEC(4, 2, 1) FMOE_DEC(4, 4, 1) FMOE_DEC(4, 1, 2) FMOE_DEC(4, 2, 2) FMOE_DEC(4, 4, 2)
   FMOE_DEC(4, 1, 4) FMOE_DEC(4, 2, 4) FMOE_DEC(4, 4, 4)
   FMOE_DEC(2, 1, 1) FMOE_DEC(2, 2, 1) FMOE_DEC(2, 4, 1) FMOE_DEC(2, 1, 2) FMOE_DEC(2, 2, 2) FMOE_DEC(2, 4, 2)

@@ -163,6 +163,15 @@ __device__ __forceinline__ float group_sum(float v, int width) {
 
 __device__ __forceinline__ float wave_sum(float v) { return group_sum(v, 64); }
 
+// Maximum over groups of `width` consecutive lanes (width 2, 4, 8 or 16).
+__device__ __forceinline__ float group_max(float v, int width) {
+  if (width >= 2) v = fmaxf(v, dpp_f<0xB1>(v));
+  if (width >= 4) v = fmaxf(v, dpp_f<0x4E>(v));
+  if (width >= 8) v = fmaxf(v, dpp_f<0x141>(v));
+  if (width >= 16) v = fmaxf(v, dpp_f<0x140>(v));
+  return v;
+}
+
 // Maximum of a 64-bit key over the wave, returned in every lane.
 __device__ __forceinline__ uint64_t wave_max_u64(uint64_t k) {
   uint32_t hi = (uint32_t)(k >> 32), lo = (uint32_t)k;
@@ -233,6 +242,36 @@ __device__ __forceinline__ void wave_topk_keys(uint64_t* keys, int n, int k, int
         if (kv == w) keys[e] = 0;
         else best = kv > best ? kv : best;
       }
+    }
+  }
+  __builtin_amdgcn_s_waitcnt(0);
+  __builtin_amdgcn_wave_barrier();
+  float ex = 0.f;
+  if (lane < k) ex = expf(lsel[lane] - lsel[0]);
+  const float denom = wave_sum(ex);
+  if (lane < k) wsel[lane] = ex / denom;
+}
+
+// Top-k of at most 64 * KPL ranked keys held in registers (key j of a lane is element
+// lane + 64 j; absent elements hold key 0). Same contract as wave_topk_keys; the keys are
+// consumed. All lanes clear the taken key and recompute their best without branches.
+template <int KPL>
+__device__ __forceinline__ void wave_topk_regs(uint64_t (&kr)[KPL], int k, int* isel, float* lsel, float* wsel) {
+  const int lane = threadIdx.x & 63;
+  uint64_t best = 0;
+#pragma unroll
+  for (int j = 0; j < KPL; ++j) best = kr[j] > best ? kr[j] : best;
+  for (int r = 0; r < k; ++r) {
+    const uint64_t w = wave_max_u64(best);
+    if (lane == 0) {
+      isel[r] = rank_key_index(w);
+      lsel[r] = rank_key_logit(w);
+    }
+    best = 0;
+#pragma unroll
+    for (int j = 0; j < KPL; ++j) {
+      kr[j] = kr[j] == w ? 0ull : kr[j];
+      best = kr[j] > best ? kr[j] : best;
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
