@@ -46,7 +46,7 @@ def algorithmic_bytes_per_layer(bits: int) -> int:
 
 def decode_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("fmoe_decode.hip", "fmoe_device.h", "fmoe_decode.h"):
+    for f in ("fmoe_decode.hip", "fmoe_device.h", "fmoe_decode.h", "fmoe_intdot.h"):
         h.update(open(os.path.join(ROOT, "quantized_expert_ffn_fmoe_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 
@@ -76,7 +76,7 @@ def build_stack(bits: int, dev):
     return blobs, routers, fm.layers_array(layers), E_ * stride * L_
 
 
-def cpu_baseline(bits: int, n_tokens: int = 2):
+def cpu_baseline(bits: int, n_tokens: int = 10):
     """The oracle, as it stands, on the host: n_tokens draws through all 60 layers.
     Expert generation (done on demand inside the oracle's provider) is timed separately
     and subtracted."""
@@ -142,6 +142,19 @@ def traffic_from_profiles(kernel_tag: str):
     return d.get("hbm_bytes_per_launch")
 
 
+def calibrate_copy(torch) -> int:
+    """Three copies of 1 GiB between two device buffers: each moves exactly 2^30 bytes in and
+    2^30 bytes out of HBM, which is what the FETCH_SIZE / WRITE_SIZE counters are scaled by."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    dst = torch.empty(n, dtype=torch.uint8, device="cuda:0")
+    for _ in range(3):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"calibration": "device copy", "bytes_read": n, "bytes_written": n, "copies": 3}), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -151,6 +164,9 @@ def main() -> int:
     ap.add_argument("--tokens", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="only run plain 1 GiB device-to-device copies (the reference kernel for scaling "
+                         "the FETCH_SIZE / WRITE_SIZE counters) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only: the whole expert stack fits in one "
@@ -162,6 +178,9 @@ def main() -> int:
         return 2
 
     import torch
+
+    if args.calibrate_copy:
+        return calibrate_copy(torch)
 
     import quantized_expert_ffn_fmoe_amd as fm
     import synth
@@ -247,6 +266,10 @@ def main() -> int:
         "inter_token_expert_reuse": {"all_layers": round(reuse, 4), "layer0": round(reuse_l0, 4)},
     }
     print(json.dumps(out), flush=True)
+    # Release the stack explicitly so that process exit has no device memory left to tear down.
+    del blobs, routers, layers, X, Hout, idx, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
     return 0
 
 

@@ -1,5 +1,5 @@
 // fmoe_decode.hip -- single-token decode through a stack of MoE layers in ONE persistent
-// kernel (one workgroup per compute unit, all co-resident).
+// kernel (one workgroup per compute unit, all co-resident; plain launch, see launch_decode_t).
 //
 // Per layer (aibit.im "Techniques de rupture" item 3 and tr.news.hada.io "Deferred GPU
 // Expert Compute": route, run the k selected experts, combine with the residual, and
@@ -533,15 +533,17 @@ int decode_grid(int* G_out) {
 template <int BITS, int CG, int CD, int HC, int IC, int EC, int KC>
 static int launch_decode_t(const DecodeParams& p, int G, size_t smem, hipStream_t s) {
   auto fn = decode_kernel<BITS, CG, CD, HC, IC, EC, KC>;
-  int occ = 0;
+  // Co-residency: G is the CU count and at least one workgroup fits per CU, so the whole
+  // grid is resident once the device has room for it. A plain launch is enough for that;
+  // every wait inside the kernel is bounded, so a grid that cannot be made resident (other
+  // long kernels holding CUs) ends with the error flag and NaN output, not a hang.
+  int occ = 0, dev = 0, cus = 0;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kDecodeThreads, smem) != hipSuccess) return FMOE_ERR_HIP;
-  if (occ < 1) return FMOE_ERR_SHAPE;
-  DecodeParams q = p;
-  void* args[] = {&q};
-  if (hipLaunchCooperativeKernel(reinterpret_cast<const void*>(fn), dim3(G), dim3(kDecodeThreads), args,
-                                 (unsigned)smem, s) != hipSuccess)
-    return FMOE_ERR_HIP;
-  return FMOE_OK;
+  if (hipGetDevice(&dev) != hipSuccess) return FMOE_ERR_HIP;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return FMOE_ERR_HIP;
+  if (occ < 1 || G > occ * cus) return FMOE_ERR_SHAPE;
+  hipLaunchKernelGGL(fn, dim3(G), dim3(kDecodeThreads), smem, s, p);
+  return hipGetLastError() == hipSuccess ? FMOE_OK : FMOE_ERR_HIP;
 }
 
 int launch_decode(const DecodeParams& p, int G, hipStream_t s) {
