@@ -65,8 +65,8 @@ def lib():
         L.oracle_round_bf16.restype = dbl
         L.oracle_round_bf16.argtypes = [dbl]
         L.oracle_layer_bf16.restype = i32
-        L.oracle_layer_bf16.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32,
-                                        vp, vp, vp, vp, vp, vp, vp, vp]
+        L.oracle_layer_bf16.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
+                                        ctypes.c_double, vp, vp, vp, vp, vp, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -225,7 +225,8 @@ def stack(provider, routers, x, inter, k, bits, group, eps, stop_margin=0.0, kee
     return dict(out=out, idx=idx, w=w, margins=margins, h_all=h_all, layers_done=done)
 
 
-def layer_bf16(provider, layer, router, X, inter, k, bits, group, a16_force=None, want_stages=False):
+def layer_bf16(provider, layer, router, X, inter, k, bits, group, a16_force=None, want_stages=False,
+               prenorm=False, eps=1e-6):
     """O7 (batched bf16 contract). Returns dict(out [T][H], idx [T][k], w [T][k], margins [T],
     a16 [T][k][inter] fp32, g/u [T][k][inter] if want_stages)."""
     router = _c(router, np.float32)
@@ -241,7 +242,7 @@ def layer_bf16(provider, layer, router, X, inter, k, bits, group, a16_force=None
     g = np.empty((T, k, inter), dtype=np.float64) if want_stages else None
     u = np.empty((T, k, inter), dtype=np.float64) if want_stages else None
     rc = lib().oracle_layer_bf16(provider.fn, provider.ctx, layer, _p(router), _p(X), T, H, inter, E, k, bits, group,
-                                 _p(out), _p(idx), _p(w), _p(margins), _p(force), _p(a16), _p(g), _p(u))
+                                 int(bool(prenorm)), float(eps), _p(out), _p(idx), _p(w), _p(margins), _p(force), _p(a16), _p(g), _p(u))
     if rc != 0:
         raise RuntimeError("expert provider failed")
     res = dict(out=out, idx=idx, w=w, margins=margins, a16=a16)

@@ -202,32 +202,31 @@ double oracle_round_bf16(double v) {
 }
 
 /* bf16 sum of w16 * x16 along one row, products and sum in fp64. */
-static double row_dot_bf16(const uint8_t* codes, const uint16_t* scale, const uint16_t* bias, int cols,
-                           int bits, int group, int r, const double* x16) {
+/* One row of exact weights against a bf16-rounded vector, summed in fp64. */
+static double row_dot_x16(const uint8_t* codes, const uint16_t* scale, const uint16_t* bias, int cols, int bits,
+                          int group, int r, const double* x16) {
   double acc = 0.0;
-  for (int c = 0; c < cols; ++c) {
-    double w16 = oracle_round_bf16(oracle_weight(codes, scale, bias, cols, bits, group, r, c));
-    acc += w16 * x16[c];
-  }
+  for (int c = 0; c < cols; ++c) acc += oracle_weight(codes, scale, bias, cols, bits, group, r, c) * x16[c];
   return acc;
 }
 
 int oracle_layer_bf16(oracle_provider_fn provide, void* ctx, int layer, const float* router, const float* x,
-                      int T, int hidden, int inter, int n_experts, int k, int bits, int group, double* out,
-                      int* idx, double* w, double* margins, const float* a16_force, float* a16_out,
-                      double* g_out, double* u_out) {
+                      int T, int hidden, int inter, int n_experts, int k, int bits, int group, int prenorm,
+                      double eps, double* out, int* idx, double* w, double* margins, const float* a16_force,
+                      float* a16_out, double* g_out, double* u_out) {
   double* xv = (double*)malloc(sizeof(double) * (size_t)hidden);
+  double* vv = (double*)malloc(sizeof(double) * (size_t)hidden);
   double* x16 = (double*)malloc(sizeof(double) * (size_t)T * hidden);
   double* ys = (double*)malloc(sizeof(double) * (size_t)T * k * hidden);
   int rc = 0;
-  /* routing of every token on the fp32 input */
+  /* v = rmsnorm(x) or x; routing on v; the experts see v rounded to bf16 */
   for (int t = 0; t < T; ++t) {
-    for (int i = 0; i < hidden; ++i) {
-      xv[i] = (double)x[(size_t)t * hidden + i];
-      x16[(size_t)t * hidden + i] = oracle_round_bf16(xv[i]);
-    }
+    for (int i = 0; i < hidden; ++i) xv[i] = (double)x[(size_t)t * hidden + i];
+    if (prenorm) oracle_rmsnorm(xv, hidden, eps, vv);
+    else memcpy(vv, xv, sizeof(double) * (size_t)hidden);
+    for (int i = 0; i < hidden; ++i) x16[(size_t)t * hidden + i] = oracle_round_bf16(vv[i]);
     double m;
-    oracle_route(router, xv, n_experts, hidden, k, idx + (size_t)t * k, w + (size_t)t * k, NULL, &m);
+    oracle_route(router, vv, n_experts, hidden, k, idx + (size_t)t * k, w + (size_t)t * k, NULL, &m);
     if (margins) margins[t] = m;
   }
   /* every (token, slot) FFN; experts fetched once each (independent computations) */
@@ -249,8 +248,8 @@ int oracle_layer_bf16(oracle_provider_fn provide, void* ctx, int layer, const fl
       const double* xt = x16 + (size_t)t * hidden;
 #pragma omp parallel for schedule(static)
       for (int j = 0; j < inter; ++j) {
-        double g = row_dot_bf16(codes[0], scale[0], bias[0], hidden, bits, group, j, xt);
-        double u = row_dot_bf16(codes[1], scale[1], bias[1], hidden, bits, group, j, xt);
+        double g = row_dot_x16(codes[0], scale[0], bias[0], hidden, bits, group, j, xt);
+        double u = row_dot_x16(codes[1], scale[1], bias[1], hidden, bits, group, j, xt);
         if (g_out) g_out[(size_t)s * inter + j] = g;
         if (u_out) u_out[(size_t)s * inter + j] = u;
         double a = oracle_swiglu(g, u);
@@ -260,7 +259,7 @@ int oracle_layer_bf16(oracle_provider_fn provide, void* ctx, int layer, const fl
       }
 #pragma omp parallel for schedule(static)
       for (int i = 0; i < hidden; ++i)
-        ys[(size_t)s * hidden + i] = row_dot_bf16(codes[2], scale[2], bias[2], inter, bits, group, i, a16);
+        ys[(size_t)s * hidden + i] = row_dot_x16(codes[2], scale[2], bias[2], inter, bits, group, i, a16);
     }
   }
   /* combine + residual per token, slots in rank order */
@@ -275,6 +274,7 @@ int oracle_layer_bf16(oracle_provider_fn provide, void* ctx, int layer, const fl
   }
   free(a16);
   free(xv);
+  free(vv);
   free(x16);
   free(ys);
   return rc;

@@ -90,18 +90,21 @@ int oracle_stack(oracle_provider_fn provide, void* ctx, const float* const* rout
 /* Round-to-nearest-even fp64 -> fp32 -> bf16 value (as double). */
 double oracle_round_bf16(double v);
 
-/* O7: the batched bf16 contract for one layer over T tokens (no pre-norm):
- *   weights w16 = bf16(fp32(q*s+b)), inputs x16 = bf16(x), gate/up sums in fp64,
- *   a = silu(g)*u in fp64, a16 = bf16(fp32(a)), down sums of w16*a16 in fp64,
- *   out = x + sum_k w_k y_k in fp64. Routing is the fp32-router O3 on x.
+/* O7: the batched bf16 contract for one layer over T tokens:
+ *   v = rmsnorm(x) (prenorm != 0) or x, in fp64; routing is O3 on v;
+ *   x16 = bf16(fp32(v)); weights exact (q*s+b); gate/up sums of w*x16 in fp64;
+ *   a = silu(g)*u in fp64, a16 = bf16(fp32(a)); down sums of w*a16 in fp64;
+ *   out = x + sum_k w_k y_k in fp64.
+ * Only the two activation vectors are rounded to bf16: the codes are small integers and
+ * the affine terms apply per group, so the weights themselves need no rounding.
  * x: [T][hidden]. out: [T][hidden]. idx, w: [T][k]. margins: [T] (nullable).
  * a16_force (nullable) [T][k][inter]: use these a16 values instead of the oracle's own
  * (teacher forcing of the down stage). a16_out (nullable) [T][k][inter]: the oracle's a16.
  * g_out/u_out (nullable) [T][k][inter]: gate/up sums. */
 int oracle_layer_bf16(oracle_provider_fn provide, void* ctx, int layer, const float* router, const float* x,
-                      int T, int hidden, int inter, int n_experts, int k, int bits, int group, double* out,
-                      int* idx, double* w, double* margins, const float* a16_force, float* a16_out,
-                      double* g_out, double* u_out);
+                      int T, int hidden, int inter, int n_experts, int k, int bits, int group, int prenorm,
+                      double eps, double* out, int* idx, double* w, double* margins, const float* a16_force,
+                      float* a16_out, double* g_out, double* u_out);
 
 #ifdef __cplusplus
 }

@@ -381,37 +381,43 @@ def test_round_bf16_matches_torch():
 
 
 def test_layer_bf16_contract():
+    """O7, the batched contract: only v and a are rounded to bf16 (round-to-nearest-even via
+    torch), weights stay exact, sums are exact fp64 algebra on those values."""
     rng = np.random.default_rng(17)
     E, H, I, k, T = 8, 128, 64, 2, 5
     experts, routers = _tiny_model(rng, 1, E, H, I, 4)
     prov = oracle.ArrayProvider(experts)
     X = rng.standard_normal((T, H)).astype(np.float32)
-    res = oracle.layer_bf16(prov, 0, routers[0], X, I, k, 4, 64, want_stages=True)
     tb = lambda a: torch.tensor(np.asarray(a, dtype=np.float32)).to(torch.bfloat16).double().numpy()
-    for t in range(T):
-        i_ref, w_ref, _, m_ref = oracle.route(routers[0], X[t].astype(np.float64), k)
-        assert res["idx"][t].tolist() == i_ref.tolist()
-        assert np.allclose(res["w"][t], w_ref, rtol=0, atol=0)
-        ref = X[t].astype(np.float64).copy()
-        for j in range(k):
-            mats = experts[0][i_ref[j]]
-            Wg16 = tb(dense_decode(*mats[0], I, H, 4, 64))
-            Wu16 = tb(dense_decode(*mats[1], I, H, 4, 64))
-            Wd16 = tb(dense_decode(*mats[2], H, I, 4, 64))
-            x16 = tb(X[t])
-            g, u = Wg16 @ x16, Wu16 @ x16
-            assert np.allclose(res["g"][t, j], g, rtol=1e-13, atol=1e-13)
-            assert np.allclose(res["u"][t, j], u, rtol=1e-13, atol=1e-13)
-            a16 = tb(g * scipy.special.expit(g) * u)
-            assert np.array_equal(res["a16"][t, j].astype(np.float64), a16)
-            ref += w_ref[j] * (Wd16 @ a16)
-        assert np.allclose(res["out"][t], ref, rtol=1e-12, atol=1e-12)
-    # teacher forcing with the oracle's own a16 changes nothing
-    forced = oracle.layer_bf16(prov, 0, routers[0], X, I, k, 4, 64, a16_force=res["a16"])
-    assert np.array_equal(forced["out"], res["out"])
-    # batch invariance: one token at a time gives the same rows
-    one = oracle.layer_bf16(prov, 0, routers[0], X[2:3], I, k, 4, 64)
-    assert np.array_equal(one["out"][0], res["out"][2])
-    # sanity band against the full-precision layer
-    full, _, _, _ = oracle.moe_layer(prov, 0, routers[0], X[2].astype(np.float64), I, k, 4, 64, 0, 1e-6)
-    assert np.linalg.norm(res["out"][2] - full) <= 1e-2 * np.linalg.norm(full)
+    for prenorm in (False, True):
+        res = oracle.layer_bf16(prov, 0, routers[0], X, I, k, 4, 64, want_stages=True, prenorm=prenorm, eps=1e-6)
+        for t in range(T):
+            xt = X[t].astype(np.float64)
+            v = xt / np.sqrt(np.mean(xt * xt) + 1e-6) if prenorm else xt
+            i_ref, w_ref, _, _ = oracle.route(routers[0], v, k)
+            assert res["idx"][t].tolist() == i_ref.tolist()
+            assert np.allclose(res["w"][t], w_ref, rtol=1e-15, atol=0)
+            ref = xt.copy()
+            for j in range(k):
+                mats = experts[0][i_ref[j]]
+                Wg = dense_decode(*mats[0], I, H, 4, 64)
+                Wu = dense_decode(*mats[1], I, H, 4, 64)
+                Wd = dense_decode(*mats[2], H, I, 4, 64)
+                x16 = tb(v)
+                g, u = Wg @ x16, Wu @ x16
+                assert np.allclose(res["g"][t, j], g, rtol=1e-13, atol=1e-13)
+                assert np.allclose(res["u"][t, j], u, rtol=1e-13, atol=1e-13)
+                a16 = tb(g * scipy.special.expit(g) * u)
+                assert np.array_equal(res["a16"][t, j].astype(np.float64), a16)
+                ref += w_ref[j] * (Wd @ a16)
+            assert np.allclose(res["out"][t], ref, rtol=1e-12, atol=1e-12)
+        # teacher forcing with the oracle's own a16 changes nothing
+        forced = oracle.layer_bf16(prov, 0, routers[0], X, I, k, 4, 64, a16_force=res["a16"], prenorm=prenorm)
+        assert np.array_equal(forced["out"], res["out"])
+        # batch invariance: one token at a time gives the same rows
+        one = oracle.layer_bf16(prov, 0, routers[0], X[2:3], I, k, 4, 64, prenorm=prenorm)
+        assert np.array_equal(one["out"][0], res["out"][2])
+        # sanity band against the full-precision layer
+        full, _, _, _ = oracle.moe_layer(prov, 0, routers[0], X[2].astype(np.float64), I, k, 4, 64,
+                                         1 if prenorm else 0, 1e-6)
+        assert np.linalg.norm(res["out"][2] - full) <= 1e-2 * np.linalg.norm(full)
