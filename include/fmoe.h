@@ -142,7 +142,8 @@ int fmoe_dequant_matvec(const fmoe_qmat* W, const float* x, float* y, int n_vec,
  *                  NaN ranks last
  *   w[t][j]      = exp(l_j - l_0) / sum_{j'<k} exp(l_j' - l_0)    (softmax over the k)
  * router: fp32 [n_experts][hidden]; x: fp32 [n_tokens][hidden]; idx: int32
- * [n_tokens][k]; w: fp32 [n_tokens][k]; logits: fp32 [n_tokens][n_experts] or NULL.
+ * [n_tokens][k]; w: fp32 [n_tokens][k]; logits: fp32 [n_tokens][n_experts] (required:
+ * it is the scratch between the two steps).
  * Limits: 1 <= n_experts <= 4096, hidden multiple of 64 and <= 16384, 1 <= k <= 16.
  */
 int fmoe_route_topk(const float* router, const float* x, int n_tokens, int n_experts, int hidden, int k,
@@ -170,16 +171,33 @@ int fmoe_expert_ffn(const fmoe_expert* e, const float* x, float* y, void* ws, si
  * [n_tokens][n_layers][k]; w_out (nullable): fp32 [n_tokens][n_layers][k].
  * n_tokens == 1 runs the single-token decode path (one persistent kernel for all
  * layers). n_tokens > 1 runs the batched path: tokens are grouped by expert and each
- * expert's gate/up/down run as bf16 matrix-core GEMMs with fp32 accumulation (weights
- * dequantized to fp32 then rounded to bf16; inputs and the SwiGLU output rounded to
- * bf16); routing and the combine stay fp32.
- * All layers must share n_experts, hidden, inter, bits and group. Limits: hidden ==
- * 4096 or a multiple of 256 up to 8192 ... see fmoe_workspace_bytes; n_tokens <= 4096;
- * n_layers <= 4096.
+ * expert's gate/up/down run as bf16 matrix-core products with fp32 accumulation. The
+ * codes enter the matrix cores exactly and each group's scale and bias are applied to
+ * its fp32 partial sums, so no weight is rounded; the activations v (the input of
+ * gate/up) and a = silu(g) * u (the input of down) are rounded to bf16. Routing, the
+ * norm and the combine stay fp32.
+ * All layers must share n_experts, hidden, inter, bits, group and expert_stride.
+ * Limits: 64 <= hidden, inter <= 8192 (multiples of 64), 1 <= n_experts <= 4096,
+ * 1 <= k <= min(16, n_experts), n_tokens <= 4096, n_layers <= 4096; the batched path
+ * (n_tokens > 1) also needs hidden % 256 == 0 and inter % 128 == 0; the decode path
+ * needs its per-workgroup state (the staged vectors, the logits and the selection)
+ * within 64 KB of LDS (FMOE_ERR_SHAPE otherwise); at hidden 4096, inter 1024, k 4 that
+ * holds up to 4096 experts.
+ * Pointers: x_in, h_out 16-byte aligned; experts 256-byte aligned; ws 256-byte aligned.
  */
 int fmoe_moe_layer(const fmoe_layer* layers, int n_layers, const float* x_in, float* h_out, int n_tokens, int k,
                    float eps, unsigned flags, int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes,
                    fmoe_stream_t stream);
+
+/*
+ * Inspection of the batched path's SwiGLU stage (for verifying it stage by stage). After
+ * an fmoe_moe_layer call with n_tokens > 1 that used workspace `ws` (same n_tokens,
+ * hidden, inter, n_experts, k and bits), enqueue on `stream` a copy of the last layer's
+ * bf16 SwiGLU outputs: a16_out[t][j][c] = bf16(silu(g) * u) for token t, slot j (the
+ * j-th selected expert), row c, as bf16 bit patterns [n_tokens][k][inter] (device memory).
+ */
+int fmoe_batched_a16(const void* ws, size_t ws_bytes, int n_tokens, int hidden, int inter, int n_experts, int k,
+                     int bits, uint16_t* a16_out, fmoe_stream_t stream);
 
 #ifdef __cplusplus
 }

@@ -23,7 +23,7 @@ OP_EXPERT_FFN, OP_MOE_LAYER = 1, 2
 
 EXPORTS = ("fmoe_status_string", "fmoe_version", "fmoe_codes_bytes", "fmoe_sb_bytes", "fmoe_expert_bytes",
            "fmoe_expert_view", "fmoe_pack", "fmoe_workspace_bytes", "fmoe_dequant_matvec", "fmoe_route_topk",
-           "fmoe_expert_ffn", "fmoe_moe_layer")
+           "fmoe_expert_ffn", "fmoe_moe_layer", "fmoe_batched_a16")
 
 
 class FmoeError(RuntimeError):
@@ -84,6 +84,8 @@ def lib():
         L.fmoe_moe_layer.restype = i32
         L.fmoe_moe_layer.argtypes = [ctypes.POINTER(Layer), i32, vp, vp, i32, i32, ctypes.c_float, u32, vp, vp, vp,
                                      sz, vp]
+        L.fmoe_batched_a16.restype = i32
+        L.fmoe_batched_a16.argtypes = [vp, sz, i32, i32, i32, i32, i32, i32, vp, vp]
         _lib = L
     return _lib
 
@@ -177,3 +179,9 @@ def moe_layer(layers, x_in, h_out, n_tokens, k, eps, flags, idx_out, w_out, ws, 
         layers = layers_array(layers)
     _check(lib().fmoe_moe_layer(layers, len(layers), _ptr(x_in), _ptr(h_out), n_tokens, k, eps, flags, _ptr(idx_out),
                                 _ptr(w_out), _ptr(ws), ws_bytes, _stream(stream)), "fmoe_moe_layer")
+
+
+def batched_a16(ws, ws_bytes, n_tokens, hidden, inter, n_experts, k, bits, a16_out, stream=None) -> None:
+    """bf16 SwiGLU outputs [n_tokens][k][inter] of the last batched fmoe_moe_layer call on ws."""
+    _check(lib().fmoe_batched_a16(_ptr(ws), ws_bytes, n_tokens, hidden, inter, n_experts, k, bits, _ptr(a16_out),
+                                  _stream(stream)), "fmoe_batched_a16")

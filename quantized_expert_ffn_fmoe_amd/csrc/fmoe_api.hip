@@ -238,12 +238,14 @@ int fmoe_moe_layer(const fmoe_layer* layers, int n_layers, const float* x_in, fl
   if (w_out && (overlaps(w_out, nk, x_in, nx) || overlaps(w_out, nk, h_out, nx) || overlaps(w_out, nk, ws, ws_bytes) ||
                 (idx_out && overlaps(w_out, nk, idx_out, nk))))
     return FMOE_ERR_OVERLAP;
+  if (n_tokens > 1 && !batched_shape_ok(H, I)) return FMOE_ERR_SHAPE;
   int rc = check_device();
   if (rc) return rc;
   hipStream_t s = (hipStream_t)stream;
 
-  if (n_tokens > 1)
+  if (n_tokens > 1) {
     return launch_batched(layers, n_layers, x_in, h_out, n_tokens, k, eps, flags, idx_out, w_out, ws, ws_bytes, s);
+  }
 
   // single-token decode: one persistent kernel per block of up to 64 layers
   int lpr_g, cpl_g, lpr_d, cpl_d;
@@ -291,6 +293,22 @@ int fmoe_moe_layer(const fmoe_layer* layers, int n_layers, const float* x_in, fl
     if ((rc = launch_decode(p, G, s))) return rc;
   }
   return FMOE_OK;
+}
+
+int fmoe_batched_a16(const void* ws, size_t ws_bytes, int n_tokens, int hidden, int inter, int n_experts, int k,
+                     int bits, uint16_t* a16_out, fmoe_stream_t stream) {
+  if (!ws || !a16_out) return FMOE_ERR_NULL;
+  if (bits != 2 && bits != 4) return FMOE_ERR_BITS;
+  if (n_tokens < 2 || n_tokens > 4096 || n_experts < 1 || n_experts > 4096) return FMOE_ERR_SHAPE;
+  if (hidden < 256 || hidden > 8192 || inter < 128 || inter > 8192 || !batched_shape_ok(hidden, inter))
+    return FMOE_ERR_SHAPE;
+  if (k < 1 || k > 16 || k > n_experts) return FMOE_ERR_K;
+  if (ws_bytes < batched_workspace_bytes(n_tokens, hidden, inter, n_experts, k)) return FMOE_ERR_WORKSPACE;
+  if (!aligned(ws, 256) || !aligned(a16_out, 2)) return FMOE_ERR_ALIGN;
+  if (overlaps(a16_out, (size_t)n_tokens * k * inter * 2, ws, ws_bytes)) return FMOE_ERR_OVERLAP;
+  int rc = check_device();
+  if (rc) return rc;
+  return launch_batched_a16(ws, n_tokens, hidden, inter, n_experts, k, bits, a16_out, (hipStream_t)stream);
 }
 
 }  // extern "C"

@@ -9,7 +9,10 @@
 
 namespace fmoe {
 
+bool batched_shape_ok(int hidden, int inter);
 size_t batched_workspace_bytes(int n_tokens, int hidden, int inter, int n_experts, int k);
+int launch_batched_a16(const void* ws, int n_tokens, int hidden, int inter, int n_experts, int k, int bits,
+                       uint16_t* out, hipStream_t s);
 int launch_batched(const fmoe_layer* layers, int n_layers, const float* x_in, float* h_out, int n_tokens, int k,
                    float eps, unsigned flags, int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes,
                    hipStream_t s);

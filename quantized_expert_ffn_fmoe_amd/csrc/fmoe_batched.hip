@@ -1,13 +1,624 @@
-// fmoe_batched.hip -- placeholder until the grouped bf16 matrix-core path is in.
+// fmoe_batched.hip -- the multi-token path of fmoe_moe_layer: tokens grouped by expert,
+// each expert's gate/up and down projections as bf16 matrix-core products (gfx950
+// v_mfma_f32_16x16x32_bf16) with fp32 accumulation.
+//
+// Per layer (the same block as the decode path: route, run the selected experts, combine
+// with the residual; aibit.im "Techniques de rupture" items 3-4, tr.news.hada.io "Model
+// mimarisi"), with the batch of tokens sorted by expert so that every expert's weights
+// are read once per call:
+//   1. stage: v = h (or rmsnorm(h)); its bf16 image v16 in operand order and, per group
+//      of 64 columns, the fp32 sum of the bf16 values;
+//   2. route: fp32 router logits and top-k with softmax (the standalone route kernels);
+//   3. sort: counting sort of the (token, slot) pairs by expert; the list of experts
+//      that received at least one pair;
+//   4. gate/up: per (active expert, block of 128 rows): g and u for all of the expert's
+//      tokens, a = silu(g) * u, rounded to bf16 (a16) in the down operand's order, plus
+//      the group sums of a16;
+//   5. down: per (active expert, block of 256 rows): y = Wd a16 for the expert's tokens,
+//      one fp32 row per (token, slot) pair;
+//   6. combine: h' = h + sum_j w_j y_j in slot order.
+//
+// Matrix-core form of the affine dequantization. A weight is q*s + b with (s, b) per
+// group of 64 columns of a row (the nibble*scale+bias form of aibit.im "Techniques de
+// rupture" item 2). The codes enter the bf16 matrix core as the exact values
+// c = 1 + q/16 (4-bit; bf16 bits 0x3F80 | q << 3) or c = 1 + q/4 (2-bit; 0x3F80 | q << 5),
+// built from a code dword with one shift and one and-or per pair of codes. For one group,
+// with X = sum of the group's bf16 activations and P = sum x*c from the matrix core,
+//   sum x (q s + b) = F s P + (b - F s) X,   F = 16 (4-bit) or 4 (2-bit),
+// applied once per group to the fp32 partial product (the per-group factorisation
+// s*sum(q x) + b*sum(x)). No weight is rounded; only v and a are (to bf16).
+//
+// Operand order. For 16x16x32 bf16 products lane l holds, for the A operand, row l % 16
+// and the 8 consecutive K indices 8*(l/16)..+7; the same for B with column l % 16; the
+// result holds D[4*(l/16) + i][l % 16] in element i. Tokens are the rows (A), weight rows
+// the columns (B). Within one group of 64 K indices, lane block kb = l/16 takes the 16
+// columns 16*kb..+15 (two products of 8), so a lane reads 8 (4-bit) or 4 (2-bit) code
+// bytes of its row per group. Because the pairs of codes come out of a code dword as
+// (q_j, q_j+4) (4-bit) or (q_j, q_j+8) (2-bit), the activation operands are stored
+// permuted within every block of 16 columns the same way (perm_col / perm_pos).
+#include <stdint.h>
+
 #include "fmoe_batched.h"
+#include "fmoe_device.h"
+#include "fmoe_internal.h"
 
 namespace fmoe {
+namespace {
 
-size_t batched_workspace_bytes(int, int, int, int, int) { return 256; }
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-int launch_batched(const fmoe_layer*, int, const float*, float*, int, int, float, unsigned, int32_t*, float*, void*,
-                   size_t, hipStream_t) {
-  return FMOE_ERR_SHAPE;
+constexpr int kBT = 256;          // threads per workgroup
+constexpr int kGuRowsWave = 32;   // rows of gate (and of up) per wave
+constexpr int kGuRowsWg = 128;
+constexpr int kDnRowsWave = 64;   // rows of down per wave
+constexpr int kDnRowsWg = 256;
+constexpr int kMaxMT = 4;         // 16-token tiles per pass over an expert's weights
+constexpr int kSortThreads = 1024;
+
+// Column (0..15) of a 16-column block held at operand position p.
+template <int BITS>
+__host__ __device__ constexpr int perm_col(int p) {
+  return BITS == 4 ? 8 * (p >> 3) + ((p & 7) >> 1) + 4 * (p & 1) : 4 * (p >> 3) + ((p & 7) >> 1) + 8 * (p & 1);
+}
+// Operand position of column c (inverse of perm_col).
+template <int BITS>
+__host__ __device__ constexpr int perm_pos(int c) {
+  return BITS == 4 ? 8 * (c >> 3) + 2 * (c & 3) + ((c & 7) >> 2) : 8 * ((c & 7) >> 2) + 2 * (c & 3) + (c >> 3);
+}
+
+// fp32 -> bf16 bits, round to nearest even (NaN stays NaN).
+__device__ __forceinline__ uint32_t bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0u;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return u >> 16;
+}
+__device__ __forceinline__ float bf16_val(uint32_t b) { return __uint_as_float(b << 16); }
+
+template <int SH>
+__device__ __forceinline__ uint32_t shift(uint32_t w) {
+  if constexpr (SH >= 0) return w >> SH;
+  else return w << (-SH);
+}
+
+// The two 8-element B operands of one group from this lane's code bytes (see header).
+template <int BITS>
+__device__ __forceinline__ void build_b(const uint32_t* w, u32x4& b0, u32x4& b1) {
+  if constexpr (BITS == 4) {
+    // w[h] holds columns 8h..8h+7 of the lane's 16, nibble p = column 8h + p
+    b0.x = 0x3F803F80u | (shift<-3>(w[0]) & 0x00780078u);
+    b0.y = 0x3F803F80u | (shift<1>(w[0]) & 0x00780078u);
+    b0.z = 0x3F803F80u | (shift<5>(w[0]) & 0x00780078u);
+    b0.w = 0x3F803F80u | (shift<9>(w[0]) & 0x00780078u);
+    b1.x = 0x3F803F80u | (shift<-3>(w[1]) & 0x00780078u);
+    b1.y = 0x3F803F80u | (shift<1>(w[1]) & 0x00780078u);
+    b1.z = 0x3F803F80u | (shift<5>(w[1]) & 0x00780078u);
+    b1.w = 0x3F803F80u | (shift<9>(w[1]) & 0x00780078u);
+  } else {
+    // w[0] holds the lane's 16 columns, column i in bits 2i; half h, pair j takes columns
+    // 4h + j and 4h + j + 8
+    const uint32_t d = w[0];
+    b0.x = 0x3F803F80u | (shift<-5>(d) & 0x00600060u);
+    b0.y = 0x3F803F80u | (shift<-3>(d) & 0x00600060u);
+    b0.z = 0x3F803F80u | (shift<-1>(d) & 0x00600060u);
+    b0.w = 0x3F803F80u | (shift<1>(d) & 0x00600060u);
+    b1.x = 0x3F803F80u | (shift<3>(d) & 0x00600060u);
+    b1.y = 0x3F803F80u | (shift<5>(d) & 0x00600060u);
+    b1.z = 0x3F803F80u | (shift<7>(d) & 0x00600060u);
+    b1.w = 0x3F803F80u | (shift<9>(d) & 0x00600060u);
+  }
+}
+
+__device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
+                                                 0, 0);
+}
+
+struct BParams {
+  const uint8_t* experts;
+  size_t stride;
+  int H, I, k;
+  const int32_t* pairs;    // [P] pair ids (t * k + j) sorted by expert
+  const int32_t* act_e;    // [n_act] active experts
+  const int32_t* act_off;  // [n_act] first position in pairs
+  const int32_t* act_cnt;  // [n_act] number of pairs
+  const int32_t* n_act;
+  const uint16_t* v16;  // [T][H] bf16, operand order
+  const float* xg;      // [T][H/64] group sums of v16
+  uint16_t* a16;        // [P][I] bf16, operand order (pair-id rows)
+  float* ag;            // [P][I/64] group sums of a16
+  float* ys;            // [P][H] down outputs (pair-id rows)
+};
+
+// ---------------------------------------------------------------- 1. stage
+template <int BITS>
+__global__ void __launch_bounds__(kBT) stage_kernel(const float* __restrict__ h, int H, int prenorm, float eps,
+                                                    float* __restrict__ v, uint16_t* __restrict__ v16,
+                                                    float* __restrict__ xg) {
+  const int t = blockIdx.x;
+  const float* hr = h + (size_t)t * H;
+  __shared__ float red[kBT / 64];
+  float inv = 1.f;
+  if (prenorm) {
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < H / 4; i += kBT) {
+      const float4 q = reinterpret_cast<const float4*>(hr)[i];
+      ss = fmaf(q.x, q.x, ss);
+      ss = fmaf(q.y, q.y, ss);
+      ss = fmaf(q.z, q.z, ss);
+      ss = fmaf(q.w, q.w, ss);
+    }
+    ss = wave_sum(ss);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int w = 0; w < kBT / 64; ++w) tot += red[w];
+    inv = 1.0f / sqrtf(tot / (float)H + eps);
+  }
+  // one 16-column block per thread; the 4 blocks of a group sit on 4 consecutive lanes
+  for (int blk = threadIdx.x; blk < H / 16; blk += kBT) {
+    float x[16];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const float4 f = reinterpret_cast<const float4*>(hr + blk * 16)[q];
+      x[4 * q] = f.x * inv;
+      x[4 * q + 1] = f.y * inv;
+      x[4 * q + 2] = f.z * inv;
+      x[4 * q + 3] = f.w * inv;
+    }
+    float* vo = v + (size_t)t * H + blk * 16;
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      reinterpret_cast<float4*>(vo)[q] = make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
+    uint32_t r[16];
+    float s = 0.f;
+#pragma unroll
+    for (int c = 0; c < 16; ++c) {
+      r[c] = bf16_rne(x[c]);
+      s += bf16_val(r[c]);
+    }
+    uint32_t o[8];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) o[q] = r[perm_col<BITS>(2 * q)] | (r[perm_col<BITS>(2 * q + 1)] << 16);
+    u32x4* dst = reinterpret_cast<u32x4*>(v16 + (size_t)t * H + blk * 16);
+    dst[0] = u32x4{o[0], o[1], o[2], o[3]};
+    dst[1] = u32x4{o[4], o[5], o[6], o[7]};
+    s = group_sum(s, 4);
+    if ((blk & 3) == 0) xg[(size_t)t * (H / 64) + blk / 4] = s;
+  }
+}
+
+// ---------------------------------------------------------------- 3. sort by expert
+// One workgroup. Pair s = t * k + j goes to expert idx[s]; pairs of one expert are
+// contiguous in `pairs` (their order inside an expert does not affect any result: every
+// token's rows are computed independently).
+__global__ void __launch_bounds__(kSortThreads) sort_kernel(const int32_t* __restrict__ idx, int P, int E,
+                                                            int32_t* __restrict__ pairs, int32_t* __restrict__ act_e,
+                                                            int32_t* __restrict__ act_off,
+                                                            int32_t* __restrict__ act_cnt, int32_t* __restrict__ n_act) {
+  extern __shared__ int sh[];
+  int* cnt = sh;        // [E]
+  int* cur = sh + E;    // [E]
+  int* sc = sh + 2 * E; // [2][kSortThreads]
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += kSortThreads) cnt[e] = 0;
+  __syncthreads();
+  for (int s = tid; s < P; s += kSortThreads) atomicAdd(&cnt[idx[s]], 1);
+  __syncthreads();
+  const int per = (E + kSortThreads - 1) / kSortThreads;
+  const int lo = min(tid * per, E), hi = min(lo + per, E);
+  int c = 0, a = 0;
+  for (int e = lo; e < hi; ++e) {
+    c += cnt[e];
+    a += cnt[e] > 0;
+  }
+  // inclusive scans of (c, a) over the threads (Hillis-Steele)
+  sc[tid] = c;
+  sc[kSortThreads + tid] = a;
+  __syncthreads();
+  for (int d = 1; d < kSortThreads; d <<= 1) {
+    const int vc = sc[tid] + (tid >= d ? sc[tid - d] : 0);
+    const int va = sc[kSortThreads + tid] + (tid >= d ? sc[kSortThreads + tid - d] : 0);
+    __syncthreads();
+    sc[tid] = vc;
+    sc[kSortThreads + tid] = va;
+    __syncthreads();
+  }
+  int off = sc[tid] - c, act = sc[kSortThreads + tid] - a;
+  for (int e = lo; e < hi; ++e) {
+    cur[e] = off;
+    if (cnt[e] > 0) {
+      act_e[act] = e;
+      act_off[act] = off;
+      act_cnt[act] = cnt[e];
+      ++act;
+    }
+    off += cnt[e];
+  }
+  if (tid == kSortThreads - 1) *n_act = sc[kSortThreads + tid];
+  __syncthreads();
+  for (int s = tid; s < P; s += kSortThreads) pairs[atomicAdd(&cur[idx[s]], 1)] = s;
+}
+
+// ---------------------------------------------------------------- 4./5. expert products
+// Token operand of one m-tile: lane row nl of the tile, K block kb.
+struct TokRow {
+  const uint16_t* p;  // start of the lane's 16 columns in group 0
+  bool valid;
+};
+
+// Stage the per-group activation sums of the pass's m-tiles: xs[mt][g][m].
+__device__ __forceinline__ void stage_sums(float* xs, const BParams& p, const float* sums, int G, int off, int cnt,
+                                           int m0, int nmt, bool by_token) {
+  for (int i = threadIdx.x; i < nmt * G * 16; i += kBT) {
+    const int m = i & 15, g = (i >> 4) % G, mt = (i >> 4) / G;
+    const int r = m0 + mt * 16 + m;
+    float val = 0.f;
+    if (r < cnt) {
+      const int s = p.pairs[off + r];
+      const int row = by_token ? s / p.k : s;
+      val = sums[(size_t)row * G + g];
+    }
+    xs[(mt * G + g) * 16 + m] = val;
+  }
+}
+
+// acc[mt][tile] += the affine group products of one group g for NT weight tiles.
+template <int BITS, int NT>
+__device__ __forceinline__ void group_products(f32x4 (&acc)[kMaxMT][NT], const uint8_t* const (&cptr)[NT],
+                                               const uint32_t* const (&sptr)[NT], const TokRow (&tr)[kMaxMT],
+                                               const float* xs, int G, int g, int nmt, int kb) {
+  constexpr int BPG = BITS * 8;  // code bytes per row per group
+  constexpr float F = BITS == 4 ? 16.f : 4.f;
+  u32x4 b0[NT], b1[NT];
+  float cs[NT], cb[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    uint32_t w[2];
+    if constexpr (BITS == 4) {
+      const uint2 q = *reinterpret_cast<const uint2*>(cptr[t] + (size_t)g * BPG);
+      w[0] = q.x;
+      w[1] = q.y;
+    } else {
+      w[0] = *reinterpret_cast<const uint32_t*>(cptr[t] + (size_t)g * BPG);
+      w[1] = 0;
+    }
+    build_b<BITS>(w, b0[t], b1[t]);
+    const uint32_t sb = sptr[t][g];
+    cs[t] = F * bf16_lo(sb);
+    cb[t] = bf16_hi(sb) - cs[t];
+  }
+  const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int mt = 0; mt < kMaxMT; ++mt) {
+    if (mt < nmt) {
+      u32x4 a0 = {0u, 0u, 0u, 0u}, a1 = {0u, 0u, 0u, 0u};
+      if (tr[mt].valid) {
+        const u32x4* ap = reinterpret_cast<const u32x4*>(tr[mt].p + (size_t)g * 64);
+        a0 = ap[0];
+        a1 = ap[1];
+      }
+      const float4 x4 = *reinterpret_cast<const float4*>(xs + (mt * G + g) * 16 + 4 * kb);
+#pragma unroll
+      for (int t = 0; t < NT; ++t) {
+        f32x4 P = mfma(a0, b0[t], zero);
+        P = mfma(a1, b1[t], P);
+        acc[mt][t][0] = fmaf(cb[t], x4.x, fmaf(cs[t], P[0], acc[mt][t][0]));
+        acc[mt][t][1] = fmaf(cb[t], x4.y, fmaf(cs[t], P[1], acc[mt][t][1]));
+        acc[mt][t][2] = fmaf(cb[t], x4.z, fmaf(cs[t], P[2], acc[mt][t][2]));
+        acc[mt][t][3] = fmaf(cb[t], x4.w, fmaf(cs[t], P[3], acc[mt][t][3]));
+      }
+    }
+  }
+}
+
+template <int BITS>
+__global__ void __launch_bounds__(kBT) gate_up_kernel(BParams p) {
+  const int item = blockIdx.y;
+  if (item >= *p.n_act) return;
+  const int e = p.act_e[item], off = p.act_off[item], cnt = p.act_cnt[item];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nl = lane & 15, kb = lane >> 4;
+  const int H = p.H, I = p.I, G = H / 64;
+  const uint8_t* blob = p.experts + (size_t)e * p.stride;
+  const size_t cbytes = (size_t)I * H * BITS / 8, sbytes = (size_t)I * G * 4;
+  const size_t rowb = (size_t)H * BITS / 8;
+  const int row0 = blockIdx.x * kGuRowsWg + wave * kGuRowsWave;
+  const uint8_t* cptr[4];
+  const uint32_t* sptr[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int r = row0 + 16 * (t & 1) + nl;
+    const size_t mat = t < 2 ? 0 : 1;  // gate, up
+    cptr[t] = blob + mat * cbytes + r * rowb + kb * (BITS * 2);
+    sptr[t] = reinterpret_cast<const uint32_t*>(blob + 3 * cbytes + mat * sbytes) + (size_t)r * G;
+  }
+  extern __shared__ float xs[];                 // [kMaxMT][G][16]
+  __shared__ float agp[kBT / 64][kMaxMT][16];  // per-wave sums of a16 over its 32 rows
+  const int Gd = I / 64;
+  for (int m0 = 0; m0 < cnt; m0 += 16 * kMaxMT) {
+    const int nmt = min(kMaxMT, (cnt - m0 + 15) / 16);
+    __syncthreads();
+    stage_sums(xs, p, p.xg, G, off, cnt, m0, nmt, true);
+    __syncthreads();
+    TokRow tr[kMaxMT];
+#pragma unroll
+    for (int mt = 0; mt < kMaxMT; ++mt) {
+      const int r = m0 + mt * 16 + nl;
+      tr[mt].valid = mt < nmt && r < cnt;
+      tr[mt].p = p.v16 + (tr[mt].valid ? (size_t)(p.pairs[off + r] / p.k) * H : 0) + kb * 16;
+    }
+    f32x4 acc[kMaxMT][4];
+#pragma unroll
+    for (int mt = 0; mt < kMaxMT; ++mt)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < G; ++g) group_products<BITS, 4>(acc, cptr, sptr, tr, xs, G, g, nmt, kb);
+    // epilogue: a = silu(g) * u -> bf16; group sums of the rounded values
+#pragma unroll
+    for (int mt = 0; mt < kMaxMT; ++mt) {
+      if (mt < nmt) {
+        float part[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+          const int n = row0 + 16 * t + nl;
+          const int col = (n & ~15) + perm_pos<BITS>(n & 15);
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int r = m0 + mt * 16 + 4 * kb + i;
+            const uint32_t b = bf16_rne(swiglu(acc[mt][t][i], acc[mt][t + 2][i]));
+            if (r < cnt) {
+              p.a16[(size_t)p.pairs[off + r] * I + col] = (uint16_t)b;
+              part[i] += bf16_val(b);
+            }
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part[i] = group_sum(part[i], 16);
+        if (nl == 0) {
+#pragma unroll
+          for (int i = 0; i < 4; ++i) agp[wave][mt][4 * kb + i] = part[i];
+        }
+      }
+    }
+    __syncthreads();
+    // waves 2q and 2q+1 cover the 64 rows of down group 2 * blockIdx.x + q
+    for (int i = threadIdx.x; i < 2 * nmt * 16; i += kBT) {
+      const int q = i / (nmt * 16), rest = i % (nmt * 16), mt = rest / 16, m = rest % 16;
+      const int r = m0 + mt * 16 + m;
+      if (r < cnt)
+        p.ag[(size_t)p.pairs[off + r] * Gd + 2 * blockIdx.x + q] = agp[2 * q][mt][m] + agp[2 * q + 1][mt][m];
+    }
+  }
+}
+
+template <int BITS>
+__global__ void __launch_bounds__(kBT) down_kernel(BParams p) {
+  const int item = blockIdx.y;
+  if (item >= *p.n_act) return;
+  const int e = p.act_e[item], off = p.act_off[item], cnt = p.act_cnt[item];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nl = lane & 15, kb = lane >> 4;
+  const int H = p.H, I = p.I, G = I / 64;
+  const uint8_t* blob = p.experts + (size_t)e * p.stride;
+  const size_t cbytes = (size_t)I * H * BITS / 8, sbytes = (size_t)H * G * 4;
+  const size_t rowb = (size_t)I * BITS / 8;
+  const int row0 = blockIdx.x * kDnRowsWg + wave * kDnRowsWave;
+  const uint8_t* cptr[4];
+  const uint32_t* sptr[4];
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const int r = row0 + 16 * t + nl;
+    cptr[t] = blob + 2 * cbytes + r * rowb + kb * (BITS * 2);
+    sptr[t] = reinterpret_cast<const uint32_t*>(blob + 3 * cbytes + 2 * sbytes) + (size_t)r * G;
+  }
+  extern __shared__ float xs[];  // [kMaxMT][G][16]
+  for (int m0 = 0; m0 < cnt; m0 += 16 * kMaxMT) {
+    const int nmt = min(kMaxMT, (cnt - m0 + 15) / 16);
+    __syncthreads();
+    stage_sums(xs, p, p.ag, G, off, cnt, m0, nmt, false);
+    __syncthreads();
+    TokRow tr[kMaxMT];
+#pragma unroll
+    for (int mt = 0; mt < kMaxMT; ++mt) {
+      const int r = m0 + mt * 16 + nl;
+      tr[mt].valid = mt < nmt && r < cnt;
+      tr[mt].p = p.a16 + (tr[mt].valid ? (size_t)p.pairs[off + r] * I : 0) + kb * 16;
+    }
+    f32x4 acc[kMaxMT][4];
+#pragma unroll
+    for (int mt = 0; mt < kMaxMT; ++mt)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int g = 0; g < G; ++g) group_products<BITS, 4>(acc, cptr, sptr, tr, xs, G, g, nmt, kb);
+#pragma unroll
+    for (int mt = 0; mt < kMaxMT; ++mt) {
+      if (mt < nmt) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int r = m0 + mt * 16 + 4 * kb + i;
+          if (r < cnt) {
+            float* y = p.ys + (size_t)p.pairs[off + r] * H + row0 + nl;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) y[16 * t] = acc[mt][t][i];
+          }
+        }
+      }
+    }
+  }
+}
+
+// ---------------------------------------------------------------- 6. combine
+__global__ void __launch_bounds__(kBT) combine_kernel(const float* __restrict__ h, const float* __restrict__ ys,
+                                                      const int32_t* __restrict__ idx, const float* __restrict__ w,
+                                                      int H, int k, float* __restrict__ h_next,
+                                                      int32_t* __restrict__ idx_out, float* __restrict__ w_out,
+                                                      int layer, int n_layers) {
+  const int t = blockIdx.y;
+  const int i4 = blockIdx.x * kBT + threadIdx.x;
+  if (i4 < H / 4) {
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j = 0; j < k; ++j) {
+      const float wj = w[t * k + j];
+      const float4 y = reinterpret_cast<const float4*>(ys + ((size_t)t * k + j) * H)[i4];
+      s.x = fmaf(wj, y.x, s.x);
+      s.y = fmaf(wj, y.y, s.y);
+      s.z = fmaf(wj, y.z, s.z);
+      s.w = fmaf(wj, y.w, s.w);
+    }
+    const float4 hv = reinterpret_cast<const float4*>(h + (size_t)t * H)[i4];
+    reinterpret_cast<float4*>(h_next + (size_t)t * H)[i4] = make_float4(hv.x + s.x, hv.y + s.y, hv.z + s.z, hv.w + s.w);
+  }
+  if (blockIdx.x == 0 && (int)threadIdx.x < k) {
+    const size_t o = ((size_t)t * n_layers + layer) * k + threadIdx.x;
+    if (idx_out) idx_out[o] = idx[t * k + threadIdx.x];
+    if (w_out) w_out[o] = w[t * k + threadIdx.x];
+  }
+}
+
+// a16 (operand order, pair-id rows) -> natural column order.
+template <int BITS>
+__global__ void __launch_bounds__(kBT) a16_natural_kernel(const uint16_t* __restrict__ a16, int P, int I,
+                                                          uint16_t* __restrict__ out) {
+  const size_t n = (size_t)P * I;
+  for (size_t i = blockIdx.x * (size_t)kBT + threadIdx.x; i < n; i += (size_t)gridDim.x * kBT) {
+    const size_t row = i / I;
+    const int c = (int)(i % I);
+    out[i] = a16[row * I + (c & ~15) + perm_pos<BITS>(c & 15)];
+  }
+}
+
+// ---------------------------------------------------------------- workspace
+struct BatchedWs {
+  float* h[2];
+  float* v;
+  uint16_t* v16;
+  float* xg;
+  float* logits;
+  int32_t* idx;
+  float* w;
+  int32_t* pairs;
+  int32_t* act_e;
+  int32_t* act_off;
+  int32_t* act_cnt;
+  int32_t* n_act;
+  uint16_t* a16;
+  float* ag;
+  float* ys;
+  size_t bytes;
+};
+
+size_t up256(size_t b) { return (b + 255) / 256 * 256; }
+
+BatchedWs carve(void* base, int T, int H, int I, int E, int k) {
+  BatchedWs w;
+  char* p = static_cast<char*>(base);
+  size_t o = 0;
+  auto take = [&](size_t b) {
+    char* q = p ? p + o : nullptr;
+    o += up256(b);
+    return q;
+  };
+  const size_t P = (size_t)T * k;
+  w.h[0] = reinterpret_cast<float*>(take((size_t)T * H * 4));
+  w.h[1] = reinterpret_cast<float*>(take((size_t)T * H * 4));
+  w.v = reinterpret_cast<float*>(take((size_t)T * H * 4));
+  w.v16 = reinterpret_cast<uint16_t*>(take((size_t)T * H * 2));
+  w.xg = reinterpret_cast<float*>(take((size_t)T * (H / 64) * 4));
+  w.logits = reinterpret_cast<float*>(take((size_t)T * E * 4));
+  w.idx = reinterpret_cast<int32_t*>(take(P * 4));
+  w.w = reinterpret_cast<float*>(take(P * 4));
+  w.pairs = reinterpret_cast<int32_t*>(take(P * 4));
+  w.act_e = reinterpret_cast<int32_t*>(take((size_t)E * 4));
+  w.act_off = reinterpret_cast<int32_t*>(take((size_t)E * 4));
+  w.act_cnt = reinterpret_cast<int32_t*>(take((size_t)E * 4));
+  w.n_act = reinterpret_cast<int32_t*>(take(4));
+  w.a16 = reinterpret_cast<uint16_t*>(take(P * I * 2));
+  w.ag = reinterpret_cast<float*>(take(P * (I / 64) * 4));
+  w.ys = reinterpret_cast<float*>(take(P * H * 4));
+  w.bytes = o;
+  return w;
+}
+
+template <int BITS>
+int run_layers(const fmoe_layer* layers, int n_layers, const float* x_in, float* h_out, int T, int k, float eps,
+               unsigned flags, int32_t* idx_out, float* w_out, const BatchedWs& ws, hipStream_t s) {
+  const fmoe_layer& L0 = layers[0];
+  const int H = L0.hidden, I = L0.inter, E = L0.n_experts, P = T * k;
+  const int max_items = E < P ? E : P;
+  const size_t xs_gu = (size_t)kMaxMT * (H / 64) * 16 * 4, xs_dn = (size_t)kMaxMT * (I / 64) * 16 * 4;
+  const size_t sort_smem = (size_t)(2 * E + 2 * kSortThreads) * 4;
+  for (int l = 0; l < n_layers; ++l) {
+    const float* hin = l == 0 ? x_in : ws.h[(l - 1) & 1];
+    float* hnext = l == n_layers - 1 ? h_out : ws.h[l & 1];
+    const fmoe_layer& L = layers[l];
+    hipLaunchKernelGGL(stage_kernel<BITS>, dim3(T), dim3(kBT), 0, s, hin, H, (flags & FMOE_PRENORM) ? 1 : 0, eps,
+                       ws.v, ws.v16, ws.xg);
+    if (hipGetLastError() != hipSuccess) return FMOE_ERR_HIP;
+    int rc = launch_route(L.router, ws.v, T, E, H, k, ws.idx, ws.w, ws.logits, s);
+    if (rc) return rc;
+    hipLaunchKernelGGL(sort_kernel, dim3(1), dim3(kSortThreads), sort_smem, s, ws.idx, P, E, ws.pairs, ws.act_e,
+                       ws.act_off, ws.act_cnt, ws.n_act);
+    if (hipGetLastError() != hipSuccess) return FMOE_ERR_HIP;
+    BParams bp;
+    bp.experts = static_cast<const uint8_t*>(L.experts);
+    bp.stride = L.expert_stride;
+    bp.H = H;
+    bp.I = I;
+    bp.k = k;
+    bp.pairs = ws.pairs;
+    bp.act_e = ws.act_e;
+    bp.act_off = ws.act_off;
+    bp.act_cnt = ws.act_cnt;
+    bp.n_act = ws.n_act;
+    bp.v16 = ws.v16;
+    bp.xg = ws.xg;
+    bp.a16 = ws.a16;
+    bp.ag = ws.ag;
+    bp.ys = ws.ys;
+    hipLaunchKernelGGL(gate_up_kernel<BITS>, dim3(I / kGuRowsWg, max_items), dim3(kBT), xs_gu, s, bp);
+    if (hipGetLastError() != hipSuccess) return FMOE_ERR_HIP;
+    hipLaunchKernelGGL(down_kernel<BITS>, dim3(H / kDnRowsWg, max_items), dim3(kBT), xs_dn, s, bp);
+    if (hipGetLastError() != hipSuccess) return FMOE_ERR_HIP;
+    hipLaunchKernelGGL(combine_kernel, dim3((H / 4 + kBT - 1) / kBT, T), dim3(kBT), 0, s, hin, ws.ys, ws.idx, ws.w,
+                       H, k, hnext, idx_out, w_out, l, n_layers);
+    if (hipGetLastError() != hipSuccess) return FMOE_ERR_HIP;
+  }
+  return FMOE_OK;
+}
+
+}  // namespace
+
+bool batched_shape_ok(int hidden, int inter) { return hidden % kDnRowsWg == 0 && inter % kGuRowsWg == 0; }
+
+size_t batched_workspace_bytes(int n_tokens, int hidden, int inter, int n_experts, int k) {
+  return carve(nullptr, n_tokens, hidden, inter, n_experts, k).bytes;
+}
+
+int launch_batched(const fmoe_layer* layers, int n_layers, const float* x_in, float* h_out, int n_tokens, int k,
+                   float eps, unsigned flags, int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes,
+                   hipStream_t s) {
+  const fmoe_layer& L0 = layers[0];
+  if (!batched_shape_ok(L0.hidden, L0.inter)) return FMOE_ERR_SHAPE;
+  const BatchedWs w = carve(ws, n_tokens, L0.hidden, L0.inter, L0.n_experts, k);
+  if (w.bytes > ws_bytes) return FMOE_ERR_WORKSPACE;
+  if (L0.bits == 4) return run_layers<4>(layers, n_layers, x_in, h_out, n_tokens, k, eps, flags, idx_out, w_out, w, s);
+  return run_layers<2>(layers, n_layers, x_in, h_out, n_tokens, k, eps, flags, idx_out, w_out, w, s);
+}
+
+int launch_batched_a16(const void* ws, int n_tokens, int hidden, int inter, int n_experts, int k, int bits,
+                       uint16_t* out, hipStream_t s) {
+  const BatchedWs w = carve(const_cast<void*>(ws), n_tokens, hidden, inter, n_experts, k);
+  const int P = n_tokens * k;
+  const size_t n = (size_t)P * inter;
+  size_t blocks = (n + kBT - 1) / kBT;
+  if (blocks > 4096) blocks = 4096;
+  if (bits == 4)
+    hipLaunchKernelGGL(a16_natural_kernel<4>, dim3((unsigned)blocks), dim3(kBT), 0, s, w.a16, P, inter, out);
+  else
+    hipLaunchKernelGGL(a16_natural_kernel<2>, dim3((unsigned)blocks), dim3(kBT), 0, s, w.a16, P, inter, out);
+  return hipGetLastError() == hipSuccess ? FMOE_OK : FMOE_ERR_HIP;
 }
 
 }  // namespace fmoe

@@ -132,6 +132,36 @@ def uniform_at(seed: int, tag: int, a: int, b: int, c: int, i: int) -> float:
     return float(lib().synth_uniform_at(seed, tag, a, b, c, i))
 
 
+def zipf_experts(seed: int, draw: int, n_experts: int, k: int, s: float = 1.1) -> np.ndarray:
+    """k distinct experts for token `draw`, drawn one after another without replacement from
+    p(e) proportional to (e + 1)^-s (expert 0 the most popular). Uniforms come from stream
+    (TAG_PLANT, draw); the j-th pick uses index j."""
+    p = (np.arange(n_experts, dtype=np.float64) + 1.0) ** (-s)
+    out = np.empty(k, dtype=np.int32)
+    for j in range(k):
+        u = uniform_at(seed, TAG_PLANT, draw >> 32, draw & 0xFFFFFFFF, 0, j) * p.sum()
+        e = int(np.searchsorted(np.cumsum(p), u, side="right"))
+        e = min(e, n_experts - 1)
+        while p[e] == 0.0:  # u landed on the edge of a removed expert
+            e -= 1
+        out[j] = e
+        p[e] = 0.0
+    return out
+
+
+def planted_token(seed: int, draw: int, router: np.ndarray, k: int, gammas=(8.0, 7.0, 6.0, 5.0),
+                  s: float = 1.1):
+    """Token whose router winners are planted: x = z + sum_j gamma_j * r_e_j / |r_e_j| with
+    z ~ N(0, I) (stream TAG_NOISE, draw) and e_j = zipf_experts(...). Returns (x fp32, experts)."""
+    E, H = router.shape
+    experts = zipf_experts(seed, draw, E, k, s)
+    z = normal(seed, TAG_NOISE, draw >> 32, draw & 0xFFFFFFFF, 0, H).astype(np.float64)
+    for j, e in enumerate(experts):
+        r = router[e].astype(np.float64)
+        z += gammas[j % len(gammas)] * r / np.linalg.norm(r)
+    return z.astype(np.float32), experts
+
+
 def bf16_bits(x: np.ndarray) -> np.ndarray:
     """fp32 -> bf16 bit patterns, round to nearest even (NaN kept quiet)."""
     b = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)

@@ -15,7 +15,7 @@ FAKE = 0x100000  # aligned stand-in address, never dereferenced (validation fail
 
 def header_functions():
     text = open(os.path.join(ROOT, "include", "fmoe.h")).read()
-    return sorted(set(re.findall(r"\b(fmoe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(fmoe_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_exports_every_declared_function():
@@ -161,6 +161,31 @@ def test_moe_layer_validation():
     _raises(fm.ERR_BITS, call, layers=[L6])
     L7 = fm.Layer(FAKE, 1 << 32, stride, E, H, I, 4, 128)
     _raises(fm.ERR_GROUP, call, layers=[L7])
+
+
+def test_batched_validation():
+    H, I, E, k, T = 4096, 1024, 512, 4, 64
+    stride = fm.expert_bytes(H, I, 4)
+    L = fm.Layer(FAKE, 1 << 32, stride, E, H, I, 4, 64)
+    x, h, ws = FAKE + (1 << 30), FAKE + (2 << 30), FAKE + (3 << 30)
+    wsb = fm.workspace_bytes(fm.OP_MOE_LAYER, T, H, I, E, k)
+    assert wsb > fm.workspace_bytes(fm.OP_MOE_LAYER, 1, H, I, E, k)
+    # the grouped path needs hidden % 256 == 0 and inter % 128 == 0
+    H2 = 4096 + 64
+    L2 = fm.Layer(FAKE, 1 << 32, fm.expert_bytes(H2, I, 4) // 256 * 256 + 256, E, H2, I, 4, 64)
+    _raises(fm.ERR_SHAPE, fm.moe_layer, [L2], x, h, T, k, 1e-6, 0, None, None, ws,
+            fm.workspace_bytes(fm.OP_MOE_LAYER, T, H2, I, E, k), stream=0)
+    _raises(fm.ERR_WORKSPACE, fm.moe_layer, [L], x, h, T, k, 1e-6, 0, None, None, ws, wsb - 1, stream=0)
+    # inspection of a16
+    out = FAKE + (5 << 30)
+    _raises(fm.ERR_NULL, fm.batched_a16, None, wsb, T, H, I, E, k, 4, out, stream=0)
+    _raises(fm.ERR_BITS, fm.batched_a16, ws, wsb, T, H, I, E, k, 3, out, stream=0)
+    _raises(fm.ERR_SHAPE, fm.batched_a16, ws, wsb, 1, H, I, E, k, 4, out, stream=0)
+    _raises(fm.ERR_SHAPE, fm.batched_a16, ws, wsb, T, H, I + 64, E, k, 4, out, stream=0)
+    _raises(fm.ERR_K, fm.batched_a16, ws, wsb, T, H, I, E, 0, 4, out, stream=0)
+    _raises(fm.ERR_WORKSPACE, fm.batched_a16, ws, wsb - 1, T, H, I, E, k, 4, out, stream=0)
+    _raises(fm.ERR_ALIGN, fm.batched_a16, ws + 16, wsb, T, H, I, E, k, 4, out, stream=0)
+    _raises(fm.ERR_OVERLAP, fm.batched_a16, ws, wsb, T, H, I, E, k, 4, ws + 512, stream=0)
 
 
 def test_pack_validation():

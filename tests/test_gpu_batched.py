@@ -1,0 +1,178 @@
+"""GPU parity of the batched (grouped, bf16 matrix-core) path of fmoe_moe_layer against the
+oracle's O7 contract (only v and a = silu(g)*u rounded to bf16; weights exact):
+
+  (i)   expert indices bit-exact (tokens accepted with oracle top-k margin >= 1e-3);
+  (ii)  a16: every GPU value equal to the oracle's or one bf16 step away (fp32 vs fp64 g, u
+        can straddle a rounding boundary), at least 99 % equal; and with the oracle's down
+        stage fed the GPU's a16 (teacher forcing), outputs within relative L2 1e-5;
+  (iii) end to end against O7 within 2^-8 relative L2;
+  (iv)  the distance to the full-precision layer (O5) is reported, not asserted: it is a
+        property of the bf16 contract (a few per cent on tokens whose expert outputs cancel).
+"""
+from __future__ import annotations
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import quantized_expert_ffn_fmoe_amd as fm
+import synth
+from gpu_util import DevStack, rel_l2, to_dev
+
+pytestmark = pytest.mark.gpu
+EPS = 1e-6
+
+
+def _ordered(b: np.ndarray) -> np.ndarray:
+    b = b.astype(np.int64)
+    return np.where(b & 0x8000, 0x8000 - (b & 0x7FFF), 0x8000 + b)
+
+
+def _prenormed(x: np.ndarray) -> np.ndarray:
+    x = x.astype(np.float64)
+    return x / np.sqrt(np.mean(x * x) + EPS)
+
+
+def accepted_tokens(router, T, k, prenorm=False, start=0, margin=1e-3):
+    """First T draws whose oracle routing margin is >= margin."""
+    E, H = router.shape
+    X, draws, d = [], [], start
+    while len(X) < T:
+        x = synth.token(0, d, H)
+        v = _prenormed(x) if prenorm else x.astype(np.float64)
+        _, _, _, m = oracle.route(router, v, k)
+        if k == E or m >= margin:
+            X.append(x)
+            draws.append(d)
+        d += 1
+    return np.stack(X), draws
+
+
+def planted_tokens(router, T, k, margin=1e-3):
+    """First T planted Zipf(1.1) draws whose oracle winners are the planted set (margin >= margin)."""
+    X, sets, d = [], [], 0
+    while len(X) < T:
+        x, ex = synth.planted_token(0, d, router, k)
+        idx, _, _, m = oracle.route(router, x.astype(np.float64), k)
+        if set(idx.tolist()) == set(ex.tolist()) and m >= margin:
+            X.append(x)
+            sets.append(ex)
+        d += 1
+    return np.stack(X), sets
+
+
+def run_gpu(st: DevStack, X: np.ndarray, k: int, prenorm: bool, n_layers: int | None = None, layer0: int = 0):
+    T = X.shape[0]
+    n_layers = st.L - layer0 if n_layers is None else n_layers
+    layers = fm.layers_array([st.layers[layer0 + l] for l in range(n_layers)])
+    x = to_dev(X.astype(np.float32))
+    h = torch.empty_like(x)
+    idx = torch.full((T, n_layers, k), -1, dtype=torch.int32, device="cuda")
+    w = torch.zeros((T, n_layers, k), dtype=torch.float32, device="cuda")
+    wsb = fm.workspace_bytes(fm.OP_MOE_LAYER, T, st.H, st.I, st.E, k)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    fm.moe_layer(layers, x, h, T, k, EPS, fm.PRENORM if prenorm else 0, idx, w, ws, wsb)
+    a16 = torch.empty((T, k, st.I), dtype=torch.int16, device="cuda")
+    fm.batched_a16(ws, wsb, T, st.H, st.I, st.E, k, st.bits, a16)
+    torch.cuda.synchronize()
+    a16_bits = a16.cpu().numpy().view(np.uint16)
+    return (h.cpu().numpy().astype(np.float64), idx.cpu().numpy(), w.cpu().numpy().astype(np.float64), a16_bits)
+
+
+def check_layer(st: DevStack, X: np.ndarray, k: int, prenorm: bool, layer: int = 0, label: str = ""):
+    out, idx, w, a16_bits = run_gpu(st, X, k, prenorm, n_layers=1, layer0=layer)
+    prov = st.provider()
+    R = st.routers_np[layer]
+    ref = oracle.layer_bf16(prov, layer, R, X, st.I, k, st.bits, 64, prenorm=prenorm, eps=EPS)
+    # (i) indices
+    assert np.array_equal(idx[:, 0, :], ref["idx"]), f"{label}: expert indices differ"
+    assert np.allclose(w[:, 0, :], ref["w"], rtol=1e-5, atol=1e-7), f"{label}: routing weights differ"
+    # (ii) a16 vs the oracle's, then teacher forcing of the down stage
+    ref_bits = synth.bf16_bits(ref["a16"].astype(np.float32))
+    ulp = np.abs(_ordered(a16_bits) - _ordered(ref_bits))
+    a16_gpu = synth.bf16_to_f32(a16_bits).astype(np.float64)
+    a_ref = ref["a16"].astype(np.float64)
+    rms = np.sqrt(np.mean(a_ref * a_ref, axis=-1, keepdims=True))
+    # one bf16 step, or (for values near zero, where the fp32 sums' absolute error decides
+    # the rounding) an absolute difference far below the row's scale
+    bad = (ulp > 1) & (np.abs(a16_gpu - a_ref) > 1e-5 * rms)
+    assert not bad.any(), f"{label}: {int(bad.sum())} a16 values off (max {ulp.max()} steps)"
+    eq = float(np.mean(ulp == 0))
+    assert eq >= 0.99, f"{label}: only {eq:.4f} of a16 equal"
+    forced = oracle.layer_bf16(prov, layer, R, X, st.I, k, st.bits, 64, a16_force=a16_gpu, prenorm=prenorm, eps=EPS)
+    tf = max(rel_l2(out[t], forced["out"][t]) for t in range(X.shape[0]))
+    assert tf <= 1e-5, f"{label}: teacher-forced rel L2 {tf:.3e}"
+    print(f"{label}: a16 equal {eq:.5f}, max steps {ulp.max()}, teacher-forced {tf:.2e}")
+    # (iii) end to end against O7
+    e2e = [rel_l2(out[t], ref["out"][t]) for t in range(X.shape[0])]
+    assert max(e2e) <= 2.0 ** -8, f"{label}: end-to-end rel L2 {max(e2e):.3e}"
+    # (iv) distance to the full-precision layer, on a few tokens (reported: it measures the
+    # bf16 contract itself, which loses a few per cent on tokens whose expert outputs cancel)
+    band = []
+    for t in range(0, X.shape[0], max(1, X.shape[0] // 3)):
+        full, _, _, _ = oracle.moe_layer(prov, layer, R, X[t].astype(np.float64), st.I, k, st.bits, 64,
+                                         1 if prenorm else 0, EPS)
+        band.append(rel_l2(out[t], full))
+    print(f"{label}: end-to-end vs O7 max {max(e2e):.2e}; vs full precision median {np.median(band):.2e} "
+          f"max {max(band):.2e}")
+    return {"a16_equal": eq, "tf": tf, "e2e_max": max(e2e), "e2e_le_1e-5": float(np.mean(np.array(e2e) <= 1e-5))}
+
+
+@pytest.mark.parametrize("E,H,I,k,T,bits", [
+    (64, 512, 256, 4, 37, 4),   # ragged m-tiles, several row blocks
+    (64, 512, 256, 4, 37, 2),
+    (32, 768, 384, 2, 2, 4),    # smallest batch, odd numbers of row blocks
+    (16, 512, 256, 1, 20, 4),   # k = 1
+    (32, 512, 256, 16, 9, 4),   # k = 16
+    (4, 512, 128, 4, 80, 4),    # k = E: every expert gets 80 tokens (two passes of 64)
+    (4, 512, 128, 4, 80, 2),
+])
+def test_batched_layer(E, H, I, k, T, bits):
+    st = DevStack(1, E, H, I, bits)
+    X, _ = accepted_tokens(st.routers_np[0], T, k)
+    check_layer(st, X, k, prenorm=False, label=f"E{E} H{H} I{I} k{k} T{T} b{bits}")
+
+
+def test_batched_planted_zipf_hot_experts():
+    """Zipf(1.1) popularity planted through the router: the hottest experts get several
+    16-token tiles."""
+    st = DevStack(1, 64, 512, 256, 4)
+    X, sets = planted_tokens(st.routers_np[0], 70, 4)
+    counts = np.bincount(np.concatenate(sets), minlength=64)
+    assert counts.max() > 32
+    check_layer(st, X, 4, prenorm=False, label="planted")
+
+
+def test_batched_prenorm_two_layers():
+    st = DevStack(2, 32, 512, 256, 4)
+    X, _ = accepted_tokens(st.routers_np[0], 24, 4, prenorm=True)
+    out2, idx2, w2, _ = run_gpu(st, X, 4, True)  # both layers in one call
+    out_a, idx_a, _, _ = run_gpu(st, X, 4, True, n_layers=1, layer0=0)
+    out_b, idx_b, _, _ = run_gpu(st, out_a.astype(np.float32), 4, True, n_layers=1, layer0=1)
+    assert np.array_equal(out2, out_b)
+    assert np.array_equal(idx2[:, 0, :], idx_a[:, 0, :]) and np.array_equal(idx2[:, 1, :], idx_b[:, 0, :])
+    check_layer(st, X, 4, prenorm=True, layer=0, label="prenorm layer 0")
+    # layer 1 on the GPU's layer-0 output: only tokens whose layer-1 margin is safe
+    h1 = out_a.astype(np.float32)
+    keep = [t for t in range(h1.shape[0]) if oracle.route(st.routers_np[1], _prenormed(h1[t]), 4)[3] >= 1e-3]
+    assert len(keep) >= 2
+    check_layer(st, h1[keep], 4, prenorm=True, layer=1, label="prenorm layer 1")
+
+
+def test_batched_deterministic():
+    st = DevStack(1, 64, 512, 256, 4)
+    X, _ = accepted_tokens(st.routers_np[0], 33, 4)
+    a = run_gpu(st, X, 4, False)
+    b = run_gpu(st, X, 4, False)
+    for u, v in zip(a, b):
+        assert np.array_equal(u, v)
+
+
+def test_batched_full_size_planted():
+    """64 tokens through one 512-expert 4-bit layer at hidden 4096 / inter 1024, Zipf(1.1)
+    popularity planted through the router."""
+    st = DevStack(1, 512, 4096, 1024, 4, gpu_fill=True)
+    X, sets = planted_tokens(st.routers_np[0], 64, 4)
+    r = check_layer(st, X, 4, prenorm=False, label="full size")
+    print("full size:", r, "distinct experts", len(set(np.concatenate(sets).tolist())))
