@@ -8,7 +8,7 @@
 // are read once per call:
 //   1. stage: v = h (or rmsnorm(h)); its bf16 image v16 in operand order and, per group
 //      of 64 columns, the fp32 sum of the bf16 values;
-//   2. route: fp32 router logits and top-k with softmax (the standalone route kernels);
+//   2. route: fp32 router logits (fp32 matrix cores) and top-k with softmax;
 //   3. sort: counting sort of the (token, slot) pairs by expert; the list of experts
 //      that received at least one pair;
 //   4. gate/up: per (active expert, block of 128 rows): g and u for all of the expert's
@@ -188,6 +188,99 @@ __global__ void __launch_bounds__(kBT) stage_kernel(const float* __restrict__ h,
     dst[1] = u32x4{o[4], o[5], o[6], o[7]};
     s = group_sum(s, 4);
     if ((blk & 3) == 0) xg[(size_t)t * (H / 64) + blk / 4] = s;
+  }
+}
+
+// ---------------------------------------------------------------- 2. route
+// Router logits as an fp32 matrix-core product (v_mfma_f32_16x16x4f32: lane l holds
+// A[l % 16][l / 16], B[l / 16][l % 16], result as above). Workgroup (e-tile, slice):
+// 16 experts x one 512-column slice of K, wave w taking 128 columns of it; the four
+// waves' tiles are added in LDS in wave order and written as the slice's partial
+// logits part[slice][t][e]. A lane loads 4 consecutive columns of its token / expert row
+// and feeds them to 4 products, so each group of 4 products covers 16 columns.
+constexpr int kRtSlice = 512;
+constexpr int kRtWaveCols = kRtSlice / (kBT / 64);
+
+__device__ __forceinline__ f32x4 mfma4(float a, float b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+}
+
+__global__ void __launch_bounds__(kBT) router_kernel_mfma(const float* __restrict__ R, const float* __restrict__ v,
+                                                          int T, int E, int H, float* __restrict__ part) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nl = lane & 15, kb = lane >> 4;
+  const int e0 = blockIdx.x * 16, ks = blockIdx.y;
+  const int k_lo = ks * kRtSlice + wave * kRtWaveCols;
+  const int k_hi = min(k_lo + kRtWaveCols, H);
+  const bool e_ok = e0 + nl < E;
+  const float* rrow = R + (size_t)(e_ok ? e0 + nl : 0) * H;
+  __shared__ float red[kBT / 64][4][256];  // [wave][m-tile][16 tokens x 16 experts]
+  for (int t0 = 0; t0 < T; t0 += 64) {
+    const int nmt = min(4, (T - t0 + 15) / 16);
+    f32x4 acc[4];
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k = k_lo; k < k_hi; k += 16) {
+      const float4 b = e_ok ? *reinterpret_cast<const float4*>(rrow + k + 4 * kb) : make_float4(0.f, 0.f, 0.f, 0.f);
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        if (mt < nmt) {
+          const int tok = t0 + mt * 16 + nl;
+          const float4 a = tok < T ? *reinterpret_cast<const float4*>(v + (size_t)tok * H + k + 4 * kb)
+                                   : make_float4(0.f, 0.f, 0.f, 0.f);
+          acc[mt] = mfma4(a.x, b.x, acc[mt]);
+          acc[mt] = mfma4(a.y, b.y, acc[mt]);
+          acc[mt] = mfma4(a.z, b.z, acc[mt]);
+          acc[mt] = mfma4(a.w, b.w, acc[mt]);
+        }
+      }
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave][mt][(4 * kb + i) * 16 + nl] = acc[mt][i];
+    __syncthreads();
+    for (int i = threadIdx.x; i < nmt * 256; i += kBT) {
+      const int mt = i >> 8, m = (i >> 4) & 15, n = i & 15;
+      const int tok = t0 + mt * 16 + m, e = e0 + n;
+      const float s = ((red[0][mt][m * 16 + n] + red[1][mt][m * 16 + n]) + red[2][mt][m * 16 + n]) +
+                      red[3][mt][m * 16 + n];
+      if (tok < T && e < E) part[((size_t)ks * T + tok) * E + e] = s;
+    }
+    __syncthreads();
+  }
+}
+
+// Per token: the workgroup's four waves add the slice partials (slice order) into LDS
+// and write the logits out; wave 0 then takes the top-k by rank key and the softmax over
+// the selected logits.
+__global__ void __launch_bounds__(kBT) topk_parts_kernel(const float* __restrict__ part, int n_part, int T, int E,
+                                                         int k, float* __restrict__ logits, int32_t* __restrict__ idx,
+                                                         float* __restrict__ w) {
+  const int t = blockIdx.x, lane = threadIdx.x & 63;
+  __shared__ uint64_t keys[4096];
+  __shared__ float lsel[16], wsel[16];
+  __shared__ int isel[16];
+  for (int e = threadIdx.x; e < E; e += kBT) {
+    float l = 0.f;
+    for (int s = 0; s < n_part; ++s) l += part[((size_t)s * T + t) * E + e];
+    logits[(size_t)t * E + e] = l;
+    keys[e] = rank_key(l, e);
+  }
+  __syncthreads();
+  if (threadIdx.x < 64) {
+    if (E <= 512) {
+      uint64_t kr[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) kr[j] = lane + 64 * j < E ? keys[lane + 64 * j] : 0ull;
+      wave_topk_regs<8>(kr, k, isel, lsel, wsel);
+    } else {
+      wave_topk_keys(keys, E, k, isel, lsel, wsel);
+    }
+  }
+  __syncthreads();
+  if (threadIdx.x < k) {
+    idx[(size_t)t * k + threadIdx.x] = isel[threadIdx.x];
+    w[(size_t)t * k + threadIdx.x] = wsel[threadIdx.x];
   }
 }
 
@@ -496,6 +589,7 @@ struct BatchedWs {
   uint16_t* v16;
   float* xg;
   float* logits;
+  float* part;
   int32_t* idx;
   float* w;
   int32_t* pairs;
@@ -527,6 +621,7 @@ BatchedWs carve(void* base, int T, int H, int I, int E, int k) {
   w.v16 = reinterpret_cast<uint16_t*>(take((size_t)T * H * 2));
   w.xg = reinterpret_cast<float*>(take((size_t)T * (H / 64) * 4));
   w.logits = reinterpret_cast<float*>(take((size_t)T * E * 4));
+  w.part = reinterpret_cast<float*>(take((size_t)((H + kRtSlice - 1) / kRtSlice) * T * E * 4));
   w.idx = reinterpret_cast<int32_t*>(take(P * 4));
   w.w = reinterpret_cast<float*>(take(P * 4));
   w.pairs = reinterpret_cast<int32_t*>(take(P * 4));
@@ -556,8 +651,12 @@ int run_layers(const fmoe_layer* layers, int n_layers, const float* x_in, float*
     hipLaunchKernelGGL(stage_kernel<BITS>, dim3(T), dim3(kBT), 0, s, hin, H, (flags & FMOE_PRENORM) ? 1 : 0, eps,
                        ws.v, ws.v16, ws.xg);
     if (hipGetLastError() != hipSuccess) return FMOE_ERR_HIP;
-    int rc = launch_route(L.router, ws.v, T, E, H, k, ws.idx, ws.w, ws.logits, s);
-    if (rc) return rc;
+    const int n_part = (H + kRtSlice - 1) / kRtSlice;
+    hipLaunchKernelGGL(router_kernel_mfma, dim3((E + 15) / 16, n_part), dim3(kBT), 0, s, L.router, ws.v, T, E, H,
+                       ws.part);
+    if (hipGetLastError() != hipSuccess) return FMOE_ERR_HIP;
+    hipLaunchKernelGGL(topk_parts_kernel, dim3(T), dim3(kBT), 0, s, ws.part, n_part, T, E, k, ws.logits, ws.idx, ws.w);
+    if (hipGetLastError() != hipSuccess) return FMOE_ERR_HIP;
     hipLaunchKernelGGL(sort_kernel, dim3(1), dim3(kSortThreads), sort_smem, s, ws.idx, P, E, ws.pairs, ws.act_e,
                        ws.act_off, ws.act_cnt, ws.n_act);
     if (hipGetLastError() != hipSuccess) return FMOE_ERR_HIP;
