@@ -45,8 +45,8 @@ int check_qmat(const fmoe_qmat* W) {
 struct DecodeWs {
   uint32_t* flags;
   uint64_t* logits;
-  float* h;
-  float* a;
+  uint64_t* h;
+  uint64_t* a;
   uint32_t* err;
   size_t bytes;
 };
@@ -63,10 +63,10 @@ DecodeWs carve_decode(void* ws, int hidden, int inter, int n_experts, int k) {
   off += up256((size_t)kRep * n_experts * 8);
   d.err = reinterpret_cast<uint32_t*>(b + off);
   off += 256;
-  d.h = reinterpret_cast<float*>(b + off);
-  off += up256((size_t)kRep * hidden * 4);
-  d.a = reinterpret_cast<float*>(b + off);
-  off += up256((size_t)kRep * k * inter * 4);
+  d.h = reinterpret_cast<uint64_t*>(b + off);
+  off += up256((size_t)kRep * hidden * 8);
+  d.a = reinterpret_cast<uint64_t*>(b + off);
+  off += up256((size_t)kRep * k * inter * 8);
   d.bytes = off;
   return d;
 }

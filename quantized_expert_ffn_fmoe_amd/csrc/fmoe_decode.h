@@ -9,7 +9,7 @@ namespace fmoe {
 
 constexpr int kMaxLayersPerLaunch = 64;
 constexpr int kMaxGrid = 1024;  // workgroups of the persistent kernel (>= compute units)
-constexpr int kRep = 8;         // replicas of every exchanged item (flags, logits, h, a)
+constexpr int kRep = 8;         // replicas of every exchanged item (logits, h, a)
 
 struct DecodeParams {
   const float* router[kMaxLayersPerLaunch];
@@ -28,10 +28,10 @@ struct DecodeParams {
   int32_t* idx_out;  // [n_layers_total][k] or null (single token)
   float* w_out;
   // workspace
-  float* h;            // [kRep][hidden]
-  float* a;            // [kRep][k][inter]
+  uint64_t* h;         // [kRep][hidden], tagged (value | epoch << 32)
+  uint64_t* a;         // [kRep][k][inter], tagged
   uint64_t* logits;    // [kRep][n_experts], tagged
-  uint32_t* flags_arr; // [kRep][kMaxGrid], zero-filled before the first call on a workspace
+  uint32_t* flags_arr; // [kRep][kMaxGrid] epoch slots, zero-filled before the first call on a workspace
   uint32_t* err;       // [1]
 };
 

@@ -52,6 +52,7 @@ constexpr int kDecodeThreads = 256;
 constexpr int kDecodeWaves = kDecodeThreads / 64;
 constexpr unsigned kSpinLimit = 1u << 21;
 constexpr int kBatchN = 16;     // h / a values loaded together per thread
+constexpr int kPollN = 8;       // tagged h / a words polled together per thread
 constexpr int kBatchR = 2;      // router slices per wave loaded ahead
 constexpr int kKeysInRegs = 8;  // top-k from registers when n_experts <= 512
 
@@ -75,27 +76,48 @@ __device__ __forceinline__ bool spin_failed(unsigned spins, const uint32_t* err)
   return spins > kSpinLimit || ((spins & 63u) == 63u && ld_dev_u32(err) != 0u);
 }
 
-// Wave 0 only: raise this workgroup's flag (every replica) to `epoch`, then wait until
-// every flag of replica `rep` reached it. The caller has made sure that every wave's
-// stores completed (s_waitcnt + workgroup barrier). Returns false when the wait gave up.
-__device__ bool flag_arrive_and_wait(uint32_t* flags, int G, int rep, uint32_t epoch, uint32_t* err, int* fail) {
-  const int lane = threadIdx.x & 63;
-  if (lane < kRep) st_dev_u32(flags + (size_t)lane * kMaxGrid + blockIdx.x, epoch);
-  const uint32_t* mine = flags + (size_t)rep * kMaxGrid;
+// Tagged exchange words: value bits (low half) | epoch (high half).
+__device__ __forceinline__ uint64_t tagged(float v, uint32_t epoch) {
+  return ((uint64_t)epoch << 32) | __float_as_uint(v);
+}
+
+// Read n tagged values src[i0 + u * kDecodeThreads] (u < kPollN, i < n), waiting until
+// each carries `epoch`; only stale words are read again. Returns false (after raising the
+// error word) when the wait gave up.
+__device__ __forceinline__ bool poll_batch(const uint64_t* src, int n, int i0, uint32_t epoch, float (&out)[kPollN],
+                                           uint32_t* err) {
+  uint64_t v[kPollN];
+#pragma unroll
+  for (int u = 0; u < kPollN; ++u) {
+    const int i = i0 + u * kDecodeThreads;
+    v[u] = i < n ? ld_dev_u64(src + i) : tagged(0.f, epoch);
+  }
   unsigned spins = 0;
   while (true) {
     bool ok = true;
-    for (int j = lane; j < G; j += 64) ok &= (int32_t)(ld_dev_u32(mine + j) - epoch) >= 0;
-    if (__all(ok)) return true;
+#pragma unroll
+    for (int u = 0; u < kPollN; ++u) ok &= (uint32_t)(v[u] >> 32) == epoch;
+    if (ok) break;
     if (spin_failed(++spins, err)) {
-      if (lane == 0) {
-        st_dev_u32(err, 1u);
-        *fail = 1;
-      }
+      st_dev_u32(err, 1u);
       return false;
     }
     __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+    for (int u = 0; u < kPollN; ++u) {
+      const int i = i0 + u * kDecodeThreads;
+      if ((uint32_t)(v[u] >> 32) != epoch) v[u] = ld_dev_u64(src + i);
+    }
   }
+#pragma unroll
+  for (int u = 0; u < kPollN; ++u) out[u] = __uint_as_float((uint32_t)v[u]);
+  return true;
+}
+
+// Wait until wave 0's top-k progress word (LDS) reached r.
+__device__ __forceinline__ void wait_ready(const int* ready, int r) {
+  while (__hip_atomic_load(const_cast<int*>(ready), __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < r)
+    __builtin_amdgcn_s_sleep(0);
 }
 
 template <int BITS, int CPL_G, int CPL_D, int HC, int IC, int EC, int KC>
@@ -126,18 +148,21 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
   dig.n_chunks = H / CC;
   float* part = dig.xsum + max_chunks;  // [router items]
   float* ybuf = part + p.router_items;  // [k][rows per workgroup]
-  float* red = ybuf + K * p.rows_per_wg;
+  float* hraw = ybuf + K * p.rows_per_wg;  // [rows per workgroup] this workgroup's rows of h
+  float* red = hraw + p.rows_per_wg;
   float* wsel = red + kDecodeWaves;
   float* lsel = wsel + 16;
   int* isel = reinterpret_cast<int*>(lsel + 16);
   int* fail = isel + 16;
-  uint32_t* base = reinterpret_cast<uint32_t*>(fail + 1);
+  int* ready = fail + 1;
+  uint32_t* base = reinterpret_cast<uint32_t*>(ready + 1);
 
   if (tid == 0) {
     *fail = 0;
-    // Every flag holds the same value F when a launch starts: 0 in a zero-filled
-    // workspace, else the last epoch of the previous launch (all workgroups reach it).
-    // This launch's epochs and logit tags are F + 1, F + 2, ...
+    base[1] = 0;  // digit-builder arrivals (3 per layer)
+    // Epochs: every workgroup's slot holds the same value F when a launch starts (0 in a
+    // zero-filled workspace, else the last epoch of the previous launch). Layer l of this
+    // launch tags its logits F + 3l + 1, its a F + 3l + 2 and its output h F + 3l + 3.
     *base = ld_dev_u32(p.flags_arr + (size_t)rep * kMaxGrid + blockIdx.x);
   }
   __syncthreads();
@@ -164,8 +189,15 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
   const int S = (H + 1023) / 1024;  // router slices per row
   const int my_experts = (E - g + G - 1) / G;
   const int n_ritems = my_experts * S;
-  const float* h_rep = p.h + (size_t)rep * H;
-  const float* a_rep = p.a + (size_t)rep * KI;
+  // gate/up: a contiguous run of blocks (rpwG consecutive items each) per workgroup; the
+  // last slot it touches is the top-k round the workgroup has to wait for
+  const int n_blocks = (KI + rpwG - 1) / rpwG;
+  const int per_wg = (n_blocks + G - 1) / G;
+  const int blk_lo = g * per_wg, blk_hi = min(n_blocks, blk_lo + per_wg);
+  const int gu_last = min(blk_hi * rpwG, KI) - 1;
+  const int gu_need = blk_lo < blk_hi ? gu_last / I + 1 : 0;
+  const uint64_t* h_rep = p.h + (size_t)rep * H;
+  const uint64_t* a_rep = p.a + (size_t)rep * KI;
   const uint64_t* logits_rep = p.logits + (size_t)rep * E;
 
   // router slice `it` of layer `lr`: up to 4 float4 per lane
@@ -189,26 +221,36 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
   for (int l = 0; l < p.n_layers; ++l) {
     const int lg = p.layer0 + l;
     const uint8_t* X = p.experts[l];
+    const uint32_t ep = F + 3u * (uint32_t)l;
 
-    // ---- 1. v = rmsnorm(h) or h, in LDS (padded); loads issued kBatchN at a time
+    // ---- 1. h (the previous layer's tagged output, or x_in), v = rmsnorm(h) or h in LDS
     float ss = 0.f;
-    for (int i0 = tid; i0 < H; i0 += kDecodeThreads * kBatchN) {
-      float hv[kBatchN];
+    for (int i0 = tid; i0 < H; i0 += kDecodeThreads * kPollN) {
+      float hv[kPollN];
+      if (lg == 0) {
 #pragma unroll
-      for (int u = 0; u < kBatchN; ++u) {
-        const int i = i0 + u * kDecodeThreads;
-        hv[u] = i < H ? ((lg == 0) ? p.x_in[i] : ld_dev(h_rep + i)) : 0.f;
+        for (int u = 0; u < kPollN; ++u) {
+          const int i = i0 + u * kDecodeThreads;
+          hv[u] = i < H ? p.x_in[i] : 0.f;
+        }
+      } else if (!poll_batch(h_rep, H, i0, ep, hv, p.err)) {
+        *fail = 1;
       }
 #pragma unroll
-      for (int u = 0; u < kBatchN; ++u) {
+      for (int u = 0; u < kPollN; ++u) {
         const int i = i0 + u * kDecodeThreads;
-        if (i < H) vec[padded<CC>(i)] = hv[u];
-        ss = fmaf(hv[u], hv[u], ss);
+        if (i < H) {
+          vec[padded<CC>(i)] = hv[u];
+          if (i >= r0 && i < r0 + nr) hraw[i - r0] = hv[u];
+          ss = fmaf(hv[u], hv[u], ss);
+        }
       }
     }
     ss = wave_sum(ss);
     if (lane == 0) red[wave] = ss;
+    if (tid == 0) *ready = 0;
     __syncthreads();
+    if (*fail) break;
     float inv = 1.f;
     if (p.flags & FMOE_PRENORM) {
       float tot = 0.f;
@@ -241,10 +283,10 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
       if (lane == 0) part[it] = acc;
     }
     __syncthreads();
-    const uint64_t tag = (uint64_t)(F + (uint32_t)l + 1u) << 32;
+    const uint64_t tag = (uint64_t)(ep + 1u) << 32;
 
-    // ---- 3. publish this workgroup's logits and gather all of them (wave 0); the
-    // other waves build the digit image of v meanwhile
+    // ---- 3. publish this workgroup's logits and gather all of them (wave 0), then the
+    // top-k, released round by round; the other waves build the digit image of v
     if (wave == 0) {
       for (int t = lane; t < my_experts * kRep; t += 64) {
         const int el = t / kRep, rr = t % kRep;
@@ -253,6 +295,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
         st_dev_u64(p.logits + (size_t)rr * E + g + el * G, tag | __float_as_uint(lsum));
       }
       unsigned spins = 0;
+      bool failed = false;
       uint64_t kr[kKeysInRegs];  // E <= 64 * kKeysInRegs: keys stay in registers
       while (true) {
         bool ok = true;
@@ -276,44 +319,47 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
         }
         if (__all(ok)) break;
         if (spin_failed(++spins, p.err)) {
-          if (lane == 0) {
-            st_dev_u32(p.err, 1u);
-            *fail = 1;
-          }
+          failed = true;
           break;
         }
         __builtin_amdgcn_s_sleep(1);
       }
-      if (*fail) {
+      if (failed) {
+        if (lane == 0) {
+          st_dev_u32(p.err, 1u);
+          *fail = 1;
+        }
         if (lane < K) {
           isel[lane] = 0;
           wsel[lane] = 0.f;
         }
-      } else if (E <= 64 * kKeysInRegs) {
-        wave_topk_regs<kKeysInRegs>(kr, K, isel, lsel, wsel);
+        topk_progress(ready, K + 1);
       } else {
-        wave_topk_keys(key, E, K, isel, lsel, wsel);
-      }
-      if (g == 0 && lane < K) {
-        size_t o = ((size_t)lg) * K + lane;
-        if (p.idx_out) p.idx_out[o] = isel[lane];
-        if (p.w_out) p.w_out[o] = wsel[lane];
+        if (E <= 64 * kKeysInRegs) wave_topk_regs<kKeysInRegs>(kr, K, isel, lsel, wsel, ready);
+        else wave_topk_keys(key, E, K, isel, lsel, wsel, ready);
+        if (g == 0 && lane < K) {
+          size_t o = ((size_t)lg) * K + lane;
+          if (p.idx_out) p.idx_out[o] = isel[lane];
+          if (p.w_out) p.w_out[o] = wsel[lane];
+        }
       }
     } else {
       build_digits<BITS>(dig, H, [&](int i) { return vec[padded<CC>(i)]; }, kDecodeThreads - 64, tid - 64);
+      // the digit image is complete once every builder wave has passed this point
+      if (lane == 0) __hip_atomic_fetch_add(base + 1, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      wait_ready(ready, gu_need);
     }
-    __syncthreads();
-    if (*fail) break;
+    // every wave (wave 0 included) waits for the three builder waves of this layer
+    while (__hip_atomic_load(base + 1, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < 3u * (uint32_t)(l + 1))
+      __builtin_amdgcn_s_sleep(0);
+    if (*fail) break;  // set by wave 0 before it released the waiters
 
-    // ---- 4. gate/up + SwiGLU: workgroup g owns a contiguous run of blocks (rpwG
-    // consecutive items each; consecutive rows of one expert, so few distinct pages),
-    // dealt to its waves in runs of kBatchGU blocks whose loads are issued together
+    // ---- 4. gate/up + SwiGLU over this workgroup's run of blocks, dealt to its waves in
+    // runs of kBatchGU blocks whose loads are issued together; a is published tagged
     {
       DChunk<BITS> dc[CPL_G];
       bool dc_loaded = false;  // the digits are read from LDS after the first loads are issued
-      const int n_blocks = (KI + rpwG - 1) / rpwG;
-      const int per_wg = (n_blocks + G - 1) / G;
-      const int blk_lo = g * per_wg, blk_hi = min(n_blocks, blk_lo + per_wg);
+      const uint64_t atag = (uint64_t)(ep + 2u) << 32;
       for (int b0 = blk_lo + wave * kBatchGU; b0 < blk_hi; b0 += kDecodeWaves * kBatchGU) {
         uint4 wg[kBatchGU][CPL_G], wu[kBatchGU][CPL_G];
         uint32_t sg[kBatchGU][CPL_G], su[kBatchGU][CPL_G];
@@ -366,16 +412,17 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
           gs = group_sum(gs, lprG);
           us = group_sum(us, lprG);
           if (valid && subG == 0) {
-            const float av = swiglu(gs, us);
+            const uint64_t av = atag | __float_as_uint(swiglu(gs, us));
 #pragma unroll
-            for (int rr = 0; rr < kRep; ++rr) st_dev(p.a + (size_t)rr * KI + item, av);
+            for (int rr = 0; rr < kRep; ++rr) st_dev_u64(p.a + (size_t)rr * KI + item, av);
           }
         }
       }
     }
-    wait_vmem();  // this wave's a-stores are at the coherence point
 
-    // ---- prefetch: every wave issues the loads of its first kBatchD down items
+    // ---- prefetch: every wave issues the loads of its first kBatchD down items (all k
+    // experts must be known)
+    wait_ready(ready, K);
     uint4 wd[kBatchD][CPL_D];
     uint32_t sd[kBatchD][CPL_D];
     auto down_load = [&](int m, int u) {
@@ -402,33 +449,27 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
 #pragma unroll
     for (int u = 0; u < kBatchD; ++u) down_load(u, u);
 
-    // ---- 5. all of a is published
-    __syncthreads();
-    if (wave == 0) flag_arrive_and_wait(p.flags_arr, G, rep, F + 2u * l + 1u, p.err, fail);
-    __syncthreads();
-    if (*fail) break;
-    for (int i0 = tid; i0 < KI; i0 += kDecodeThreads * kBatchN) {
-      float av[kBatchN];
+    // ---- 5. all of a (tagged), into LDS; the next layer's router slices are read
+    // meanwhile
+    __syncthreads();  // every wave is done with the digit image of v
+    for (int i0 = tid; i0 < KI; i0 += kDecodeThreads * kPollN) {
+      float av[kPollN];
+      if (!poll_batch(a_rep, KI, i0, ep + 2u, av, p.err)) *fail = 1;
 #pragma unroll
-      for (int u = 0; u < kBatchN; ++u) {
-        const int i = i0 + u * kDecodeThreads;
-        av[u] = i < KI ? ld_dev(a_rep + i) : 0.f;
-      }
-#pragma unroll
-      for (int u = 0; u < kBatchN; ++u) {
+      for (int u = 0; u < kPollN; ++u) {
         const int i = i0 + u * kDecodeThreads;
         if (i < KI) vec[padded<CC>(i)] = av[u];
       }
     }
-    // the next layer's router slices are read while the down projection runs
 #pragma unroll
     for (int u = 0; u < kBatchR; ++u) router_load(l + 1, wave + kDecodeWaves * u, u);
     __syncthreads();
+    if (*fail) break;
     dig.n_chunks = KI / CC;
     build_digits<BITS>(dig, KI, [&](int i) { return vec[padded<CC>(i)]; }, kDecodeThreads, tid);
     __syncthreads();
 
-    // ---- 6. down (every wave), then combine + residual (wave 0)
+    // ---- 6. down (every wave), then combine + residual (wave 0), published tagged
     {
       int cur_j = -1;
       DChunk<BITS> dc[CPL_D];
@@ -468,28 +509,26 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
     dig.n_chunks = H / CC;
     const bool last = (l == p.n_layers - 1) && p.is_final;
     if (wave == 0) {
+      const uint32_t htag = ep + 3u;
       for (int rl = lane; rl < nr; rl += 64) {
         const int r = r0 + rl;
-        float hv = (lg == 0) ? p.x_in[r] : ld_dev(h_rep + r);
         float c = 0.f;
         for (int j = 0; j < K; ++j) c = fmaf(wsel[j], ybuf[j * rows_wg + rl], c);
-        float hn = hv + c;
+        const float hn = hraw[rl] + c;
+        const uint64_t hv = tagged(hn, htag);
 #pragma unroll
-        for (int rr = 0; rr < kRep; ++rr) st_dev(p.h + (size_t)rr * H + r, hn);
+        for (int rr = 0; rr < kRep; ++rr) st_dev_u64(p.h + (size_t)rr * H + r, hv);
         if (last) p.h_out[r] = hn;
       }
-      wait_vmem();
-    }
-    // ---- 7. all of h is published
-    if (l + 1 < p.n_layers) {
-      __syncthreads();
-      if (wave == 0) flag_arrive_and_wait(p.flags_arr, G, rep, F + 2u * l + 2u, p.err, fail);
-      __syncthreads();
-      if (*fail) break;
     }
   }
-  if (*fail && p.is_final) {
-    for (int r = r0 + tid; r < r0 + nr; r += kDecodeThreads) p.h_out[r] = __uint_as_float(0x7fc00000u);
+  __syncthreads();
+  if (*fail) {
+    if (p.is_final)
+      for (int r = r0 + tid; r < r0 + nr; r += kDecodeThreads) p.h_out[r] = __uint_as_float(0x7fc00000u);
+  } else if (tid == 0) {
+    // the epoch the next launch starts from
+    st_dev_u32(p.flags_arr + (size_t)rep * kMaxGrid + blockIdx.x, F + 3u * (uint32_t)p.n_layers);
   }
 }
 
@@ -517,7 +556,7 @@ size_t decode_smem_bytes(int hidden, int inter, int n_experts, int k, int G, int
   int my_experts = (n_experts + G - 1) / G;
   int S = (hidden + 1023) / 1024;
   size_t words = vec_len + vec_len / cc + (size_t)nw * max_chunks + 2 * max_chunks + (size_t)my_experts * S +
-                 (size_t)k * rows_per_wg + kDecodeWaves + 16 + 16 + 16 + 2;
+                 (size_t)k * rows_per_wg + rows_per_wg + kDecodeWaves + 16 + 16 + 16 + 4;
   return (size_t)n_experts * 8 + words * 4;
 }
 

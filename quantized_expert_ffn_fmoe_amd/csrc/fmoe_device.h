@@ -219,13 +219,19 @@ __device__ __forceinline__ bool ranks_before(float la, int ia, float lb, int ib)
   return ia < ib;
 }
 
+// Top-k progress published to the other waves of the workgroup (LDS word): r after
+// round r, and k + 1 once the softmax weights are written.
+__device__ __forceinline__ void topk_progress(int* ready, int r) {
+  if (ready && (threadIdx.x & 63) == 0) __hip_atomic_store(ready, r, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+}
+
 // Top-k of n ranked keys held in LDS (one wave; keys are consumed). Round r takes the
 // wave-wide maximum key; its owner lane clears it and rescans its own keys. Lane 0 writes
 // isel[r] (expert index) and lsel[r] (logit); then lanes < k turn the logits into the
 // softmax over the selected experts, shifted by the largest: wsel[j] = e^(l_j - l_0) /
 // sum_j' e^(l_j' - l_0).
 __device__ __forceinline__ void wave_topk_keys(uint64_t* keys, int n, int k, int* isel, float* lsel,
-                                               float* wsel) {
+                                               float* wsel, int* ready = nullptr) {
   const int lane = threadIdx.x & 63;
   uint64_t best = 0;
   for (int e = lane; e < n; e += 64) best = keys[e] > best ? keys[e] : best;
@@ -235,6 +241,7 @@ __device__ __forceinline__ void wave_topk_keys(uint64_t* keys, int n, int k, int
       isel[r] = rank_key_index(w);
       lsel[r] = rank_key_logit(w);
     }
+    topk_progress(ready, r + 1);
     if (best == w && w != 0) {
       best = 0;
       for (int e = lane; e < n; e += 64) {
@@ -250,13 +257,15 @@ __device__ __forceinline__ void wave_topk_keys(uint64_t* keys, int n, int k, int
   if (lane < k) ex = expf(lsel[lane] - lsel[0]);
   const float denom = wave_sum(ex);
   if (lane < k) wsel[lane] = ex / denom;
+  topk_progress(ready, k + 1);
 }
 
 // Top-k of at most 64 * KPL ranked keys held in registers (key j of a lane is element
 // lane + 64 j; absent elements hold key 0). Same contract as wave_topk_keys; the keys are
 // consumed. All lanes clear the taken key and recompute their best without branches.
 template <int KPL>
-__device__ __forceinline__ void wave_topk_regs(uint64_t (&kr)[KPL], int k, int* isel, float* lsel, float* wsel) {
+__device__ __forceinline__ void wave_topk_regs(uint64_t (&kr)[KPL], int k, int* isel, float* lsel, float* wsel,
+                                               int* ready = nullptr) {
   const int lane = threadIdx.x & 63;
   uint64_t best = 0;
 #pragma unroll
@@ -267,6 +276,7 @@ __device__ __forceinline__ void wave_topk_regs(uint64_t (&kr)[KPL], int k, int* 
       isel[r] = rank_key_index(w);
       lsel[r] = rank_key_logit(w);
     }
+    topk_progress(ready, r + 1);
     best = 0;
 #pragma unroll
     for (int j = 0; j < KPL; ++j) {
@@ -280,6 +290,7 @@ __device__ __forceinline__ void wave_topk_regs(uint64_t (&kr)[KPL], int k, int* 
   if (lane < k) ex = expf(lsel[lane] - lsel[0]);
   const float denom = wave_sum(ex);
   if (lane < k) wsel[lane] = ex / denom;
+  topk_progress(ready, k + 1);
 }
 
 // silu(g) * u with silu(g) = g / (1 + exp(-g)); for very negative g, exp(-g) is +inf
