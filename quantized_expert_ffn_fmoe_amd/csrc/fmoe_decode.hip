@@ -297,32 +297,56 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
       unsigned spins = 0;
       bool failed = false;
       uint64_t kr[kKeysInRegs];  // E <= 64 * kKeysInRegs: keys stay in registers
-      while (true) {
-        bool ok = true;
-        if (E <= 64 * kKeysInRegs) {
+      if (E <= 64 * kKeysInRegs) {
+        // one poll batch in flight; words that arrived are kept, only stale ones are read
+        // again
+        uint64_t t[kKeysInRegs];
+        uint32_t got = 0, want = 0;
+#pragma unroll
+        for (int j = 0; j < kKeysInRegs; ++j) {
+          const int e = lane + 64 * j;
+          kr[j] = 0;
+          if (e < E) {
+            want |= 1u << j;
+            t[j] = ld_dev_u64(logits_rep + e);
+          }
+        }
+        while (true) {
 #pragma unroll
           for (int j = 0; j < kKeysInRegs; ++j) {
             const int e = lane + 64 * j;
-            kr[j] = 0;
-            if (e < E) {
-              const uint64_t t = ld_dev_u64(logits_rep + e);
-              ok &= (t & 0xffffffff00000000ull) == tag;
-              kr[j] = rank_key(__uint_as_float((uint32_t)t), e);
+            if (((want & ~got) >> j) & 1u) {
+              if ((t[j] & 0xffffffff00000000ull) == tag) {
+                kr[j] = rank_key(__uint_as_float((uint32_t)t[j]), e);
+                got |= 1u << j;
+              }
             }
           }
-        } else {
+          if (__all(got == want)) break;
+          if (spin_failed(++spins, p.err)) {
+            failed = true;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+          for (int j = 0; j < kKeysInRegs; ++j)
+            if (((want & ~got) >> j) & 1u) t[j] = ld_dev_u64(logits_rep + lane + 64 * j);
+        }
+      } else {
+        while (true) {
+          bool ok = true;
           for (int e = lane; e < E; e += 64) {
             const uint64_t t = ld_dev_u64(logits_rep + e);
             ok &= (t & 0xffffffff00000000ull) == tag;
             key[e] = rank_key(__uint_as_float((uint32_t)t), e);
           }
+          if (__all(ok)) break;
+          if (spin_failed(++spins, p.err)) {
+            failed = true;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
         }
-        if (__all(ok)) break;
-        if (spin_failed(++spins, p.err)) {
-          failed = true;
-          break;
-        }
-        __builtin_amdgcn_s_sleep(1);
       }
       if (failed) {
         if (lane == 0) {

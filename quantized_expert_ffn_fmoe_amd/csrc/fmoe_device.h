@@ -260,28 +260,60 @@ __device__ __forceinline__ void wave_topk_keys(uint64_t* keys, int n, int k, int
   topk_progress(ready, k + 1);
 }
 
+// Maximum of a 32-bit value over the wave (every lane gets it; wave-uniform).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u<0xB1>(v));
+  v = max(v, dpp_u<0x4E>(v));
+  v = max(v, dpp_u<0x141>(v));
+  v = max(v, dpp_u<0x140>(v));
+  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
+  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
+  return max(max(a, b), max(c, d));
+}
+
+template <int N>
+__device__ __forceinline__ void cmp_swap_desc(uint64_t (&k)[N], int i, int j) {
+  const uint64_t a = k[i], b = k[j];
+  const bool sw = b > a;
+  k[i] = sw ? b : a;
+  k[j] = sw ? a : b;
+}
+
 // Top-k of at most 64 * KPL ranked keys held in registers (key j of a lane is element
 // lane + 64 j; absent elements hold key 0). Same contract as wave_topk_keys; the keys are
-// consumed. All lanes clear the taken key and recompute their best without branches.
+// consumed. Each lane first sorts its keys (descending); a round then takes the wave-wide
+// maximum of the lanes' heads: the 32-bit maximum of the high words (the ordered logits),
+// then, only when several lanes hold that logit, the maximum of their low words (lower
+// index first); the winning lane drops its head.
 template <int KPL>
 __device__ __forceinline__ void wave_topk_regs(uint64_t (&kr)[KPL], int k, int* isel, float* lsel, float* wsel,
                                                int* ready = nullptr) {
+  static_assert(KPL == 8, "sorting network for 8 keys per lane");
   const int lane = threadIdx.x & 63;
-  uint64_t best = 0;
-#pragma unroll
-  for (int j = 0; j < KPL; ++j) best = kr[j] > best ? kr[j] : best;
+  // Batcher's odd-even merge sort, 8 inputs (19 compare-exchanges)
+  cmp_swap_desc(kr, 0, 1); cmp_swap_desc(kr, 2, 3); cmp_swap_desc(kr, 4, 5); cmp_swap_desc(kr, 6, 7);
+  cmp_swap_desc(kr, 0, 2); cmp_swap_desc(kr, 1, 3); cmp_swap_desc(kr, 4, 6); cmp_swap_desc(kr, 5, 7);
+  cmp_swap_desc(kr, 1, 2); cmp_swap_desc(kr, 5, 6);
+  cmp_swap_desc(kr, 0, 4); cmp_swap_desc(kr, 1, 5); cmp_swap_desc(kr, 2, 6); cmp_swap_desc(kr, 3, 7);
+  cmp_swap_desc(kr, 2, 4); cmp_swap_desc(kr, 3, 5);
+  cmp_swap_desc(kr, 1, 2); cmp_swap_desc(kr, 3, 4); cmp_swap_desc(kr, 5, 6);
   for (int r = 0; r < k; ++r) {
-    const uint64_t w = wave_max_u64(best);
+    const uint32_t hi = (uint32_t)(kr[0] >> 32), lo = (uint32_t)kr[0];
+    const uint32_t m = wave_max_u32(hi);
+    const uint64_t tied = __ballot(hi == m);
+    uint32_t lw;
+    if (__popcll(tied) == 1) lw = (uint32_t)__builtin_amdgcn_readlane((int)lo, (int)__ffsll((long long)tied) - 1);
+    else lw = wave_max_u32(hi == m ? lo : 0u);
+    const uint64_t w = ((uint64_t)m << 32) | lw;
     if (lane == 0) {
       isel[r] = rank_key_index(w);
       lsel[r] = rank_key_logit(w);
     }
     topk_progress(ready, r + 1);
-    best = 0;
+    if (kr[0] == w) {
 #pragma unroll
-    for (int j = 0; j < KPL; ++j) {
-      kr[j] = kr[j] == w ? 0ull : kr[j];
-      best = kr[j] > best ? kr[j] : best;
+      for (int j = 0; j + 1 < KPL; ++j) kr[j] = kr[j + 1];
+      kr[KPL - 1] = 0;
     }
   }
   __builtin_amdgcn_s_waitcnt(0);
