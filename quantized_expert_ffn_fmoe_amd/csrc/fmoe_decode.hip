@@ -128,7 +128,8 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
   constexpr int CC = C::kCodes;
   constexpr int NW = Digits<BITS>::kWords;
   extern __shared__ float smem_raw[];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: per-wave indexing on the scalar unit
   const int G = gridDim.x, g = blockIdx.x, rep = g % kRep;
   const int H = HC ? HC : p.hidden;
   const int I = IC ? IC : p.inter;
@@ -473,8 +474,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
 #pragma unroll
     for (int u = 0; u < kBatchD; ++u) down_load(u, u);
 
-    // ---- 5. all of a (tagged), into LDS; the next layer's router slices are read
-    // meanwhile
+    // ---- 5. all of a (tagged), into LDS
     __syncthreads();  // every wave is done with the digit image of v
     for (int i0 = tid; i0 < KI; i0 += kDecodeThreads * kPollN) {
       float av[kPollN];
@@ -485,15 +485,15 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
         if (i < KI) vec[padded<CC>(i)] = av[u];
       }
     }
-#pragma unroll
-    for (int u = 0; u < kBatchR; ++u) router_load(l + 1, wave + kDecodeWaves * u, u);
     __syncthreads();
     if (*fail) break;
     dig.n_chunks = KI / CC;
     build_digits<BITS>(dig, KI, [&](int i) { return vec[padded<CC>(i)]; }, kDecodeThreads, tid);
     __syncthreads();
 
-    // ---- 6. down (every wave), then combine + residual (wave 0), published tagged
+    // ---- 6. down (every wave), then combine + residual (wave 0), published tagged; the
+    // next layer's router slices are requested after the down loop (their latency hides
+    // behind the combine and the exchange of h)
     {
       int cur_j = -1;
       DChunk<BITS> dc[CPL_D];
@@ -529,6 +529,8 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
         }
       }
     }
+#pragma unroll
+    for (int u = 0; u < kBatchR; ++u) router_load(l + 1, wave + kDecodeWaves * u, u);
     __syncthreads();
     dig.n_chunks = H / CC;
     const bool last = (l == p.n_layers - 1) && p.is_final;
