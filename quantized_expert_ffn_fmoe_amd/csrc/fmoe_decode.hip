@@ -126,6 +126,12 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
   constexpr int kBatchD = batch_d<CPL_D>();
   using C = Chunk<BITS>;
   constexpr int CC = C::kCodes;
+  // With the shape fixed at compile time, a wave reduces all of its gate/up or down items
+  // in one transposed pass (reduce_transposed) instead of one cross-lane reduction each.
+  constexpr int kLprG = HC ? lanes_per_row(HC / CC) : 0;
+  constexpr int kLprD = IC ? lanes_per_row(IC / CC) : 0;
+  constexpr bool kFastGU = kLprG == 64 && kBatchGU == 4;
+  constexpr bool kFastD = kLprD >= 16 && kBatchD >= 2 && kBatchD <= 8;
   constexpr int NW = Digits<BITS>::kWords;
   extern __shared__ float smem_raw[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -261,8 +267,33 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
     for (int i = tid; i < H; i += kDecodeThreads) vec[padded<CC>(i)] *= inv;
     __syncthreads();
 
-    // ---- 2. router: dot the loaded slices with v
-    for (int m = 0; wave + kDecodeWaves * m < n_ritems; ++m) {
+    // ---- 2. router: dot the loaded slices with v (the first two of a wave reduced together)
+    int m_first = 0;
+    if (kBatchR == 2 && wave + kDecodeWaves < n_ritems) {
+      float acc2[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int s = (wave + kDecodeWaves * u) % S;
+        const int c0 = s * 256, c1 = min(H / 4, c0 + 256);
+        float acc = 0.f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = c0 + lane + 64 * q;
+          if (c < c1) {
+            const int pi = padded<CC>(4 * c);
+            acc = fmaf(rv[u][q].x, vec[pi + 0], acc);
+            acc = fmaf(rv[u][q].y, vec[pi + 1], acc);
+            acc = fmaf(rv[u][q].z, vec[pi + 2], acc);
+            acc = fmaf(rv[u][q].w, vec[pi + 3], acc);
+          }
+        }
+        acc2[u] = acc;
+      }
+      const float sum = reduce_transposed<2, 64>(acc2);
+      if (lane < 2) part[wave + kDecodeWaves * lane] = sum;  // lane u holds slice u's total
+      m_first = 2;
+    }
+    for (int m = m_first; wave + kDecodeWaves * m < n_ritems; ++m) {
       const int it = wave + kDecodeWaves * m;
       const int u = m < kBatchR ? m : kBatchR - 1;
       if (m >= kBatchR) router_load(l, it, u);
@@ -418,6 +449,33 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
           }
           dc_loaded = true;
         }
+        if constexpr (kFastGU) {
+          // one row per item (64 lanes per row): the 4 gate and 4 up sums of the batch are
+          // reduced together; afterwards an even lane 8r + 2b1 + 4b2 holds the gate sum of
+          // item 2b1 + b2 and its odd neighbour the up sum, and stores a to replica r.
+          // Items past the run (uniform tail) were not loaded; their sums are not stored.
+          float vals[8];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            float gs = 0.f, us = 0.f;
+#pragma unroll
+            for (int q = 0; q < CPL_G; ++q) {
+              int c = lane + 64 * q;
+              if (c < nchG) {
+                gs += chunk_dot_int<BITS>(wg[u][q], sg[u][q], dc[q]);
+                us += chunk_dot_int<BITS>(wu[u][q], su[u][q], dc[q]);
+              }
+            }
+            vals[u] = gs;
+            vals[4 + u] = us;
+          }
+          const float sum = reduce_transposed<8, 64>(vals);
+          const float up_sum = xlane<1>(sum);
+          const int u = 2 * ((lane >> 1) & 1) + ((lane >> 2) & 1);
+          if (!(lane & 1) && b0 + u < blk_hi)
+            st_dev_u64(p.a + (size_t)(lane >> 3) * KI + (b0 + u), atag | __float_as_uint(swiglu(sum, up_sum)));
+          continue;
+        }
 #pragma unroll
         for (int u = 0; u < kBatchGU; ++u) {
           if (b0 + u >= blk_hi) break;  // uniform over the wave
@@ -494,7 +552,36 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
     // ---- 6. down (every wave), then combine + residual (wave 0), published tagged; the
     // next layer's router slices are requested after the down loop (their latency hides
     // behind the combine and the exchange of h)
-    {
+    // a wave whose items all belong to one slot and fit one batch (all of them prefetched)
+    // reduces them together; lane i < kBatchD of a row group then holds the sum of item
+    // transposed_index(i)
+    const int j_lo = d_lo / n_rb;
+    const bool fast_d = kFastD && d_hi > d_lo && d_hi - d_lo <= kBatchD && (d_hi - 1) / n_rb == j_lo;
+    if (fast_d) {
+      if constexpr (kFastD) {
+        DChunk<BITS> dc[CPL_D];
+#pragma unroll
+        for (int q = 0; q < CPL_D; ++q) {
+          int c = subD + kLprD * q;
+          if (c < nchD) load_dchunk<BITS>(dc[q], dig, j_lo * nchD + c);
+        }
+        float acc[kBatchD];
+#pragma unroll
+        for (int u = 0; u < kBatchD; ++u) {
+          float a_ = 0.f;
+#pragma unroll
+          for (int q = 0; q < CPL_D; ++q) {
+            int c = subD + kLprD * q;
+            if (c < nchD) a_ += chunk_dot_int<BITS>(wd[u][q], sd[u][q], dc[q]);
+          }
+          acc[u] = a_;
+        }
+        const float sum = reduce_transposed<kBatchD, kLprD>(acc);
+        const int u = transposed_index<kBatchD>(lane);
+        const int rl = (d_lo - j_lo * n_rb + u) * rpwD + rselD;
+        if (subD < kBatchD && d_lo + u < d_hi && rl < nr) ybuf[j_lo * rows_wg + rl] = sum;
+      }
+    } else {
       int cur_j = -1;
       DChunk<BITS> dc[CPL_D];
       for (int m0 = 0; d_lo + m0 < d_hi; m0 += kBatchD) {
@@ -535,16 +622,20 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
     dig.n_chunks = H / CC;
     const bool last = (l == p.n_layers - 1) && p.is_final;
     if (wave == 0) {
+      // 16 rows at a time; the four lanes of a row (lane & 15) share its replica stores
       const uint32_t htag = ep + 3u;
-      for (int rl = lane; rl < nr; rl += 64) {
-        const int r = r0 + rl;
-        float c = 0.f;
-        for (int j = 0; j < K; ++j) c = fmaf(wsel[j], ybuf[j * rows_wg + rl], c);
-        const float hn = hraw[rl] + c;
-        const uint64_t hv = tagged(hn, htag);
+      for (int rb = 0; rb < nr; rb += 16) {
+        const int rl = rb + (lane & 15);
+        if (rl < nr) {
+          const int r = r0 + rl;
+          float c = 0.f;
+          for (int j = 0; j < K; ++j) c = fmaf(wsel[j], ybuf[j * rows_wg + rl], c);
+          const float hn = hraw[rl] + c;
+          const uint64_t hv = tagged(hn, htag);
 #pragma unroll
-        for (int rr = 0; rr < kRep; ++rr) st_dev_u64(p.h + (size_t)rr * H + r, hv);
-        if (last) p.h_out[r] = hn;
+          for (int rr = lane >> 4; rr < kRep; rr += 4) st_dev_u64(p.h + (size_t)rr * H + r, hv);
+          if (last && lane < 16) p.h_out[r] = hn;
+        }
       }
     }
   }

@@ -133,7 +133,7 @@ __device__ __forceinline__ float chunk_dot(const uint4& w, uint32_t sb, const XC
 
 // Cross-lane data movement with DPP (no LDS round trip). Controls (GFX9 encoding):
 // quad_perm [1,0,3,2] = 0xB1, quad_perm [2,3,0,1] = 0x4E, row_half_mirror = 0x141,
-// row_mirror = 0x140.
+// row_mirror = 0x140, row_ror:4 = 0x124, row_ror:8 = 0x128.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
@@ -162,6 +162,69 @@ __device__ __forceinline__ float group_sum(float v, int width) {
 }
 
 __device__ __forceinline__ float wave_sum(float v) { return group_sum(v, 64); }
+
+// The value of the lane at distance D in the pairing used by reduce_transposed: D = 1, 2
+// exchange with lane ^ D (quad_perm), D = 4 and 8 rotate each 16-lane row by 4 and 8
+// (row_ror), D = 16 exchanges with lane ^ 16 (ds_swizzle, bit mode), D = 32 with
+// lane ^ 32 (ds_bpermute).
+template <int D>
+__device__ __forceinline__ float xlane(float v) {
+  if constexpr (D == 1) return dpp_f<0xB1>(v);
+  else if constexpr (D == 2) return dpp_f<0x4E>(v);
+  else if constexpr (D == 4) return dpp_f<0x124>(v);
+  else if constexpr (D == 8) return dpp_f<0x128>(v);
+  else if constexpr (D == 16) return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+  else return __int_as_float(__builtin_amdgcn_ds_bpermute((int)((threadIdx.x & 63) ^ 32) << 2, __float_as_int(v)));
+}
+
+// One halving step of a transposed reduction: a lane whose bit D is set keeps the upper
+// half of its values and sends the lower half to its partner, and the other way round, so
+// that after the step each lane holds NV/2 values summed over the pair.
+template <int D, int NV>
+__device__ __forceinline__ void transpose_step(float (&v)[8]) {
+  const bool up = (threadIdx.x & D) != 0;
+#pragma unroll
+  for (int k = 0; k < NV / 2; ++k) {
+    const float keep = up ? v[NV / 2 + k] : v[k];
+    const float send = up ? v[k] : v[NV / 2 + k];
+    v[k] = keep + xlane<D>(send);
+  }
+}
+
+// Sum NV values (NV = 1, 2, 4 or 8) each over its group of W consecutive lanes (W = 16,
+// 32 or 64) in one pass: the first log2(NV) steps split the values between partner lanes
+// instead of reducing each one separately, so NV sums cost about as many cross-lane
+// operations as 2 single ones. Afterwards every lane of a group holds the total of value
+// transposed_index<NV>(lane). The rotation at distance 4 pairs quad q of a row with quad
+// q - 1; the rotation at distance 8 then adds the remaining two quads, so every quad of
+// the row is counted once.
+template <int NV, int W>
+__device__ __forceinline__ float reduce_transposed(const float (&in)[NV]) {
+  static_assert(NV == 1 || NV == 2 || NV == 4 || NV == 8, "NV must be 1, 2, 4 or 8");
+  static_assert(W == 16 || W == 32 || W == 64, "W must be 16, 32 or 64");
+  float v[8];
+#pragma unroll
+  for (int i = 0; i < NV; ++i) v[i] = in[i];
+  if constexpr (NV >= 2) transpose_step<1, NV>(v);
+  else v[0] += xlane<1>(v[0]);
+  if constexpr (NV >= 4) transpose_step<2, NV / 2>(v);
+  else v[0] += xlane<2>(v[0]);
+  if constexpr (NV >= 8) transpose_step<4, 2>(v);
+  else v[0] += xlane<4>(v[0]);
+  v[0] += xlane<8>(v[0]);
+  if constexpr (W >= 32) v[0] += xlane<16>(v[0]);
+  if constexpr (W >= 64) v[0] += xlane<32>(v[0]);
+  return v[0];
+}
+
+// Which of the NV values a lane holds after reduce_transposed<NV, W>.
+template <int NV>
+__device__ __forceinline__ int transposed_index(int lane) {
+  if constexpr (NV == 8) return 4 * (lane & 1) + 2 * ((lane >> 1) & 1) + ((lane >> 2) & 1);
+  else if constexpr (NV == 4) return 2 * (lane & 1) + ((lane >> 1) & 1);
+  else if constexpr (NV == 2) return lane & 1;
+  else return 0;
+}
 
 // Maximum over groups of `width` consecutive lanes (width 2, 4, 8 or 16).
 __device__ __forceinline__ float group_max(float v, int width) {
