@@ -5,39 +5,38 @@
 // Expert Compute": route, run the k selected experts, combine with the residual, and
 // normalize for the next layer; the pages route on the CPU, here routing stays on the
 // device):
-//   1. v = h * inv_rms(h) (or v = h without pre-norm), staged in LDS by every workgroup;
+//   1. every workgroup gathers h (x on the first layer) into LDS and its sum of squares;
+//      v = h * inv_rms(h) (or v = h without pre-norm) is never formed, inv_rms scales the
+//      router sums and v's digit image instead;
 //   2. router: workgroup g owns experts g, g+G, ...; its waves dot 1024-column slices of
-//      those rows (loaded during the previous layer) with v; the logits are published
-//      with a tag (value | epoch << 32);
-//   3. every workgroup polls the tagged logits, then selects the top-k and their softmax
-//      weights itself (no extra round trip); meanwhile the digit image of v (see
-//      fmoe_intdot.h) is built in LDS;
+//      those rows (loaded during the previous layer) with h; the logits are published;
+//   3. every workgroup gathers the logits; wave 0 selects the top-k and the softmax
+//      weights (no extra round trip) and releases the slots one by one, while the other
+//      waves build the digit image of v (see fmoe_intdot.h);
 //   4. gate/up: workgroup g owns a contiguous run of (slot j, row i) items (consecutive
 //      rows of one expert); each item reads gate row i and up row i of expert idx[j] and
-//      publishes a[j][i] = silu(g)*u; every wave then issues the loads of its share of
-//      the down-projection rows (prefetch);
-//   5. grid barrier (arrival flags);
+//      publishes a[j][i] = silu(g)*u; every wave then issues the loads of its down rows;
+//   5. a: each wave gathers the a values of the slot(s) its down rows belong to and
+//      builds their digit image;
 //   6. down + combine + residual: workgroup g owns a contiguous block of h rows and
-//      computes h[r] += sum_j w_j * (Wd_j[r] . a_j) for them (fixed slot order); the
-//      next layer's router rows are loaded meanwhile;
-//   7. grid barrier, next layer.
+//      computes h[r] += sum_j w_j * (Wd_j[r] . a_j) for them (fixed slot order), published
+//      for the next layer.
 //
-// Exchange between workgroups. Everything shared (h, a, logits, flags) is written and
-// read with device-scope relaxed atomic accesses, which are performed at the device
-// coherence point (no cache write-back or invalidation needed). A wave waits for its own
-// stores (s_waitcnt) before its workgroup raises its flag, and reads exchanged data only
-// after it has observed the flags. Each shared item is written to kRep replicas and
-// workgroup g reads replica g % kRep, so that no memory line is polled by more than
-// G / kRep workgroups at once (polling one line from all 256 workgroups serializes at the
-// memory side and costs microseconds per round).
-//
-// Wave 0 raises the flags and polls. A wave's loads return in issue order, so its poll
-// completes only after its own prefetched down rows have arrived; those are needed right
-// after the barrier anyway.
+// Exchange between workgroups. h, a and the logits are exchanged as 64-bit words
+// (fp32 value | epoch << 32), written and read with device-scope relaxed atomic accesses,
+// which are performed at the device coherence point (no cache write-back or invalidation
+// needed). A reader polls its words until each carries the epoch of the current layer, so
+// no flag or barrier is needed: a value and its readiness arrive in one access. Epochs
+// grow by 3 per layer and continue across launches (the last one is kept in the
+// workspace), so an old word is never taken for a current one. Each word is written to
+// kRep replicas and workgroup g reads replica g % kRep, so that no memory line is polled
+// by more than G / kRep workgroups at once. Every wait is bounded (spin limit, then the
+// error word and NaN outputs).
 //
 // Shapes. The template parameters HC, IC, EC, KC fix hidden, inter, n_experts and k at
-// compile time (0 = read them from the parameters); the decode shape of the 60-layer
-// 512-expert stack gets its own instantiation so that every index is a constant.
+// compile time (0 = read them from the parameters); the decode shapes of the 60-layer
+// 512-expert stack get their own instantiations so that every index is a constant and the
+// waves reduce all of their items together.
 //
 // LDS layout. fp32 vectors are stored with one padding word after every chunk of kCodes
 // values, so that threads reading consecutive chunks hit different banks.
@@ -53,6 +52,7 @@ constexpr int kDecodeWaves = kDecodeThreads / 64;
 constexpr unsigned kSpinLimit = 1u << 21;
 constexpr int kBatchN = 16;     // h / a values loaded together per thread
 constexpr int kPollN = 8;       // tagged h / a words polled together per thread
+constexpr int kPollA = 16;      // tagged a words of one slot polled together per lane
 constexpr int kBatchR = 2;      // router slices per wave loaded ahead
 constexpr int kKeysInRegs = 8;  // top-k from registers when n_experts <= 512
 
@@ -81,22 +81,23 @@ __device__ __forceinline__ uint64_t tagged(float v, uint32_t epoch) {
   return ((uint64_t)epoch << 32) | __float_as_uint(v);
 }
 
-// Read n tagged values src[i0 + u * kDecodeThreads] (u < kPollN, i < n), waiting until
-// each carries `epoch`; only stale words are read again. Returns false (after raising the
-// error word) when the wait gave up.
-__device__ __forceinline__ bool poll_batch(const uint64_t* src, int n, int i0, uint32_t epoch, float (&out)[kPollN],
+// Read n tagged values src[i0 + u * STRIDE] (u < N, i < n), waiting until each carries
+// `epoch`; only stale words are read again. Returns false (after raising the error word)
+// when the wait gave up.
+template <int N, int STRIDE>
+__device__ __forceinline__ bool poll_batch(const uint64_t* src, int n, int i0, uint32_t epoch, float (&out)[N],
                                            uint32_t* err) {
-  uint64_t v[kPollN];
+  uint64_t v[N];
 #pragma unroll
-  for (int u = 0; u < kPollN; ++u) {
-    const int i = i0 + u * kDecodeThreads;
+  for (int u = 0; u < N; ++u) {
+    const int i = i0 + u * STRIDE;
     v[u] = i < n ? ld_dev_u64(src + i) : tagged(0.f, epoch);
   }
   unsigned spins = 0;
   while (true) {
     bool ok = true;
 #pragma unroll
-    for (int u = 0; u < kPollN; ++u) ok &= (uint32_t)(v[u] >> 32) == epoch;
+    for (int u = 0; u < N; ++u) ok &= (uint32_t)(v[u] >> 32) == epoch;
     if (ok) break;
     if (spin_failed(++spins, err)) {
       st_dev_u32(err, 1u);
@@ -104,13 +105,13 @@ __device__ __forceinline__ bool poll_batch(const uint64_t* src, int n, int i0, u
     }
     __builtin_amdgcn_s_sleep(1);
 #pragma unroll
-    for (int u = 0; u < kPollN; ++u) {
-      const int i = i0 + u * kDecodeThreads;
+    for (int u = 0; u < N; ++u) {
+      const int i = i0 + u * STRIDE;
       if ((uint32_t)(v[u] >> 32) != epoch) v[u] = ld_dev_u64(src + i);
     }
   }
 #pragma unroll
-  for (int u = 0; u < kPollN; ++u) out[u] = __uint_as_float((uint32_t)v[u]);
+  for (int u = 0; u < N; ++u) out[u] = __uint_as_float((uint32_t)v[u]);
   return true;
 }
 
@@ -163,6 +164,11 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
   int* fail = isel + 16;
   int* ready = fail + 1;
   uint32_t* base = reinterpret_cast<uint32_t*>(ready + 1);
+  DigitStore dig_a;  // digit image of a (v keeps its own until the next layer)
+  dig_a.n_chunks = KI / CC;
+  dig_a.words = base + 4;
+  dig_a.step = reinterpret_cast<float*>(dig_a.words + (size_t)NW * dig_a.n_chunks);
+  dig_a.xsum = dig_a.step + dig_a.n_chunks;
 
   if (tid == 0) {
     *fail = 0;
@@ -240,7 +246,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
           const int i = i0 + u * kDecodeThreads;
           hv[u] = i < H ? p.x_in[i] : 0.f;
         }
-      } else if (!poll_batch(h_rep, H, i0, ep, hv, p.err)) {
+      } else if (!poll_batch<kPollN, kDecodeThreads>(h_rep, H, i0, ep, hv, p.err)) {
         *fail = 1;
       }
 #pragma unroll
@@ -258,14 +264,14 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
     if (tid == 0) *ready = 0;
     __syncthreads();
     if (*fail) break;
+    // v = inv * h is never formed: the router sums are scaled by inv, and so are the
+    // steps and sums of v's digit image
     float inv = 1.f;
     if (p.flags & FMOE_PRENORM) {
       float tot = 0.f;
       for (int w2 = 0; w2 < kDecodeWaves; ++w2) tot += red[w2];
       inv = 1.0f / sqrtf(tot / (float)H + p.eps);
     }
-    for (int i = tid; i < H; i += kDecodeThreads) vec[padded<CC>(i)] *= inv;
-    __syncthreads();
 
     // ---- 2. router: dot the loaded slices with v (the first two of a wave reduced together)
     int m_first = 0;
@@ -290,7 +296,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
         acc2[u] = acc;
       }
       const float sum = reduce_transposed<2, 64>(acc2);
-      if (lane < 2) part[wave + kDecodeWaves * lane] = sum;  // lane u holds slice u's total
+      if (lane < 2) part[wave + kDecodeWaves * lane] = sum * inv;  // lane u holds slice u's total
       m_first = 2;
     }
     for (int m = m_first; wave + kDecodeWaves * m < n_ritems; ++m) {
@@ -312,7 +318,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
         }
       }
       acc = wave_sum(acc);
-      if (lane == 0) part[it] = acc;
+      if (lane == 0) part[it] = acc * inv;
     }
     __syncthreads();
     const uint64_t tag = (uint64_t)(ep + 1u) << 32;
@@ -400,7 +406,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
         }
       }
     } else {
-      build_digits<BITS>(dig, H, [&](int i) { return vec[padded<CC>(i)]; }, kDecodeThreads - 64, tid - 64);
+      build_digits<BITS>(dig, 0, H, [&](int i) { return vec[padded<CC>(i)]; }, kDecodeThreads - 64, tid - 64, inv);
       // the digit image is complete once every builder wave has passed this point
       if (lane == 0) __hip_atomic_fetch_add(base + 1, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
       wait_ready(ready, gu_need);
@@ -532,56 +538,69 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
 #pragma unroll
     for (int u = 0; u < kBatchD; ++u) down_load(u, u);
 
-    // ---- 5. all of a (tagged), into LDS
-    __syncthreads();  // every wave is done with the digit image of v
-    for (int i0 = tid; i0 < KI; i0 += kDecodeThreads * kPollN) {
-      float av[kPollN];
-      if (!poll_batch(a_rep, KI, i0, ep + 2u, av, p.err)) *fail = 1;
-#pragma unroll
-      for (int u = 0; u < kPollN; ++u) {
-        const int i = i0 + u * kDecodeThreads;
-        if (i < KI) vec[padded<CC>(i)] = av[u];
-      }
-    }
-    __syncthreads();
-    if (*fail) break;
-    dig.n_chunks = KI / CC;
-    build_digits<BITS>(dig, KI, [&](int i) { return vec[padded<CC>(i)]; }, kDecodeThreads, tid);
-    __syncthreads();
-
-    // ---- 6. down (every wave), then combine + residual (wave 0), published tagged; the
-    // next layer's router slices are requested after the down loop (their latency hides
-    // behind the combine and the exchange of h)
-    // a wave whose items all belong to one slot and fit one batch (all of them prefetched)
-    // reduces them together; lane i < kBatchD of a row group then holds the sum of item
-    // transposed_index(i)
+    // ---- 5./6. a, then down. When every wave's down items belong to one slot and fit one
+    // batch (the compiled decode shapes), each wave gathers only its slot's a (written by
+    // the workgroups that ran that slot's gate/up), builds that slot's digit image in its
+    // own range of the store and reduces its items together, with no workgroup barrier
+    // before the combine. Otherwise the workgroup gathers all of a, digitises it once and
+    // reduces the down items one by one. (v's LDS image is free by now: the router and the
+    // digit builders of v finished before any wave started gate/up.)
     const int j_lo = d_lo / n_rb;
-    const bool fast_d = kFastD && d_hi > d_lo && d_hi - d_lo <= kBatchD && (d_hi - 1) / n_rb == j_lo;
+    const bool fast_d = kFastD && d_per <= kBatchD && n_rb % d_per == 0;  // uniform over the workgroup
     if (fast_d) {
       if constexpr (kFastD) {
-        DChunk<BITS> dc[CPL_D];
+        if (d_lo < d_hi) {
+          const uint64_t* a_j = a_rep + (size_t)j_lo * I;
+          for (int i0 = lane; i0 < I; i0 += 64 * kPollA) {
+            float av[kPollA];
+            if (!poll_batch<kPollA, 64>(a_j, I, i0, ep + 2u, av, p.err)) *fail = 1;
 #pragma unroll
-        for (int q = 0; q < CPL_D; ++q) {
-          int c = subD + kLprD * q;
-          if (c < nchD) load_dchunk<BITS>(dc[q], dig, j_lo * nchD + c);
-        }
-        float acc[kBatchD];
-#pragma unroll
-        for (int u = 0; u < kBatchD; ++u) {
-          float a_ = 0.f;
+            for (int u = 0; u < kPollA; ++u) {
+              const int i = i0 + 64 * u;
+              if (i < I) vec[padded<CC>(j_lo * I + i)] = av[u];
+            }
+          }
+          __builtin_amdgcn_wave_barrier();
+          build_digits<BITS>(dig_a, j_lo * nchD, I, [&](int i) { return vec[padded<CC>(i)]; }, 64, lane);
+          __builtin_amdgcn_wave_barrier();
+          DChunk<BITS> dc[CPL_D];
 #pragma unroll
           for (int q = 0; q < CPL_D; ++q) {
             int c = subD + kLprD * q;
-            if (c < nchD) a_ += chunk_dot_int<BITS>(wd[u][q], sd[u][q], dc[q]);
+            if (c < nchD) load_dchunk<BITS>(dc[q], dig_a, j_lo * nchD + c);
           }
-          acc[u] = a_;
+          float acc[kBatchD];
+#pragma unroll
+          for (int u = 0; u < kBatchD; ++u) {
+            float a_ = 0.f;
+#pragma unroll
+            for (int q = 0; q < CPL_D; ++q) {
+              int c = subD + kLprD * q;
+              if (c < nchD) a_ += chunk_dot_int<BITS>(wd[u][q], sd[u][q], dc[q]);
+            }
+            acc[u] = a_;
+          }
+          // lane i < kBatchD of a row group holds the sum of item transposed_index(i)
+          const float sum = reduce_transposed<kBatchD, kLprD>(acc);
+          const int u = transposed_index<kBatchD>(lane);
+          const int rl = (d_lo - j_lo * n_rb + u) * rpwD + rselD;
+          if (subD < kBatchD && d_lo + u < d_hi && rl < nr) ybuf[j_lo * rows_wg + rl] = sum;
         }
-        const float sum = reduce_transposed<kBatchD, kLprD>(acc);
-        const int u = transposed_index<kBatchD>(lane);
-        const int rl = (d_lo - j_lo * n_rb + u) * rpwD + rselD;
-        if (subD < kBatchD && d_lo + u < d_hi && rl < nr) ybuf[j_lo * rows_wg + rl] = sum;
       }
     } else {
+      for (int i0 = tid; i0 < KI; i0 += kDecodeThreads * kPollN) {
+        float av[kPollN];
+        if (!poll_batch<kPollN, kDecodeThreads>(a_rep, KI, i0, ep + 2u, av, p.err)) *fail = 1;
+#pragma unroll
+        for (int u = 0; u < kPollN; ++u) {
+          const int i = i0 + u * kDecodeThreads;
+          if (i < KI) vec[padded<CC>(i)] = av[u];
+        }
+      }
+      __syncthreads();
+      if (*fail) break;
+      build_digits<BITS>(dig_a, 0, KI, [&](int i) { return vec[padded<CC>(i)]; }, kDecodeThreads, tid);
+      __syncthreads();
       int cur_j = -1;
       DChunk<BITS> dc[CPL_D];
       for (int m0 = 0; d_lo + m0 < d_hi; m0 += kBatchD) {
@@ -599,7 +618,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
 #pragma unroll
             for (int q = 0; q < CPL_D; ++q) {
               int c = subD + lprD * q;
-              if (c < nchD) load_dchunk<BITS>(dc[q], dig, j * nchD + c);
+              if (c < nchD) load_dchunk<BITS>(dc[q], dig_a, j * nchD + c);
             }
             cur_j = j;
           }
@@ -616,10 +635,12 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
         }
       }
     }
+    // the next layer's router slices are requested now; their latency hides behind the
+    // combine and the exchange of h
 #pragma unroll
     for (int u = 0; u < kBatchR; ++u) router_load(l + 1, wave + kDecodeWaves * u, u);
     __syncthreads();
-    dig.n_chunks = H / CC;
+    if (*fail) break;
     const bool last = (l == p.n_layers - 1) && p.is_final;
     if (wave == 0) {
       // 16 rows at a time; the four lanes of a row (lane & 15) share its replica stores
@@ -672,8 +693,10 @@ size_t decode_smem_bytes(int hidden, int inter, int n_experts, int k, int G, int
   const size_t max_chunks = vec_len / cc;
   int my_experts = (n_experts + G - 1) / G;
   int S = (hidden + 1023) / 1024;
+  const size_t a_chunks = ki / cc;
   size_t words = vec_len + vec_len / cc + (size_t)nw * max_chunks + 2 * max_chunks + (size_t)my_experts * S +
-                 (size_t)k * rows_per_wg + rows_per_wg + kDecodeWaves + 16 + 16 + 16 + 4;
+                 (size_t)k * rows_per_wg + rows_per_wg + kDecodeWaves + 16 + 16 + 16 + 4 + (size_t)nw * a_chunks +
+                 2 * a_chunks;
   return (size_t)n_experts * 8 + words * 4;
 }
 

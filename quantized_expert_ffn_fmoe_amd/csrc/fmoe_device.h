@@ -314,7 +314,7 @@ __device__ __forceinline__ void wave_topk_keys(uint64_t* keys, int n, int k, int
       }
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_wave_barrier();
   float ex = 0.f;
   if (lane < k) ex = expf(lsel[lane] - lsel[0]);
@@ -379,7 +379,7 @@ __device__ __forceinline__ void wave_topk_regs(uint64_t (&kr)[KPL], int k, int* 
       kr[KPL - 1] = 0;
     }
   }
-  __builtin_amdgcn_s_waitcnt(0);
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
   __builtin_amdgcn_wave_barrier();
   float ex = 0.f;
   if (lane < k) ex = expf(lsel[lane] - lsel[0]);

@@ -4,9 +4,9 @@
 // Per chunk of activation values (the columns one 16-byte code chunk covers: 32 at 4
 // bits, 64 at 2 bits) the values are put on a common fixed-point grid:
 //   step = 2^(e - 22) with max|x| < 2^e,   X_j = rint(x_j / step),  |X_j| < 2^22,
-// and stored as U_j = X_j + 2^23 (0 <= U_j < 2^24) in six 4-bit digits d_k(U_j). For a
+// and stored as U_j = X_j + 2^22 (0 <= U_j < 2^23) in six 4-bit digits d_k(U_j). For a
 // row with codes q_j, sum_j q_j x_j ~= step * sum_j q_j X_j, and
-//   sum_j q_j X_j = sum_k 16^k D_k - 2^23 N,  D_k = sum_j q_j d_k(U_j),  N = sum_j q_j,
+//   sum_j q_j X_j = sum_k 16^k D_k - 2^22 N,  D_k = sum_j q_j d_k(U_j),  N = sum_j q_j,
 // where every D_k and N is one v_dot8 chain per code dword (exact integers). The only
 // rounding is that of x to the grid (at most step/2 = 2^-23 of the chunk's largest
 // magnitude) and the final conversion to fp32; the per-group affine form is then
@@ -86,7 +86,7 @@ __device__ __forceinline__ float chunk_qx_int(const uint4& w, const DChunk<BITS>
     }
   }
   const int lo = (int)(D[0] + (D[1] << 4) + (D[2] << 8));
-  const int hi = (int)(D[3] + (D[4] << 4) + (D[5] << 8)) - (int)(N << 11);
+  const int hi = (int)(D[3] + (D[4] << 4) + (D[5] << 8)) - (int)(N << 10);
   return fmaf(4096.f, (float)hi, (float)lo) * dc.step;
 }
 
@@ -95,17 +95,53 @@ __device__ __forceinline__ float chunk_dot_int(const uint4& w, uint32_t sb, cons
   return fmaf(bf16_lo(sb), chunk_qx_int<BITS>(w, dc), bf16_hi(sb) * dc.xsum);
 }
 
-// Build the digit store of an fp32 vector x[0..n) (n a multiple of the chunk size),
-// readable through xat(i). Work items are 8-column digit sets; the sets of one chunk sit
-// on consecutive lanes, which share the chunk's maximum and sum through DPP. Run by
-// `nthreads` threads (a multiple of 64) with thread index t; no barrier inside.
+// Six 4-bit digit words of 8 values: word k holds nibble k of u[p] in nibble p (an 8 x 8
+// nibble transpose of which rows 0..5 are kept; nibbles 6 and 7 of the inputs are
+// ignored). Three block-swap stages: 4-nibble and 2-nibble blocks move as whole bytes
+// (v_perm_b32), single nibbles with a bit-field insert.
+__device__ __forceinline__ void nibble_transpose6(const uint32_t (&u)[8], uint32_t (&d)[6]) {
+  uint32_t r[8];
+  // stage 1: nibbles 4..7 of row p <-> nibbles 0..3 of row p + 4
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    r[p] = __builtin_amdgcn_perm(u[p + 4], u[p], 0x05040100u);      // [a0 a1 b0 b1]
+    r[p + 4] = __builtin_amdgcn_perm(u[p + 4], u[p], 0x07060302u);  // [a2 a3 b2 b3]
+  }
+  // stage 2: bytes 1, 3 of row p <-> bytes 0, 2 of row p + 2
+#pragma unroll
+  for (int p : {0, 1, 4, 5}) {
+    const uint32_t a = r[p], b = r[p + 2];
+    r[p] = __builtin_amdgcn_perm(b, a, 0x06020400u);      // [a0 b0 a2 b2]
+    r[p + 2] = __builtin_amdgcn_perm(b, a, 0x07030501u);  // [a1 b1 a3 b3]
+  }
+  // stage 3: odd nibbles of row p <-> even nibbles of row p + 1 (rows 6, 7 not needed)
+#pragma unroll
+  for (int p = 0; p < 6; p += 2) {
+    const uint32_t a = r[p], b = r[p + 1];
+    d[p] = (a & 0x0F0F0F0Fu) | ((b << 4) & 0xF0F0F0F0u);
+    d[p + 1] = ((a >> 4) & 0x0F0F0F0Fu) | (b & 0xF0F0F0F0u);
+  }
+}
+
+// Build the digit store entries of chunks c0 .. c0 + n / CC of an fp32 vector (n a
+// multiple of the chunk size), whose column i is read through xat(i); the stored step and
+// sum are multiplied by `scale` (a vector v = scale * x is digitised through x). Work
+// items are 8-column digit sets; the sets of one chunk sit on consecutive lanes, which
+// share the chunk's maximum and sum through DPP. Run by `nthreads` threads (a multiple of
+// 64) with thread index t; no barrier inside.
+//
+// Rounding to the grid: with |x / step| < 2^22, fma(x, 1/step, 1.5 * 2^23) lies in
+// [2^23, 2^24), where fp32 has unit spacing, so the single rounding of the fma is the
+// round-to-nearest-even of x / step and the low 23 bits of the result are
+// rint(x / step) + 2^22 = U.
 template <int BITS, typename XAt>
-__device__ __forceinline__ void build_digits(const DigitStore& st, int n, XAt xat, int nthreads, int t) {
+__device__ __forceinline__ void build_digits(const DigitStore& st, int c0, int n, XAt xat, int nthreads, int t,
+                                             float scale = 1.f) {
   constexpr int CC = Digits<BITS>::kCodes;
   constexpr int SETS = Digits<BITS>::kSets;
   const int n_sets = (n / CC) * SETS;
   for (int it = t; it < n_sets; it += nthreads) {
-    const int c = it / SETS, set = it % SETS;
+    const int c = c0 + it / SETS, set = it % SETS;
     float x[8];
     float m = 0.f, s = 0.f;
 #pragma unroll
@@ -125,19 +161,16 @@ __device__ __forceinline__ void build_digits(const DigitStore& st, int n, XAt xa
     const float step = tiny ? 1.f : ldexpf(1.f, e - 22);
     const float inv = tiny ? 0.f : ldexpf(1.f, 22 - e);
     if (set == 0) {
-      st.step[c] = step;
-      st.xsum[c] = s;
+      st.step[c] = step * scale;
+      st.xsum[c] = s * scale;
     }
     uint32_t u[8];
 #pragma unroll
-    for (int p = 0; p < 8; ++p) u[p] = (uint32_t)((int)rintf(x[p] * inv) + (1 << 23));
+    for (int p = 0; p < 8; ++p) u[p] = __float_as_uint(fmaf(x[p], inv, 12582912.0f));
+    uint32_t d[6];
+    nibble_transpose6(u, d);
 #pragma unroll
-    for (int k = 0; k < 6; ++k) {
-      uint32_t d = 0;
-#pragma unroll
-      for (int p = 0; p < 8; ++p) d |= ((u[p] >> (4 * k)) & 15u) << (4 * p);
-      st.words[(set * 6 + k) * st.n_chunks + c] = d;
-    }
+    for (int k = 0; k < 6; ++k) st.words[(set * 6 + k) * st.n_chunks + c] = d[k];
   }
 }
 
