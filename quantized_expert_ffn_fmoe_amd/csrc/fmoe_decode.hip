@@ -213,20 +213,20 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
   const uint64_t* a_rep = p.a + (size_t)rep * KI;
   const uint64_t* logits_rep = p.logits + (size_t)rep * E;
 
-  // router slice `it` of layer `lr`: up to 4 float4 per lane
+  // router slice `it` of layer `lr`: up to 4 float4 per lane. The loads are unconditional
+  // (an index past the end is clamped to a valid row whose values go unused): a
+  // conditional load would make the compiler wait for it on the spot to merge the old
+  // register contents, instead of where the values are used.
   float4 rv[kBatchR][4];
   auto router_load = [&](int lr, int it, int u) {
-    if (it < n_ritems && lr < p.n_layers) {
-      const int el = it / S, s = it % S;
-      const int e = g + el * G;
-      const int c0 = s * 256, c1 = min(H / 4, c0 + 256);
-      const float4* row = reinterpret_cast<const float4*>(p.router[lr] + (size_t)e * H);
+    const int lc = min(lr, p.n_layers - 1);
+    const int itc = max(0, min(it, n_ritems - 1));
+    const int el = itc / S, s = itc % S;
+    const int e = min(g + el * G, E - 1);
+    const int c0 = s * 256, c1 = min(H / 4, c0 + 256);
+    const float4* row = reinterpret_cast<const float4*>(p.router[lc] + (size_t)e * H);
 #pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        const int c = c0 + lane + 64 * q;
-        if (c < c1) rv[u][q] = row[c];
-      }
-    }
+    for (int q = 0; q < 4; ++q) rv[u][q] = row[min(c0 + lane + 64 * q, c1 - 1)];
   };
 #pragma unroll
   for (int u = 0; u < kBatchR; ++u) router_load(0, wave + kDecodeWaves * u, u);
@@ -427,8 +427,10 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
         uint32_t sg[kBatchGU][CPL_G], su[kBatchGU][CPL_G];
 #pragma unroll
         for (int u = 0; u < kBatchGU; ++u) {
-          const int item = (b0 + u) * rpwG + rselG;
-          if (b0 + u < blk_hi && item < KI) {
+          // fast path: unconditional loads (an item past the run reads the run's last row,
+          // whose result is not stored), so that each item waits only for its own loads
+          const int item = kFastGU ? min(b0 + u, blk_hi - 1) : (b0 + u) * rpwG + rselG;
+          if (kFastGU || (b0 + u < blk_hi && item < KI)) {
             const int j = item / I, i = item % I;
             const uint8_t* bp = X + (size_t)isel[j] * p.expert_stride;
             const uint4* gp = reinterpret_cast<const uint4*>(bp + (size_t)i * rowH);
@@ -438,7 +440,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
 #pragma unroll
             for (int q = 0; q < CPL_G; ++q) {
               int c = subG + lprG * q;
-              if (c < nchG) {
+              if (kFastGU || c < nchG) {  // the fast path covers exactly nchG chunks per row
                 wg[u][q] = gp[c];
                 wu[u][q] = up[c];
                 sg[u][q] = gsb[c / C::kPerGroup];
@@ -474,6 +476,9 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
             }
             vals[u] = gs;
             vals[4 + u] = us;
+            // keep the items in load order, so each waits only for its own rows and its
+            // arithmetic overlaps the arrival of the next ones
+            __builtin_amdgcn_sched_barrier(0);
           }
           const float sum = reduce_transposed<8, 64>(vals);
           const float up_sum = xlane<1>(sum);
