@@ -332,6 +332,10 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
         for (int s = 0; s < S; ++s) lsum += part[el * S + s];
         st_dev_u64(p.logits + (size_t)rr * E + g + el * G, tag | __float_as_uint(lsum));
       }
+      // poll only once the own logits are acknowledged: a first read issued right behind
+      // the stores samples memory too early (its result waits for the stores anyway) and
+      // costs one more round trip
+      wait_vmem();
       unsigned spins = 0;
       bool failed = false;
       uint64_t kr[kKeysInRegs];  // E <= 64 * kKeysInRegs: keys stay in registers
