@@ -238,6 +238,9 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
 
     // ---- 1. h (the previous layer's tagged output, or x_in), v = rmsnorm(h) or h in LDS
     float ss = 0.f;
+    // the first read of h waits for the router rows requested at the end of the previous
+    // layer anyway (loads complete in order); issuing it after them samples h later
+    if (lg != 0) wait_vmem();
     for (int i0 = tid; i0 < H; i0 += kDecodeThreads * kPollN) {
       float hv[kPollN];
       if (lg == 0) {
@@ -560,6 +563,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
       if constexpr (kFastD) {
         if (d_lo < d_hi) {
           const uint64_t* a_j = a_rep + (size_t)j_lo * I;
+          wait_vmem();  // as for h: the first read of a would wait for the down rows anyway
           for (int i0 = lane; i0 < I; i0 += 64 * kPollA) {
             float av[kPollA];
             if (!poll_batch<kPollA, 64>(a_j, I, i0, ep + 2u, av, p.err)) *fail = 1;
