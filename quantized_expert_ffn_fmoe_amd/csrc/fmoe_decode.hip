@@ -707,10 +707,12 @@ size_t decode_smem_bytes(int hidden, int inter, int n_experts, int k, int G, int
   int my_experts = (n_experts + G - 1) / G;
   int S = (hidden + 1023) / 1024;
   const size_t a_chunks = ki / cc;
+  // after the padded vector and v's digit store: router partials, ybuf, hraw, red, wsel,
+  // lsel, isel (16 each), fail, ready, base[4], then a's digit store
   size_t words = vec_len + vec_len / cc + (size_t)nw * max_chunks + 2 * max_chunks + (size_t)my_experts * S +
-                 (size_t)k * rows_per_wg + rows_per_wg + kDecodeWaves + 16 + 16 + 16 + 4 + (size_t)nw * a_chunks +
+                 (size_t)k * rows_per_wg + rows_per_wg + kDecodeWaves + 16 + 16 + 16 + 6 + (size_t)nw * a_chunks +
                  2 * a_chunks;
-  return (size_t)n_experts * 8 + words * 4;
+  return (size_t)n_experts * 8 + words * 4;  // rank keys first
 }
 
 int decode_grid(int* G_out) {

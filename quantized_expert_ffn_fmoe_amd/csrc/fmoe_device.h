@@ -133,7 +133,8 @@ __device__ __forceinline__ float chunk_dot(const uint4& w, uint32_t sb, const XC
 
 // Cross-lane data movement with DPP (no LDS round trip). Controls (GFX9 encoding):
 // quad_perm [1,0,3,2] = 0xB1, quad_perm [2,3,0,1] = 0x4E, row_half_mirror = 0x141,
-// row_mirror = 0x140, row_ror:4 = 0x124, row_ror:8 = 0x128.
+// row_mirror = 0x140, row_ror:4 = 0x124, row_ror:8 = 0x128, row_bcast:15 = 0x142,
+// row_bcast:31 = 0x143.
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
   return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
@@ -153,10 +154,15 @@ __device__ __forceinline__ float group_sum(float v, int width) {
   if (width >= 4) v += dpp_f<0x4E>(v);
   if (width >= 8) v += dpp_f<0x141>(v);
   if (width >= 16) v += dpp_f<0x140>(v);
-  if (width >= 32) {
+  if (width == 32) {
     const float r0 = readlane_f(v, 0), r1 = readlane_f(v, 16), r2 = readlane_f(v, 32), r3 = readlane_f(v, 48);
-    if (width == 32) v = (threadIdx.x & 32) ? (r2 + r3) : (r0 + r1);
-    else v = (r0 + r1) + (r2 + r3);
+    v = (threadIdx.x & 32) ? (r2 + r3) : (r0 + r1);
+  } else if (width >= 64) {
+    // rows 1 and 3 add lane 15 of the row before (row_bcast:15), then rows 2 and 3 add
+    // lane 31 (row_bcast:31): lane 63 ends with the total
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x142, 0xA, 0xF, false));
+    v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x143, 0xC, 0xF, false));
+    v = readlane_f(v, 63);
   }
   return v;
 }
@@ -329,9 +335,37 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   v = max(v, dpp_u<0x4E>(v));
   v = max(v, dpp_u<0x141>(v));
   v = max(v, dpp_u<0x140>(v));
-  const uint32_t a = (uint32_t)__builtin_amdgcn_readlane((int)v, 0), b = (uint32_t)__builtin_amdgcn_readlane((int)v, 16);
-  const uint32_t c = (uint32_t)__builtin_amdgcn_readlane((int)v, 32), d = (uint32_t)__builtin_amdgcn_readlane((int)v, 48);
-  return max(max(a, b), max(c, d));
+  // across rows as in group_sum (row_bcast:15, then row_bcast:31); lanes outside the row
+  // mask keep their own value
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x142, 0xA, 0xF, false));
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, 0x143, 0xC, 0xF, false));
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, 63);
+}
+
+// The wave-wide maximum of one rank key per lane (0 = no key): the 32-bit maximum of the
+// high words (the ordered logits), then, only when several lanes hold that logit, the
+// maximum of their low words (lower index first). Wave-uniform result.
+__device__ __forceinline__ uint64_t wave_max_key(uint64_t key) {
+  const uint32_t hi = (uint32_t)(key >> 32), lo = (uint32_t)key;
+  const uint32_t m = wave_max_u32(hi);
+  const uint64_t tied = __ballot(hi == m);
+  uint32_t lw;
+  if (__popcll(tied) == 1) lw = (uint32_t)__builtin_amdgcn_readlane((int)lo, (int)__ffsll((long long)tied) - 1);
+  else lw = wave_max_u32(hi == m ? lo : 0u);
+  return ((uint64_t)m << 32) | lw;
+}
+
+// One round of a top-k over per-lane key lists sorted in descending order: the wave
+// maximum of the heads; the lane holding it drops its head. Returns the winner.
+template <int KPL>
+__device__ __forceinline__ uint64_t topk_round(uint64_t (&kr)[KPL]) {
+  const uint64_t w = wave_max_key(kr[0]);
+  if (kr[0] == w) {
+#pragma unroll
+    for (int j = 0; j + 1 < KPL; ++j) kr[j] = kr[j + 1];
+    kr[KPL - 1] = 0;
+  }
+  return w;
 }
 
 template <int N>
@@ -340,6 +374,30 @@ __device__ __forceinline__ void cmp_swap_desc(uint64_t (&k)[N], int i, int j) {
   const bool sw = b > a;
   k[i] = sw ? b : a;
   k[j] = sw ? a : b;
+}
+
+// k rounds of topk_round over sorted per-lane lists, recording each winner (index and
+// logit, lane 0) and releasing progress r + 1 after round r; then the softmax over the k
+// selected logits (max-subtracted) and progress k + 1.
+template <int KPL>
+__device__ __forceinline__ void topk_select(uint64_t (&kr)[KPL], int k, int* isel, float* lsel, float* wsel,
+                                            int* ready) {
+  const int lane = threadIdx.x & 63;
+  for (int r = 0; r < k; ++r) {
+    const uint64_t w = topk_round(kr);
+    if (lane == 0) {
+      isel[r] = rank_key_index(w);
+      lsel[r] = rank_key_logit(w);
+    }
+    topk_progress(ready, r + 1);
+  }
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_wave_barrier();
+  float ex = 0.f;
+  if (lane < k) ex = expf(lsel[lane] - lsel[0]);
+  const float denom = wave_sum(ex);
+  if (lane < k) wsel[lane] = ex / denom;
+  topk_progress(ready, k + 1);
 }
 
 // Top-k of at most 64 * KPL ranked keys held in registers (key j of a lane is element
@@ -360,33 +418,10 @@ __device__ __forceinline__ void wave_topk_regs(uint64_t (&kr)[KPL], int k, int* 
   cmp_swap_desc(kr, 0, 4); cmp_swap_desc(kr, 1, 5); cmp_swap_desc(kr, 2, 6); cmp_swap_desc(kr, 3, 7);
   cmp_swap_desc(kr, 2, 4); cmp_swap_desc(kr, 3, 5);
   cmp_swap_desc(kr, 1, 2); cmp_swap_desc(kr, 3, 4); cmp_swap_desc(kr, 5, 6);
-  for (int r = 0; r < k; ++r) {
-    const uint32_t hi = (uint32_t)(kr[0] >> 32), lo = (uint32_t)kr[0];
-    const uint32_t m = wave_max_u32(hi);
-    const uint64_t tied = __ballot(hi == m);
-    uint32_t lw;
-    if (__popcll(tied) == 1) lw = (uint32_t)__builtin_amdgcn_readlane((int)lo, (int)__ffsll((long long)tied) - 1);
-    else lw = wave_max_u32(hi == m ? lo : 0u);
-    const uint64_t w = ((uint64_t)m << 32) | lw;
-    if (lane == 0) {
-      isel[r] = rank_key_index(w);
-      lsel[r] = rank_key_logit(w);
-    }
-    topk_progress(ready, r + 1);
-    if (kr[0] == w) {
-#pragma unroll
-      for (int j = 0; j + 1 < KPL; ++j) kr[j] = kr[j + 1];
-      kr[KPL - 1] = 0;
-    }
-  }
-  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
-  __builtin_amdgcn_wave_barrier();
-  float ex = 0.f;
-  if (lane < k) ex = expf(lsel[lane] - lsel[0]);
-  const float denom = wave_sum(ex);
-  if (lane < k) wsel[lane] = ex / denom;
-  topk_progress(ready, k + 1);
+  topk_select(kr, k, isel, lsel, wsel, ready);
 }
+
+
 
 // silu(g) * u with silu(g) = g / (1 + exp(-g)); for very negative g, exp(-g) is +inf
 // and the quotient is -0 (never NaN).
