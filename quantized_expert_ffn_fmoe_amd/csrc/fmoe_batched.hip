@@ -54,7 +54,6 @@ constexpr int kGuRowsWave = 32;   // rows of gate (and of up) per wave
 constexpr int kGuRowsWg = 128;
 constexpr int kDnRowsWave = 64;   // rows of down per wave
 constexpr int kDnRowsWg = 256;
-constexpr int kMaxMT = 4;         // 16-token tiles per pass over an expert's weights
 constexpr int kSortThreads = 1024;
 
 // Column (0..15) of a 16-column block held at operand position p.
@@ -337,12 +336,6 @@ __global__ void __launch_bounds__(kSortThreads) sort_kernel(const int32_t* __res
 }
 
 // ---------------------------------------------------------------- 4./5. expert products
-// Token operand of one m-tile: lane row nl of the tile, K block kb.
-struct TokRow {
-  const uint16_t* p;  // start of the lane's 16 columns in group 0
-  bool valid;
-};
-
 // Stage the per-group activation sums of the pass's m-tiles: xs[mt][g][m].
 __device__ __forceinline__ void stage_sums(float* xs, const BParams& p, const float* sums, int G, int off, int cnt,
                                            int m0, int nmt, bool by_token) {
@@ -359,53 +352,184 @@ __device__ __forceinline__ void stage_sums(float* xs, const BParams& p, const fl
   }
 }
 
-// acc[mt][tile] += the affine group products of one group g for NT weight tiles.
-template <int BITS, int NT>
-__device__ __forceinline__ void group_products(f32x4 (&acc)[kMaxMT][NT], const uint8_t* const (&cptr)[NT],
-                                               const uint32_t* const (&sptr)[NT], const TokRow (&tr)[kMaxMT],
-                                               const float* xs, int G, int g, int nmt, int kb) {
-  constexpr int BPG = BITS * 8;  // code bytes per row per group
-  constexpr float F = BITS == 4 ? 16.f : 4.f;
-  u32x4 b0[NT], b1[NT];
-  float cs[NT], cb[NT];
+// Each wave owns 64 weight rows (4 tiles of 16) and streams them through a private,
+// double-buffered LDS region in stages of GC groups: one 16-byte LDS-DMA
+// (global_load_lds) per lane moves 1 KB of whole row segments per instruction, so every
+// memory line is fetched once, in full (a direct fragment load would touch 16 rows x 32
+// bytes per instruction). The scale/bias words of a stage arrive as one 16-byte load per
+// tile, and the token operands as two 16-byte loads per group; both go to registers.
+// Stage layout in LDS: instruction j carries rows j * RPI .. + RPI - 1; lane i of it
+// brings 16-byte segment i / RPI of row j * RPI + i % RPI, stored at j * 1024 + 16 i.
+constexpr int kWaveRows = 64;
+
+template <int BITS, int GC>
+struct StageGeom {
+  static constexpr int kBPG = BITS * 8;          // code bytes per row per group
+  static constexpr int kRS = GC * kBPG;          // bytes per row per stage
+  static constexpr int kRPI = 1024 / kRS;        // rows per DMA instruction
+  static constexpr int kNJ = kWaveRows / kRPI;   // DMA instructions per stage
+  static constexpr int kBytes = kWaveRows * kRS;  // LDS bytes of one stage
+  static constexpr int kLoads = kNJ + 4 + 2 * GC;  // vector memory instructions per stage
+};
+
+__device__ __forceinline__ void dma16(const void* g, char* lds) {
+  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+}
+// Wait until at most N of this wave's vector memory instructions are outstanding (the
+// compiler does not wait for LDS-DMA data by itself).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
+__device__ __forceinline__ void wait_lgkm() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+
+// Register part of one stage: scale/bias words of its GC groups for the 4 tiles, and the
+// token operand of each group (two 8-element halves).
+template <int GC>
+struct StageRegs {
+  uint32_t sb[4][GC];
+  u32x4 a[GC][2];
+};
+
+template <int BITS, int GC>
+__device__ __forceinline__ void issue_stage(char* buf, StageRegs<GC>& r,
+                                            const uint8_t* const (&dmarow)[StageGeom<BITS, GC>::kNJ],
+                                            const uint32_t* const (&sptr)[4], const uint16_t* tp, int g0, int lane) {
+  using SG = StageGeom<BITS, GC>;
 #pragma unroll
-  for (int t = 0; t < NT; ++t) {
-    uint32_t w[2];
-    if constexpr (BITS == 4) {
-      const uint2 q = *reinterpret_cast<const uint2*>(cptr[t] + (size_t)g * BPG);
-      w[0] = q.x;
-      w[1] = q.y;
+  for (int j = 0; j < SG::kNJ; ++j) dma16(dmarow[j] + (size_t)g0 * SG::kBPG + 16 * (lane / SG::kRPI), buf + j * 1024);
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    if constexpr (GC == 4) {
+      const uint4 q = *reinterpret_cast<const uint4*>(sptr[t] + g0);
+      r.sb[t][0] = q.x;
+      r.sb[t][1] = q.y;
+      r.sb[t][2] = q.z;
+      r.sb[t][3] = q.w;
     } else {
-      w[0] = *reinterpret_cast<const uint32_t*>(cptr[t] + (size_t)g * BPG);
-      w[1] = 0;
+      const uint2 q = *reinterpret_cast<const uint2*>(sptr[t] + g0);
+      r.sb[t][0] = q.x;
+      r.sb[t][1] = q.y;
     }
-    build_b<BITS>(w, b0[t], b1[t]);
-    const uint32_t sb = sptr[t][g];
-    cs[t] = F * bf16_lo(sb);
-    cb[t] = bf16_hi(sb) - cs[t];
   }
+#pragma unroll
+  for (int gl = 0; gl < GC; ++gl) {
+    const u32x4* ap = reinterpret_cast<const u32x4*>(tp + (size_t)(g0 + gl) * 64);
+    r.a[gl][0] = ap[0];
+    r.a[gl][1] = ap[1];
+  }
+}
+
+// acc[tile] += the affine group products of the GC groups of one stage (see the header:
+// codes enter the matrix core as exact bf16 values, F s P + (b - F s) X per group).
+template <int BITS, int GC>
+__device__ __forceinline__ void compute_stage(f32x4 (&acc)[4], const char* buf, const StageRegs<GC>& r,
+                                              const float* xs, int g0, int nl, int kb) {
+  using SG = StageGeom<BITS, GC>;
+  constexpr float F = BITS == 4 ? 16.f : 4.f;
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int mt = 0; mt < kMaxMT; ++mt) {
-    if (mt < nmt) {
-      u32x4 a0 = {0u, 0u, 0u, 0u}, a1 = {0u, 0u, 0u, 0u};
-      if (tr[mt].valid) {
-        const u32x4* ap = reinterpret_cast<const u32x4*>(tr[mt].p + (size_t)g * 64);
-        a0 = ap[0];
-        a1 = ap[1];
-      }
-      const float4 x4 = *reinterpret_cast<const float4*>(xs + (mt * G + g) * 16 + 4 * kb);
+  for (int gl = 0; gl < GC; ++gl) {
+    const float4 x4 = *reinterpret_cast<const float4*>(xs + (g0 + gl) * 16 + 4 * kb);
 #pragma unroll
-      for (int t = 0; t < NT; ++t) {
-        f32x4 P = mfma(a0, b0[t], zero);
-        P = mfma(a1, b1[t], P);
-        acc[mt][t][0] = fmaf(cb[t], x4.x, fmaf(cs[t], P[0], acc[mt][t][0]));
-        acc[mt][t][1] = fmaf(cb[t], x4.y, fmaf(cs[t], P[1], acc[mt][t][1]));
-        acc[mt][t][2] = fmaf(cb[t], x4.z, fmaf(cs[t], P[2], acc[mt][t][2]));
-        acc[mt][t][3] = fmaf(cb[t], x4.w, fmaf(cs[t], P[3], acc[mt][t][3]));
+    for (int t = 0; t < 4; ++t) {
+      const int R = 16 * t + nl;
+      const int off = gl * SG::kBPG + kb * (BITS * 2);  // the lane's code bytes in the row's stage segment
+      const char* src = buf + (R / SG::kRPI) * 1024 + ((off / 16) * SG::kRPI + R % SG::kRPI) * 16 + off % 16;
+      uint32_t w[2];
+      if constexpr (BITS == 4) {
+        const uint2 q = *reinterpret_cast<const uint2*>(src);
+        w[0] = q.x;
+        w[1] = q.y;
+      } else {
+        w[0] = *reinterpret_cast<const uint32_t*>(src);
+        w[1] = 0;
       }
+      u32x4 b0, b1;
+      build_b<BITS>(w, b0, b1);
+      const float cs = F * bf16_lo(r.sb[t][gl]);
+      const float cb = bf16_hi(r.sb[t][gl]) - cs;
+      f32x4 P = mfma(r.a[gl][0], b0, zero);
+      P = mfma(r.a[gl][1], b1, P);
+      acc[t][0] = fmaf(cb, x4.x, fmaf(cs, P[0], acc[t][0]));
+      acc[t][1] = fmaf(cb, x4.y, fmaf(cs, P[1], acc[t][1]));
+      acc[t][2] = fmaf(cb, x4.z, fmaf(cs, P[2], acc[t][2]));
+      acc[t][3] = fmaf(cb, x4.w, fmaf(cs, P[3], acc[t][3]));
     }
   }
+}
+
+// All G groups of a pass (GC * U divides G): blocks of U stages, two stages in flight
+// inside a block (stage u + 2 is requested once stage u has been read). A block issues
+// and consumes all of its own loads, so nothing is in flight across the loop's back edge.
+template <int BITS, int GC, int U>
+__device__ __forceinline__ void expert_pass(f32x4 (&acc)[4], char* wbuf,
+                                            const uint8_t* const (&dmarow)[StageGeom<BITS, GC>::kNJ],
+                                            const uint32_t* const (&sptr)[4], const uint16_t* tp, const float* xs,
+                                            int G, int lane, int nl, int kb) {
+  using SG = StageGeom<BITS, GC>;
+  for (int s0 = 0; s0 < G / GC; s0 += U) {
+    StageRegs<GC> r[2];
+    issue_stage<BITS, GC>(wbuf, r[0], dmarow, sptr, tp, s0 * GC, lane);
+    if constexpr (U > 1) issue_stage<BITS, GC>(wbuf + SG::kBytes, r[1], dmarow, sptr, tp, (s0 + 1) * GC, lane);
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      if (u + 1 < U) wait_vmcnt<SG::kLoads>();
+      else wait_vmcnt<0>();
+      compute_stage<BITS, GC>(acc, wbuf + (u % 2) * SG::kBytes, r[u % 2], xs, (s0 + u) * GC, nl, kb);
+      if (u + 2 < U) {
+        wait_lgkm();  // the stage's reads of this buffer are done before the DMA refills it
+        issue_stage<BITS, GC>(wbuf + (u % 2) * SG::kBytes, r[u % 2], dmarow, sptr, tp, (s0 + u + 2) * GC, lane);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  }
+}
+
+// Stage width and block length for G groups (G even for every accepted shape).
+template <int BITS, typename RowOf>
+__device__ __forceinline__ void expert_pass_any(f32x4 (&acc)[4], char* wbuf, RowOf row_of,
+                                                const uint32_t* const (&sptr)[4], const uint16_t* tp, const float* xs,
+                                                int G, int lane, int nl, int kb) {
+  if (G % 4 == 0) {
+    using SG = StageGeom<BITS, 4>;
+    const uint8_t* dmarow[SG::kNJ];
+#pragma unroll
+    for (int j = 0; j < SG::kNJ; ++j) dmarow[j] = row_of(j * SG::kRPI + lane % SG::kRPI);
+    const int NS = G / 4;
+    if (NS % 4 == 0) expert_pass<BITS, 4, 4>(acc, wbuf, dmarow, sptr, tp, xs, G, lane, nl, kb);
+    else expert_pass<BITS, 4, 1>(acc, wbuf, dmarow, sptr, tp, xs, G, lane, nl, kb);
+  } else {
+    using SG = StageGeom<BITS, 2>;
+    const uint8_t* dmarow[SG::kNJ];
+#pragma unroll
+    for (int j = 0; j < SG::kNJ; ++j) dmarow[j] = row_of(j * SG::kRPI + lane % SG::kRPI);
+    expert_pass<BITS, 2, 1>(acc, wbuf, dmarow, sptr, tp, xs, G, lane, nl, kb);
+  }
+}
+
+// LDS of one wave's stage buffers (the larger of the two stage widths).
+template <int BITS>
+constexpr int wave_stage_bytes() {
+  return 2 * (StageGeom<BITS, 4>::kBytes > StageGeom<BITS, 2>::kBytes ? StageGeom<BITS, 4>::kBytes
+                                                                       : StageGeom<BITS, 2>::kBytes);
+}
+
+// Token operand row of the lane for the pass's 16-token tile: rows past the expert's count
+// point at its last pair (their products land in output rows that are never stored).
+__device__ __forceinline__ const uint16_t* token_row(const uint16_t* base, const BParams& p, int off, int cnt, int m0,
+                                                     int nl, int kb, size_t row_len, bool by_token) {
+  const int r = min(m0 + nl, cnt - 1);
+  const int s = p.pairs[off + r];
+  return base + (size_t)(by_token ? s / p.k : s) * row_len + kb * 16;
+}
+
+// Dynamic LDS of the expert kernels: group sums of the pass's tokens, then the waves'
+// stage buffers.
+template <int BITS>
+size_t expert_smem_bytes(int G) {
+  return (size_t)G * 16 * 4 + (size_t)(kBT / 64) * wave_stage_bytes<BITS>();
 }
 
 template <int BITS>
@@ -419,70 +543,60 @@ __global__ void __launch_bounds__(kBT) gate_up_kernel(BParams p) {
   const size_t cbytes = (size_t)I * H * BITS / 8, sbytes = (size_t)I * G * 4;
   const size_t rowb = (size_t)H * BITS / 8;
   const int row0 = blockIdx.x * kGuRowsWg + wave * kGuRowsWave;
-  const uint8_t* cptr[4];
+  // tiles 0, 1: gate rows row0 .. row0 + 31; tiles 2, 3: the same rows of up
   const uint32_t* sptr[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int r = row0 + 16 * (t & 1) + nl;
-    const size_t mat = t < 2 ? 0 : 1;  // gate, up
-    cptr[t] = blob + mat * cbytes + r * rowb + kb * (BITS * 2);
-    sptr[t] = reinterpret_cast<const uint32_t*>(blob + 3 * cbytes + mat * sbytes) + (size_t)r * G;
+    sptr[t] = reinterpret_cast<const uint32_t*>(blob + 3 * cbytes + (t < 2 ? 0 : sbytes)) + (size_t)r * G;
   }
-  extern __shared__ float xs[];                 // [kMaxMT][G][16]
-  __shared__ float agp[kBT / 64][kMaxMT][16];  // per-wave sums of a16 over its 32 rows
+  auto row_of = [&](int R) {  // wave row R (tile R / 16, row R % 16)
+    const int t = R / 16;
+    return blob + (t < 2 ? 0 : cbytes) + (size_t)(row0 + 16 * (t & 1) + R % 16) * rowb;
+  };
+  extern __shared__ float smem_f[];
+  float* xs = smem_f;  // [G][16]
+  char* wbuf = reinterpret_cast<char*>(smem_f + G * 16) + wave * wave_stage_bytes<BITS>();
+  __shared__ float agp[kBT / 64][16];  // per-wave sums of a16 over its 32 rows
   const int Gd = I / 64;
-  for (int m0 = 0; m0 < cnt; m0 += 16 * kMaxMT) {
-    const int nmt = min(kMaxMT, (cnt - m0 + 15) / 16);
+  for (int m0 = 0; m0 < cnt; m0 += 16) {
     __syncthreads();
-    stage_sums(xs, p, p.xg, G, off, cnt, m0, nmt, true);
+    stage_sums(xs, p, p.xg, G, off, cnt, m0, 1, true);
     __syncthreads();
-    TokRow tr[kMaxMT];
+    const uint16_t* tp = token_row(p.v16, p, off, cnt, m0, nl, kb, (size_t)H, true);
+    f32x4 acc[4];
 #pragma unroll
-    for (int mt = 0; mt < kMaxMT; ++mt) {
-      const int r = m0 + mt * 16 + nl;
-      tr[mt].valid = mt < nmt && r < cnt;
-      tr[mt].p = p.v16 + (tr[mt].valid ? (size_t)(p.pairs[off + r] / p.k) * H : 0) + kb * 16;
-    }
-    f32x4 acc[kMaxMT][4];
+    for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    expert_pass_any<BITS>(acc, wbuf, row_of, sptr, tp, xs, G, lane, nl, kb);
+    // epilogue: a = silu(g) * u -> bf16 in the down operand's order; group sums of the
+    // rounded values
+    float part[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int mt = 0; mt < kMaxMT; ++mt)
+    for (int t = 0; t < 2; ++t) {
+      const int n = row0 + 16 * t + nl;
+      const int col = (n & ~15) + perm_pos<BITS>(n & 15);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int g = 0; g < G; ++g) group_products<BITS, 4>(acc, cptr, sptr, tr, xs, G, g, nmt, kb);
-    // epilogue: a = silu(g) * u -> bf16; group sums of the rounded values
-#pragma unroll
-    for (int mt = 0; mt < kMaxMT; ++mt) {
-      if (mt < nmt) {
-        float part[4] = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int t = 0; t < 2; ++t) {
-          const int n = row0 + 16 * t + nl;
-          const int col = (n & ~15) + perm_pos<BITS>(n & 15);
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int r = m0 + mt * 16 + 4 * kb + i;
-            const uint32_t b = bf16_rne(swiglu(acc[mt][t][i], acc[mt][t + 2][i]));
-            if (r < cnt) {
-              p.a16[(size_t)p.pairs[off + r] * I + col] = (uint16_t)b;
-              part[i] += bf16_val(b);
-            }
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) part[i] = group_sum(part[i], 16);
-        if (nl == 0) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) agp[wave][mt][4 * kb + i] = part[i];
+      for (int i = 0; i < 4; ++i) {
+        const int r = m0 + 4 * kb + i;
+        const uint32_t b = bf16_rne(swiglu(acc[t][i], acc[t + 2][i]));
+        if (r < cnt) {
+          p.a16[(size_t)p.pairs[off + r] * I + col] = (uint16_t)b;
+          part[i] += bf16_val(b);
         }
       }
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part[i] = group_sum(part[i], 16);
+    if (nl == 0) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) agp[wave][4 * kb + i] = part[i];
+    }
     __syncthreads();
     // waves 2q and 2q+1 cover the 64 rows of down group 2 * blockIdx.x + q
-    for (int i = threadIdx.x; i < 2 * nmt * 16; i += kBT) {
-      const int q = i / (nmt * 16), rest = i % (nmt * 16), mt = rest / 16, m = rest % 16;
-      const int r = m0 + mt * 16 + m;
-      if (r < cnt)
-        p.ag[(size_t)p.pairs[off + r] * Gd + 2 * blockIdx.x + q] = agp[2 * q][mt][m] + agp[2 * q + 1][mt][m];
+    for (int i = threadIdx.x; i < 2 * 16; i += kBT) {
+      const int q = i / 16, m = i % 16;
+      const int r = m0 + m;
+      if (r < cnt) p.ag[(size_t)p.pairs[off + r] * Gd + 2 * blockIdx.x + q] = agp[2 * q][m] + agp[2 * q + 1][m];
     }
   }
 }
@@ -498,45 +612,32 @@ __global__ void __launch_bounds__(kBT) down_kernel(BParams p) {
   const size_t cbytes = (size_t)I * H * BITS / 8, sbytes = (size_t)H * G * 4;
   const size_t rowb = (size_t)I * BITS / 8;
   const int row0 = blockIdx.x * kDnRowsWg + wave * kDnRowsWave;
-  const uint8_t* cptr[4];
   const uint32_t* sptr[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     const int r = row0 + 16 * t + nl;
-    cptr[t] = blob + 2 * cbytes + r * rowb + kb * (BITS * 2);
     sptr[t] = reinterpret_cast<const uint32_t*>(blob + 3 * cbytes + 2 * sbytes) + (size_t)r * G;
   }
-  extern __shared__ float xs[];  // [kMaxMT][G][16]
-  for (int m0 = 0; m0 < cnt; m0 += 16 * kMaxMT) {
-    const int nmt = min(kMaxMT, (cnt - m0 + 15) / 16);
+  auto row_of = [&](int R) { return blob + 2 * cbytes + (size_t)(row0 + R) * rowb; };
+  extern __shared__ float smem_f[];
+  float* xs = smem_f;  // [G][16]
+  char* wbuf = reinterpret_cast<char*>(smem_f + G * 16) + wave * wave_stage_bytes<BITS>();
+  for (int m0 = 0; m0 < cnt; m0 += 16) {
     __syncthreads();
-    stage_sums(xs, p, p.ag, G, off, cnt, m0, nmt, false);
+    stage_sums(xs, p, p.ag, G, off, cnt, m0, 1, false);
     __syncthreads();
-    TokRow tr[kMaxMT];
+    const uint16_t* tp = token_row(p.a16, p, off, cnt, m0, nl, kb, (size_t)I, false);
+    f32x4 acc[4];
 #pragma unroll
-    for (int mt = 0; mt < kMaxMT; ++mt) {
-      const int r = m0 + mt * 16 + nl;
-      tr[mt].valid = mt < nmt && r < cnt;
-      tr[mt].p = p.a16 + (tr[mt].valid ? (size_t)p.pairs[off + r] * I : 0) + kb * 16;
-    }
-    f32x4 acc[kMaxMT][4];
+    for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+    expert_pass_any<BITS>(acc, wbuf, row_of, sptr, tp, xs, G, lane, nl, kb);
 #pragma unroll
-    for (int mt = 0; mt < kMaxMT; ++mt)
+    for (int i = 0; i < 4; ++i) {
+      const int r = m0 + 4 * kb + i;
+      if (r < cnt) {
+        float* y = p.ys + (size_t)p.pairs[off + r] * H + row0 + nl;
 #pragma unroll
-      for (int t = 0; t < 4; ++t) acc[mt][t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int g = 0; g < G; ++g) group_products<BITS, 4>(acc, cptr, sptr, tr, xs, G, g, nmt, kb);
-#pragma unroll
-    for (int mt = 0; mt < kMaxMT; ++mt) {
-      if (mt < nmt) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int r = m0 + mt * 16 + 4 * kb + i;
-          if (r < cnt) {
-            float* y = p.ys + (size_t)p.pairs[off + r] * H + row0 + nl;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) y[16 * t] = acc[mt][t][i];
-          }
-        }
+        for (int t = 0; t < 4; ++t) y[16 * t] = acc[t][i];
       }
     }
   }
@@ -642,7 +743,13 @@ int run_layers(const fmoe_layer* layers, int n_layers, const float* x_in, float*
   const fmoe_layer& L0 = layers[0];
   const int H = L0.hidden, I = L0.inter, E = L0.n_experts, P = T * k;
   const int max_items = E < P ? E : P;
-  const size_t xs_gu = (size_t)kMaxMT * (H / 64) * 16 * 4, xs_dn = (size_t)kMaxMT * (I / 64) * 16 * 4;
+  const size_t sm_gu = expert_smem_bytes<BITS>(H / 64), sm_dn = expert_smem_bytes<BITS>(I / 64);
+  // the stage buffers take the expert kernels past the default 64 KB of dynamic LDS
+  if (hipFuncSetAttribute(reinterpret_cast<const void*>(&gate_up_kernel<BITS>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm_gu) != hipSuccess ||
+      hipFuncSetAttribute(reinterpret_cast<const void*>(&down_kernel<BITS>),
+                          hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm_dn) != hipSuccess)
+    return FMOE_ERR_HIP;
   const size_t sort_smem = (size_t)(2 * E + 2 * kSortThreads) * 4;
   for (int l = 0; l < n_layers; ++l) {
     const float* hin = l == 0 ? x_in : ws.h[(l - 1) & 1];
@@ -676,9 +783,9 @@ int run_layers(const fmoe_layer* layers, int n_layers, const float* x_in, float*
     bp.a16 = ws.a16;
     bp.ag = ws.ag;
     bp.ys = ws.ys;
-    hipLaunchKernelGGL(gate_up_kernel<BITS>, dim3(I / kGuRowsWg, max_items), dim3(kBT), xs_gu, s, bp);
+    hipLaunchKernelGGL(gate_up_kernel<BITS>, dim3(I / kGuRowsWg, max_items), dim3(kBT), sm_gu, s, bp);
     if (hipGetLastError() != hipSuccess) return FMOE_ERR_HIP;
-    hipLaunchKernelGGL(down_kernel<BITS>, dim3(H / kDnRowsWg, max_items), dim3(kBT), xs_dn, s, bp);
+    hipLaunchKernelGGL(down_kernel<BITS>, dim3(H / kDnRowsWg, max_items), dim3(kBT), sm_dn, s, bp);
     if (hipGetLastError() != hipSuccess) return FMOE_ERR_HIP;
     hipLaunchKernelGGL(combine_kernel, dim3((H / 4 + kBT - 1) / kBT, T), dim3(kBT), 0, s, hin, ws.ys, ws.idx, ws.w,
                        H, k, hnext, idx_out, w_out, l, n_layers);
