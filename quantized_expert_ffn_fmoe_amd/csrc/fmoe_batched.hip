@@ -457,6 +457,7 @@ __device__ __forceinline__ void compute_stage(f32x4 (&acc)[4], const char* buf, 
       acc[t][2] = fmaf(cb, x4.z, fmaf(cs, P[2], acc[t][2]));
       acc[t][3] = fmaf(cb, x4.w, fmaf(cs, P[3], acc[t][3]));
     }
+    __builtin_amdgcn_sched_barrier(0);  // one group at a time: bounds the live fragments
   }
 }
 
@@ -498,7 +499,7 @@ __device__ __forceinline__ void expert_pass_any(f32x4 (&acc)[4], char* wbuf, Row
 #pragma unroll
     for (int j = 0; j < SG::kNJ; ++j) dmarow[j] = row_of(j * SG::kRPI + lane % SG::kRPI);
     const int NS = G / 4;
-    if (NS % 4 == 0) expert_pass<BITS, 4, 4>(acc, wbuf, dmarow, sptr, tp, xs, G, lane, nl, kb);
+    if (NS % 2 == 0) expert_pass<BITS, 4, 2>(acc, wbuf, dmarow, sptr, tp, xs, G, lane, nl, kb);
     else expert_pass<BITS, 4, 1>(acc, wbuf, dmarow, sptr, tp, xs, G, lane, nl, kb);
   } else {
     using SG = StageGeom<BITS, 2>;
@@ -533,7 +534,7 @@ size_t expert_smem_bytes(int G) {
 }
 
 template <int BITS>
-__global__ void __launch_bounds__(kBT) gate_up_kernel(BParams p) {
+__global__ void __launch_bounds__(kBT, 2) gate_up_kernel(BParams p) {
   const int item = blockIdx.y;
   if (item >= *p.n_act) return;
   const int e = p.act_e[item], off = p.act_off[item], cnt = p.act_cnt[item];
@@ -602,7 +603,7 @@ __global__ void __launch_bounds__(kBT) gate_up_kernel(BParams p) {
 }
 
 template <int BITS>
-__global__ void __launch_bounds__(kBT) down_kernel(BParams p) {
+__global__ void __launch_bounds__(kBT, 2) down_kernel(BParams p) {
   const int item = blockIdx.y;
   if (item >= *p.n_act) return;
   const int e = p.act_e[item], off = p.act_off[item], cnt = p.act_cnt[item];
