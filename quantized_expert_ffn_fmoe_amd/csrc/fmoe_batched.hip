@@ -120,9 +120,9 @@ struct BParams {
   size_t stride;
   int H, I, k;
   const int32_t* pairs;    // [P] pair ids (t * k + j) sorted by expert
-  const int32_t* act_e;    // [n_act] active experts
-  const int32_t* act_off;  // [n_act] first position in pairs
-  const int32_t* act_cnt;  // [n_act] number of pairs
+  const int32_t* act_e;    // [n_act] expert of each work unit
+  const int32_t* act_off;  // [n_act] first position of the unit in pairs
+  const int32_t* act_cnt;  // [n_act] number of pairs of the unit (1..16)
   const int32_t* n_act;
   const uint16_t* v16;  // [T][H] bf16, operand order
   const float* xg;      // [T][H/64] group sums of v16
@@ -286,7 +286,8 @@ __global__ void __launch_bounds__(kBT) topk_parts_kernel(const float* __restrict
 // ---------------------------------------------------------------- 3. sort by expert
 // One workgroup. Pair s = t * k + j goes to expert idx[s]; pairs of one expert are
 // contiguous in `pairs` (their order inside an expert does not affect any result: every
-// token's rows are computed independently).
+// token's rows are computed independently). The work list holds one unit per 16 pairs of
+// an expert (expert, first position, count), so a hot expert's passes run in parallel.
 __global__ void __launch_bounds__(kSortThreads) sort_kernel(const int32_t* __restrict__ idx, int P, int E,
                                                             int32_t* __restrict__ pairs, int32_t* __restrict__ act_e,
                                                             int32_t* __restrict__ act_off,
@@ -305,7 +306,7 @@ __global__ void __launch_bounds__(kSortThreads) sort_kernel(const int32_t* __res
   int c = 0, a = 0;
   for (int e = lo; e < hi; ++e) {
     c += cnt[e];
-    a += cnt[e] > 0;
+    a += (cnt[e] + 15) / 16;
   }
   // inclusive scans of (c, a) over the threads (Hillis-Steele)
   sc[tid] = c;
@@ -322,10 +323,10 @@ __global__ void __launch_bounds__(kSortThreads) sort_kernel(const int32_t* __res
   int off = sc[tid] - c, act = sc[kSortThreads + tid] - a;
   for (int e = lo; e < hi; ++e) {
     cur[e] = off;
-    if (cnt[e] > 0) {
+    for (int u = 0; 16 * u < cnt[e]; ++u) {  // one work unit per 16 pairs of the expert
       act_e[act] = e;
-      act_off[act] = off;
-      act_cnt[act] = cnt[e];
+      act_off[act] = off + 16 * u;
+      act_cnt[act] = min(16, cnt[e] - 16 * u);
       ++act;
     }
     off += cnt[e];
@@ -685,6 +686,10 @@ __global__ void __launch_bounds__(kBT) a16_natural_kernel(const uint16_t* __rest
 }
 
 // ---------------------------------------------------------------- workspace
+// Work units of the expert kernels: 16 pairs of one expert each (at most one partial unit
+// per active expert).
+inline size_t max_units(int P, int E) { return (size_t)(E < P ? E : P) + (size_t)P / 16; }
+
 struct BatchedWs {
   float* h[2];
   float* v;
@@ -727,9 +732,10 @@ BatchedWs carve(void* base, int T, int H, int I, int E, int k) {
   w.idx = reinterpret_cast<int32_t*>(take(P * 4));
   w.w = reinterpret_cast<float*>(take(P * 4));
   w.pairs = reinterpret_cast<int32_t*>(take(P * 4));
-  w.act_e = reinterpret_cast<int32_t*>(take((size_t)E * 4));
-  w.act_off = reinterpret_cast<int32_t*>(take((size_t)E * 4));
-  w.act_cnt = reinterpret_cast<int32_t*>(take((size_t)E * 4));
+  const size_t units = max_units(P, E);
+  w.act_e = reinterpret_cast<int32_t*>(take(units * 4));
+  w.act_off = reinterpret_cast<int32_t*>(take(units * 4));
+  w.act_cnt = reinterpret_cast<int32_t*>(take(units * 4));
   w.n_act = reinterpret_cast<int32_t*>(take(4));
   w.a16 = reinterpret_cast<uint16_t*>(take(P * I * 2));
   w.ag = reinterpret_cast<float*>(take(P * (I / 64) * 4));
@@ -743,7 +749,7 @@ int run_layers(const fmoe_layer* layers, int n_layers, const float* x_in, float*
                unsigned flags, int32_t* idx_out, float* w_out, const BatchedWs& ws, hipStream_t s) {
   const fmoe_layer& L0 = layers[0];
   const int H = L0.hidden, I = L0.inter, E = L0.n_experts, P = T * k;
-  const int max_items = E < P ? E : P;
+  const int max_items = (int)max_units(P, E);
   const size_t sm_gu = expert_smem_bytes<BITS>(H / 64), sm_dn = expert_smem_bytes<BITS>(I / 64);
   // the stage buffers take the expert kernels past the default 64 KB of dynamic LDS
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(&gate_up_kernel<BITS>),
