@@ -199,6 +199,8 @@ __global__ void __launch_bounds__(kBT) stage_kernel(const float* __restrict__ h,
 // and feeds them to 4 products, so each group of 4 products covers 16 columns.
 constexpr int kRtSlice = 512;
 constexpr int kRtWaveCols = kRtSlice / (kBT / 64);
+constexpr int kRtSteps = kRtWaveCols / 16;
+constexpr int kRtMaxParts = 16;  // slices of a hidden size up to 8192
 
 __device__ __forceinline__ f32x4 mfma4(float a, float b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
@@ -209,7 +211,6 @@ __global__ void __launch_bounds__(kBT) router_kernel_mfma(const float* __restric
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nl = lane & 15, kb = lane >> 4;
   const int e0 = blockIdx.x * 16, ks = blockIdx.y;
   const int k_lo = ks * kRtSlice + wave * kRtWaveCols;
-  const int k_hi = min(k_lo + kRtWaveCols, H);
   const bool e_ok = e0 + nl < E;
   const float* rrow = R + (size_t)(e_ok ? e0 + nl : 0) * H;
   __shared__ float red[kBT / 64][4][256];  // [wave][m-tile][16 tokens x 16 experts]
@@ -218,18 +219,32 @@ __global__ void __launch_bounds__(kBT) router_kernel_mfma(const float* __restric
     f32x4 acc[4];
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int k = k_lo; k < k_hi; k += 16) {
-      const float4 b = e_ok ? *reinterpret_cast<const float4*>(rrow + k + 4 * kb) : make_float4(0.f, 0.f, 0.f, 0.f);
+    // A wave's 128 columns are 8 steps of 16; all of a step's loads are issued before the
+    // first product so that one memory round trip covers the whole slice. The loads are
+    // unconditional: rows past the token count read the last token and rows past the
+    // expert count the first expert's row, and their products only reach sums that are
+    // never stored. A wave past the end of K (H % 512 == 256) has no columns.
+    if (k_lo < H) {  // uniform
+      const float* brow = rrow + k_lo + 4 * kb;
+      float4 b[kRtSteps], a[4][kRtSteps];
+#pragma unroll
+      for (int j = 0; j < kRtSteps; ++j) b[j] = *reinterpret_cast<const float4*>(brow + 16 * j);
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt) {
-        if (mt < nmt) {
-          const int tok = t0 + mt * 16 + nl;
-          const float4 a = tok < T ? *reinterpret_cast<const float4*>(v + (size_t)tok * H + k + 4 * kb)
-                                   : make_float4(0.f, 0.f, 0.f, 0.f);
-          acc[mt] = mfma4(a.x, b.x, acc[mt]);
-          acc[mt] = mfma4(a.y, b.y, acc[mt]);
-          acc[mt] = mfma4(a.z, b.z, acc[mt]);
-          acc[mt] = mfma4(a.w, b.w, acc[mt]);
+        const float* arow = v + (size_t)min(t0 + mt * 16 + nl, T - 1) * H + k_lo + 4 * kb;
+#pragma unroll
+        for (int j = 0; j < kRtSteps; ++j) a[mt][j] = *reinterpret_cast<const float4*>(arow + 16 * j);
+      }
+#pragma unroll
+      for (int mt = 0; mt < 4; ++mt) {
+        if (mt < nmt) {  // uniform
+#pragma unroll
+          for (int j = 0; j < kRtSteps; ++j) {
+            acc[mt] = mfma4(a[mt][j].x, b[j].x, acc[mt]);
+            acc[mt] = mfma4(a[mt][j].y, b[j].y, acc[mt]);
+            acc[mt] = mfma4(a[mt][j].z, b[j].z, acc[mt]);
+            acc[mt] = mfma4(a[mt][j].w, b[j].w, acc[mt]);
+          }
         }
       }
     }
@@ -260,8 +275,13 @@ __global__ void __launch_bounds__(kBT) topk_parts_kernel(const float* __restrict
   __shared__ float lsel[16], wsel[16];
   __shared__ int isel[16];
   for (int e = threadIdx.x; e < E; e += kBT) {
+    // all slices' loads first (clamped, unconditional), then the sum in slice order
+    float x[kRtMaxParts];
+#pragma unroll
+    for (int s = 0; s < kRtMaxParts; ++s) x[s] = part[((size_t)min(s, n_part - 1) * T + t) * E + e];
     float l = 0.f;
-    for (int s = 0; s < n_part; ++s) l += part[((size_t)s * T + t) * E + e];
+#pragma unroll
+    for (int s = 0; s < kRtMaxParts; ++s) l = s < n_part ? l + x[s] : l;
     logits[(size_t)t * E + e] = l;
     keys[e] = rank_key(l, e);
   }
