@@ -21,10 +21,11 @@
 // Matrix-core form of the affine dequantization. A weight is q*s + b with (s, b) per
 // group of 64 columns of a row (the nibble*scale+bias form of aibit.im "Techniques de
 // rupture" item 2). The codes enter the bf16 matrix core as the exact values
-// c = 1 + q/16 (4-bit; bf16 bits 0x3F80 | q << 3) or c = 1 + q/4 (2-bit; 0x3F80 | q << 5),
-// built from a code dword with one shift and one and-or per pair of codes. For one group,
-// with X = sum of the group's bf16 activations and P = sum x*c from the matrix core,
-//   sum x (q s + b) = F s P + (b - F s) X,   F = 16 (4-bit) or 4 (2-bit),
+// c = (1 + q/128) / 2, whose bf16 bits are 0x3F00 | q (q in the low mantissa bits, for
+// both code widths): one AND isolates a dword's codes byte-wise and one byte permute pairs
+// two of them with the 0x3F high bytes, per bf16 pair. For one group, with X = sum of the
+// group's bf16 activations and P = sum x*c from the matrix core,
+//   sum x (q s + b) = 256 s P + (b - 128 s) X,
 // applied once per group to the fp32 partial product (the per-group factorisation
 // s*sum(q x) + b*sum(x)). No weight is rounded; only v and a are (to bf16).
 //
@@ -83,30 +84,40 @@ __device__ __forceinline__ uint32_t shift(uint32_t w) {
 }
 
 // The two 8-element B operands of one group from this lane's code bytes (see header).
+// v_perm_b32 byte selectors: 0-3 take bytes of the second operand, 4 the 0x3F byte.
+constexpr uint32_t kHiBytes = 0x3F3F3F3Fu;
+constexpr uint32_t kSelEven = 0x04020400u;  // [x.b0, 3F, x.b2, 3F]
+constexpr uint32_t kSelOdd = 0x04030401u;   // [x.b1, 3F, x.b3, 3F]
 template <int BITS>
 __device__ __forceinline__ void build_b(const uint32_t* w, u32x4& b0, u32x4& b1) {
   if constexpr (BITS == 4) {
-    // w[h] holds columns 8h..8h+7 of the lane's 16, nibble p = column 8h + p
-    b0.x = 0x3F803F80u | (shift<-3>(w[0]) & 0x00780078u);
-    b0.y = 0x3F803F80u | (shift<1>(w[0]) & 0x00780078u);
-    b0.z = 0x3F803F80u | (shift<5>(w[0]) & 0x00780078u);
-    b0.w = 0x3F803F80u | (shift<9>(w[0]) & 0x00780078u);
-    b1.x = 0x3F803F80u | (shift<-3>(w[1]) & 0x00780078u);
-    b1.y = 0x3F803F80u | (shift<1>(w[1]) & 0x00780078u);
-    b1.z = 0x3F803F80u | (shift<5>(w[1]) & 0x00780078u);
-    b1.w = 0x3F803F80u | (shift<9>(w[1]) & 0x00780078u);
+    // w[h] holds columns 8h..8h+7 of the lane's 16, nibble p = column 8h + p; pair j of
+    // half h is (8h + j, 8h + j + 4): the even nibbles sit in the bytes of w & 0x0F0F0F0F,
+    // the odd ones in those of (w >> 4) & 0x0F0F0F0F
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t ev = w[h] & 0x0F0F0F0Fu, od = (w[h] >> 4) & 0x0F0F0F0Fu;
+      u32x4& b = h ? b1 : b0;
+      b.x = __builtin_amdgcn_perm(kHiBytes, ev, kSelEven);
+      b.y = __builtin_amdgcn_perm(kHiBytes, od, kSelEven);
+      b.z = __builtin_amdgcn_perm(kHiBytes, ev, kSelOdd);
+      b.w = __builtin_amdgcn_perm(kHiBytes, od, kSelOdd);
+    }
   } else {
-    // w[0] holds the lane's 16 columns, column i in bits 2i; half h, pair j takes columns
-    // 4h + j and 4h + j + 8
+    // w[0] holds the lane's 16 columns, column i in bits 2i; byte m of
+    // (w >> 2 r) & 0x03030303 holds column 4m + r, and half h, pair r takes columns
+    // 4h + r and 4h + r + 8
     const uint32_t d = w[0];
-    b0.x = 0x3F803F80u | (shift<-5>(d) & 0x00600060u);
-    b0.y = 0x3F803F80u | (shift<-3>(d) & 0x00600060u);
-    b0.z = 0x3F803F80u | (shift<-1>(d) & 0x00600060u);
-    b0.w = 0x3F803F80u | (shift<1>(d) & 0x00600060u);
-    b1.x = 0x3F803F80u | (shift<3>(d) & 0x00600060u);
-    b1.y = 0x3F803F80u | (shift<5>(d) & 0x00600060u);
-    b1.z = 0x3F803F80u | (shift<7>(d) & 0x00600060u);
-    b1.w = 0x3F803F80u | (shift<9>(d) & 0x00600060u);
+    const uint32_t t0 = d & 0x03030303u, t1 = (d >> 2) & 0x03030303u;
+    const uint32_t t2 = (d >> 4) & 0x03030303u, t3 = (d >> 6) & 0x03030303u;
+    b0.x = __builtin_amdgcn_perm(kHiBytes, t0, kSelEven);
+    b0.y = __builtin_amdgcn_perm(kHiBytes, t1, kSelEven);
+    b0.z = __builtin_amdgcn_perm(kHiBytes, t2, kSelEven);
+    b0.w = __builtin_amdgcn_perm(kHiBytes, t3, kSelEven);
+    b1.x = __builtin_amdgcn_perm(kHiBytes, t0, kSelOdd);
+    b1.y = __builtin_amdgcn_perm(kHiBytes, t1, kSelOdd);
+    b1.z = __builtin_amdgcn_perm(kHiBytes, t2, kSelOdd);
+    b1.w = __builtin_amdgcn_perm(kHiBytes, t3, kSelOdd);
   }
 }
 
@@ -381,6 +392,15 @@ __device__ __forceinline__ void stage_sums(float* xs, const BParams& p, const fl
 // tile, and the token operands as two 16-byte loads per group; both go to registers.
 // Stage layout in LDS: instruction j carries rows j * RPI .. + RPI - 1; lane i of it
 // brings 16-byte segment i / RPI of row j * RPI + i % RPI, stored at j * 1024 + 16 i.
+//
+// Waits. The LDS-DMA is issued from asm and the stage buffers are read from asm, so the
+// compiler neither sees the DMA in flight nor places waits of its own for it: with an
+// LDS-DMA pending it would wait for every outstanding load before the first use of any
+// loaded register, which serialises the stages. The compiler's waits for the register
+// loads stay correct (it counts only the loads it knows of, which can only make a wait
+// stricter). A wave's vector loads, LDS-DMA included, complete in issue order, so the
+// explicit wait before a stage is read lets exactly the loads of the stages issued after
+// it stay in flight.
 constexpr int kWaveRows = 64;
 
 template <int BITS, int GC>
@@ -390,11 +410,22 @@ struct StageGeom {
   static constexpr int kRPI = 1024 / kRS;        // rows per DMA instruction
   static constexpr int kNJ = kWaveRows / kRPI;   // DMA instructions per stage
   static constexpr int kBytes = kWaveRows * kRS;  // LDS bytes of one stage
-  static constexpr int kLoads = kNJ + 4 + 2 * GC;  // vector memory instructions per stage
+  static constexpr int kLoads = 4 + 2 * GC + kNJ;  // vector memory instructions per stage
 };
 
-__device__ __forceinline__ void dma16(const void* g, char* lds) {
-  __builtin_amdgcn_global_load_lds(g, (__attribute__((address_space(3))) void*)lds, 16, 0, 0);
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// 16 bytes per lane from global memory to LDS: lane i's bytes land at lds + 16 i (lds is
+// the wave-uniform LDS byte address, passed through M0).
+__device__ __forceinline__ void dma16(const void* g, uint32_t lds) {
+  asm volatile(
+      "s_mov_b32 m0, %1\n\t"
+      "s_nop 0\n\t"
+      "global_load_lds_dwordx4 %0, off" ::"v"(g),
+      "s"(__builtin_amdgcn_readfirstlane(lds))
+      : "memory", "m0");
 }
 // Wait until at most N of this wave's vector memory instructions are outstanding (the
 // compiler does not wait for LDS-DMA data by itself).
@@ -419,8 +450,6 @@ __device__ __forceinline__ void issue_stage(char* buf, StageRegs<GC>& r,
                                             const uint32_t* const (&sptr)[4], const uint16_t* tp, int g0, int lane) {
   using SG = StageGeom<BITS, GC>;
 #pragma unroll
-  for (int j = 0; j < SG::kNJ; ++j) dma16(dmarow[j] + (size_t)g0 * SG::kBPG + 16 * (lane / SG::kRPI), buf + j * 1024);
-#pragma unroll
   for (int t = 0; t < 4; ++t) {
     if constexpr (GC == 4) {
       const uint4 q = *reinterpret_cast<const uint4*>(sptr[t] + g0);
@@ -440,43 +469,87 @@ __device__ __forceinline__ void issue_stage(char* buf, StageRegs<GC>& r,
     r.a[gl][0] = ap[0];
     r.a[gl][1] = ap[1];
   }
+  const uint32_t lb = lds_addr(buf);
+#pragma unroll
+  for (int j = 0; j < SG::kNJ; ++j) dma16(dmarow[j] + (size_t)g0 * SG::kBPG + 16 * (lane / SG::kRPI), lb + j * 1024);
+}
+
+// Byte offset in a stage buffer of weight row R's code bytes at offset `off` of its stage
+// segment (layout above). For R = 16 t + nl and off = gl * kBPG + lane part it is the sum of
+// a per-lane term, a per-tile term and a per-group term.
+template <int BITS, int GC>
+__host__ __device__ constexpr int stage_off(int R, int off) {
+  using SG = StageGeom<BITS, GC>;
+  return (R / SG::kRPI) * 1024 + ((off / 16) * SG::kRPI + R % SG::kRPI) * 16 + off % 16;
+}
+
+// One group's LDS operands: the lane's code bytes of the 4 tiles (at base + T1 * t) and its
+// 4 group sums (at xaddr), read in one asm block that also waits for them. The reads are
+// written in asm because the compiler, unable to tell them apart from the stage buffers
+// that LDS-DMA is still filling, would otherwise wait for every load in flight before them.
+template <int T1, int T2, int T3>
+__device__ __forceinline__ void read_group4(uint32_t base, uint32_t xaddr, uint32_t (&w)[4][2], f32x4& x4) {
+  typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+  u32x2 q0, q1, q2, q3;
+  asm volatile(
+      "ds_read_b64 %0, %5\n"
+      "ds_read_b64 %1, %5 offset:%7\n"
+      "ds_read_b64 %2, %5 offset:%8\n"
+      "ds_read_b64 %3, %5 offset:%9\n"
+      "ds_read_b128 %4, %6\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(q0), "=&v"(q1), "=&v"(q2), "=&v"(q3), "=&v"(x4)
+      : "v"(base), "v"(xaddr), "n"(T1), "n"(T2), "n"(T3)
+      : "memory");
+  w[0][0] = q0.x, w[0][1] = q0.y, w[1][0] = q1.x, w[1][1] = q1.y;
+  w[2][0] = q2.x, w[2][1] = q2.y, w[3][0] = q3.x, w[3][1] = q3.y;
+}
+template <int T1, int T2, int T3>
+__device__ __forceinline__ void read_group2(uint32_t base, uint32_t xaddr, uint32_t (&w)[4][2], f32x4& x4) {
+  uint32_t q0, q1, q2, q3;
+  asm volatile(
+      "ds_read_b32 %0, %5\n"
+      "ds_read_b32 %1, %5 offset:%7\n"
+      "ds_read_b32 %2, %5 offset:%8\n"
+      "ds_read_b32 %3, %5 offset:%9\n"
+      "ds_read_b128 %4, %6\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(q0), "=&v"(q1), "=&v"(q2), "=&v"(q3), "=&v"(x4)
+      : "v"(base), "v"(xaddr), "n"(T1), "n"(T2), "n"(T3)
+      : "memory");
+  w[0][0] = q0, w[1][0] = q1, w[2][0] = q2, w[3][0] = q3;
+  w[0][1] = w[1][1] = w[2][1] = w[3][1] = 0;
 }
 
 // acc[tile] += the affine group products of the GC groups of one stage (see the header:
-// codes enter the matrix core as exact bf16 values, F s P + (b - F s) X per group).
+// codes enter the matrix core as exact bf16 values, 256 s P + (b - 128 s) X per group).
 template <int BITS, int GC>
 __device__ __forceinline__ void compute_stage(f32x4 (&acc)[4], const char* buf, const StageRegs<GC>& r,
                                               const float* xs, int g0, int nl, int kb) {
   using SG = StageGeom<BITS, GC>;
-  constexpr float F = BITS == 4 ? 16.f : 4.f;
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
+  const uint32_t lane_base = lds_addr(buf) + stage_off<BITS, GC>(nl, kb * (BITS * 2));
+  const uint32_t x_base = lds_addr(xs + g0 * 16 + 4 * kb);
 #pragma unroll
   for (int gl = 0; gl < GC; ++gl) {
-    const float4 x4 = *reinterpret_cast<const float4*>(xs + (g0 + gl) * 16 + 4 * kb);
+    uint32_t w[4][2];
+    f32x4 x4;
+    const uint32_t gbase = lane_base + stage_off<BITS, GC>(0, gl * SG::kBPG);
+    constexpr int T1 = stage_off<BITS, GC>(16, 0), T2 = stage_off<BITS, GC>(32, 0), T3 = stage_off<BITS, GC>(48, 0);
+    if constexpr (BITS == 4) read_group4<T1, T2, T3>(gbase, x_base + gl * 64, w, x4);
+    else read_group2<T1, T2, T3>(gbase, x_base + gl * 64, w, x4);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const int R = 16 * t + nl;
-      const int off = gl * SG::kBPG + kb * (BITS * 2);  // the lane's code bytes in the row's stage segment
-      const char* src = buf + (R / SG::kRPI) * 1024 + ((off / 16) * SG::kRPI + R % SG::kRPI) * 16 + off % 16;
-      uint32_t w[2];
-      if constexpr (BITS == 4) {
-        const uint2 q = *reinterpret_cast<const uint2*>(src);
-        w[0] = q.x;
-        w[1] = q.y;
-      } else {
-        w[0] = *reinterpret_cast<const uint32_t*>(src);
-        w[1] = 0;
-      }
       u32x4 b0, b1;
-      build_b<BITS>(w, b0, b1);
-      const float cs = F * bf16_lo(r.sb[t][gl]);
-      const float cb = bf16_hi(r.sb[t][gl]) - cs;
+      build_b<BITS>(w[t], b0, b1);
+      const float cs = 256.f * bf16_lo(r.sb[t][gl]);
+      const float cb = fmaf(-0.5f, cs, bf16_hi(r.sb[t][gl]));
       f32x4 P = mfma(r.a[gl][0], b0, zero);
       P = mfma(r.a[gl][1], b1, P);
-      acc[t][0] = fmaf(cb, x4.x, fmaf(cs, P[0], acc[t][0]));
-      acc[t][1] = fmaf(cb, x4.y, fmaf(cs, P[1], acc[t][1]));
-      acc[t][2] = fmaf(cb, x4.z, fmaf(cs, P[2], acc[t][2]));
-      acc[t][3] = fmaf(cb, x4.w, fmaf(cs, P[3], acc[t][3]));
+      acc[t][0] = fmaf(cb, x4[0], fmaf(cs, P[0], acc[t][0]));
+      acc[t][1] = fmaf(cb, x4[1], fmaf(cs, P[1], acc[t][1]));
+      acc[t][2] = fmaf(cb, x4[2], fmaf(cs, P[2], acc[t][2]));
+      acc[t][3] = fmaf(cb, x4[3], fmaf(cs, P[3], acc[t][3]));
     }
     __builtin_amdgcn_sched_barrier(0);  // one group at a time: bounds the live fragments
   }
@@ -520,7 +593,8 @@ __device__ __forceinline__ void expert_pass_any(f32x4 (&acc)[4], char* wbuf, Row
 #pragma unroll
     for (int j = 0; j < SG::kNJ; ++j) dmarow[j] = row_of(j * SG::kRPI + lane % SG::kRPI);
     const int NS = G / 4;
-    if (NS % 2 == 0) expert_pass<BITS, 4, 2>(acc, wbuf, dmarow, sptr, tp, xs, G, lane, nl, kb);
+    if (NS % 4 == 0) expert_pass<BITS, 4, 4>(acc, wbuf, dmarow, sptr, tp, xs, G, lane, nl, kb);
+    else if (NS % 2 == 0) expert_pass<BITS, 4, 2>(acc, wbuf, dmarow, sptr, tp, xs, G, lane, nl, kb);
     else expert_pass<BITS, 4, 1>(acc, wbuf, dmarow, sptr, tp, xs, G, lane, nl, kb);
   } else {
     using SG = StageGeom<BITS, 2>;
