@@ -46,7 +46,7 @@ def algorithmic_bytes_per_layer(bits: int) -> int:
 
 def decode_source_hash() -> str:
     h = hashlib.sha256()
-    for f in ("fmoe_decode.hip", "fmoe_device.h", "fmoe_decode.h", "fmoe_intdot.h"):
+    for f in ("fmoe_decode.hip", "fmoe_device.h", "fmoe_decode.h", "fmoe_intdot.h", "fmoe_layout.h"):
         h.update(open(os.path.join(ROOT, "quantized_expert_ffn_fmoe_amd", "csrc", f), "rb").read())
     return h.hexdigest()[:16]
 

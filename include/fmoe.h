@@ -29,9 +29,17 @@
  *  - Alignment: codes, sb, activation and output pointers must be 16-byte aligned.
  *
  * Quantized matrix layout (the library's packed layout, produced by fmoe_pack)
- *  - codes: row-major, rows x (cols*bits/8) bytes. 4-bit: byte j of a row holds column
- *    2j in bits 0-3 and column 2j+1 in bits 4-7. 2-bit: byte j holds column 4j+t in bits
- *    2t..2t+1. (This equals the canonical layout, so fmoe_pack copies codes unchanged.)
+ *  - canonical codes (fmoe_pack's input): row-major, rows x (cols*bits/8) bytes. 4-bit:
+ *    byte j of a row holds column 2j in bits 0-3 and column 2j+1 in bits 4-7. 2-bit: byte
+ *    j holds column 4j+t in bits 2t..2t+1.
+ *  - packed codes: the same rows * cols*bits/8 bytes, regrouped in blocks of 32
+ *    consecutive rows. Each row is cut into pieces of 4 groups of 64 columns (128 bytes at
+ *    4 bits, 64 at 2 bits); piece p of a block's rows is stored contiguously in row order,
+ *    at block start + p * rows_in_block * piece bytes (a final block may hold fewer than
+ *    32 rows); inside its piece, row r's 16-byte chunk k sits at position
+ *    (k + rot) mod (chunks in the piece), rot = r mod 8 (4-bit) or (r mod 16) / 4 (2-bit);
+ *    a row that ends in a shorter piece stores it the same way with its own size. 16-byte
+ *    chunks keep their canonical contents.
  *  - sb: uint32 [rows][cols/group]; bits 0-15 = bf16 scale s, bits 16-31 = bf16 bias b
  *    of the group. Weight (r, c) is q*s + b with s, b of group floor(c/group)
  *    ([aibit] "Techniques de rupture" item 2 and [hada] "FMA optimize dequant cekirdegi":
@@ -110,9 +118,10 @@ size_t fmoe_expert_bytes(int hidden, int inter, int bits, int group);
 /* Views of the three matrices of the expert blob at `blob` (no device access). */
 int fmoe_expert_view(const void* blob, int hidden, int inter, int bits, int group, fmoe_expert* out);
 
-/* Canonical -> packed. codes_canon: uint8 [rows][cols*bits/8] (the canonical layout,
- * identical to the packed one); scale, bias: bf16 bit patterns [rows][cols/group].
- * Writes codes_out (skipped when codes_out == codes_canon) and sb_out. Device pointers. */
+/* Canonical -> packed. codes_canon: uint8 [rows][cols*bits/8] (canonical layout);
+ * scale, bias: bf16 bit patterns [rows][cols/group]. Writes codes_out (packed layout,
+ * fmoe_codes_bytes bytes; it must not overlap codes_canon, FMOE_ERR_OVERLAP) and sb_out.
+ * Device pointers. */
 int fmoe_pack(const uint8_t* codes_canon, const uint16_t* scale, const uint16_t* bias, int rows, int cols,
               int bits, int group, void* codes_out, uint32_t* sb_out, fmoe_stream_t stream);
 

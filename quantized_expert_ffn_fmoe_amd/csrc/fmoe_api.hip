@@ -135,7 +135,7 @@ int fmoe_pack(const uint8_t* codes_canon, const uint16_t* scale, const uint16_t*
       !aligned(bias, 2))
     return FMOE_ERR_ALIGN;
   size_t cb = fmoe_codes_bytes(rows, cols, bits), nsb = fmoe_sb_bytes(rows, cols, group);
-  if (codes_out != codes_canon && overlaps(codes_out, cb, codes_canon, cb)) return FMOE_ERR_OVERLAP;
+  if (overlaps(codes_out, cb, codes_canon, cb)) return FMOE_ERR_OVERLAP;  // the layout permutes 16-byte chunks
   if (overlaps(sb_out, nsb, scale, nsb / 2) || overlaps(sb_out, nsb, bias, nsb / 2)) return FMOE_ERR_OVERLAP;
   int rc = check_device();
   if (rc) return rc;

@@ -42,6 +42,7 @@
 #include "fmoe_batched.h"
 #include "fmoe_device.h"
 #include "fmoe_internal.h"
+#include "fmoe_layout.h"
 
 namespace fmoe {
 namespace {
@@ -444,10 +445,10 @@ struct StageRegs {
   u32x4 a[GC][2];
 };
 
-template <int BITS, int GC>
-__device__ __forceinline__ void issue_stage(char* buf, StageRegs<GC>& r,
-                                            const uint8_t* const (&dmarow)[StageGeom<BITS, GC>::kNJ],
-                                            const uint32_t* const (&sptr)[4], const uint16_t* tp, int g0, int lane) {
+// src(j, g0): the lane's 16 source bytes for DMA instruction j of the stage at group g0.
+template <int BITS, int GC, typename Src>
+__device__ __forceinline__ void issue_stage(char* buf, StageRegs<GC>& r, Src src, const uint32_t* const (&sptr)[4],
+                                            const uint16_t* tp, int g0, int lane) {
   using SG = StageGeom<BITS, GC>;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -471,7 +472,7 @@ __device__ __forceinline__ void issue_stage(char* buf, StageRegs<GC>& r,
   }
   const uint32_t lb = lds_addr(buf);
 #pragma unroll
-  for (int j = 0; j < SG::kNJ; ++j) dma16(dmarow[j] + (size_t)g0 * SG::kBPG + 16 * (lane / SG::kRPI), lb + j * 1024);
+  for (int j = 0; j < SG::kNJ; ++j) dma16(src(j, g0), lb + j * 1024);
 }
 
 // Byte offset in a stage buffer of weight row R's code bytes at offset `off` of its stage
@@ -523,19 +524,34 @@ __device__ __forceinline__ void read_group2(uint32_t base, uint32_t xaddr, uint3
 
 // acc[tile] += the affine group products of the GC groups of one stage (see the header:
 // codes enter the matrix core as exact bf16 values, 256 s P + (b - 128 s) X per group).
+// Stage buffer layouts. 4-group stages hold the code layout's own bytes (fmoe_layout.h):
+// instruction j's KB holds rows j * kRPI .. + kRPI - 1, each row's piece contiguous with
+// its 16-byte chunks rotated by rot(row). 2-group stages use the layout of stage_off.
 template <int BITS, int GC>
 __device__ __forceinline__ void compute_stage(f32x4 (&acc)[4], const char* buf, const StageRegs<GC>& r,
                                               const float* xs, int g0, int nl, int kb) {
   using SG = StageGeom<BITS, GC>;
+  using CL = CodeLayout<BITS>;
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
-  const uint32_t lane_base = lds_addr(buf) + stage_off<BITS, GC>(nl, kb * (BITS * 2));
+  constexpr bool kPiece = GC == 4;  // the stage is one piece of the code layout
+  const int lane_part = kb * (BITS * 2);  // the lane's code bytes within a group's kBPG
+  const uint32_t lane_base = kPiece ? lds_addr(buf) + (nl / SG::kRPI) * 1024 + (nl % SG::kRPI) * SG::kRS + lane_part % 16
+                                    : lds_addr(buf) + stage_off<BITS, GC>(nl, lane_part);
   const uint32_t x_base = lds_addr(xs + g0 * 16 + 4 * kb);
 #pragma unroll
   for (int gl = 0; gl < GC; ++gl) {
     uint32_t w[4][2];
     f32x4 x4;
-    const uint32_t gbase = lane_base + stage_off<BITS, GC>(0, gl * SG::kBPG);
-    constexpr int T1 = stage_off<BITS, GC>(16, 0), T2 = stage_off<BITS, GC>(32, 0), T3 = stage_off<BITS, GC>(48, 0);
+    uint32_t gbase;
+    if constexpr (kPiece) {
+      const int k = (gl * SG::kBPG + lane_part) / 16;  // the lane's chunk of the row's piece
+      gbase = lane_base + ((k + CL::rot(nl)) % (SG::kRS / 16)) * 16;
+    } else {
+      gbase = lane_base + stage_off<BITS, GC>(0, gl * SG::kBPG);
+    }
+    constexpr int T1 = kPiece ? (16 / SG::kRPI) * 1024 : stage_off<BITS, GC>(16, 0);
+    constexpr int T2 = kPiece ? 2 * T1 : stage_off<BITS, GC>(32, 0);
+    constexpr int T3 = kPiece ? 3 * T1 : stage_off<BITS, GC>(48, 0);
     if constexpr (BITS == 4) read_group4<T1, T2, T3>(gbase, x_base + gl * 64, w, x4);
     else read_group2<T1, T2, T3>(gbase, x_base + gl * 64, w, x4);
 #pragma unroll
@@ -558,16 +574,14 @@ __device__ __forceinline__ void compute_stage(f32x4 (&acc)[4], const char* buf, 
 // All G groups of a pass (GC * U divides G): blocks of U stages, two stages in flight
 // inside a block (stage u + 2 is requested once stage u has been read). A block issues
 // and consumes all of its own loads, so nothing is in flight across the loop's back edge.
-template <int BITS, int GC, int U>
-__device__ __forceinline__ void expert_pass(f32x4 (&acc)[4], char* wbuf,
-                                            const uint8_t* const (&dmarow)[StageGeom<BITS, GC>::kNJ],
-                                            const uint32_t* const (&sptr)[4], const uint16_t* tp, const float* xs,
-                                            int G, int lane, int nl, int kb) {
+template <int BITS, int GC, int U, typename Src>
+__device__ __forceinline__ void expert_pass(f32x4 (&acc)[4], char* wbuf, Src src, const uint32_t* const (&sptr)[4],
+                                            const uint16_t* tp, const float* xs, int G, int lane, int nl, int kb) {
   using SG = StageGeom<BITS, GC>;
   for (int s0 = 0; s0 < G / GC; s0 += U) {
     StageRegs<GC> r[2];
-    issue_stage<BITS, GC>(wbuf, r[0], dmarow, sptr, tp, s0 * GC, lane);
-    if constexpr (U > 1) issue_stage<BITS, GC>(wbuf + SG::kBytes, r[1], dmarow, sptr, tp, (s0 + 1) * GC, lane);
+    issue_stage<BITS, GC>(wbuf, r[0], src, sptr, tp, s0 * GC, lane);
+    if constexpr (U > 1) issue_stage<BITS, GC>(wbuf + SG::kBytes, r[1], src, sptr, tp, (s0 + 1) * GC, lane);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (u + 1 < U) wait_vmcnt<SG::kLoads>();
@@ -575,33 +589,53 @@ __device__ __forceinline__ void expert_pass(f32x4 (&acc)[4], char* wbuf,
       compute_stage<BITS, GC>(acc, wbuf + (u % 2) * SG::kBytes, r[u % 2], xs, (s0 + u) * GC, nl, kb);
       if (u + 2 < U) {
         wait_lgkm();  // the stage's reads of this buffer are done before the DMA refills it
-        issue_stage<BITS, GC>(wbuf + (u % 2) * SG::kBytes, r[u % 2], dmarow, sptr, tp, (s0 + u + 2) * GC, lane);
+        issue_stage<BITS, GC>(wbuf + (u % 2) * SG::kBytes, r[u % 2], src, sptr, tp, (s0 + u + 2) * GC, lane);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
   }
 }
 
-// Stage width and block length for G groups (G even for every accepted shape).
-template <int BITS, typename RowOf>
-__device__ __forceinline__ void expert_pass_any(f32x4 (&acc)[4], char* wbuf, RowOf row_of,
-                                                const uint32_t* const (&sptr)[4], const uint16_t* tp, const float* xs,
-                                                int G, int lane, int nl, int kb) {
+// Stage width and block length for G groups (G even for every accepted shape). Wave row R
+// lives in the matrix at mat_of(R) (rows_of rows of row_bytes bytes), row row_of(R).
+// With 4-group stages every stage is one piece of the code layout (fmoe_layout.h): the
+// instructions of a 32-row half read one contiguous run of it, and a lane's source is its
+// base for stage 0 plus one run per stage; 2-group stages (G % 4 == 2, where a row ends in
+// a half piece) take the general offset.
+template <int BITS, typename MatOf, typename RowOf>
+__device__ __forceinline__ void expert_pass_any(f32x4 (&acc)[4], char* wbuf, MatOf mat_of, RowOf row_of,
+                                                int rows_of, size_t row_bytes, const uint32_t* const (&sptr)[4],
+                                                const uint16_t* tp, const float* xs, int G, int lane, int nl, int kb) {
   if (G % 4 == 0) {
     using SG = StageGeom<BITS, 4>;
+    static_assert(SG::kRPI == CodeLayout<BITS>::kSubRows && SG::kRS == CodeLayout<BITS>::kPieceBytes,
+                  "a 4-group stage instruction is one contiguous KB of the code layout");
     const uint8_t* dmarow[SG::kNJ];
 #pragma unroll
-    for (int j = 0; j < SG::kNJ; ++j) dmarow[j] = row_of(j * SG::kRPI + lane % SG::kRPI);
+    for (int j = 0; j < SG::kNJ; ++j) {  // rows j * kRPI .. (consecutive, kRPI-aligned): lane l takes byte 16 l
+      const int R = j * SG::kRPI;
+      dmarow[j] = mat_of(R) + code_offset<BITS>(rows_of, row_bytes, row_of(R), 0) + 16 * lane;
+    }
+    auto src = [&](int j, int g0) { return dmarow[j] + (size_t)(g0 / 4) * CodeLayout<BITS>::kRunBytes; };
     const int NS = G / 4;
-    if (NS % 4 == 0) expert_pass<BITS, 4, 4>(acc, wbuf, dmarow, sptr, tp, xs, G, lane, nl, kb);
-    else if (NS % 2 == 0) expert_pass<BITS, 4, 2>(acc, wbuf, dmarow, sptr, tp, xs, G, lane, nl, kb);
-    else expert_pass<BITS, 4, 1>(acc, wbuf, dmarow, sptr, tp, xs, G, lane, nl, kb);
+    if (NS % 4 == 0) expert_pass<BITS, 4, 4>(acc, wbuf, src, sptr, tp, xs, G, lane, nl, kb);
+    else if (NS % 2 == 0) expert_pass<BITS, 4, 2>(acc, wbuf, src, sptr, tp, xs, G, lane, nl, kb);
+    else expert_pass<BITS, 4, 1>(acc, wbuf, src, sptr, tp, xs, G, lane, nl, kb);
   } else {
     using SG = StageGeom<BITS, 2>;
-    const uint8_t* dmarow[SG::kNJ];
+    const uint8_t* mat[SG::kNJ];
+    int row[SG::kNJ];
 #pragma unroll
-    for (int j = 0; j < SG::kNJ; ++j) dmarow[j] = row_of(j * SG::kRPI + lane % SG::kRPI);
-    expert_pass<BITS, 2, 1>(acc, wbuf, dmarow, sptr, tp, xs, G, lane, nl, kb);
+    for (int j = 0; j < SG::kNJ; ++j) {
+      const int R = j * SG::kRPI + lane % SG::kRPI;
+      mat[j] = mat_of(R);
+      row[j] = row_of(R);
+    }
+    const int seg = 16 * (lane / SG::kRPI);
+    auto src = [&](int j, int g0) {
+      return mat[j] + code_offset<BITS>(rows_of, row_bytes, row[j], (size_t)g0 * SG::kBPG + seg);
+    };
+    expert_pass<BITS, 2, 1>(acc, wbuf, src, sptr, tp, xs, G, lane, nl, kb);
   }
 }
 
@@ -646,10 +680,9 @@ __global__ void __launch_bounds__(kBT, 2) gate_up_kernel(BParams p) {
     const int r = row0 + 16 * (t & 1) + nl;
     sptr[t] = reinterpret_cast<const uint32_t*>(blob + 3 * cbytes + (t < 2 ? 0 : sbytes)) + (size_t)r * G;
   }
-  auto row_of = [&](int R) {  // wave row R (tile R / 16, row R % 16)
-    const int t = R / 16;
-    return blob + (t < 2 ? 0 : cbytes) + (size_t)(row0 + 16 * (t & 1) + R % 16) * rowb;
-  };
+  // wave row R: tile R / 16 (0, 1 gate; 2, 3 up), row R % 16 of it
+  auto mat_of = [&](int R) { return blob + (R < 32 ? 0 : cbytes); };
+  auto row_of = [&](int R) { return row0 + 16 * ((R / 16) & 1) + R % 16; };
   extern __shared__ float smem_f[];
   float* xs = smem_f;  // [G][16]
   char* wbuf = reinterpret_cast<char*>(smem_f + G * 16) + wave * wave_stage_bytes<BITS>();
@@ -663,7 +696,7 @@ __global__ void __launch_bounds__(kBT, 2) gate_up_kernel(BParams p) {
     f32x4 acc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    expert_pass_any<BITS>(acc, wbuf, row_of, sptr, tp, xs, G, lane, nl, kb);
+    expert_pass_any<BITS>(acc, wbuf, mat_of, row_of, I, rowb, sptr, tp, xs, G, lane, nl, kb);
     // epilogue: a = silu(g) * u -> bf16 in the down operand's order; group sums of the
     // rounded values
     float part[4] = {0.f, 0.f, 0.f, 0.f};
@@ -714,7 +747,8 @@ __global__ void __launch_bounds__(kBT, 2) down_kernel(BParams p) {
     const int r = row0 + 16 * t + nl;
     sptr[t] = reinterpret_cast<const uint32_t*>(blob + 3 * cbytes + 2 * sbytes) + (size_t)r * G;
   }
-  auto row_of = [&](int R) { return blob + 2 * cbytes + (size_t)(row0 + R) * rowb; };
+  auto mat_of = [&](int) { return blob + 2 * cbytes; };
+  auto row_of = [&](int R) { return row0 + R; };
   extern __shared__ float smem_f[];
   float* xs = smem_f;  // [G][16]
   char* wbuf = reinterpret_cast<char*>(smem_f + G * 16) + wave * wave_stage_bytes<BITS>();
@@ -726,7 +760,7 @@ __global__ void __launch_bounds__(kBT, 2) down_kernel(BParams p) {
     f32x4 acc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    expert_pass_any<BITS>(acc, wbuf, row_of, sptr, tp, xs, G, lane, nl, kb);
+    expert_pass_any<BITS>(acc, wbuf, mat_of, row_of, H, rowb, sptr, tp, xs, G, lane, nl, kb);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = m0 + 4 * kb + i;

@@ -44,6 +44,7 @@
 #include "fmoe_device.h"
 #include "fmoe_internal.h"
 #include "fmoe_intdot.h"
+#include "fmoe_layout.h"
 
 namespace fmoe {
 
@@ -440,16 +441,16 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
           if (kFastGU || (b0 + u < blk_hi && item < KI)) {
             const int j = item / I, i = item % I;
             const uint8_t* bp = X + (size_t)isel[j] * p.expert_stride;
-            const uint4* gp = reinterpret_cast<const uint4*>(bp + (size_t)i * rowH);
-            const uint4* up = reinterpret_cast<const uint4*>(bp + cbH + (size_t)i * rowH);
+            const uint8_t* gp = bp;  // gate codes; up codes follow at cbH
             const uint32_t* gsb = reinterpret_cast<const uint32_t*>(bp + 3 * cbH) + (size_t)i * ngH;
             const uint32_t* usb = reinterpret_cast<const uint32_t*>(bp + 3 * cbH + sbb) + (size_t)i * ngH;
 #pragma unroll
             for (int q = 0; q < CPL_G; ++q) {
               int c = subG + lprG * q;
               if (kFastGU || c < nchG) {  // the fast path covers exactly nchG chunks per row
-                wg[u][q] = gp[c];
-                wu[u][q] = up[c];
+                const size_t off = code_offset<BITS>(I, rowH, i, (size_t)c * 16);
+                wg[u][q] = *reinterpret_cast<const uint4*>(gp + off);
+                wu[u][q] = *reinterpret_cast<const uint4*>(gp + cbH + off);
                 sg[u][q] = gsb[c / C::kPerGroup];
                 su[u][q] = usb[c / C::kPerGroup];
               }
@@ -534,13 +535,13 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
         if (rl < nr) {
           const int r = r0 + rl;
           const uint8_t* bp = X + (size_t)isel[j] * p.expert_stride;
-          const uint4* dp = reinterpret_cast<const uint4*>(bp + 2 * cbH + (size_t)r * rowI);
+          const uint8_t* dp = bp + 2 * cbH;  // down codes
           const uint32_t* dsb = reinterpret_cast<const uint32_t*>(bp + 3 * cbH + 2 * sbb) + (size_t)r * ngI;
 #pragma unroll
           for (int q = 0; q < CPL_D; ++q) {
             int c = subD + lprD * q;
             if (c < nchD) {
-              wd[u][q] = dp[c];
+              wd[u][q] = *reinterpret_cast<const uint4*>(dp + code_offset<BITS>(H, rowI, r, (size_t)c * 16));
               sd[u][q] = dsb[c / C::kPerGroup];
             }
           }

@@ -5,6 +5,7 @@
 // the down matvec then reuses the standalone dequantized matvec kernel.
 #include "fmoe_device.h"
 #include "fmoe_internal.h"
+#include "fmoe_layout.h"
 
 namespace fmoe {
 
@@ -35,16 +36,15 @@ __global__ void __launch_bounds__(256) gate_up_kernel(const uint8_t* __restrict_
     const int r = rb + rsel;
     float g = 0.f, u = 0.f;
     if (r < rows) {
-      const uint4* gp = reinterpret_cast<const uint4*>(gcodes + (size_t)r * row_bytes);
-      const uint4* up = reinterpret_cast<const uint4*>(ucodes + (size_t)r * row_bytes);
       uint4 wg[CPL], wu[CPL];
       uint32_t sg[CPL], su[CPL];
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
         int c = sub + lpr * j;
         if (c < n_chunks) {
-          wg[j] = gp[c];
-          wu[j] = up[c];
+          const size_t off = code_offset<BITS>(rows, row_bytes, r, (size_t)c * 16);
+          wg[j] = *reinterpret_cast<const uint4*>(gcodes + off);
+          wu[j] = *reinterpret_cast<const uint4*>(ucodes + off);
           sg[j] = gsb[(size_t)r * ngroups + c / C::kPerGroup];
           su[j] = usb[(size_t)r * ngroups + c / C::kPerGroup];
         }

@@ -7,6 +7,7 @@
 // the matching activation values in registers for every row it visits.
 #include "fmoe_device.h"
 #include "fmoe_internal.h"
+#include "fmoe_layout.h"
 
 namespace fmoe {
 
@@ -37,7 +38,6 @@ __global__ void __launch_bounds__(256) matvec_kernel(const uint8_t* __restrict__
     const int r = rb + rsel;
     float acc = 0.f;
     if (r < rows) {
-      const uint4* rowp = reinterpret_cast<const uint4*>(codes + (size_t)r * row_bytes);
       const uint32_t* sbp = sb + (size_t)r * ngroups;
       uint4 w[CPL];
       uint32_t s[CPL];
@@ -45,7 +45,7 @@ __global__ void __launch_bounds__(256) matvec_kernel(const uint8_t* __restrict__
       for (int j = 0; j < CPL; ++j) {
         int c = sub + lpr * j;
         if (c < n_chunks) {
-          w[j] = rowp[c];
+          w[j] = *reinterpret_cast<const uint4*>(codes + code_offset<BITS>(rows, row_bytes, r, (size_t)c * 16));
           s[j] = sbp[c / C::kPerGroup];
         }
       }
@@ -60,15 +60,21 @@ __global__ void __launch_bounds__(256) matvec_kernel(const uint8_t* __restrict__
   }
 }
 
+// Canonical (row-major) codes -> the packed layout of fmoe_layout.h, one 16-byte chunk per
+// thread step (chunks never straddle a piece); scale and bias interleaved into sb words.
+template <int BITS>
 __global__ void pack_kernel(const uint8_t* __restrict__ codes_in, const uint16_t* __restrict__ scale,
                             const uint16_t* __restrict__ bias, uint8_t* __restrict__ codes_out,
-                            uint32_t* __restrict__ sb_out, size_t n_code16, size_t n_groups) {
+                            uint32_t* __restrict__ sb_out, int rows, size_t row_bytes, size_t n_groups) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n_groups; i += stride)
     sb_out[i] = (uint32_t)scale[i] | ((uint32_t)bias[i] << 16);
-  if (codes_out != codes_in) {
-    for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n_code16; i += stride)
-      reinterpret_cast<uint4*>(codes_out)[i] = reinterpret_cast<const uint4*>(codes_in)[i];
+  const size_t per_row = row_bytes / 16, n_code16 = (size_t)rows * per_row;
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n_code16; i += stride) {
+    const int r = (int)(i / per_row);
+    const size_t b = (i % per_row) * 16;
+    *reinterpret_cast<uint4*>(codes_out + code_offset<BITS>(rows, row_bytes, r, b)) =
+        reinterpret_cast<const uint4*>(codes_in)[i];
   }
 }
 
@@ -163,8 +169,13 @@ int launch_pack(const uint8_t* codes_in, const uint16_t* scale, const uint16_t* 
   size_t work = n_code16 > n_groups ? n_code16 : n_groups;
   size_t blocks = (work + 255) / 256;
   if (blocks > 65536) blocks = 65536;
-  hipLaunchKernelGGL(pack_kernel, dim3((unsigned)blocks), dim3(256), 0, s, codes_in, scale, bias,
-                     static_cast<uint8_t*>(codes_out), sb_out, n_code16, n_groups);
+  const size_t row_bytes = (size_t)cols * bits / 8;
+  if (bits == 4)
+    hipLaunchKernelGGL(pack_kernel<4>, dim3((unsigned)blocks), dim3(256), 0, s, codes_in, scale, bias,
+                       static_cast<uint8_t*>(codes_out), sb_out, rows, row_bytes, n_groups);
+  else
+    hipLaunchKernelGGL(pack_kernel<2>, dim3((unsigned)blocks), dim3(256), 0, s, codes_in, scale, bias,
+                       static_cast<uint8_t*>(codes_out), sb_out, rows, row_bytes, n_groups);
   return hipGetLastError() == hipSuccess ? FMOE_OK : FMOE_ERR_HIP;
 }
 

@@ -47,11 +47,12 @@ def fill_experts_cpu(blob: torch.Tensor, stride: int, layer: int, n_experts: int
 def fill_experts_gpu(blob: torch.Tensor, stride: int, layer: int, n_experts: int, H: int, I: int, bits: int,
                      seed: int = 0, chunk: int = 128) -> None:
     """Same as fill_experts_cpu but generated on the device (GPU fixture), in chunks of experts.
-    Codes are generated straight into the blob (the packed codes layout is the canonical one);
-    scales/biases go to a scratch buffer and are interleaved by fmoe_pack."""
+    Canonical codes and the scales/biases go to scratch buffers; fmoe_pack writes them into
+    the blob in the library's packed layout."""
     dev = blob.device
     cb = fm.codes_bytes(I, H, bits)
     ngrp = I * H // 64
+    codes = torch.empty((chunk, cb), dtype=torch.uint8, device=dev)
     scale = torch.empty((chunk, ngrp), dtype=torch.int16, device=dev)
     bias = torch.empty((chunk, ngrp), dtype=torch.int16, device=dev)
     stream = torch.cuda.current_stream().cuda_stream
@@ -60,12 +61,12 @@ def fill_experts_gpu(blob: torch.Tensor, stride: int, layer: int, n_experts: int
         base = blob.data_ptr() + e0 * stride
         for m in range(3):
             rows, cols = (I, H) if m < 2 else (H, I)
-            synth.gpu_matrix(seed, layer, e0, ne, m, rows, cols, bits, 64, base + m * cb, stride,
+            synth.gpu_matrix(seed, layer, e0, ne, m, rows, cols, bits, 64, codes.data_ptr(), cb,
                              scale.data_ptr(), bias.data_ptr(), ngrp * 2, stream)
             for j in range(ne):
                 view = fm.expert_view(base + j * stride, H, I, bits)
                 q = (view.gate, view.up, view.down)[m]
-                fm.pack(q.codes, scale[j], bias[j], rows, cols, bits, 64, q.codes, q.sb)
+                fm.pack(codes[j], scale[j], bias[j], rows, cols, bits, 64, q.codes, q.sb)
 
 
 class DevStack:

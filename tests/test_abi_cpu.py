@@ -195,6 +195,9 @@ def test_pack_validation():
     _raises(fm.ERR_ALIGN, fm.pack, FAKE + 2, FAKE, FAKE, 4, 64, 4, 64, FAKE + 4096, FAKE + 8192, stream=0)
     _raises(fm.ERR_OVERLAP, fm.pack, FAKE, FAKE + (1 << 20), FAKE + (2 << 20), 4, 64, 4, 64, FAKE + 16, FAKE + (3 << 20),
             stream=0)
+    # the packed layout permutes 16-byte chunks, so packing in place is refused too
+    _raises(fm.ERR_OVERLAP, fm.pack, FAKE, FAKE + (1 << 20), FAKE + (2 << 20), 4, 64, 4, 64, FAKE, FAKE + (3 << 20),
+            stream=0)
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -40,6 +40,52 @@ def _run_matvec(codes, scale, bias, rows, cols, bits, X):
 
 
 # ------------------------------------------------------------------ generator fixture and packing
+def _layout_offset(bits, rows, row_bytes, r, b):
+    """The packed code layout written out independently of the library: blocks of 32 rows,
+    each row cut into pieces of 4 groups (128 bytes at 4 bits, 64 at 2 bits), piece p of the
+    block's rows stored together in row order, a row's 16-byte chunks rotated inside its
+    piece by r mod 8 (4-bit) or (r mod 16) // 4 (2-bit); short last pieces and short last
+    blocks use their own sizes."""
+    rb = 32
+    pb = 32 * bits
+    r0 = r // rb * rb
+    nr = min(rb, rows - r0)
+    p = b // pb
+    piece = min(pb, row_bytes - p * pb)
+    rot = r % 8 if bits == 4 else (r % 16) // 4
+    pos = ((b % pb) // 16 + rot) % (piece // 16)
+    return r0 * row_bytes + p * nr * pb + (r - r0) * piece + pos * 16 + b % 16
+
+
+@pytest.mark.parametrize("bits,rows,cols", [(4, 64, 4096), (4, 13, 192), (4, 40, 320), (2, 96, 1024),
+                                            (2, 19, 128), (2, 45, 448)])
+def test_pack_layout(bits, rows, cols):
+    """fmoe_pack puts every 16-byte chunk of the canonical rows where the layout says, and
+    the matrix occupies exactly rows * cols * bits / 8 bytes."""
+    rng = np.random.default_rng(rows * 1000 + cols + bits)
+    row_bytes = cols * bits // 8
+    canon = rng.integers(0, 256, size=(rows, row_bytes), dtype=np.uint8)
+    ng = rows * cols // 64
+    scale = rng.integers(0, 1 << 16, size=ng, dtype=np.uint16)
+    bias = rng.integers(0, 1 << 16, size=ng, dtype=np.uint16)
+    cb = fm.codes_bytes(rows, cols, bits)
+    assert cb == rows * row_bytes
+    out = torch.full((cb + 64,), 0xA5, dtype=torch.uint8, device="cuda")  # guard bytes after the matrix
+    sb = torch.empty(ng, dtype=torch.int32, device="cuda")
+    fm.pack(to_dev(canon), to_dev(scale), to_dev(bias), rows, cols, bits, 64, out, sb)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    want = np.empty(cb, dtype=np.uint8)
+    for r in range(rows):
+        for b in range(0, row_bytes, 16):
+            o = _layout_offset(bits, rows, row_bytes, r, b)
+            want[o:o + 16] = canon[r, b:b + 16]
+    assert np.array_equal(got[:cb], want)
+    assert np.all(got[cb:] == 0xA5)
+    sbw = sb.cpu().numpy().view(np.uint32)
+    assert np.array_equal(sbw, scale.astype(np.uint32) | (bias.astype(np.uint32) << 16))
+
+
 @pytest.mark.parametrize("bits", [4, 2])
 def test_gpu_fixture_matches_cpu_generator(bits):
     H, I = 4096, 1024
