@@ -40,8 +40,11 @@
  *    (k + rot) mod (chunks in the piece), rot = r mod 8 (4-bit) or (r mod 16) / 4 (2-bit);
  *    a row that ends in a shorter piece stores it the same way with its own size. 16-byte
  *    chunks keep their canonical contents.
- *  - sb: uint32 [rows][cols/group]; bits 0-15 = bf16 scale s, bits 16-31 = bf16 bias b
- *    of the group. Weight (r, c) is q*s + b with s, b of group floor(c/group)
+ *  - sb: one uint32 per (row, group); bits 0-15 = bf16 scale s, bits 16-31 = bf16 bias b
+ *    of the group; blocked like the codes: blocks of 32 rows, each row's words cut into
+ *    pieces of 4 groups, piece p of a block's rows stored together in row order (short
+ *    last pieces and blocks keep their own sizes). fmoe_pack's scale and bias inputs are
+ *    row-major [rows][cols/group]. Weight (r, c) is q*s + b with s, b of group floor(c/group)
  *    ([aibit] "Techniques de rupture" item 2 and [hada] "FMA optimize dequant cekirdegi":
  *    the affine nibble*scale+bias form).
  *  - group must be 64 and cols a multiple of 64.

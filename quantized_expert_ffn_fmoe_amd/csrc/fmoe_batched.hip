@@ -445,21 +445,22 @@ struct StageRegs {
   u32x4 a[GC][2];
 };
 
-// src(j, g0): the lane's 16 source bytes for DMA instruction j of the stage at group g0.
-template <int BITS, int GC, typename Src>
-__device__ __forceinline__ void issue_stage(char* buf, StageRegs<GC>& r, Src src, const uint32_t* const (&sptr)[4],
-                                            const uint16_t* tp, int g0, int lane) {
+// src(j, g0): the lane's 16 source bytes for DMA instruction j of the stage at group g0;
+// sbs(t, g0): the lane's scale/bias words of tile t for groups g0 .. g0 + GC - 1.
+template <int BITS, int GC, typename Src, typename SbSrc>
+__device__ __forceinline__ void issue_stage(char* buf, StageRegs<GC>& r, Src src, SbSrc sbs, const uint16_t* tp,
+                                            int g0, int lane) {
   using SG = StageGeom<BITS, GC>;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
     if constexpr (GC == 4) {
-      const uint4 q = *reinterpret_cast<const uint4*>(sptr[t] + g0);
+      const uint4 q = *reinterpret_cast<const uint4*>(sbs(t, g0));
       r.sb[t][0] = q.x;
       r.sb[t][1] = q.y;
       r.sb[t][2] = q.z;
       r.sb[t][3] = q.w;
     } else {
-      const uint2 q = *reinterpret_cast<const uint2*>(sptr[t] + g0);
+      const uint2 q = *reinterpret_cast<const uint2*>(sbs(t, g0));
       r.sb[t][0] = q.x;
       r.sb[t][1] = q.y;
     }
@@ -574,8 +575,8 @@ __device__ __forceinline__ void compute_stage(f32x4 (&acc)[4], const char* buf, 
 // All G groups of a pass (GC * U divides G): blocks of U stages, two stages in flight
 // inside a block (stage u + 2 is requested once stage u has been read). A block issues
 // and consumes all of its own loads, so nothing is in flight across the loop's back edge.
-template <int BITS, int GC, int U, typename Src>
-__device__ __forceinline__ void expert_pass(f32x4 (&acc)[4], char* wbuf, Src src, const uint32_t* const (&sptr)[4],
+template <int BITS, int GC, int U, typename Src, typename SbSrc>
+__device__ __forceinline__ void expert_pass(f32x4 (&acc)[4], char* wbuf, Src src, SbSrc sptr,
                                             const uint16_t* tp, const float* xs, int G, int lane, int nl, int kb) {
   using SG = StageGeom<BITS, GC>;
   for (int s0 = 0; s0 < G / GC; s0 += U) {
@@ -604,7 +605,8 @@ __device__ __forceinline__ void expert_pass(f32x4 (&acc)[4], char* wbuf, Src src
 // a half piece) take the general offset.
 template <int BITS, typename MatOf, typename RowOf>
 __device__ __forceinline__ void expert_pass_any(f32x4 (&acc)[4], char* wbuf, MatOf mat_of, RowOf row_of,
-                                                int rows_of, size_t row_bytes, const uint32_t* const (&sptr)[4],
+                                                int rows_of, size_t row_bytes, const uint32_t* const (&sbm)[4],
+                                                const int (&sbr)[4],
                                                 const uint16_t* tp, const float* xs, int G, int lane, int nl, int kb) {
   if (G % 4 == 0) {
     using SG = StageGeom<BITS, 4>;
@@ -617,6 +619,10 @@ __device__ __forceinline__ void expert_pass_any(f32x4 (&acc)[4], char* wbuf, Mat
       dmarow[j] = mat_of(R) + code_offset<BITS>(rows_of, row_bytes, row_of(R), 0) + 16 * lane;
     }
     auto src = [&](int j, int g0) { return dmarow[j] + (size_t)(g0 / 4) * CodeLayout<BITS>::kRunBytes; };
+    const uint32_t* sp[4];  // the lane's scale/bias piece at stage 0; a stage is 32 rows x 4 words further
+#pragma unroll
+    for (int t = 0; t < 4; ++t) sp[t] = sbm[t] + sb_offset(rows_of, G, sbr[t], 0);
+    auto sptr = [&](int t, int g0) { return sp[t] + (g0 / 4) * 128; };
     const int NS = G / 4;
     if (NS % 4 == 0) expert_pass<BITS, 4, 4>(acc, wbuf, src, sptr, tp, xs, G, lane, nl, kb);
     else if (NS % 2 == 0) expert_pass<BITS, 4, 2>(acc, wbuf, src, sptr, tp, xs, G, lane, nl, kb);
@@ -635,6 +641,7 @@ __device__ __forceinline__ void expert_pass_any(f32x4 (&acc)[4], char* wbuf, Mat
     auto src = [&](int j, int g0) {
       return mat[j] + code_offset<BITS>(rows_of, row_bytes, row[j], (size_t)g0 * SG::kBPG + seg);
     };
+    auto sptr = [&](int t, int g0) { return sbm[t] + sb_offset(rows_of, G, sbr[t], g0); };
     expert_pass<BITS, 2, 1>(acc, wbuf, src, sptr, tp, xs, G, lane, nl, kb);
   }
 }
@@ -674,11 +681,12 @@ __global__ void __launch_bounds__(kBT, 2) gate_up_kernel(BParams p) {
   const size_t rowb = (size_t)H * BITS / 8;
   const int row0 = blockIdx.x * kGuRowsWg + wave * kGuRowsWave;
   // tiles 0, 1: gate rows row0 .. row0 + 31; tiles 2, 3: the same rows of up
-  const uint32_t* sptr[4];
+  const uint32_t* sbm[4];  // scale/bias matrix and row of each tile (blocked layout, fmoe_layout.h)
+  int sbr[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int r = row0 + 16 * (t & 1) + nl;
-    sptr[t] = reinterpret_cast<const uint32_t*>(blob + 3 * cbytes + (t < 2 ? 0 : sbytes)) + (size_t)r * G;
+    sbr[t] = row0 + 16 * (t & 1) + nl;
+    sbm[t] = reinterpret_cast<const uint32_t*>(blob + 3 * cbytes + (t < 2 ? 0 : sbytes));
   }
   // wave row R: tile R / 16 (0, 1 gate; 2, 3 up), row R % 16 of it
   auto mat_of = [&](int R) { return blob + (R < 32 ? 0 : cbytes); };
@@ -696,7 +704,7 @@ __global__ void __launch_bounds__(kBT, 2) gate_up_kernel(BParams p) {
     f32x4 acc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    expert_pass_any<BITS>(acc, wbuf, mat_of, row_of, I, rowb, sptr, tp, xs, G, lane, nl, kb);
+    expert_pass_any<BITS>(acc, wbuf, mat_of, row_of, I, rowb, sbm, sbr, tp, xs, G, lane, nl, kb);
     // epilogue: a = silu(g) * u -> bf16 in the down operand's order; group sums of the
     // rounded values
     float part[4] = {0.f, 0.f, 0.f, 0.f};
@@ -741,11 +749,12 @@ __global__ void __launch_bounds__(kBT, 2) down_kernel(BParams p) {
   const size_t cbytes = (size_t)I * H * BITS / 8, sbytes = (size_t)H * G * 4;
   const size_t rowb = (size_t)I * BITS / 8;
   const int row0 = blockIdx.x * kDnRowsWg + wave * kDnRowsWave;
-  const uint32_t* sptr[4];
+  const uint32_t* sbm[4];
+  int sbr[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
-    const int r = row0 + 16 * t + nl;
-    sptr[t] = reinterpret_cast<const uint32_t*>(blob + 3 * cbytes + 2 * sbytes) + (size_t)r * G;
+    sbr[t] = row0 + 16 * t + nl;
+    sbm[t] = reinterpret_cast<const uint32_t*>(blob + 3 * cbytes + 2 * sbytes);
   }
   auto mat_of = [&](int) { return blob + 2 * cbytes; };
   auto row_of = [&](int R) { return row0 + R; };
@@ -760,7 +769,7 @@ __global__ void __launch_bounds__(kBT, 2) down_kernel(BParams p) {
     f32x4 acc[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
-    expert_pass_any<BITS>(acc, wbuf, mat_of, row_of, H, rowb, sptr, tp, xs, G, lane, nl, kb);
+    expert_pass_any<BITS>(acc, wbuf, mat_of, row_of, H, rowb, sbm, sbr, tp, xs, G, lane, nl, kb);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int r = m0 + 4 * kb + i;

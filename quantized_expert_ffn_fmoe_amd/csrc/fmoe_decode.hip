@@ -442,8 +442,8 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
             const int j = item / I, i = item % I;
             const uint8_t* bp = X + (size_t)isel[j] * p.expert_stride;
             const uint8_t* gp = bp;  // gate codes; up codes follow at cbH
-            const uint32_t* gsb = reinterpret_cast<const uint32_t*>(bp + 3 * cbH) + (size_t)i * ngH;
-            const uint32_t* usb = reinterpret_cast<const uint32_t*>(bp + 3 * cbH + sbb) + (size_t)i * ngH;
+            const uint32_t* gsb = reinterpret_cast<const uint32_t*>(bp + 3 * cbH);  // blocked, fmoe_layout.h
+            const uint32_t* usb = reinterpret_cast<const uint32_t*>(bp + 3 * cbH + sbb);
 #pragma unroll
             for (int q = 0; q < CPL_G; ++q) {
               int c = subG + lprG * q;
@@ -451,8 +451,9 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
                 const size_t off = code_offset<BITS>(I, rowH, i, (size_t)c * 16);
                 wg[u][q] = *reinterpret_cast<const uint4*>(gp + off);
                 wu[u][q] = *reinterpret_cast<const uint4*>(gp + cbH + off);
-                sg[u][q] = gsb[c / C::kPerGroup];
-                su[u][q] = usb[c / C::kPerGroup];
+                const size_t so = sb_offset(I, ngH, i, c / C::kPerGroup);
+                sg[u][q] = gsb[so];
+                su[u][q] = usb[so];
               }
             }
           }
@@ -536,13 +537,13 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
           const int r = r0 + rl;
           const uint8_t* bp = X + (size_t)isel[j] * p.expert_stride;
           const uint8_t* dp = bp + 2 * cbH;  // down codes
-          const uint32_t* dsb = reinterpret_cast<const uint32_t*>(bp + 3 * cbH + 2 * sbb) + (size_t)r * ngI;
+          const uint32_t* dsb = reinterpret_cast<const uint32_t*>(bp + 3 * cbH + 2 * sbb);  // blocked
 #pragma unroll
           for (int q = 0; q < CPL_D; ++q) {
             int c = subD + lprD * q;
             if (c < nchD) {
               wd[u][q] = *reinterpret_cast<const uint4*>(dp + code_offset<BITS>(H, rowI, r, (size_t)c * 16));
-              sd[u][q] = dsb[c / C::kPerGroup];
+              sd[u][q] = dsb[sb_offset(H, ngI, r, c / C::kPerGroup)];
             }
           }
         }

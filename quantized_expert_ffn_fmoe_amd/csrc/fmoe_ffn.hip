@@ -45,8 +45,9 @@ __global__ void __launch_bounds__(256) gate_up_kernel(const uint8_t* __restrict_
           const size_t off = code_offset<BITS>(rows, row_bytes, r, (size_t)c * 16);
           wg[j] = *reinterpret_cast<const uint4*>(gcodes + off);
           wu[j] = *reinterpret_cast<const uint4*>(ucodes + off);
-          sg[j] = gsb[(size_t)r * ngroups + c / C::kPerGroup];
-          su[j] = usb[(size_t)r * ngroups + c / C::kPerGroup];
+          const size_t so = sb_offset(rows, ngroups, r, c / C::kPerGroup);
+          sg[j] = gsb[so];
+          su[j] = usb[so];
         }
       }
 #pragma unroll

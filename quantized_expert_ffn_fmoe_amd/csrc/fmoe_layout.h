@@ -51,4 +51,18 @@ __host__ __device__ __forceinline__ size_t code_offset(int rows, size_t row_byte
   return (size_t)r0 * row_bytes + p * (size_t)nr * P + (size_t)(r - r0) * piece + pos * 16 + b % 16;
 }
 
+// Scale/bias words (one uint32 per (row, group)) are blocked the same way: blocks of 32
+// rows, each row's words cut into pieces of 4 groups (16 bytes), piece p of the block's
+// rows stored together in row order (a short last piece and a short last block keep their
+// own sizes). A 4-group stage's words for 32 rows are then one contiguous 512 bytes, and
+// the words of one (row, piece) stay one 16-byte load. Word offset of group g of row r:
+__host__ __device__ __forceinline__ size_t sb_offset(int rows, int groups, int r, int g) {
+  constexpr int RB = 32, PG = 4;
+  const int r0 = r / RB * RB;
+  const int nr = rows - r0 < RB ? rows - r0 : RB;
+  const int p = g / PG;
+  const int pg = groups - p * PG < PG ? groups - p * PG : PG;  // groups of this piece
+  return (size_t)r0 * groups + (size_t)p * nr * PG + (size_t)(r - r0) * pg + g % PG;
+}
+
 }  // namespace fmoe

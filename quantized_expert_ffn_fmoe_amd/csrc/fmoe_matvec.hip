@@ -38,7 +38,6 @@ __global__ void __launch_bounds__(256) matvec_kernel(const uint8_t* __restrict__
     const int r = rb + rsel;
     float acc = 0.f;
     if (r < rows) {
-      const uint32_t* sbp = sb + (size_t)r * ngroups;
       uint4 w[CPL];
       uint32_t s[CPL];
 #pragma unroll
@@ -46,7 +45,7 @@ __global__ void __launch_bounds__(256) matvec_kernel(const uint8_t* __restrict__
         int c = sub + lpr * j;
         if (c < n_chunks) {
           w[j] = *reinterpret_cast<const uint4*>(codes + code_offset<BITS>(rows, row_bytes, r, (size_t)c * 16));
-          s[j] = sbp[c / C::kPerGroup];
+          s[j] = sb[sb_offset(rows, ngroups, r, c / C::kPerGroup)];
         }
       }
 #pragma unroll
@@ -61,14 +60,17 @@ __global__ void __launch_bounds__(256) matvec_kernel(const uint8_t* __restrict__
 }
 
 // Canonical (row-major) codes -> the packed layout of fmoe_layout.h, one 16-byte chunk per
-// thread step (chunks never straddle a piece); scale and bias interleaved into sb words.
+// thread step (chunks never straddle a piece); scale and bias interleaved into sb words,
+// placed in the blocked sb order of the same header.
 template <int BITS>
 __global__ void pack_kernel(const uint8_t* __restrict__ codes_in, const uint16_t* __restrict__ scale,
                             const uint16_t* __restrict__ bias, uint8_t* __restrict__ codes_out,
                             uint32_t* __restrict__ sb_out, int rows, size_t row_bytes, size_t n_groups) {
   const size_t stride = (size_t)gridDim.x * blockDim.x;
+  const int groups = (int)(n_groups / rows);
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n_groups; i += stride)
-    sb_out[i] = (uint32_t)scale[i] | ((uint32_t)bias[i] << 16);
+    sb_out[sb_offset(rows, groups, (int)(i / groups), (int)(i % groups))] =
+        (uint32_t)scale[i] | ((uint32_t)bias[i] << 16);
   const size_t per_row = row_bytes / 16, n_code16 = (size_t)rows * per_row;
   for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n_code16; i += stride) {
     const int r = (int)(i / per_row);

@@ -57,11 +57,22 @@ def _layout_offset(bits, rows, row_bytes, r, b):
     return r0 * row_bytes + p * nr * pb + (r - r0) * piece + pos * 16 + b % 16
 
 
+def _sb_layout_offset(rows, groups, r, g):
+    """The blocked scale/bias order written out independently of the library: blocks of 32
+    rows, each row's words cut into pieces of 4 groups, piece p of the block's rows stored
+    together in row order; short last pieces and blocks keep their own sizes."""
+    r0 = r // 32 * 32
+    nr = min(32, rows - r0)
+    p = g // 4
+    pg = min(4, groups - p * 4)
+    return r0 * groups + p * nr * 4 + (r - r0) * pg + g % 4
+
+
 @pytest.mark.parametrize("bits,rows,cols", [(4, 64, 4096), (4, 13, 192), (4, 40, 320), (2, 96, 1024),
                                             (2, 19, 128), (2, 45, 448)])
 def test_pack_layout(bits, rows, cols):
-    """fmoe_pack puts every 16-byte chunk of the canonical rows where the layout says, and
-    the matrix occupies exactly rows * cols * bits / 8 bytes."""
+    """fmoe_pack puts every 16-byte chunk of the canonical rows and every scale/bias word
+    where the layout says, and the matrix occupies exactly rows * cols * bits / 8 bytes."""
     rng = np.random.default_rng(rows * 1000 + cols + bits)
     row_bytes = cols * bits // 8
     canon = rng.integers(0, 256, size=(rows, row_bytes), dtype=np.uint8)
@@ -83,7 +94,13 @@ def test_pack_layout(bits, rows, cols):
     assert np.array_equal(got[:cb], want)
     assert np.all(got[cb:] == 0xA5)
     sbw = sb.cpu().numpy().view(np.uint32)
-    assert np.array_equal(sbw, scale.astype(np.uint32) | (bias.astype(np.uint32) << 16))
+    words = scale.astype(np.uint32) | (bias.astype(np.uint32) << 16)
+    groups = cols // 64
+    want_sb = np.empty(ng, dtype=np.uint32)
+    for r in range(rows):
+        for g in range(groups):
+            want_sb[_sb_layout_offset(rows, groups, r, g)] = words[r * groups + g]
+    assert np.array_equal(sbw, want_sb)
 
 
 @pytest.mark.parametrize("bits", [4, 2])
