@@ -146,9 +146,11 @@ size_t fmoe_workspace_bytes(int op, int n_tokens, int hidden, int inter, int n_e
   if (n_tokens < 1 || hidden < 64 || inter < 64 || n_experts < 1 || k < 1 || k > 16) return 0;
   if (op == FMOE_OP_EXPERT_FFN) return up256((size_t)inter * 4);
   if (op == FMOE_OP_MOE_LAYER) {
-    size_t d = carve_decode(nullptr, hidden, inter, n_experts, k).bytes;
+    // the decode kernel's synchronization state first, the multi-token scratch after it:
+    // a multi-token call must leave that state as the single-token calls expect it
+    size_t d = up256(carve_decode(nullptr, hidden, inter, n_experts, k).bytes);
     size_t bt = n_tokens > 1 ? batched_workspace_bytes(n_tokens, hidden, inter, n_experts, k) : 0;
-    return d > bt ? d : bt;
+    return d + bt;
   }
   return 0;
 }
@@ -244,7 +246,9 @@ int fmoe_moe_layer(const fmoe_layer* layers, int n_layers, const float* x_in, fl
   hipStream_t s = (hipStream_t)stream;
 
   if (n_tokens > 1) {
-    return launch_batched(layers, n_layers, x_in, h_out, n_tokens, k, eps, flags, idx_out, w_out, ws, ws_bytes, s);
+    const size_t d = up256(carve_decode(nullptr, H, I, E, k).bytes);
+    return launch_batched(layers, n_layers, x_in, h_out, n_tokens, k, eps, flags, idx_out, w_out,
+                          static_cast<char*>(ws) + d, ws_bytes - d, s);
   }
 
   // single-token decode: one persistent kernel per block of up to 64 layers
@@ -303,12 +307,15 @@ int fmoe_batched_a16(const void* ws, size_t ws_bytes, int n_tokens, int hidden, 
   if (hidden < 256 || hidden > 8192 || inter < 128 || inter > 8192 || !batched_shape_ok(hidden, inter))
     return FMOE_ERR_SHAPE;
   if (k < 1 || k > 16 || k > n_experts) return FMOE_ERR_K;
-  if (ws_bytes < batched_workspace_bytes(n_tokens, hidden, inter, n_experts, k)) return FMOE_ERR_WORKSPACE;
+  if (ws_bytes < fmoe_workspace_bytes(FMOE_OP_MOE_LAYER, n_tokens, hidden, inter, n_experts, k))
+    return FMOE_ERR_WORKSPACE;
   if (!aligned(ws, 256) || !aligned(a16_out, 2)) return FMOE_ERR_ALIGN;
   if (overlaps(a16_out, (size_t)n_tokens * k * inter * 2, ws, ws_bytes)) return FMOE_ERR_OVERLAP;
   int rc = check_device();
   if (rc) return rc;
-  return launch_batched_a16(ws, n_tokens, hidden, inter, n_experts, k, bits, a16_out, (hipStream_t)stream);
+  const size_t d = up256(carve_decode(nullptr, hidden, inter, n_experts, k).bytes);
+  return launch_batched_a16(static_cast<const char*>(ws) + d, n_tokens, hidden, inter, n_experts, k, bits, a16_out,
+                            (hipStream_t)stream);
 }
 
 }  // extern "C"

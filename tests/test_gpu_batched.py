@@ -169,6 +169,41 @@ def test_batched_deterministic():
         assert np.array_equal(u, v)
 
 
+def test_decode_after_batched_on_one_workspace():
+    """A multi-token call leaves a workspace ready for single-token calls: the decode kernel's
+    synchronization state sits apart from the multi-token scratch, so a decode after a
+    batched call on the same (zero-filled) workspace equals a decode on a fresh one."""
+    st = DevStack(2, 64, 512, 256, 4)
+    layers = fm.layers_array(st.layers)
+    T, k = 12, 4
+    X = np.stack([synth.token(st.seed, d, st.H) for d in range(T)]).astype(np.float32)
+    wsb = fm.workspace_bytes(fm.OP_MOE_LAYER, T, st.H, st.I, st.E, k)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+
+    def decode(ws_, wsb_, x):
+        xd = to_dev(x)
+        hd = torch.empty(st.H, dtype=torch.float32, device="cuda")
+        idx = torch.empty((st.L, k), dtype=torch.int32, device="cuda")
+        w = torch.empty((st.L, k), dtype=torch.float32, device="cuda")
+        fm.moe_layer(layers, xd, hd, 1, k, EPS, fm.PRENORM, idx, w, ws_, wsb_)
+        torch.cuda.synchronize()
+        return hd.cpu().numpy(), idx.cpu().numpy(), w.cpu().numpy()
+
+    x = synth.token(st.seed, 1000, st.H).astype(np.float32)
+    fresh_b = fm.workspace_bytes(fm.OP_MOE_LAYER, 1, st.H, st.I, st.E, k)
+    want = decode(torch.zeros(fresh_b, dtype=torch.uint8, device="cuda"), fresh_b, x)
+    first = decode(ws, wsb, x)  # decode, then batched, then decode again on one workspace
+    xb = to_dev(X)
+    hb = torch.empty_like(xb)
+    fm.moe_layer(layers, xb, hb, T, k, EPS, fm.PRENORM, None, None, ws, wsb)
+    torch.cuda.synchronize()
+    assert np.all(np.isfinite(hb.cpu().numpy()))
+    after = decode(ws, wsb, x)
+    for got in (first, after):
+        for u, v in zip(got, want):
+            assert np.array_equal(u, v)
+
+
 def test_batched_full_size_planted():
     """64 tokens through one 512-expert 4-bit layer at hidden 4096 / inter 1024, Zipf(1.1)
     popularity planted through the router."""
