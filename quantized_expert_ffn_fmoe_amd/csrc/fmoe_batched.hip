@@ -6,11 +6,12 @@
 // with the residual; aibit.im "Techniques de rupture" items 3-4, tr.news.hada.io "Model
 // mimarisi"), with the batch of tokens sorted by expert so that every expert's weights
 // are read once per call:
-//   1. stage: v = h (or rmsnorm(h)); its bf16 image v16 in operand order and, per group
-//      of 64 columns, the fp32 sum of the bf16 values;
-//   2. route: fp32 router logits (fp32 matrix cores) and top-k with softmax;
-//   3. sort: counting sort of the (token, slot) pairs by expert; the list of experts
-//      that received at least one pair;
+//   1. route: fp32 router logits of the raw h (fp32 matrix cores), as column-slice partials;
+//   2. per token: 1 / rms(h) under the pre-norm, the logits (partials summed, times that
+//      factor), top-k with softmax; v = h / rms(h) (or h) as its bf16 image v16 in operand
+//      order and, per group of 64 columns, the fp32 sum of the bf16 values;
+//   3. sort (by the last workgroup of step 2): counting sort of the (token, slot) pairs by
+//      expert; the list of work units (16 pairs of one expert each);
 //   4. gate/up: per (active expert, block of 128 rows): g and u for all of the expert's
 //      tokens, a = silu(g) * u, rounded to bf16 (a16) in the down operand's order, plus
 //      the group sums of a16;
@@ -56,7 +57,6 @@ constexpr int kGuRowsWave = 32;   // rows of gate (and of up) per wave
 constexpr int kGuRowsWg = 128;
 constexpr int kDnRowsWave = 64;   // rows of down per wave
 constexpr int kDnRowsWg = 256;
-constexpr int kSortThreads = 1024;
 
 // Column (0..15) of a 16-column block held at operand position p.
 template <int BITS>
@@ -143,34 +143,15 @@ struct BParams {
   float* ys;            // [P][H] down outputs (pair-id rows)
 };
 
-// ---------------------------------------------------------------- 1. stage
+// ---------------------------------------------------------------- 1. stage (one token)
+// x = h * inv (inv = 1 / rms(h), or 1 without the pre-norm) as bf16 in operand order (v16)
+// and, per group of 64 columns, the fp32 sum of the bf16 values (xg). One 16-column block
+// per thread step; the 4 blocks of a group sit on 4 consecutive lanes (nthreads and the
+// first thread's index are multiples of 64, so every group's lanes are active together).
 template <int BITS>
-__global__ void __launch_bounds__(kBT) stage_kernel(const float* __restrict__ h, int H, int prenorm, float eps,
-                                                    float* __restrict__ v, uint16_t* __restrict__ v16,
-                                                    float* __restrict__ xg) {
-  const int t = blockIdx.x;
-  const float* hr = h + (size_t)t * H;
-  __shared__ float red[kBT / 64];
-  float inv = 1.f;
-  if (prenorm) {
-    float ss = 0.f;
-    for (int i = threadIdx.x; i < H / 4; i += kBT) {
-      const float4 q = reinterpret_cast<const float4*>(hr)[i];
-      ss = fmaf(q.x, q.x, ss);
-      ss = fmaf(q.y, q.y, ss);
-      ss = fmaf(q.z, q.z, ss);
-      ss = fmaf(q.w, q.w, ss);
-    }
-    ss = wave_sum(ss);
-    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-    __syncthreads();
-    float tot = 0.f;
-#pragma unroll
-    for (int w = 0; w < kBT / 64; ++w) tot += red[w];
-    inv = 1.0f / sqrtf(tot / (float)H + eps);
-  }
-  // one 16-column block per thread; the 4 blocks of a group sit on 4 consecutive lanes
-  for (int blk = threadIdx.x; blk < H / 16; blk += kBT) {
+__device__ __forceinline__ void stage_token(const float* __restrict__ hr, int H, float inv, uint16_t* __restrict__ v16r,
+                                            float* __restrict__ xgr, int tid, int nthreads) {
+  for (int blk = tid; blk < H / 16; blk += nthreads) {
     float x[16];
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
@@ -180,10 +161,6 @@ __global__ void __launch_bounds__(kBT) stage_kernel(const float* __restrict__ h,
       x[4 * q + 2] = f.z * inv;
       x[4 * q + 3] = f.w * inv;
     }
-    float* vo = v + (size_t)t * H + blk * 16;
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      reinterpret_cast<float4*>(vo)[q] = make_float4(x[4 * q], x[4 * q + 1], x[4 * q + 2], x[4 * q + 3]);
     uint32_t r[16];
     float s = 0.f;
 #pragma unroll
@@ -194,16 +171,18 @@ __global__ void __launch_bounds__(kBT) stage_kernel(const float* __restrict__ h,
     uint32_t o[8];
 #pragma unroll
     for (int q = 0; q < 8; ++q) o[q] = r[perm_col<BITS>(2 * q)] | (r[perm_col<BITS>(2 * q + 1)] << 16);
-    u32x4* dst = reinterpret_cast<u32x4*>(v16 + (size_t)t * H + blk * 16);
+    u32x4* dst = reinterpret_cast<u32x4*>(v16r + blk * 16);
     dst[0] = u32x4{o[0], o[1], o[2], o[3]};
     dst[1] = u32x4{o[4], o[5], o[6], o[7]};
     s = group_sum(s, 4);
-    if ((blk & 3) == 0) xg[(size_t)t * (H / 64) + blk / 4] = s;
+    if ((blk & 3) == 0) xgr[blk / 4] = s;
   }
 }
 
 // ---------------------------------------------------------------- 2. route
-// Router logits as an fp32 matrix-core product (v_mfma_f32_16x16x4f32: lane l holds
+// Router logits as an fp32 matrix-core product on the raw h (the pre-norm's 1 / rms is a
+// per-token factor, applied to the summed logits by route_stage_kernel), with
+// v_mfma_f32_16x16x4f32 (lane l holds
 // A[l % 16][l / 16], B[l / 16][l % 16], result as above). Workgroup (e-tile, slice):
 // 16 experts x one 512-column slice of K, wave w taking 128 columns of it; the four
 // waves' tiles are added in LDS in wave order and written as the slice's partial
@@ -276,24 +255,105 @@ __global__ void __launch_bounds__(kBT) router_kernel_mfma(const float* __restric
   }
 }
 
-// Per token: the workgroup's four waves add the slice partials (slice order) into LDS
-// and write the logits out; wave 0 then takes the top-k by rank key and the softmax over
-// the selected logits.
-__global__ void __launch_bounds__(kBT) topk_parts_kernel(const float* __restrict__ part, int n_part, int T, int E,
-                                                         int k, float* __restrict__ logits, int32_t* __restrict__ idx,
-                                                         float* __restrict__ w) {
+// ---------------------------------------------------------------- 3. sort by expert
+// Pair s = t * k + j goes to expert idx[s]; pairs of one expert are contiguous in `pairs`
+// (their order inside an expert does not affect any result: every token's rows are
+// computed independently). The work list holds one unit per 16 pairs of an expert
+// (expert, first position, count), so a hot expert's passes run in parallel. Run by the
+// NT threads of one workgroup; cnt and cur are E ints of LDS each, sc 2 * NT ints.
+template <int NT>
+__device__ void sort_pairs(const int32_t* __restrict__ idx, int P, int E, int32_t* __restrict__ pairs,
+                           int32_t* __restrict__ act_e, int32_t* __restrict__ act_off, int32_t* __restrict__ act_cnt,
+                           int32_t* __restrict__ n_act, int* cnt, int* cur, int* sc) {
+  const int tid = threadIdx.x;
+  for (int e = tid; e < E; e += NT) cnt[e] = 0;
+  __syncthreads();
+  for (int s = tid; s < P; s += NT) atomicAdd(&cnt[idx[s]], 1);
+  __syncthreads();
+  const int per = (E + NT - 1) / NT;
+  const int lo = min(tid * per, E), hi = min(lo + per, E);
+  int c = 0, a = 0;
+  for (int e = lo; e < hi; ++e) {
+    c += cnt[e];
+    a += (cnt[e] + 15) / 16;
+  }
+  // inclusive scans of (c, a) over the threads (Hillis-Steele)
+  sc[tid] = c;
+  sc[NT + tid] = a;
+  __syncthreads();
+  for (int d = 1; d < NT; d <<= 1) {
+    const int vc = sc[tid] + (tid >= d ? sc[tid - d] : 0);
+    const int va = sc[NT + tid] + (tid >= d ? sc[NT + tid - d] : 0);
+    __syncthreads();
+    sc[tid] = vc;
+    sc[NT + tid] = va;
+    __syncthreads();
+  }
+  int off = sc[tid] - c, act = sc[NT + tid] - a;
+  for (int e = lo; e < hi; ++e) {
+    cur[e] = off;
+    for (int u = 0; 16 * u < cnt[e]; ++u) {  // one work unit per 16 pairs of the expert
+      act_e[act] = e;
+      act_off[act] = off + 16 * u;
+      act_cnt[act] = min(16, cnt[e] - 16 * u);
+      ++act;
+    }
+    off += cnt[e];
+  }
+  if (tid == NT - 1) *n_act = sc[NT + tid];
+  __syncthreads();
+  for (int s = tid; s < P; s += NT) pairs[atomicAdd(&cur[idx[s]], 1)] = s;
+}
+
+// Per token t (one workgroup): 1 / rms(h_t) under the pre-norm; the logits (slice partials
+// summed in slice order, times that factor) written out and ranked; wave 0 takes the top-k
+// and the softmax over the selected logits while waves 1-3 write the token's v16 and group
+// sums. The workgroup that finishes last (a device-scope counter, released after each
+// workgroup's stores and acquired by the last) sorts all T * k pairs by expert and resets
+// the counter for the next call.
+template <int BITS>
+__global__ void __launch_bounds__(kBT) route_stage_kernel(const float* __restrict__ h, int prenorm, float eps,
+                                                          const float* __restrict__ part, int n_part, int T, int E,
+                                                          int H, int k, float* __restrict__ logits,
+                                                          int32_t* __restrict__ idx, float* __restrict__ w,
+                                                          uint16_t* __restrict__ v16, float* __restrict__ xg,
+                                                          int32_t* __restrict__ pairs, int32_t* __restrict__ act_e,
+                                                          int32_t* __restrict__ act_off, int32_t* __restrict__ act_cnt,
+                                                          int32_t* __restrict__ n_act, uint32_t* __restrict__ done) {
   const int t = blockIdx.x, lane = threadIdx.x & 63;
-  __shared__ uint64_t keys[4096];
-  __shared__ float lsel[16], wsel[16];
+  const float* hr = h + (size_t)t * H;
+  __shared__ uint64_t keys[4096];  // also the sort's two E-int arrays
+  __shared__ int sc[2 * kBT];
+  __shared__ float lsel[16], wsel[16], red[kBT / 64];
   __shared__ int isel[16];
+  __shared__ int is_last;
+  float inv = 1.f;
+  if (prenorm) {
+    float ss = 0.f;
+    for (int i = threadIdx.x; i < H / 4; i += kBT) {
+      const float4 q = reinterpret_cast<const float4*>(hr)[i];
+      ss = fmaf(q.x, q.x, ss);
+      ss = fmaf(q.y, q.y, ss);
+      ss = fmaf(q.z, q.z, ss);
+      ss = fmaf(q.w, q.w, ss);
+    }
+    ss = wave_sum(ss);
+    if (lane == 0) red[threadIdx.x >> 6] = ss;
+    __syncthreads();
+    float tot = 0.f;
+#pragma unroll
+    for (int q = 0; q < kBT / 64; ++q) tot += red[q];
+    inv = 1.0f / sqrtf(tot / (float)H + eps);
+  }
   for (int e = threadIdx.x; e < E; e += kBT) {
     // all slices' loads first (clamped, unconditional), then the sum in slice order
     float x[kRtMaxParts];
 #pragma unroll
-    for (int s = 0; s < kRtMaxParts; ++s) x[s] = part[((size_t)min(s, n_part - 1) * T + t) * E + e];
+    for (int q = 0; q < kRtMaxParts; ++q) x[q] = part[((size_t)min(q, n_part - 1) * T + t) * E + e];
     float l = 0.f;
 #pragma unroll
-    for (int s = 0; s < kRtMaxParts; ++s) l = s < n_part ? l + x[s] : l;
+    for (int q = 0; q < kRtMaxParts; ++q) l = q < n_part ? l + x[q] : l;
+    l *= inv;
     logits[(size_t)t * E + e] = l;
     keys[e] = rank_key(l, e);
   }
@@ -307,65 +367,23 @@ __global__ void __launch_bounds__(kBT) topk_parts_kernel(const float* __restrict
     } else {
       wave_topk_keys(keys, E, k, isel, lsel, wsel);
     }
+  } else {
+    stage_token<BITS>(hr, H, inv, v16 + (size_t)t * H, xg + (size_t)t * (H / 64), threadIdx.x - 64, kBT - 64);
   }
   __syncthreads();
   if (threadIdx.x < k) {
     idx[(size_t)t * k + threadIdx.x] = isel[threadIdx.x];
     w[(size_t)t * k + threadIdx.x] = wsel[threadIdx.x];
   }
-}
-
-// ---------------------------------------------------------------- 3. sort by expert
-// One workgroup. Pair s = t * k + j goes to expert idx[s]; pairs of one expert are
-// contiguous in `pairs` (their order inside an expert does not affect any result: every
-// token's rows are computed independently). The work list holds one unit per 16 pairs of
-// an expert (expert, first position, count), so a hot expert's passes run in parallel.
-__global__ void __launch_bounds__(kSortThreads) sort_kernel(const int32_t* __restrict__ idx, int P, int E,
-                                                            int32_t* __restrict__ pairs, int32_t* __restrict__ act_e,
-                                                            int32_t* __restrict__ act_off,
-                                                            int32_t* __restrict__ act_cnt, int32_t* __restrict__ n_act) {
-  extern __shared__ int sh[];
-  int* cnt = sh;        // [E]
-  int* cur = sh + E;    // [E]
-  int* sc = sh + 2 * E; // [2][kSortThreads]
-  const int tid = threadIdx.x;
-  for (int e = tid; e < E; e += kSortThreads) cnt[e] = 0;
+  __threadfence();  // release this workgroup's idx (and everything else) at device scope
   __syncthreads();
-  for (int s = tid; s < P; s += kSortThreads) atomicAdd(&cnt[idx[s]], 1);
+  if (threadIdx.x == 0) is_last = atomicAdd(done, 1u) == (uint32_t)(T - 1);
   __syncthreads();
-  const int per = (E + kSortThreads - 1) / kSortThreads;
-  const int lo = min(tid * per, E), hi = min(lo + per, E);
-  int c = 0, a = 0;
-  for (int e = lo; e < hi; ++e) {
-    c += cnt[e];
-    a += (cnt[e] + 15) / 16;
-  }
-  // inclusive scans of (c, a) over the threads (Hillis-Steele)
-  sc[tid] = c;
-  sc[kSortThreads + tid] = a;
-  __syncthreads();
-  for (int d = 1; d < kSortThreads; d <<= 1) {
-    const int vc = sc[tid] + (tid >= d ? sc[tid - d] : 0);
-    const int va = sc[kSortThreads + tid] + (tid >= d ? sc[kSortThreads + tid - d] : 0);
-    __syncthreads();
-    sc[tid] = vc;
-    sc[kSortThreads + tid] = va;
-    __syncthreads();
-  }
-  int off = sc[tid] - c, act = sc[kSortThreads + tid] - a;
-  for (int e = lo; e < hi; ++e) {
-    cur[e] = off;
-    for (int u = 0; 16 * u < cnt[e]; ++u) {  // one work unit per 16 pairs of the expert
-      act_e[act] = e;
-      act_off[act] = off + 16 * u;
-      act_cnt[act] = min(16, cnt[e] - 16 * u);
-      ++act;
-    }
-    off += cnt[e];
-  }
-  if (tid == kSortThreads - 1) *n_act = sc[kSortThreads + tid];
-  __syncthreads();
-  for (int s = tid; s < P; s += kSortThreads) pairs[atomicAdd(&cur[idx[s]], 1)] = s;
+  if (!is_last) return;  // uniform over the workgroup
+  __threadfence();  // acquire the other workgroups' idx
+  int* cnt = reinterpret_cast<int*>(keys);
+  sort_pairs<kBT>(idx, T * k, E, pairs, act_e, act_off, act_cnt, n_act, cnt, cnt + E, sc);
+  if (threadIdx.x == 0) *done = 0;
 }
 
 // ---------------------------------------------------------------- 4./5. expert products
@@ -829,7 +847,6 @@ inline size_t max_units(int P, int E) { return (size_t)(E < P ? E : P) + (size_t
 
 struct BatchedWs {
   float* h[2];
-  float* v;
   uint16_t* v16;
   float* xg;
   float* logits;
@@ -841,6 +858,7 @@ struct BatchedWs {
   int32_t* act_off;
   int32_t* act_cnt;
   int32_t* n_act;
+  uint32_t* done;  // workgroups of route_stage_kernel finished (0 between calls)
   uint16_t* a16;
   float* ag;
   float* ys;
@@ -861,7 +879,6 @@ BatchedWs carve(void* base, int T, int H, int I, int E, int k) {
   const size_t P = (size_t)T * k;
   w.h[0] = reinterpret_cast<float*>(take((size_t)T * H * 4));
   w.h[1] = reinterpret_cast<float*>(take((size_t)T * H * 4));
-  w.v = reinterpret_cast<float*>(take((size_t)T * H * 4));
   w.v16 = reinterpret_cast<uint16_t*>(take((size_t)T * H * 2));
   w.xg = reinterpret_cast<float*>(take((size_t)T * (H / 64) * 4));
   w.logits = reinterpret_cast<float*>(take((size_t)T * E * 4));
@@ -874,6 +891,7 @@ BatchedWs carve(void* base, int T, int H, int I, int E, int k) {
   w.act_off = reinterpret_cast<int32_t*>(take(units * 4));
   w.act_cnt = reinterpret_cast<int32_t*>(take(units * 4));
   w.n_act = reinterpret_cast<int32_t*>(take(4));
+  w.done = reinterpret_cast<uint32_t*>(take(4));
   w.a16 = reinterpret_cast<uint16_t*>(take(P * I * 2));
   w.ag = reinterpret_cast<float*>(take(P * (I / 64) * 4));
   w.ys = reinterpret_cast<float*>(take(P * H * 4));
@@ -894,22 +912,17 @@ int run_layers(const fmoe_layer* layers, int n_layers, const float* x_in, float*
       hipFuncSetAttribute(reinterpret_cast<const void*>(&down_kernel<BITS>),
                           hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm_dn) != hipSuccess)
     return FMOE_ERR_HIP;
-  const size_t sort_smem = (size_t)(2 * E + 2 * kSortThreads) * 4;
   for (int l = 0; l < n_layers; ++l) {
     const float* hin = l == 0 ? x_in : ws.h[(l - 1) & 1];
     float* hnext = l == n_layers - 1 ? h_out : ws.h[l & 1];
     const fmoe_layer& L = layers[l];
-    hipLaunchKernelGGL(stage_kernel<BITS>, dim3(T), dim3(kBT), 0, s, hin, H, (flags & FMOE_PRENORM) ? 1 : 0, eps,
-                       ws.v, ws.v16, ws.xg);
-    if (hipGetLastError() != hipSuccess) return FMOE_ERR_HIP;
     const int n_part = (H + kRtSlice - 1) / kRtSlice;
-    hipLaunchKernelGGL(router_kernel_mfma, dim3((E + 15) / 16, n_part), dim3(kBT), 0, s, L.router, ws.v, T, E, H,
+    hipLaunchKernelGGL(router_kernel_mfma, dim3((E + 15) / 16, n_part), dim3(kBT), 0, s, L.router, hin, T, E, H,
                        ws.part);
     if (hipGetLastError() != hipSuccess) return FMOE_ERR_HIP;
-    hipLaunchKernelGGL(topk_parts_kernel, dim3(T), dim3(kBT), 0, s, ws.part, n_part, T, E, k, ws.logits, ws.idx, ws.w);
-    if (hipGetLastError() != hipSuccess) return FMOE_ERR_HIP;
-    hipLaunchKernelGGL(sort_kernel, dim3(1), dim3(kSortThreads), sort_smem, s, ws.idx, P, E, ws.pairs, ws.act_e,
-                       ws.act_off, ws.act_cnt, ws.n_act);
+    hipLaunchKernelGGL(route_stage_kernel<BITS>, dim3(T), dim3(kBT), 0, s, hin, (flags & FMOE_PRENORM) ? 1 : 0, eps,
+                       ws.part, n_part, T, E, H, k, ws.logits, ws.idx, ws.w, ws.v16, ws.xg, ws.pairs, ws.act_e,
+                       ws.act_off, ws.act_cnt, ws.n_act, ws.done);
     if (hipGetLastError() != hipSuccess) return FMOE_ERR_HIP;
     BParams bp;
     bp.experts = static_cast<const uint8_t*>(L.experts);
