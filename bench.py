@@ -272,6 +272,8 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=1)
     ap.add_argument("--config", choices=["stack4", "stack2", "batch64"], default="stack4")
     ap.add_argument("--tokens", type=int, default=256)
+    ap.add_argument("--top-k", type=int, default=4,
+                    help="experts per token for the stack configs (the headline workload is top-4)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -294,6 +296,11 @@ def main() -> int:
 
     if args.config == "batch64":
         return run_batch64(args, torch)
+    global K_
+    if not 1 <= args.top_k <= 14:
+        print(json.dumps({"error": "--top-k must be 1..14 at this layer shape"}))
+        return 2
+    K_ = args.top_k
 
     import quantized_expert_ffn_fmoe_amd as fm
     import synth
@@ -343,17 +350,18 @@ def main() -> int:
     reuse = float(np.mean([len(set(ids[t, l]) & set(ids[t - 1, l])) / K_ for t in range(1, T) for l in range(L_)]))
     reuse_l0 = float(np.mean([len(set(ids[t, 0]) & set(ids[t - 1, 0])) / K_ for t in range(1, T)]))
     log(f"{tok_s:.1f} tok/s, kernel avg {avg_kernel_s * 1e6:.1f} us, {achieved:.0f} GB/s")
-    parity = None if args.no_parity else parity_check(layers, bits, dev, ws, wsb)
+    parity = None if (args.no_parity or K_ != 4) else parity_check(layers, bits, dev, ws, wsb)  # golden is top-4
     if parity is not None:
         log(f"parity: {parity}")
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
         cpu = cpu_baseline(bits)
-    kernel_tag = f"decode_stack{bits}"
+    kernel_tag = f"decode_stack{bits}" + ("" if K_ == 4 else f"_top{K_}")
     traffic = traffic_from_profiles(kernel_tag)
     out = {
-        "metric": METRIC if bits == 4 else METRIC.replace("4-bit", "2-bit"),
+        "metric": (METRIC if bits == 4 else METRIC.replace("4-bit", "2-bit")).replace(
+            "4-bit)", f"4-bit, top-{K_})" if K_ != 4 else "4-bit)"),
         "value": round(tok_s, 2),
         "unit": "tokens/s",
         "n_gpus": 1,
@@ -365,8 +373,8 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": "f32",
         "data": "synthetic",
-        "config": {"workload": f"{L_}-layer x {E_}-expert {bits}-bit MoE expert-block decode stack, "
-                               f"{T} consecutive single tokens per step",
+        "config": {"workload": f"{L_}-layer x {E_}-expert {bits}-bit MoE expert-block decode stack"
+                               + ("" if K_ == 4 else f" (top-{K_})") + f", {T} consecutive single tokens per step",
                    "layers": L_, "experts": E_, "hidden": H_, "inter": I_, "top_k": K_, "bits": bits, "group": 64,
                    "tokens_per_step": T, "resident_expert_bytes": int(resident)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",

@@ -193,8 +193,8 @@ int fmoe_expert_ffn(const fmoe_expert* e, const float* x, float* y, void* ws, si
  * 1 <= k <= min(16, n_experts), n_tokens <= 4096, n_layers <= 4096; the batched path
  * (n_tokens > 1) also needs hidden % 256 == 0 and inter % 128 == 0; the decode path
  * needs its per-workgroup state (the staged vectors, the logits and the selection)
- * within 64 KB of LDS (FMOE_ERR_SHAPE otherwise); at hidden 4096, inter 1024, k 4 that
- * holds up to 4096 experts.
+ * within 160 KB of LDS (FMOE_ERR_SHAPE otherwise); at hidden 4096, inter 1024 that holds
+ * k 4 with up to 4096 experts and, with 512 experts, k up to 14 (4-bit) or 15 (2-bit).
  * Pointers: x_in, h_out 16-byte aligned; experts 256-byte aligned; ws 256-byte aligned.
  */
 int fmoe_moe_layer(const fmoe_layer* layers, int n_layers, const float* x_in, float* h_out, int n_tokens, int k,

@@ -258,7 +258,7 @@ int fmoe_moe_layer(const fmoe_layer* layers, int n_layers, const float* x_in, fl
   if ((rc = decode_grid(&G))) return rc;
   if (G > kMaxGrid) G = kMaxGrid;
   const int rows_per_wg = (H + G - 1) / G;
-  if (decode_smem_bytes(H, I, E, k, G, rows_per_wg, bits) > 64 * 1024) return FMOE_ERR_SHAPE;
+  if (decode_smem_bytes(H, I, E, k, G, rows_per_wg, bits) > kDecodeMaxLds) return FMOE_ERR_SHAPE;
   DecodeWs d = carve_decode(ws, H, I, E, k);
   DecodeParams p;
   memset(&p, 0, sizeof(p));

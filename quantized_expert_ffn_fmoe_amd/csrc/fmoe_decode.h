@@ -10,6 +10,7 @@ namespace fmoe {
 constexpr int kMaxLayersPerLaunch = 64;
 constexpr int kMaxGrid = 1024;  // workgroups of the persistent kernel (>= compute units)
 constexpr int kRep = 8;         // replicas of every exchanged item (logits, h, a)
+constexpr size_t kDecodeMaxLds = 160 * 1024;  // a gfx950 workgroup's LDS (beyond 64 KB by opt-in)
 
 struct DecodeParams {
   const float* router[kMaxLayersPerLaunch];

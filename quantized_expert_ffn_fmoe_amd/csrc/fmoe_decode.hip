@@ -734,6 +734,11 @@ static int launch_decode_t(const DecodeParams& p, int G, size_t smem, hipStream_
   // every wait inside the kernel is bounded, so a grid that cannot be made resident (other
   // long kernels holding CUs) ends with the error flag and NaN output, not a hang.
   int occ = 0, dev = 0, cus = 0;
+  // shapes whose LDS passes the 64 KB default (top-k with large k * inter) opt in
+  if (smem > 64 * 1024 &&
+      hipFuncSetAttribute(reinterpret_cast<const void*>(fn), hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem) !=
+          hipSuccess)
+    return FMOE_ERR_HIP;
   if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kDecodeThreads, smem) != hipSuccess) return FMOE_ERR_HIP;
   if (hipGetDevice(&dev) != hipSuccess) return FMOE_ERR_HIP;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return FMOE_ERR_HIP;
@@ -745,10 +750,15 @@ static int launch_decode_t(const DecodeParams& p, int G, size_t smem, hipStream_
 int launch_decode(const DecodeParams& p, int G, hipStream_t s) {
   const size_t smem = decode_smem_bytes(p.hidden, p.inter, p.n_experts, p.k, G, p.rows_per_wg, p.bits);
   int cg = p.cpl_g, cd = p.cpl_d;
-  // the decode shape of the 512-expert stack: hidden 4096, inter 1024, top-4
+  // the decode shapes of the 512-expert stack: hidden 4096, inter 1024, top-4 (and the
+  // top-10 routing of the same layer)
   if (p.hidden == 4096 && p.inter == 1024 && p.n_experts == 512 && p.k == 4) {
     if (p.bits == 4) return launch_decode_t<4, 2, 1, 4096, 1024, 512, 4>(p, G, smem, s);
     return launch_decode_t<2, 1, 1, 4096, 1024, 512, 4>(p, G, smem, s);
+  }
+  if (p.hidden == 4096 && p.inter == 1024 && p.n_experts == 512 && p.k == 10) {
+    if (p.bits == 4) return launch_decode_t<4, 2, 1, 4096, 1024, 512, 10>(p, G, smem, s);
+    return launch_decode_t<2, 1, 1, 4096, 1024, 512, 10>(p, G, smem, s);
   }
 #define FMOE_DEC(B, X, Y) \
   if (p.bits == B && cg == X && cd == Y) return launch_decode_t<B, X, Y, 0, 0, 0, 0>(p, G, smem, s);

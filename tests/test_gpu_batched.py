@@ -169,6 +169,14 @@ def test_batched_deterministic():
         assert np.array_equal(u, v)
 
 
+def test_batched_full_size_top10():
+    """Top-10 routing at the full layer shape: 16 tokens through one 512-expert 4-bit layer
+    (hidden 4096, inter 1024), 160 (token, slot) pairs."""
+    st = DevStack(1, 512, 4096, 1024, 4, gpu_fill=True)
+    X, _ = accepted_tokens(st.routers_np[0], 16, 10)
+    check_layer(st, X, 10, prenorm=False, label="full size top-10")
+
+
 def test_decode_after_batched_on_one_workspace():
     """A multi-token call leaves a workspace ready for single-token calls: the decode kernel's
     synchronization state sits apart from the multi-token scratch, so a decode after a

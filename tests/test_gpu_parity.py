@@ -283,6 +283,17 @@ def test_decode_stack(L, E, H, I, k, bits):
         assert rel_l2(h, ref["out"]) <= TOL
 
 
+def test_decode_stack_full_size_top10():
+    """Top-10 routing (k as a free parameter) at the full layer shape: two pre-normed layers
+    of 512 experts, hidden 4096, inter 1024, 4-bit."""
+    stack = DevStack(2, 512, 4096, 1024, 4, gpu_fill=True)
+    for x, ref in _stack_tokens(stack, 10, 2):
+        h, idx, w = _decode(stack, x, 10)
+        assert np.array_equal(idx, ref["idx"])
+        assert rel_l2(w, ref["w"]) <= TOL
+        assert rel_l2(h, ref["out"]) <= TOL
+
+
 def test_decode_many_layers_chunked():
     """More layers than one persistent launch holds (64): chunked launches share the state."""
     stack = DevStack(70, 8, 128, 64, 4)
