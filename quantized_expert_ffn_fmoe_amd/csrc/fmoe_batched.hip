@@ -268,7 +268,7 @@ __device__ void sort_pairs(const int32_t* __restrict__ idx, int P, int E, int32_
   const int tid = threadIdx.x;
   for (int e = tid; e < E; e += NT) cnt[e] = 0;
   __syncthreads();
-  for (int s = tid; s < P; s += NT) atomicAdd(&cnt[idx[s]], 1);
+  for (int s = tid; s < P; s += NT) atomicAdd(&cnt[ld_dev_u32(reinterpret_cast<const uint32_t*>(idx) + s)], 1);
   __syncthreads();
   const int per = (E + NT - 1) / NT;
   const int lo = min(tid * per, E), hi = min(lo + per, E);
@@ -302,15 +302,17 @@ __device__ void sort_pairs(const int32_t* __restrict__ idx, int P, int E, int32_
   }
   if (tid == NT - 1) *n_act = sc[NT + tid];
   __syncthreads();
-  for (int s = tid; s < P; s += NT) pairs[atomicAdd(&cur[idx[s]], 1)] = s;
+  for (int s = tid; s < P; s += NT) pairs[atomicAdd(&cur[ld_dev_u32(reinterpret_cast<const uint32_t*>(idx) + s)], 1)] = s;
 }
 
 // Per token t (one workgroup): 1 / rms(h_t) under the pre-norm; the logits (slice partials
 // summed in slice order, times that factor) written out and ranked; wave 0 takes the top-k
 // and the softmax over the selected logits while waves 1-3 write the token's v16 and group
-// sums. The workgroup that finishes last (a device-scope counter, released after each
-// workgroup's stores and acquired by the last) sorts all T * k pairs by expert and resets
-// the counter for the next call.
+// sums. The selected experts are stored at the device coherence point; once they are
+// acknowledged the workgroup counts itself on a device-scope counter, and the workgroup
+// that finishes last reads all T * k selections back from the coherence point, sorts the
+// pairs by expert and resets the counter for the next call. (A device-scope fence instead
+// would write back this XCD's whole L2.)
 template <int BITS>
 __global__ void __launch_bounds__(kBT) route_stage_kernel(const float* __restrict__ h, int prenorm, float eps,
                                                           const float* __restrict__ part, int n_part, int T, int E,
@@ -372,18 +374,17 @@ __global__ void __launch_bounds__(kBT) route_stage_kernel(const float* __restric
   }
   __syncthreads();
   if (threadIdx.x < k) {
-    idx[(size_t)t * k + threadIdx.x] = isel[threadIdx.x];
+    st_dev_u32(reinterpret_cast<uint32_t*>(idx) + (size_t)t * k + threadIdx.x, (uint32_t)isel[threadIdx.x]);
     w[(size_t)t * k + threadIdx.x] = wsel[threadIdx.x];
   }
-  __threadfence();  // release this workgroup's idx (and everything else) at device scope
+  wait_vmem();  // idx acknowledged at the device coherence point (read by the last workgroup)
   __syncthreads();
   if (threadIdx.x == 0) is_last = atomicAdd(done, 1u) == (uint32_t)(T - 1);
   __syncthreads();
   if (!is_last) return;  // uniform over the workgroup
-  __threadfence();  // acquire the other workgroups' idx
   int* cnt = reinterpret_cast<int*>(keys);
   sort_pairs<kBT>(idx, T * k, E, pairs, act_e, act_off, act_cnt, n_act, cnt, cnt + E, sc);
-  if (threadIdx.x == 0) *done = 0;
+  if (threadIdx.x == 0) st_dev_u32(done, 0u);
 }
 
 // ---------------------------------------------------------------- 4./5. expert products
