@@ -632,12 +632,15 @@ __device__ __forceinline__ void expert_pass_any(f32x4 (&acc)[4], char* wbuf, Mat
     static_assert(SG::kRPI == CodeLayout<BITS>::kSubRows && SG::kRS == CodeLayout<BITS>::kPieceBytes,
                   "a 4-group stage instruction is one contiguous KB of the code layout");
     const uint8_t* dmarow[SG::kNJ];
+    int run[SG::kNJ];  // bytes from one piece of the instruction's rows to the next
 #pragma unroll
     for (int j = 0; j < SG::kNJ; ++j) {  // rows j * kRPI .. (consecutive, kRPI-aligned): lane l takes byte 16 l
       const int R = j * SG::kRPI;
-      dmarow[j] = mat_of(R) + code_offset<BITS>(rows_of, row_bytes, row_of(R), 0) + 16 * lane;
+      const size_t o0 = code_offset<BITS>(rows_of, row_bytes, row_of(R), 0);
+      dmarow[j] = mat_of(R) + o0 + 16 * lane;
+      run[j] = (int)(code_offset<BITS>(rows_of, row_bytes, row_of(R), SG::kRS) - o0);
     }
-    auto src = [&](int j, int g0) { return dmarow[j] + (size_t)(g0 / 4) * CodeLayout<BITS>::kRunBytes; };
+    auto src = [&](int j, int g0) { return dmarow[j] + (size_t)(g0 / 4) * run[j]; };
     const uint32_t* sp[4];  // the lane's scale/bias piece at stage 0; a stage is 32 rows x 4 words further
 #pragma unroll
     for (int t = 0; t < 4; ++t) sp[t] = sbm[t] + sb_offset(rows_of, G, sbr[t], 0);

