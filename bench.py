@@ -13,7 +13,8 @@ achieved HBM bandwidth against the 8 TB/s peak (HIP events around every launch),
 spot check of the full-size stack against stored oracle results, the measured inter-token
 expert reuse, and the CPU oracle's throughput on a small sample (cpu_baseline).
 
-Usage: python bench.py [--gpus 1] [--steps 5] [--warmup 1] [--config stack4|stack2]
+Usage: python bench.py [--gpus 1] [--steps 5] [--warmup 1] [--config stack4|stack2|batch64|batch64_2bit]
+       [--top-k K]
 """
 from __future__ import annotations
 
@@ -155,20 +156,20 @@ def calibrate_copy(torch) -> int:
     return 0
 
 
-def run_batch64(args, torch) -> int:
+def run_batch64(args, torch, bits: int = 4) -> int:
     """64 tokens x 1 layer through the grouped (bf16 matrix-core) path, rotating over 8
-    independent 512-expert 4-bit layers so that no call finds its experts in cache. Expert
+    independent 512-expert layers so that no call finds its experts in cache. Expert
     popularity is Zipf(1.1), planted through each layer's router."""
     import quantized_expert_ffn_fmoe_amd as fm
     import synth
     from gpu_util import fill_experts_gpu, to_dev
 
-    NL, T, bits = 8, 64, 4
+    NL, T = 8, 64
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     eb = fm.expert_bytes(H_, I_, bits)
     stride = (eb + 255) // 256 * 256
-    gpath = os.path.join(ROOT, "tests", "golden", "batch64_4bit.npz")
+    gpath = os.path.join(ROOT, "tests", "golden", f"batch64_{bits}bit.npz")
     golden = np.load(gpath, allow_pickle=False) if os.path.exists(gpath) else None
     log(f"building {NL} independent {E_}-expert {bits}-bit layers")
     blobs, routers, layers, Xs = [], [], [], []
@@ -227,6 +228,19 @@ def run_batch64(args, torch) -> int:
                   "tokens_within_1e-5": float(np.mean(np.array(rel) <= 1e-5)), "tolerance": 2.0 ** -8,
                   "pass": bool(exact and max(rel) <= 2.0 ** -8)}
         log(f"parity: {parity}")
+    elif not args.no_parity:
+        # no stored expected values at this width: the oracle (O7 contract) on 8 tokens of layer 0
+        import oracle
+
+        n = 8
+        ref = oracle.layer_bf16(synth.Provider(0, H_, I_, bits), 0, synth.router(0, 0, E_, H_),
+                                Xs[0][:n].cpu().numpy(), I_, K_, bits, 64)
+        out0 = outs[0][:n].cpu().numpy().astype(np.float64)
+        rel = [float(np.linalg.norm(out0[t] - ref["out"][t]) / np.linalg.norm(ref["out"][t])) for t in range(n)]
+        exact = bool(np.array_equal(ids[0, :n, 0, :], ref["idx"]))
+        parity = {"tokens": n, "experts_bit_exact": exact, "max_rel_l2_vs_bf16_contract": max(rel),
+                  "tolerance": 2.0 ** -8, "pass": bool(exact and max(rel) <= 2.0 ** -8), "reference": "live oracle"}
+        log(f"parity: {parity}")
     cpu = None
     if not args.no_cpu_baseline:
         import oracle
@@ -242,7 +256,7 @@ def run_batch64(args, torch) -> int:
                "sample": "16 of the 64 tokens of layer 0, O7 bf16 contract in fp64 plain loops (OpenMP over rows), "
                          "expert generation included", "seconds": round(t_or, 3)}
     out = {
-        "metric": "MoE-block batched prefill tokens/s (64 tokens x 1 layer, 4-bit) + achieved HBM GB/s vs peak",
+        "metric": f"MoE-block batched prefill tokens/s (64 tokens x 1 layer, {bits}-bit) + achieved HBM GB/s vs peak",
         "value": round(tok_s, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(elapsed * 1e3 / args.steps, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
@@ -252,7 +266,7 @@ def run_batch64(args, torch) -> int:
                    "calls_per_step": NL, "distinct_experts_per_call": distinct},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_GBS, 4), "traffic": None,
-                     "kernel": "fmoe batched layer call (stage, route, sort, gate/up, down, combine kernels)",
+                     "kernel": "fmoe batched layer call (router, route/stage/sort, gate/up, down, combine kernels)",
                      "algorithmic_bytes_per_launch": int(np.mean(bytes_call)),
                      "avg_launch_us": round(float(call_ms.mean()) * 1e3, 2)},
         "cpu_baseline": cpu,
@@ -270,7 +284,7 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--config", choices=["stack4", "stack2", "batch64"], default="stack4")
+    ap.add_argument("--config", choices=["stack4", "stack2", "batch64", "batch64_2bit"], default="stack4")
     ap.add_argument("--tokens", type=int, default=256)
     ap.add_argument("--top-k", type=int, default=4,
                     help="experts per token for the stack configs (the headline workload is top-4)")
@@ -294,8 +308,8 @@ def main() -> int:
     if args.calibrate_copy:
         return calibrate_copy(torch)
 
-    if args.config == "batch64":
-        return run_batch64(args, torch)
+    if args.config in ("batch64", "batch64_2bit"):
+        return run_batch64(args, torch, 4 if args.config == "batch64" else 2)
     global K_
     if not 1 <= args.top_k <= 14:
         print(json.dumps({"error": "--top-k must be 1..14 at this layer shape"}))

@@ -177,6 +177,14 @@ def test_batched_full_size_top10():
     check_layer(st, X, 10, prenorm=False, label="full size top-10")
 
 
+def test_batched_full_size_2bit():
+    """2-bit experts at the full layer shape: 24 tokens through one 512-expert layer (hidden
+    4096, inter 1024)."""
+    st = DevStack(1, 512, 4096, 1024, 2, gpu_fill=True)
+    X, _ = accepted_tokens(st.routers_np[0], 24, 4)
+    check_layer(st, X, 4, prenorm=False, label="full size 2-bit")
+
+
 def test_decode_after_batched_on_one_workspace():
     """A multi-token call leaves a workspace ready for single-token calls: the decode kernel's
     synchronization state sits apart from the multi-token scratch, so a decode after a
