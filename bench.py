@@ -296,7 +296,7 @@ def main() -> int:
     args = ap.parse_args()
     if args.gpus != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only: the whole expert stack fits in one "
-                                   "MI355X's HBM and the path has no multi-GPU mode (see DESIGN.md on sharding)",
+                                   "MI355X's HBM and the path has no multi-GPU mode",
                           "n_gpus": args.gpus}))
         return 2
     if int(os.environ.get("WORLD_SIZE", "1")) > 1:
