@@ -602,6 +602,59 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
           if (subD < kBatchD && d_lo + u < d_hi && rl < nr) ybuf[j_lo * rows_wg + rl] = sum;
         }
       }
+    } else if (kFastD) {
+      // compiled shapes whose waves' down items span several slots (top-k with large k):
+      // the same per-wave scheme slot by slot. A slot shared by two waves is gathered and
+      // digitised by both, which write identical values to the same LDS.
+      if constexpr (kFastD) {
+        for (int j = d_lo / n_rb; d_lo < d_hi && j * n_rb < d_hi; ++j) {  // slots < K: items < K * n_rb
+          const int t_lo = max(d_lo, j * n_rb), t_hi = min(d_hi, (j + 1) * n_rb);
+          const uint64_t* a_j = a_rep + (size_t)j * I;
+          wait_vmem();
+          for (int i0 = lane; i0 < I; i0 += 64 * kPollA) {
+            float av[kPollA];
+            if (!poll_batch<kPollA, 64>(a_j, I, i0, ep + 2u, av, p.err)) *fail = 1;
+#pragma unroll
+            for (int u = 0; u < kPollA; ++u) {
+              const int i = i0 + 64 * u;
+              if (i < I) vec[padded<CC>(j * I + i)] = av[u];
+            }
+          }
+          __builtin_amdgcn_wave_barrier();
+          build_digits<BITS>(dig_a, j * nchD, I, [&](int i) { return vec[padded<CC>(i)]; }, 64, lane);
+          __builtin_amdgcn_wave_barrier();
+          DChunk<BITS> dc[CPL_D];
+#pragma unroll
+          for (int q = 0; q < CPL_D; ++q) {
+            int c = subD + kLprD * q;
+            if (c < nchD) load_dchunk<BITS>(dc[q], dig_a, j * nchD + c);
+          }
+          for (int t0 = t_lo; t0 < t_hi; t0 += kBatchD) {
+            if (t0 != d_lo) {  // the wave's first batch was requested before the gather
+#pragma unroll
+              for (int u = 0; u < kBatchD; ++u) down_load(t0 - d_lo + u, u);
+            }
+            float acc[kBatchD];
+#pragma unroll
+            for (int u = 0; u < kBatchD; ++u) {
+              float a_ = 0.f;
+#pragma unroll
+              for (int q = 0; q < CPL_D; ++q) {
+                int c = subD + kLprD * q;
+                if (c < nchD) a_ += chunk_dot_int<BITS>(wd[u][q], sd[u][q], dc[q]);
+              }
+              acc[u] = a_;
+            }
+            // items past t_hi (another slot's or none) are reduced too; their sums are
+            // not stored
+            const float sum = reduce_transposed<kBatchD, kLprD>(acc);
+            const int u = transposed_index<kBatchD>(lane);
+            const int t = t0 + u;
+            const int rl = (t - j * n_rb) * rpwD + rselD;
+            if (subD < kBatchD && t < t_hi && rl < nr) ybuf[j * rows_wg + rl] = sum;
+          }
+        }
+      }
     } else {
       for (int i0 = tid; i0 < KI; i0 += kDecodeThreads * kPollN) {
         float av[kPollN];
