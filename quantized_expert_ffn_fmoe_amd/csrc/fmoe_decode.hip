@@ -116,6 +116,15 @@ __device__ __forceinline__ bool poll_batch(const uint64_t* src, int n, int i0, u
   return true;
 }
 
+// The same lane value, opaque to the optimizer: the code and scale offsets derived from it
+// inside the layer loop are recomputed there (a few vector operations per layer) instead
+// of being hoisted out of the loop and held in spill registers for its whole length (this
+// halves the accumulation registers used as spill space in the compiled decode shapes).
+__device__ __forceinline__ int opaque_lane(int v) {
+  asm volatile("" : "+v"(v));
+  return v;
+}
+
 // Wait until wave 0's top-k progress word (LDS) reached r.
 __device__ __forceinline__ void wait_ready(const int* ready, int r) {
   while (__hip_atomic_load(const_cast<int*>(ready), __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < r)
@@ -188,10 +197,10 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
   const int ngH = H / 64, ngI = I / 64;
   const size_t rowH = (size_t)H * BITS / 8, rowI = (size_t)I * BITS / 8;
   const int nchG = H / CC, nchD = I / CC;
-  const int lprG = HC ? lanes_per_row(HC / CC) : p.lpr_g, rpwG = 64 / lprG, subG = lane & (lprG - 1),
-            rselG = lane / lprG;
-  const int lprD = IC ? lanes_per_row(IC / CC) : p.lpr_d, rpwD = 64 / lprD, subD = lane & (lprD - 1),
-            rselD = lane / lprD;
+  const int lprG = HC ? lanes_per_row(HC / CC) : p.lpr_g, rpwG = 64 / lprG;
+  const int lprD = IC ? lanes_per_row(IC / CC) : p.lpr_d, rpwD = 64 / lprD;
+  int subG = lane & (lprG - 1), rselG = lane / lprG;  // recomputed per layer (opaque_lane)
+  int subD = lane & (lprD - 1), rselD = lane / lprD;
   const int rows_wg = p.rows_per_wg;
   const int r0 = g * rows_wg;
   const int nr = max(0, min(H - r0, rows_wg));
@@ -236,6 +245,13 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
     const int lg = p.layer0 + l;
     const uint8_t* X = p.experts[l];
     const uint32_t ep = F + 3u * (uint32_t)l;
+    {
+      const int ln = opaque_lane(lane);
+      subG = ln & (lprG - 1);
+      rselG = ln / lprG;
+      subD = ln & (lprD - 1);
+      rselD = ln / lprD;
+    }
 
     // ---- 1. h (the previous layer's tagged output, or x_in), v = rmsnorm(h) or h in LDS
     float ss = 0.f;
