@@ -146,6 +146,20 @@ size_t fmoe_workspace_bytes(int op, int n_tokens, int hidden, int inter, int n_e
 int fmoe_dequant_matvec(const fmoe_qmat* W, const float* x, float* y, int n_vec, fmoe_stream_t stream);
 
 /*
+ * Several dequantized matvecs over one input, in one launch ([radar] "Optimisations
+ * efficaces": a fused Q/K/V projection kernel reads the input vector once instead of
+ * once per matrix):  y[m][v][r] = sum_c W_m[r][c] * x[v][c]  for m < n_mats, each as
+ * fmoe_dequant_matvec. Each wave of the kernel reads its part of x into registers once
+ * and reuses it for the rows of every matrix.
+ * W: host array of n_mats descriptors (1 <= n_mats <= 8) with equal cols and bits (rows
+ * may differ); x: fp32 [n_vec][cols]; y: host array of n_mats device pointers, y[m] fp32
+ * [n_vec][W[m].rows]. No output may overlap x or another output (FMOE_ERR_OVERLAP);
+ * other limits and errors as fmoe_dequant_matvec.
+ */
+int fmoe_dequant_matvec_multi(const fmoe_qmat* W, int n_mats, const float* x, float* const* y, int n_vec,
+                              fmoe_stream_t stream);
+
+/*
  * Router + top-k for n_tokens tokens ([aibit] "Techniques de rupture" items 1 and 3,
  * [hada] "Model mimarisi": k of n_experts experts per token; the pages route on the
  * CPU, here it runs on the device):

@@ -22,8 +22,8 @@ PRENORM = 1
 OP_EXPERT_FFN, OP_MOE_LAYER = 1, 2
 
 EXPORTS = ("fmoe_status_string", "fmoe_version", "fmoe_codes_bytes", "fmoe_sb_bytes", "fmoe_expert_bytes",
-           "fmoe_expert_view", "fmoe_pack", "fmoe_workspace_bytes", "fmoe_dequant_matvec", "fmoe_route_topk",
-           "fmoe_expert_ffn", "fmoe_moe_layer", "fmoe_batched_a16")
+           "fmoe_expert_view", "fmoe_pack", "fmoe_workspace_bytes", "fmoe_dequant_matvec",
+           "fmoe_dequant_matvec_multi", "fmoe_route_topk", "fmoe_expert_ffn", "fmoe_moe_layer", "fmoe_batched_a16")
 
 
 class FmoeError(RuntimeError):
@@ -77,6 +77,8 @@ def lib():
         L.fmoe_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
         L.fmoe_dequant_matvec.restype = i32
         L.fmoe_dequant_matvec.argtypes = [ctypes.POINTER(QMat), vp, vp, i32, vp]
+        L.fmoe_dequant_matvec_multi.restype = i32
+        L.fmoe_dequant_matvec_multi.argtypes = [ctypes.POINTER(QMat), i32, vp, ctypes.POINTER(vp), i32, vp]
         L.fmoe_route_topk.restype = i32
         L.fmoe_route_topk.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp]
         L.fmoe_expert_ffn.restype = i32
@@ -154,6 +156,16 @@ def workspace_bytes(op: int, n_tokens: int, hidden: int, inter: int, n_experts: 
 def dequant_matvec(W: QMat, x, y, n_vec: int = 1, stream=None) -> None:
     _check(lib().fmoe_dequant_matvec(ctypes.byref(W), _ptr(x), _ptr(y), n_vec, _stream(stream)),
            "fmoe_dequant_matvec")
+
+
+def dequant_matvec_multi(Ws, x, ys, n_vec: int = 1, stream=None) -> None:
+    """Ws: list of QMat (equal cols and bits); ys: list of output tensors, one per matrix."""
+    if len(Ws) != len(ys):
+        raise ValueError("one output per matrix")
+    mats = (QMat * max(1, len(Ws)))(*Ws)
+    outs = (ctypes.c_void_p * max(1, len(ys)))(*[_ptr(y) for y in ys])
+    _check(lib().fmoe_dequant_matvec_multi(mats, len(Ws), _ptr(x), outs, n_vec, _stream(stream)),
+           "fmoe_dequant_matvec_multi")
 
 
 def route_topk(router, x, n_tokens, n_experts, hidden, k, idx, w, logits, stream=None) -> None:

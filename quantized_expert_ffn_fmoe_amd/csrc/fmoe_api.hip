@@ -167,6 +167,31 @@ int fmoe_dequant_matvec(const fmoe_qmat* W, const float* x, float* y, int n_vec,
   return launch_matvec(*W, x, y, n_vec, (hipStream_t)stream);
 }
 
+int fmoe_dequant_matvec_multi(const fmoe_qmat* W, int n_mats, const float* x, float* const* y, int n_vec,
+                              fmoe_stream_t stream) {
+  if (!W || !x || !y) return FMOE_ERR_NULL;
+  if (n_mats < 1 || n_mats > kMaxMulti) return FMOE_ERR_SHAPE;
+  int rc;
+  for (int m = 0; m < n_mats; ++m)
+    if ((rc = check_qmat(&W[m]))) return rc;
+  for (int m = 1; m < n_mats; ++m)
+    if (W[m].cols != W[0].cols || W[m].bits != W[0].bits) return FMOE_ERR_SHAPE;
+  if (n_vec < 1 || n_vec > 64) return FMOE_ERR_SHAPE;
+  if (!aligned(x, 16)) return FMOE_ERR_ALIGN;
+  const size_t nx = (size_t)n_vec * W[0].cols * 4;
+  for (int m = 0; m < n_mats; ++m) {
+    if (!y[m]) return FMOE_ERR_NULL;
+    if (!aligned(y[m], 16)) return FMOE_ERR_ALIGN;
+    const size_t ny = (size_t)n_vec * W[m].rows * 4;
+    if (overlaps(y[m], ny, x, nx)) return FMOE_ERR_OVERLAP;
+    for (int m2 = 0; m2 < m; ++m2)
+      if (overlaps(y[m], ny, y[m2], (size_t)n_vec * W[m2].rows * 4)) return FMOE_ERR_OVERLAP;
+  }
+  rc = check_device();
+  if (rc) return rc;
+  return launch_matvec_multi(W, n_mats, x, y, n_vec, (hipStream_t)stream);
+}
+
 int fmoe_route_topk(const float* router, const float* x, int n_tokens, int n_experts, int hidden, int k,
                     int32_t* idx, float* w, float* logits, fmoe_stream_t stream) {
   if (!router || !x || !idx || !w || !logits) return FMOE_ERR_NULL;

@@ -59,6 +59,76 @@ __global__ void __launch_bounds__(256) matvec_kernel(const uint8_t* __restrict__
   }
 }
 
+// Several matrices applied to one input (openclawradar.com "Optimisations efficaces": the
+// fused Q/K/V projection reads the input vector once instead of once per matrix). Every
+// wave loads its share of x into registers once and walks row blocks of all matrices; the
+// row space of matrix m starts at prow[m], each matrix padded to whole row blocks of the
+// wave, so a row block never spans two matrices and m is uniform over the wave.
+template <int BITS, int CPL>
+__global__ void __launch_bounds__(256) matvec_multi_kernel(MultiMat P, const float* __restrict__ x, int cols,
+                                                           int lpr) {
+  using C = Chunk<BITS>;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
+  const int rpw = kWave / lpr;
+  const int sub = lane & (lpr - 1);
+  const int rsel = lane / lpr;
+  const int n_chunks = cols / C::kCodes;
+  const int ngroups = cols / 64;
+  const size_t row_bytes = (size_t)cols * BITS / 8;
+  const float* xv = x + (size_t)blockIdx.y * cols;
+  XChunk<BITS> xc[CPL];
+#pragma unroll
+  for (int j = 0; j < CPL; ++j) {
+    int c = sub + lpr * j;
+    if (c < n_chunks) load_xchunk<BITS>(xc[j], xv + (size_t)c * C::kCodes);
+  }
+  const int waves_total = gridDim.x * (blockDim.x >> 6);
+  const int total = P.prow[P.n_mats];
+  for (int rb = (blockIdx.x * (blockDim.x >> 6) + wave) * rpw; rb < total; rb += waves_total * rpw) {
+    // the matrix of this row block, and its fields, by a select chain (no dynamic indexing
+    // of the kernel-argument arrays)
+    int m = 0;
+#pragma unroll
+    for (int i = 1; i < kMaxMulti; ++i)
+      if (i < P.n_mats && rb >= P.prow[i]) m = i;
+    const uint8_t* codes = P.codes[0];
+    const uint32_t* sb = P.sb[0];
+    float* y = P.y[0];
+    int rows = P.rows[0], r0 = P.prow[0];
+#pragma unroll
+    for (int i = 1; i < kMaxMulti; ++i)
+      if (m == i) {
+        codes = P.codes[i];
+        sb = P.sb[i];
+        y = P.y[i];
+        rows = P.rows[i];
+        r0 = P.prow[i];
+      }
+    const int r = rb - r0 + rsel;
+    float acc = 0.f;
+    if (r < rows) {
+      uint4 w[CPL];
+      uint32_t s[CPL];
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        int c = sub + lpr * j;
+        if (c < n_chunks) {
+          w[j] = *reinterpret_cast<const uint4*>(codes + code_offset<BITS>(rows, row_bytes, r, (size_t)c * 16));
+          s[j] = sb[sb_offset(rows, ngroups, r, c / C::kPerGroup)];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < CPL; ++j) {
+        int c = sub + lpr * j;
+        if (c < n_chunks) acc += chunk_dot<BITS>(w[j], s[j], xc[j]);
+      }
+    }
+    acc = group_sum(acc, lpr);
+    if (r < rows && sub == 0) y[(size_t)blockIdx.y * rows + r] = acc;
+  }
+}
+
 // Canonical (row-major) codes -> the packed layout of fmoe_layout.h, one 16-byte chunk per
 // thread step (chunks never straddle a piece); scale and bias interleaved into sb words,
 // placed in the blocked sb order of the same header.
@@ -150,6 +220,44 @@ int launch_matvec(const QMat& W, const float* x, float* y, int n_vec, hipStream_
   const uint8_t* codes = static_cast<const uint8_t*>(W.codes);
 #define FMOE_MV(B, C) hipLaunchKernelGGL((matvec_kernel<B, C>), grid, dim3(256), 0, s, codes, W.sb, x, y, W.rows, W.cols, lpr)
   if (W.bits == 4) {
+    if (cpl == 1) FMOE_MV(4, 1);
+    else if (cpl == 2) FMOE_MV(4, 2);
+    else if (cpl <= 4) FMOE_MV(4, 4);
+    else return FMOE_ERR_SHAPE;
+  } else {
+    if (cpl == 1) FMOE_MV(2, 1);
+    else if (cpl == 2) FMOE_MV(2, 2);
+    else if (cpl <= 4) FMOE_MV(2, 4);
+    else return FMOE_ERR_SHAPE;
+  }
+#undef FMOE_MV
+  return hipGetLastError() == hipSuccess ? FMOE_OK : FMOE_ERR_HIP;
+}
+
+int launch_matvec_multi(const QMat* W, int n_mats, const float* x, float* const* y, int n_vec, hipStream_t s) {
+  const int cols = W[0].cols, bits = W[0].bits;
+  const int n_chunks = cols * bits / 128;
+  int lpr = 1;
+  while (lpr < n_chunks && lpr < 64) lpr <<= 1;
+  const int cpl = (n_chunks + lpr - 1) / lpr;
+  const int rpw = 64 / lpr;
+  MultiMat P;
+  P.n_mats = n_mats;
+  P.prow[0] = 0;
+  for (int i = 0; i < kMaxMulti; ++i) {
+    const int m = i < n_mats ? i : n_mats - 1;  // unused slots repeat the last matrix
+    P.codes[i] = static_cast<const uint8_t*>(W[m].codes);
+    P.sb[i] = W[m].sb;
+    P.y[i] = y[m];
+    P.rows[i] = W[m].rows;
+    P.prow[i + 1] = P.prow[i] + (i < n_mats ? (W[i].rows + rpw - 1) / rpw * rpw : 0);
+  }
+  const int waves_needed = P.prow[n_mats] / rpw;
+  int blocks = (waves_needed + 3) / 4;
+  if (blocks > 2048) blocks = 2048;
+  dim3 grid(blocks, n_vec);
+#define FMOE_MV(B, C) hipLaunchKernelGGL((matvec_multi_kernel<B, C>), grid, dim3(256), 0, s, P, x, cols, lpr)
+  if (bits == 4) {
     if (cpl == 1) FMOE_MV(4, 1);
     else if (cpl == 2) FMOE_MV(4, 2);
     else if (cpl <= 4) FMOE_MV(4, 4);

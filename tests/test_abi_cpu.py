@@ -92,6 +92,28 @@ def test_matvec_validation():
     _raises(fm.ERR_OVERLAP, fm.dequant_matvec, W, FAKE, FAKE + 1024, stream=0)
 
 
+def test_matvec_multi_validation():
+    # Q/K/V-like projections of one x: equal cols and bits, different rows
+    q, k = fm.qmat(FAKE, FAKE, 4096, 4096, 4), fm.qmat(FAKE, FAKE, 512, 4096, 4)
+    x = FAKE + (1 << 26)
+    ys = [FAKE + (2 << 26), FAKE + (3 << 26), FAKE + (4 << 26)]
+    mv = fm.dequant_matvec_multi
+    _raises(fm.ERR_SHAPE, mv, [], x, [], stream=0)
+    _raises(fm.ERR_SHAPE, mv, [k] * 9, x, [FAKE + (i + 2 << 26) for i in range(9)], stream=0)
+    _raises(fm.ERR_SHAPE, mv, [q, fm.qmat(FAKE, FAKE, 512, 2048, 4)], x, ys[:2], stream=0)  # cols differ
+    _raises(fm.ERR_SHAPE, mv, [q, fm.qmat(FAKE, FAKE, 512, 4096, 2)], x, ys[:2], stream=0)  # bits differ
+    _raises(fm.ERR_BITS, mv, [q, fm.qmat(FAKE, FAKE, 512, 4096, 3)], x, ys[:2], stream=0)
+    _raises(fm.ERR_NULL, mv, [q, k, k], None, ys, stream=0)
+    _raises(fm.ERR_NULL, mv, [q, k, k], x, [ys[0], None, ys[2]], stream=0)
+    _raises(fm.ERR_ALIGN, mv, [q, k, k], x, [ys[0], ys[1] + 4, ys[2]], stream=0)
+    _raises(fm.ERR_ALIGN, mv, [q, k, k], x + 4, ys, stream=0)
+    _raises(fm.ERR_SHAPE, mv, [q, k, k], x, ys, 0, stream=0)
+    _raises(fm.ERR_OVERLAP, mv, [q, k, k], x, [ys[0], ys[0] + 4096 * 4 - 16, ys[2]], stream=0)  # y0 and y1
+    _raises(fm.ERR_OVERLAP, mv, [q, k, k], x, [ys[0], ys[1], x + 1024], stream=0)  # y2 and x
+    with pytest.raises(ValueError):
+        mv([q, k], x, ys, stream=0)
+
+
 def test_route_validation():
     args = dict(router=FAKE, x=FAKE + (1 << 24), n_tokens=1, n_experts=512, hidden=4096, k=4,
                 idx=FAKE + (2 << 24), w=FAKE + (3 << 24), logits=FAKE + (4 << 24), stream=0)

@@ -166,6 +166,38 @@ def test_matvec_shapes(rows, cols, bits, n_vec):
         assert rel_l2(Y[v], want) <= TOL, v
 
 
+@pytest.mark.parametrize("rows_list,cols,bits,n_vec", [
+    ([4096, 512, 512], 4096, 4, 1),     # Q/K/V-like projections of one hidden vector
+    ([4096, 512, 512], 4096, 2, 2),
+    ([100, 37, 1], 2048, 2, 3),         # ragged row counts (partial row blocks)
+    ([64] * 8, 960, 4, 2),              # the maximum of 8 matrices
+    ([5, 300], 16384, 2, 1),
+    ([33], 320, 4, 64)])
+def test_matvec_multi(rows_list, cols, bits, n_vec):
+    """fmoe_dequant_matvec_multi against the oracle's matvec of each matrix, and bit for bit
+    against fmoe_dequant_matvec of each matrix alone (same per-row arithmetic)."""
+    rng = np.random.default_rng(sum(rows_list) + cols + bits + n_vec)
+    X = rng.standard_normal((n_vec, cols)).astype(np.float32)
+    xd = to_dev(X)
+    mats, outs, host = [], [], []
+    for m, rows in enumerate(rows_list):
+        codes, scale, bias = synth.matrix(13, m, rows, cols, rows, cols, bits)
+        mats.append(DevMatrix(codes, scale, bias, rows, cols, bits))
+        outs.append(torch.full((n_vec, rows), float("nan"), dtype=torch.float32, device="cuda"))
+        host.append((codes, scale, bias, rows))
+    fm.dequant_matvec_multi([d.q for d in mats], xd, outs, n_vec)
+    torch.cuda.synchronize()
+    for m, (codes, scale, bias, rows) in enumerate(host):
+        Y = outs[m].cpu().numpy()
+        single = torch.empty((n_vec, rows), dtype=torch.float32, device="cuda")
+        fm.dequant_matvec(mats[m].q, xd, single, n_vec)
+        torch.cuda.synchronize()
+        assert np.array_equal(Y, single.cpu().numpy()), m
+        for v in range(n_vec):
+            want = oracle.matvec(codes, scale, bias, rows, cols, bits, 64, X[v])
+            assert rel_l2(Y[v], want) <= TOL, (m, v)
+
+
 # ------------------------------------------------------------------ routing
 def _route_dev(R, X, k):
     n, H = X.shape
