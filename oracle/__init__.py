@@ -58,15 +58,15 @@ def lib():
         L.oracle_expert_ffn.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
         L.oracle_moe_layer.restype = i32
         L.oracle_moe_layer.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32, dbl,
-                                       vp, vp, vp, vp]
+                                       vp, vp, vp, vp, vp, vp]
         L.oracle_stack.restype = i32
         L.oracle_stack.argtypes = [vp, vp, vp, i32, vp, i32, i32, i32, i32, i32, i32, dbl, dbl,
-                                   vp, vp, vp, vp, vp]
+                                   vp, vp, vp, vp, vp, vp, vp]
         L.oracle_round_bf16.restype = dbl
         L.oracle_round_bf16.argtypes = [dbl]
         L.oracle_layer_bf16.restype = i32
         L.oracle_layer_bf16.argtypes = [vp, vp, i32, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32,
-                                        ctypes.c_double, vp, vp, vp, vp, vp, vp, vp, vp]
+                                        ctypes.c_double, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         _lib = L
     return _lib
 
@@ -190,8 +190,10 @@ class ArrayProvider:
         return 0
 
 
-def moe_layer(provider, layer, router, h, inter, k, bits, group, prenorm, eps):
-    """O5: (out fp64 [H], idx [k], w [k], margin)."""
+def moe_layer(provider, layer, router, h, inter, k, bits, group, prenorm, eps, shared_gate=None,
+              return_shared_w=False):
+    """O5: (out fp64 [H], idx [k], w [k], margin[, shared weight]). shared_gate (fp32 [H]):
+    the layer also runs its shared expert (provider index E) with weight sigmoid(gate . v)."""
     router = _c(router, np.float32)
     E, H = router.shape
     h = _c(h, np.float64)
@@ -199,15 +201,21 @@ def moe_layer(provider, layer, router, h, inter, k, bits, group, prenorm, eps):
     idx = np.empty(k, dtype=np.int32)
     w = np.empty(k, dtype=np.float64)
     m = ctypes.c_double()
+    sw = ctypes.c_double(np.nan)
+    gate = None if shared_gate is None else _c(shared_gate, np.float32)
     rc = lib().oracle_moe_layer(provider.fn, provider.ctx, layer, _p(router), _p(h), H, inter, E, k, bits, group,
-                                int(bool(prenorm)), eps, _p(out), _p(idx), _p(w), ctypes.addressof(m))
+                                int(bool(prenorm)), eps, _p(out), _p(idx), _p(w), ctypes.addressof(m), _p(gate),
+                                ctypes.addressof(sw))
     if rc != 0:
         raise RuntimeError("expert provider failed")
+    if return_shared_w:
+        return out, idx, w, m.value, sw.value
     return out, idx, w, m.value
 
 
-def stack(provider, routers, x, inter, k, bits, group, eps, stop_margin=0.0, keep_all=True):
-    """O6: dict(out, idx [L][k], w [L][k], margins [L], h_all [L][H] or None, layers_done)."""
+def stack(provider, routers, x, inter, k, bits, group, eps, stop_margin=0.0, keep_all=True, shared_gates=None):
+    """O6: dict(out, idx [L][k], w [L][k], margins [L], h_all [L][H] or None, layers_done,
+    shared_w [L] when shared_gates (one fp32 [H] gate per layer) is given)."""
     routers = [_c(r, np.float32) for r in routers]
     L = len(routers)
     E, H = routers[0].shape
@@ -218,17 +226,22 @@ def stack(provider, routers, x, inter, k, bits, group, eps, stop_margin=0.0, kee
     w = np.zeros((L, k), dtype=np.float64)
     margins = np.full(L, np.nan, dtype=np.float64)
     h_all = np.zeros((L, H), dtype=np.float64) if keep_all else None
+    gates = None if shared_gates is None else [_c(gv, np.float32) for gv in shared_gates]
+    gptrs = None if gates is None else (ctypes.c_void_p * L)(*[_p(gv) for gv in gates])
+    sws = None if gates is None else np.full(L, np.nan, dtype=np.float64)
     done = lib().oracle_stack(provider.fn, provider.ctx, ctypes.addressof(ptrs), L, _p(x), H, inter, E, k, bits,
-                              group, eps, stop_margin, _p(out), _p(idx), _p(w), _p(margins), _p(h_all))
+                              group, eps, stop_margin, _p(out), _p(idx), _p(w), _p(margins), _p(h_all),
+                              None if gptrs is None else ctypes.addressof(gptrs), _p(sws))
     if done < 0:
         raise RuntimeError("expert provider failed")
-    return dict(out=out, idx=idx, w=w, margins=margins, h_all=h_all, layers_done=done)
+    return dict(out=out, idx=idx, w=w, margins=margins, h_all=h_all, layers_done=done, shared_w=sws)
 
 
 def layer_bf16(provider, layer, router, X, inter, k, bits, group, a16_force=None, want_stages=False,
-               prenorm=False, eps=1e-6):
+               prenorm=False, eps=1e-6, shared_gate=None, shared_a16_force=None):
     """O7 (batched bf16 contract). Returns dict(out [T][H], idx [T][k], w [T][k], margins [T],
-    a16 [T][k][inter] fp32, g/u [T][k][inter] if want_stages)."""
+    a16 [T][k][inter] fp32, g/u [T][k][inter] if want_stages; with shared_gate also
+    shared_w [T] and shared_a16 [T][inter])."""
     router = _c(router, np.float32)
     E, H = router.shape
     X = _c(X, np.float32)
@@ -241,11 +254,18 @@ def layer_bf16(provider, layer, router, X, inter, k, bits, group, a16_force=None
     force = None if a16_force is None else _c(a16_force, np.float32)
     g = np.empty((T, k, inter), dtype=np.float64) if want_stages else None
     u = np.empty((T, k, inter), dtype=np.float64) if want_stages else None
+    gate = None if shared_gate is None else _c(shared_gate, np.float32)
+    sw = None if gate is None else np.empty(T, dtype=np.float64)
+    sa16 = None if gate is None else np.empty((T, inter), dtype=np.float32)
+    sforce = None if shared_a16_force is None else _c(shared_a16_force, np.float32)
     rc = lib().oracle_layer_bf16(provider.fn, provider.ctx, layer, _p(router), _p(X), T, H, inter, E, k, bits, group,
-                                 int(bool(prenorm)), float(eps), _p(out), _p(idx), _p(w), _p(margins), _p(force), _p(a16), _p(g), _p(u))
+                                 int(bool(prenorm)), float(eps), _p(out), _p(idx), _p(w), _p(margins), _p(force),
+                                 _p(a16), _p(g), _p(u), _p(gate), _p(sw), _p(sforce), _p(sa16))
     if rc != 0:
         raise RuntimeError("expert provider failed")
     res = dict(out=out, idx=idx, w=w, margins=margins, a16=a16)
+    if gate is not None:
+        res.update(shared_w=sw, shared_a16=sa16)
     if want_stages:
         res.update(g=g, u=u)
     return res

@@ -132,9 +132,19 @@ void oracle_expert_ffn(const uint8_t* const* codes, const uint16_t* const* scale
   free(a);
 }
 
+/* Weight of the shared expert: the logistic function of the gate vector's dot product with
+ * v (reading of [hada] "Model mimarisi", one shared expert per layer, and "Metal Compute
+ * Shaders", a gate in the combine; the gate's form is not on the pages). */
+static double shared_weight(const float* gate, const double* v, int hidden) {
+  double z = 0.0;
+  for (int i = 0; i < hidden; ++i) z += (double)gate[i] * v[i];
+  return 1.0 / (1.0 + exp(-z));
+}
+
 int oracle_moe_layer(oracle_provider_fn provide, void* ctx, int layer, const float* router,
                      const double* h, int hidden, int inter, int n_experts, int k, int bits, int group,
-                     int prenorm, double eps, double* out, int* idx, double* w, double* margin) {
+                     int prenorm, double eps, double* out, int* idx, double* w, double* margin,
+                     const float* shared_gate, double* shared_w) {
   double* v = (double*)malloc(sizeof(double) * (size_t)hidden);
   double* y = (double*)malloc(sizeof(double) * (size_t)hidden);
   double* acc = (double*)calloc((size_t)hidden, sizeof(double));
@@ -155,6 +165,20 @@ int oracle_moe_layer(oracle_provider_fn provide, void* ctx, int layer, const flo
     oracle_expert_ffn(codes, scale, bias, hidden, inter, bits, group, v, y, NULL);
     for (int i = 0; i < hidden; ++i) acc[i] += w[j] * y[i];
   }
+  if (rc == 0 && shared_gate) {
+    /* the shared expert (provider index n_experts) on every token, weighted by its gate */
+    const uint8_t* codes[3];
+    const uint16_t* scale[3];
+    const uint16_t* bias[3];
+    if (provide(ctx, layer, n_experts, codes, scale, bias) != 0) {
+      rc = -1;
+    } else {
+      const double sw = shared_weight(shared_gate, v, hidden);
+      if (shared_w) *shared_w = sw;
+      oracle_expert_ffn(codes, scale, bias, hidden, inter, bits, group, v, y, NULL);
+      for (int i = 0; i < hidden; ++i) acc[i] += sw * y[i];
+    }
+  }
   for (int i = 0; i < hidden; ++i) out[i] = h[i] + acc[i];
   free(v);
   free(y);
@@ -164,7 +188,8 @@ int oracle_moe_layer(oracle_provider_fn provide, void* ctx, int layer, const flo
 
 int oracle_stack(oracle_provider_fn provide, void* ctx, const float* const* routers, int n_layers,
                  const float* x, int hidden, int inter, int n_experts, int k, int bits, int group, double eps,
-                 double stop_margin, double* out, int* idx, double* w, double* margins, double* h_all) {
+                 double stop_margin, double* out, int* idx, double* w, double* margins, double* h_all,
+                 const float* const* shared_gates, double* shared_ws) {
   double* h = (double*)malloc(sizeof(double) * (size_t)hidden);
   double* hn = (double*)malloc(sizeof(double) * (size_t)hidden);
   for (int i = 0; i < hidden; ++i) h[i] = (double)x[i];
@@ -172,7 +197,8 @@ int oracle_stack(oracle_provider_fn provide, void* ctx, const float* const* rout
   for (int l = 0; l < n_layers; ++l) {
     double m;
     int rc = oracle_moe_layer(provide, ctx, l, routers[l], h, hidden, inter, n_experts, k, bits, group, 1, eps,
-                              hn, idx + (size_t)l * k, w + (size_t)l * k, &m);
+                              hn, idx + (size_t)l * k, w + (size_t)l * k, &m, shared_gates ? shared_gates[l] : NULL,
+                              shared_ws ? shared_ws + l : NULL);
     if (rc != 0) {
       free(h);
       free(hn);
@@ -213,11 +239,14 @@ static double row_dot_x16(const uint8_t* codes, const uint16_t* scale, const uin
 int oracle_layer_bf16(oracle_provider_fn provide, void* ctx, int layer, const float* router, const float* x,
                       int T, int hidden, int inter, int n_experts, int k, int bits, int group, int prenorm,
                       double eps, double* out, int* idx, double* w, double* margins, const float* a16_force,
-                      float* a16_out, double* g_out, double* u_out) {
+                      float* a16_out, double* g_out, double* u_out, const float* shared_gate, double* shared_w,
+                      const float* shared_a16_force, float* shared_a16_out) {
   double* xv = (double*)malloc(sizeof(double) * (size_t)hidden);
   double* vv = (double*)malloc(sizeof(double) * (size_t)hidden);
   double* x16 = (double*)malloc(sizeof(double) * (size_t)T * hidden);
   double* ys = (double*)malloc(sizeof(double) * (size_t)T * k * hidden);
+  double* sws = (double*)malloc(sizeof(double) * (size_t)T);
+  double* yshared = shared_gate ? (double*)malloc(sizeof(double) * (size_t)T * hidden) : NULL;
   int rc = 0;
   /* v = rmsnorm(x) or x; routing on v; the experts see v rounded to bf16 */
   for (int t = 0; t < T; ++t) {
@@ -228,6 +257,8 @@ int oracle_layer_bf16(oracle_provider_fn provide, void* ctx, int layer, const fl
     double m;
     oracle_route(router, vv, n_experts, hidden, k, idx + (size_t)t * k, w + (size_t)t * k, NULL, &m);
     if (margins) margins[t] = m;
+    sws[t] = shared_gate ? shared_weight(shared_gate, vv, hidden) : 0.0;
+    if (shared_w) shared_w[t] = sws[t];
   }
   /* every (token, slot) FFN; experts fetched once each (independent computations) */
   double* a16 = (double*)malloc(sizeof(double) * (size_t)inter);
@@ -262,16 +293,40 @@ int oracle_layer_bf16(oracle_provider_fn provide, void* ctx, int layer, const fl
         ys[(size_t)s * hidden + i] = row_dot_x16(codes[2], scale[2], bias[2], inter, bits, group, i, a16);
     }
   }
-  /* combine + residual per token, slots in rank order */
+  /* the shared expert on every token under the same contract */
+  if (rc == 0 && shared_gate) {
+    const uint8_t* codes[3];
+    const uint16_t* scale[3];
+    const uint16_t* bias[3];
+    if (provide(ctx, layer, n_experts, codes, scale, bias) != 0) rc = -1;
+    for (int t = 0; t < T && rc == 0; ++t) {
+      const double* xt = x16 + (size_t)t * hidden;
+#pragma omp parallel for schedule(static)
+      for (int j = 0; j < inter; ++j) {
+        double g = row_dot_x16(codes[0], scale[0], bias[0], hidden, bits, group, j, xt);
+        double u = row_dot_x16(codes[1], scale[1], bias[1], hidden, bits, group, j, xt);
+        double r16 = oracle_round_bf16(oracle_swiglu(g, u));
+        if (shared_a16_out) shared_a16_out[(size_t)t * inter + j] = (float)r16;
+        a16[j] = shared_a16_force ? (double)shared_a16_force[(size_t)t * inter + j] : r16;
+      }
+#pragma omp parallel for schedule(static)
+      for (int i = 0; i < hidden; ++i)
+        yshared[(size_t)t * hidden + i] = row_dot_x16(codes[2], scale[2], bias[2], inter, bits, group, i, a16);
+    }
+  }
+  /* combine + residual per token, slots in rank order, the shared expert last */
   if (rc == 0) {
     for (int t = 0; t < T; ++t) {
       for (int i = 0; i < hidden; ++i) {
         double acc = 0.0;
         for (int j = 0; j < k; ++j) acc += w[(size_t)t * k + j] * ys[((size_t)t * k + j) * hidden + i];
+        if (yshared) acc += sws[t] * yshared[(size_t)t * hidden + i];
         out[(size_t)t * hidden + i] = (double)x[(size_t)t * hidden + i] + acc;
       }
     }
   }
+  free(sws);
+  free(yshared);
   free(a16);
   free(xv);
   free(vv);

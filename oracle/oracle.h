@@ -73,10 +73,15 @@ void oracle_expert_ffn(const uint8_t* const* codes, const uint16_t* const* scale
 
 /* O5: one MoE layer for one token: v = prenorm ? rmsnorm(h) : h; route on v; out = h +
  * sum_k w_k FFN_{idx_k}(v) ([aibit] item 3 / [hada] "Deferred GPU Expert Compute": the
- * combine + residual (+ norm for the next layer) step). idx, w: [k]; margin nullable. */
+ * combine + residual (+ norm for the next layer) step). idx, w: [k]; margin nullable.
+ * shared_gate (nullable, fp32 [hidden]): the layer also has a shared expert (provider index
+ * n_experts) that every token runs, added with weight s = 1 / (1 + exp(-gate . v)) (reading
+ * of [hada] "Model mimarisi": one shared expert, and "Metal Compute Shaders": a gate in the
+ * combine); shared_w (nullable) receives s. O6 and O7 take the same per layer. */
 int oracle_moe_layer(oracle_provider_fn provide, void* ctx, int layer, const float* router,
                      const double* h, int hidden, int inter, int n_experts, int k, int bits, int group,
-                     int prenorm, double eps, double* out, int* idx, double* w, double* margin);
+                     int prenorm, double eps, double* out, int* idx, double* w, double* margin,
+                     const float* shared_gate, double* shared_w);
 
 /* O6: n_layers layers applied in order to x, pre-normed ([hada] "Model mimarisi": 60
  * layers). routers[l] is layer l's router. idx/w: [n_layers][k]; margins: [n_layers];
@@ -85,7 +90,8 @@ int oracle_moe_layer(oracle_provider_fn provide, void* ctx, int layer, const flo
  * whose margin is below it; otherwise returns n_layers. Negative on provider error. */
 int oracle_stack(oracle_provider_fn provide, void* ctx, const float* const* routers, int n_layers,
                  const float* x, int hidden, int inter, int n_experts, int k, int bits, int group, double eps,
-                 double stop_margin, double* out, int* idx, double* w, double* margins, double* h_all);
+                 double stop_margin, double* out, int* idx, double* w, double* margins, double* h_all,
+                 const float* const* shared_gates, double* shared_ws);
 
 /* Round-to-nearest-even fp64 -> fp32 -> bf16 value (as double). */
 double oracle_round_bf16(double v);
@@ -104,7 +110,8 @@ double oracle_round_bf16(double v);
 int oracle_layer_bf16(oracle_provider_fn provide, void* ctx, int layer, const float* router, const float* x,
                       int T, int hidden, int inter, int n_experts, int k, int bits, int group, int prenorm,
                       double eps, double* out, int* idx, double* w, double* margins, const float* a16_force,
-                      float* a16_out, double* g_out, double* u_out);
+                      float* a16_out, double* g_out, double* u_out, const float* shared_gate, double* shared_w,
+                      const float* shared_a16_force, float* shared_a16_out);
 
 #ifdef __cplusplus
 }

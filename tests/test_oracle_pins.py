@@ -421,3 +421,86 @@ def test_layer_bf16_contract():
         full, _, _, _ = oracle.moe_layer(prov, 0, routers[0], X[2].astype(np.float64), I, k, 4, 64,
                                          1 if prenorm else 0, 1e-6)
         assert np.linalg.norm(res["out"][2] - full) <= 1e-2 * np.linalg.norm(full)
+
+
+# ------------------------------------------------------------------ shared expert
+def _shared_setup(rng, E, H, I, L=1):
+    """Tiny model whose expert lists hold one more (shared) expert at index E."""
+    experts, routers = _tiny_model(rng, L, E, H, I, 4)
+    for l in range(L):
+        experts[l] = list(experts[l]) + [_expert(rng, H, I, 4)]
+    return experts, routers
+
+
+@pytest.mark.parametrize("prenorm", [0, 1])
+def test_shared_expert_gate_special_cases(prenorm):
+    """The shared expert enters as s * FFN_shared(v) with s the logistic function of gate . v:
+    a zero gate gives exactly one half, a gate with gate . v = +80 gives 1 to fp64
+    precision, gate . v = -80 gives e^-80 (no contribution at this precision); the routed
+    part is unchanged (compared with the layer without a shared expert)."""
+    rng = np.random.default_rng(31)
+    E, H, I, k = 8, 128, 64, 2
+    experts, routers = _shared_setup(rng, E, H, I)
+    prov = oracle.ArrayProvider(experts)
+    h = rng.standard_normal(H)
+    v = h / np.sqrt(np.mean(h * h) + 1e-6) if prenorm else h
+    plain, idx0, w0, _ = oracle.moe_layer(prov, 0, routers[0], h, I, k, 4, 64, prenorm, 1e-6)
+    ys, _ = oracle.expert_ffn(experts[0][E], H, I, 4, 64, v)
+    vf = v.astype(np.float32).astype(np.float64)
+    cases = [(np.zeros(H), 0.5, 0.0), (80.0 * vf / np.dot(vf, v), 1.0, 1e-15), (-80.0 * vf / np.dot(vf, v), 0.0, 1e-30)]
+    # a moderate gate: s = expit(z) for z = gate . v (gate . h under pre-norm would differ)
+    g7 = (0.7 * vf / np.dot(vf, v)).astype(np.float32)
+    cases.append((g7, float(scipy.special.expit(np.dot(g7.astype(np.float64), v))), 1e-14))
+    for gate, s_ref, tol in cases:
+        out, idx, w, _, sw = oracle.moe_layer(prov, 0, routers[0], h, I, k, 4, 64, prenorm, 1e-6,
+                                              shared_gate=gate.astype(np.float32), return_shared_w=True)
+        assert idx.tolist() == idx0.tolist() and np.array_equal(w, w0)
+        assert abs(sw - s_ref) <= tol, (sw, s_ref)
+        assert np.allclose(out - plain, s_ref * ys, rtol=1e-9, atol=1e-12)
+    assert abs(cases[-1][1] - 0.6681877721681662) < 1e-6  # expit(0.7)
+
+
+def test_shared_expert_stack_and_layers():
+    """O6 with a shared expert per layer equals O5 applied layer after layer (pre-norm), and
+    with every gate at zero each layer adds exactly half of its shared expert's FFN."""
+    rng = np.random.default_rng(32)
+    L, E, H, I, k = 3, 8, 128, 64, 2
+    experts, routers = _shared_setup(rng, E, H, I, L)
+    prov = oracle.ArrayProvider(experts)
+    gates = [(0.05 * rng.standard_normal(H)).astype(np.float32) for _ in range(L)]
+    x = rng.standard_normal(H).astype(np.float32)
+    res = oracle.stack(prov, routers, x, I, k, 4, 64, 1e-6, shared_gates=gates)
+    h = x.astype(np.float64)
+    for l in range(L):
+        h, idx, w, _, sw = oracle.moe_layer(prov, l, routers[l], h, I, k, 4, 64, 1, 1e-6, shared_gate=gates[l],
+                                            return_shared_w=True)
+        assert res["idx"][l].tolist() == idx.tolist()
+        assert res["shared_w"][l] == sw
+        assert np.allclose(res["h_all"][l], h, rtol=1e-13, atol=1e-13)
+    zero = [np.zeros(H, dtype=np.float32)] * L
+    rz = oracle.stack(prov, routers[:1], x, I, k, 4, 64, 1e-6, shared_gates=zero[:1])
+    rp = oracle.stack(prov, routers[:1], x, I, k, 4, 64, 1e-6)
+    xd = x.astype(np.float64)
+    v = xd / np.sqrt(np.mean(xd * xd) + 1e-6)
+    ys, _ = oracle.expert_ffn(experts[0][E], H, I, 4, 64, v)
+    assert np.allclose(rz["out"] - rp["out"], 0.5 * ys, rtol=1e-9, atol=1e-12)
+
+
+def test_shared_expert_bf16_contract():
+    """O7 with a shared expert: with k = 1 (routed weight 1), a zero gate and the shared
+    expert equal to token 0's routed expert, token 0's update is exactly 1.5 times the
+    update without the shared expert (both FFNs are the same bf16-contract computation)."""
+    rng = np.random.default_rng(33)
+    E, H, I, T = 8, 128, 64, 3
+    experts, routers = _tiny_model(rng, 1, E, H, I, 4)
+    X = rng.standard_normal((T, H)).astype(np.float32)
+    prov = oracle.ArrayProvider(experts)
+    plain = oracle.layer_bf16(prov, 0, routers[0], X, I, 1, 4, 64)
+    e0 = int(plain["idx"][0][0])
+    prov2 = oracle.ArrayProvider([list(experts[0]) + [experts[0][e0]]])
+    res = oracle.layer_bf16(prov2, 0, routers[0], X, I, 1, 4, 64, shared_gate=np.zeros(H, dtype=np.float32))
+    assert np.array_equal(res["idx"], plain["idx"]) and np.all(res["shared_w"] == 0.5)
+    d_plain = plain["out"][0] - X[0].astype(np.float64)
+    d_sh = res["out"][0] - X[0].astype(np.float64)
+    assert np.allclose(d_sh, 1.5 * d_plain, rtol=1e-12, atol=1e-12)
+    assert np.array_equal(res["shared_a16"][0], plain["a16"][0][0])
