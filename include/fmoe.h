@@ -103,6 +103,13 @@ typedef struct fmoe_layer {
   const void* experts;  /* n_experts expert blobs, blob e at experts + e * expert_stride */
   size_t expert_stride; /* bytes; >= fmoe_expert_bytes(), multiple of 256 */
   int n_experts, hidden, inter, bits, group;
+  /* NULL, or the layer's shared expert ([hada] "Model mimarisi": one shared expert per
+   * layer; "Metal Compute Shaders": a gate in the combine): an fp32 [hidden] gate vector
+   * (16-byte aligned), and the expert set then holds n_experts + 1 blobs, the last (index
+   * n_experts) being the shared expert, which every token runs with weight
+   * 1 / (1 + exp(-gate . v)). All layers of a call have one or none. Single-token calls
+   * only (n_tokens > 1 with a shared expert: FMOE_ERR_SHAPE); k + 1 <= 16. */
+  const float* shared_gate;
 } fmoe_layer;
 
 /* Human-readable text of a status code (static storage). */
@@ -192,6 +199,7 @@ int fmoe_expert_ffn(const fmoe_expert* e, const float* x, float* y, void* ws, si
  *   v   = (flags & FMOE_PRENORM) ? h / sqrt(mean(h^2) + eps) : h
  *   idx, w = route(router_l, v, k)                  (as fmoe_route_topk)
  *   h   = h + sum_j w_j * FFN_{idx_j}(v)            (as fmoe_expert_ffn)
+ *             [+ sigmoid(shared_gate . v) * FFN_shared(v) when the layers have one]
  * with h = x_in at the start; h_out receives the final h.
  * x_in, h_out: fp32 [n_tokens][hidden], must not overlap. idx_out (nullable): int32
  * [n_tokens][n_layers][k]; w_out (nullable): fp32 [n_tokens][n_layers][k].

@@ -44,7 +44,7 @@ class Expert(ctypes.Structure):
 class Layer(ctypes.Structure):
     _fields_ = [("router", ctypes.c_void_p), ("experts", ctypes.c_void_p), ("expert_stride", ctypes.c_size_t),
                 ("n_experts", ctypes.c_int), ("hidden", ctypes.c_int), ("inter", ctypes.c_int),
-                ("bits", ctypes.c_int), ("group", ctypes.c_int)]
+                ("bits", ctypes.c_int), ("group", ctypes.c_int), ("shared_gate", ctypes.c_void_p)]
 
 
 _lib = None

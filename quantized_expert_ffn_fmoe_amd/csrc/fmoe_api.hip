@@ -60,13 +60,13 @@ DecodeWs carve_decode(void* ws, int hidden, int inter, int n_experts, int k) {
   d.flags = reinterpret_cast<uint32_t*>(b + off);
   off += up256((size_t)kRep * kMaxGrid * 4);
   d.logits = reinterpret_cast<uint64_t*>(b + off);
-  off += up256((size_t)kRep * n_experts * 8);
+  off += up256((size_t)kRep * (n_experts + 1) * 8);  // + the shared expert's gate logit
   d.err = reinterpret_cast<uint32_t*>(b + off);
   off += 256;
   d.h = reinterpret_cast<uint64_t*>(b + off);
   off += up256((size_t)kRep * hidden * 8);
   d.a = reinterpret_cast<uint64_t*>(b + off);
-  off += up256((size_t)kRep * k * inter * 8);
+  off += up256((size_t)kRep * (k + 1) * inter * 8);  // + the shared expert's slot
   d.bytes = off;
   return d;
 }
@@ -241,6 +241,9 @@ int fmoe_moe_layer(const fmoe_layer* layers, int n_layers, const float* x_in, fl
   if (H < 64 || H % 64 || I < 64 || I % 64 || H > 8192 || I > 8192) return FMOE_ERR_SHAPE;
   if (E < 1 || E > 4096) return FMOE_ERR_SHAPE;
   if (k < 1 || k > 16 || k > E) return FMOE_ERR_K;
+  const int hs = L0.shared_gate != nullptr;  // the layers have a shared expert
+  if (hs && k + 1 > 16) return FMOE_ERR_K;
+  if (hs && n_tokens > 1) return FMOE_ERR_SHAPE;  // the multi-token path has no shared expert
   const size_t eb = fmoe_expert_bytes(H, I, bits, 64);
   for (int l = 0; l < n_layers; ++l) {
     const fmoe_layer& L = layers[l];
@@ -250,6 +253,8 @@ int fmoe_moe_layer(const fmoe_layer* layers, int n_layers, const float* x_in, fl
     if (L.group != 64) return FMOE_ERR_GROUP;
     if (L.expert_stride < eb || L.expert_stride != L0.expert_stride) return FMOE_ERR_SHAPE;
     if (L.expert_stride % 256 || !aligned(L.experts, 256) || !aligned(L.router, 16)) return FMOE_ERR_ALIGN;
+    if ((L.shared_gate != nullptr) != (hs != 0)) return FMOE_ERR_SHAPE;
+    if (hs && !aligned(L.shared_gate, 16)) return FMOE_ERR_ALIGN;
   }
   if (!(eps >= 0.f) || !(eps < 1e30f)) return FMOE_ERR_SHAPE;
   if (!ws) return FMOE_ERR_WORKSPACE;
@@ -283,7 +288,7 @@ int fmoe_moe_layer(const fmoe_layer* layers, int n_layers, const float* x_in, fl
   if ((rc = decode_grid(&G))) return rc;
   if (G > kMaxGrid) G = kMaxGrid;
   const int rows_per_wg = (H + G - 1) / G;
-  if (decode_smem_bytes(H, I, E, k, G, rows_per_wg, bits) > kDecodeMaxLds) return FMOE_ERR_SHAPE;
+  if (decode_smem_bytes(H, I, E + hs, k + hs, G, rows_per_wg, bits) > kDecodeMaxLds) return FMOE_ERR_SHAPE;
   DecodeWs d = carve_decode(ws, H, I, E, k);
   DecodeParams p;
   memset(&p, 0, sizeof(p));
@@ -291,13 +296,14 @@ int fmoe_moe_layer(const fmoe_layer* layers, int n_layers, const float* x_in, fl
   p.hidden = H;
   p.inter = I;
   p.k = k;
+  p.has_shared = hs;
   p.bits = bits;
   p.lpr_g = lpr_g;
   p.cpl_g = cpl_g;
   p.lpr_d = lpr_d;
   p.cpl_d = cpl_d;
   p.rows_per_wg = rows_per_wg;
-  p.router_items = ((E + G - 1) / G) * ((H + 1023) / 1024);
+  p.router_items = ((E + hs + G - 1) / G) * ((H + 1023) / 1024);
   p.eps = eps;
   p.flags = flags;
   p.x_in = x_in;
@@ -314,6 +320,7 @@ int fmoe_moe_layer(const fmoe_layer* layers, int n_layers, const float* x_in, fl
     const int nl = (n_layers - l0) < kMaxLayersPerLaunch ? (n_layers - l0) : kMaxLayersPerLaunch;
     for (int l = 0; l < nl; ++l) {
       p.router[l] = layers[l0 + l].router;
+      p.shared_gate[l] = layers[l0 + l].shared_gate;
       p.experts[l] = static_cast<const uint8_t*>(layers[l0 + l].experts);
     }
     p.layer0 = l0;

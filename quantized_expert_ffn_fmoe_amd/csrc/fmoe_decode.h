@@ -14,12 +14,14 @@ constexpr size_t kDecodeMaxLds = 160 * 1024;  // a gfx950 workgroup's LDS (beyon
 
 struct DecodeParams {
   const float* router[kMaxLayersPerLaunch];
+  const float* shared_gate[kMaxLayersPerLaunch];  // fp32 [hidden] gates when has_shared
   const uint8_t* experts[kMaxLayersPerLaunch];
   size_t expert_stride;
   int n_layers;   // layers in this launch
   int layer0;     // global index of the first of them
   int is_final;   // this launch ends with the last layer of the call
   int n_experts, hidden, inter, k, bits;
+  int has_shared;  // 1: every layer also runs its shared expert (blob index n_experts)
   int lpr_g, cpl_g, lpr_d, cpl_d;
   int rows_per_wg, router_items;
   float eps;
@@ -30,8 +32,8 @@ struct DecodeParams {
   float* w_out;
   // workspace
   uint64_t* h;         // [kRep][hidden], tagged (value | epoch << 32)
-  uint64_t* a;         // [kRep][k][inter], tagged
-  uint64_t* logits;    // [kRep][n_experts], tagged
+  uint64_t* a;         // [kRep][k + has_shared][inter], tagged
+  uint64_t* logits;    // [kRep][n_experts + has_shared], tagged
   uint32_t* flags_arr; // [kRep][kMaxGrid] epoch slots, zero-filled before the first call on a workspace
   uint32_t* err;       // [1]
 };

@@ -151,8 +151,12 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
   const int H = HC ? HC : p.hidden;
   const int I = IC ? IC : p.inter;
   const int E = EC ? EC : p.n_experts;
-  const int K = KC ? KC : p.k;
-  const int KI = K * I;
+  const int K = KC ? KC : p.k;  // routed experts per token
+  // slots: the k routed experts, then the shared expert (index E) when the layers have one;
+  // router rows: the E experts' rows, then the shared expert's gate (generic shapes only)
+  const int KS = KC ? KC : p.k + p.has_shared;
+  const int ER = EC ? EC : p.n_experts + p.has_shared;
+  const int KI = KS * I;
   const int vec_len = H > KI ? H : KI;
   const int max_chunks = vec_len / CC;
 
@@ -166,7 +170,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
   dig.n_chunks = H / CC;
   float* part = dig.xsum + max_chunks;  // [router items]
   float* ybuf = part + p.router_items;  // [k][rows per workgroup]
-  float* hraw = ybuf + K * p.rows_per_wg;  // [rows per workgroup] this workgroup's rows of h
+  float* hraw = ybuf + KS * p.rows_per_wg;  // [rows per workgroup] this workgroup's rows of h
   float* red = hraw + p.rows_per_wg;
   float* wsel = red + kDecodeWaves;
   float* lsel = wsel + 16;
@@ -187,6 +191,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
     // zero-filled workspace, else the last epoch of the previous launch). Layer l of this
     // launch tags its logits F + 3l + 1, its a F + 3l + 2 and its output h F + 3l + 3.
     *base = ld_dev_u32(p.flags_arr + (size_t)rep * kMaxGrid + blockIdx.x);
+    if (KS > K) isel[K] = E;  // the shared expert's slot never changes
   }
   __syncthreads();
   const uint32_t F = *base;
@@ -206,11 +211,11 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
   const int nr = max(0, min(H - r0, rows_wg));
   const int n_rb = (nr + rpwD - 1) / rpwD;  // down row blocks per slot
   // down items (j, rb) of this workgroup, a contiguous run per wave
-  const int d_items = K * n_rb;
+  const int d_items = KS * n_rb;
   const int d_per = (d_items + kDecodeWaves - 1) / kDecodeWaves;
   const int d_lo = wave * d_per, d_hi = min(d_items, d_lo + d_per);
   const int S = (H + 1023) / 1024;  // router slices per row
-  const int my_experts = (E - g + G - 1) / G;
+  const int my_experts = (ER - g + G - 1) / G;
   const int n_ritems = my_experts * S;
   // gate/up: a contiguous run of blocks (rpwG consecutive items each) per workgroup; the
   // last slot it touches is the top-k round the workgroup has to wait for
@@ -218,10 +223,12 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
   const int per_wg = (n_blocks + G - 1) / G;
   const int blk_lo = g * per_wg, blk_hi = min(n_blocks, blk_lo + per_wg);
   const int gu_last = min(blk_hi * rpwG, KI) - 1;
-  const int gu_need = blk_lo < blk_hi ? gu_last / I + 1 : 0;
+  // (a run inside the shared expert's slot needs no routing round: its expert is fixed)
+  const int gu_first = blk_lo * rpwG / I, gu_lslot = gu_last / I;
+  const int gu_need = blk_lo >= blk_hi ? 0 : gu_lslot < K ? gu_lslot + 1 : gu_first < K ? K : 0;
   const uint64_t* h_rep = p.h + (size_t)rep * H;
   const uint64_t* a_rep = p.a + (size_t)rep * KI;
-  const uint64_t* logits_rep = p.logits + (size_t)rep * E;
+  const uint64_t* logits_rep = p.logits + (size_t)rep * ER;
 
   // router slice `it` of layer `lr`: up to 4 float4 per lane. The loads are unconditional
   // (an index past the end is clamped to a valid row whose values go unused): a
@@ -232,9 +239,9 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
     const int lc = min(lr, p.n_layers - 1);
     const int itc = max(0, min(it, n_ritems - 1));
     const int el = itc / S, s = itc % S;
-    const int e = min(g + el * G, E - 1);
+    const int e = min(g + el * G, ER - 1);
     const int c0 = s * 256, c1 = min(H / 4, c0 + 256);
-    const float4* row = reinterpret_cast<const float4*>(p.router[lc] + (size_t)e * H);
+    const float4* row = reinterpret_cast<const float4*>(e < E ? p.router[lc] + (size_t)e * H : p.shared_gate[lc]);
 #pragma unroll
     for (int q = 0; q < 4; ++q) rv[u][q] = row[min(c0 + lane + 64 * q, c1 - 1)];
   };
@@ -350,7 +357,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
         const int el = t / kRep, rr = t % kRep;
         float lsum = 0.f;
         for (int s = 0; s < S; ++s) lsum += part[el * S + s];
-        st_dev_u64(p.logits + (size_t)rr * E + g + el * G, tag | __float_as_uint(lsum));
+        st_dev_u64(p.logits + (size_t)rr * ER + g + el * G, tag | __float_as_uint(lsum));
       }
       // poll only once the own logits are acknowledged: a first read issued right behind
       // the stores samples memory too early (its result waits for the stores anyway) and
@@ -359,11 +366,14 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
       unsigned spins = 0;
       bool failed = false;
       uint64_t kr[kKeysInRegs];  // E <= 64 * kKeysInRegs: keys stay in registers
+      float gate_logit = 0.f;
       if (E <= 64 * kKeysInRegs) {
         // one poll batch in flight; words that arrived are kept, only stale ones are read
         // again
         uint64_t t[kKeysInRegs];
         uint32_t got = 0, want = 0;
+        // the shared expert's gate logit (lane 0; others never wait for it)
+        uint64_t tg = (KS > K && lane == 0) ? ld_dev_u64(logits_rep + E) : tag;
 #pragma unroll
         for (int j = 0; j < kKeysInRegs; ++j) {
           const int e = lane + 64 * j;
@@ -384,7 +394,8 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
               }
             }
           }
-          if (__all(got == want)) break;
+          const bool gok = (tg & 0xffffffff00000000ull) == tag;
+          if (__all(got == want && gok)) break;
           if (spin_failed(++spins, p.err)) {
             failed = true;
             break;
@@ -393,7 +404,9 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
 #pragma unroll
           for (int j = 0; j < kKeysInRegs; ++j)
             if (((want & ~got) >> j) & 1u) t[j] = ld_dev_u64(logits_rep + lane + 64 * j);
+          if (!gok) tg = ld_dev_u64(logits_rep + E);
         }
+        if (KS > K && lane == 0) gate_logit = __uint_as_float((uint32_t)tg);
       } else {
         while (true) {
           bool ok = true;
@@ -401,6 +414,11 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
             const uint64_t t = ld_dev_u64(logits_rep + e);
             ok &= (t & 0xffffffff00000000ull) == tag;
             key[e] = rank_key(__uint_as_float((uint32_t)t), e);
+          }
+          if (KS > K && lane == 0) {
+            const uint64_t t = ld_dev_u64(logits_rep + E);
+            ok &= (t & 0xffffffff00000000ull) == tag;
+            gate_logit = __uint_as_float((uint32_t)t);
           }
           if (__all(ok)) break;
           if (spin_failed(++spins, p.err)) {
@@ -415,12 +433,15 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
           st_dev_u32(p.err, 1u);
           *fail = 1;
         }
-        if (lane < K) {
-          isel[lane] = 0;
+        if (lane < KS) {
+          isel[lane] = lane < K ? 0 : E;
           wsel[lane] = 0.f;
         }
         topk_progress(ready, K + 1);
       } else {
+        // the shared expert's weight: the logistic function of its gate logit (written
+        // before the top-k releases its last round)
+        if (KS > K && lane == 0) wsel[K] = 1.0f / (1.0f + expf(-gate_logit));
         if (E <= 64 * kKeysInRegs) wave_topk_regs<kKeysInRegs>(kr, K, isel, lsel, wsel, ready);
         else wave_topk_keys(key, E, K, isel, lsel, wsel, ready);
         if (g == 0 && lane < K) {
@@ -623,7 +644,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
       // the same per-wave scheme slot by slot. A slot shared by two waves is gathered and
       // digitised by both, which write identical values to the same LDS.
       if constexpr (kFastD) {
-        for (int j = d_lo / n_rb; d_lo < d_hi && j * n_rb < d_hi; ++j) {  // slots < K: items < K * n_rb
+        for (int j = d_lo / n_rb; d_lo < d_hi && j * n_rb < d_hi; ++j) {  // slots < KS: items < KS * n_rb
           const int t_lo = max(d_lo, j * n_rb), t_hi = min(d_hi, (j + 1) * n_rb);
           const uint64_t* a_j = a_rep + (size_t)j * I;
           wait_vmem();
@@ -734,7 +755,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
         if (rl < nr) {
           const int r = r0 + rl;
           float c = 0.f;
-          for (int j = 0; j < K; ++j) c = fmaf(wsel[j], ybuf[j * rows_wg + rl], c);
+          for (int j = 0; j < KS; ++j) c = fmaf(wsel[j], ybuf[j * rows_wg + rl], c);
           const float hn = hraw[rl] + c;
           const uint64_t hv = tagged(hn, htag);
 #pragma unroll
@@ -817,15 +838,17 @@ static int launch_decode_t(const DecodeParams& p, int G, size_t smem, hipStream_
 }
 
 int launch_decode(const DecodeParams& p, int G, hipStream_t s) {
-  const size_t smem = decode_smem_bytes(p.hidden, p.inter, p.n_experts, p.k, G, p.rows_per_wg, p.bits);
+  const size_t smem = decode_smem_bytes(p.hidden, p.inter, p.n_experts + p.has_shared, p.k + p.has_shared, G,
+                                        p.rows_per_wg, p.bits);
   int cg = p.cpl_g, cd = p.cpl_d;
   // the decode shapes of the 512-expert stack: hidden 4096, inter 1024, top-4 (and the
   // top-10 routing of the same layer)
-  if (p.hidden == 4096 && p.inter == 1024 && p.n_experts == 512 && p.k == 4) {
+  // (layers with a shared expert run the generic kernel)
+  if (p.hidden == 4096 && p.inter == 1024 && p.n_experts == 512 && p.k == 4 && !p.has_shared) {
     if (p.bits == 4) return launch_decode_t<4, 2, 1, 4096, 1024, 512, 4>(p, G, smem, s);
     return launch_decode_t<2, 1, 1, 4096, 1024, 512, 4>(p, G, smem, s);
   }
-  if (p.hidden == 4096 && p.inter == 1024 && p.n_experts == 512 && p.k == 10) {
+  if (p.hidden == 4096 && p.inter == 1024 && p.n_experts == 512 && p.k == 10 && !p.has_shared) {
     if (p.bits == 4) return launch_decode_t<4, 2, 1, 4096, 1024, 512, 10>(p, G, smem, s);
     return launch_decode_t<2, 1, 1, 4096, 1024, 512, 10>(p, G, smem, s);
   }

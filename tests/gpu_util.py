@@ -72,8 +72,12 @@ def fill_experts_gpu(blob: torch.Tensor, stride: int, layer: int, n_experts: int
 class DevStack:
     """A stack of MoE layers on the device: routers (fp32) and packed expert blobs."""
 
-    def __init__(self, n_layers, E, H, I, bits, seed=0, dev="cuda", gpu_fill=False):
+    def __init__(self, n_layers, E, H, I, bits, seed=0, dev="cuda", gpu_fill=False, shared=False):
+        """shared: every layer also has a shared expert (blob index E, generated like expert E)
+        and a gate vector N(0, 0.02) from its own generator stream (layer 1000 + l)."""
         self.L, self.E, self.H, self.I, self.bits, self.seed = n_layers, E, H, I, bits, seed
+        self.gates_np, self.gates = (None, None) if not shared else ([], [])
+        nb = E + (1 if shared else 0)
         eb = fm.expert_bytes(H, I, bits)
         self.stride = (eb + 255) // 256 * 256
         self.routers_np = []
@@ -81,17 +85,23 @@ class DevStack:
         self.blobs = []
         layers = []
         for l in range(n_layers):
-            blob = torch.empty(E * self.stride, dtype=torch.uint8, device=dev)
+            blob = torch.empty(nb * self.stride, dtype=torch.uint8, device=dev)
             if gpu_fill:
-                fill_experts_gpu(blob, self.stride, l, E, H, I, bits, seed)
+                fill_experts_gpu(blob, self.stride, l, nb, H, I, bits, seed)
             else:
-                fill_experts_cpu(blob, self.stride, l, E, H, I, bits, seed)
+                fill_experts_cpu(blob, self.stride, l, nb, H, I, bits, seed)
             R = synth.router(seed, l, E, H)
             self.routers_np.append(R)
             Rd = to_dev(R, dev)
             self.routers.append(Rd)
             self.blobs.append(blob)
-            layers.append(fm.Layer(Rd.data_ptr(), blob.data_ptr(), self.stride, E, H, I, bits, 64))
+            gate = 0
+            if shared:
+                gn = synth.router(seed, 1000 + l, 1, H)[0]
+                self.gates_np.append(gn)
+                self.gates.append(to_dev(gn, dev))
+                gate = self.gates[-1].data_ptr()
+            layers.append(fm.Layer(Rd.data_ptr(), blob.data_ptr(), self.stride, E, H, I, bits, 64, gate))
         self.layers = fm.layers_array(layers)
 
     def provider(self):

@@ -289,7 +289,8 @@ def _stack_tokens(stack, k, n, prenorm=True, start=0):
     while len(out) < n:
         x = synth.token(stack.seed, d, stack.H)
         if prenorm:
-            ref = oracle.stack(prov, stack.routers_np, x, stack.I, k, stack.bits, 64, 1e-6, stop_margin=1e-3)
+            ref = oracle.stack(prov, stack.routers_np, x, stack.I, k, stack.bits, 64, 1e-6, stop_margin=1e-3,
+                               shared_gates=stack.gates_np)
             ok = ref["layers_done"] == stack.L and np.min(ref["margins"]) >= 1e-3
         else:
             assert stack.L == 1
@@ -313,6 +314,66 @@ def test_decode_stack(L, E, H, I, k, bits):
         assert np.array_equal(idx, ref["idx"])
         assert rel_l2(w, ref["w"]) <= TOL
         assert rel_l2(h, ref["out"]) <= TOL
+
+
+@pytest.mark.parametrize("L,E,H,I,k,bits", [
+    (3, 64, 1024, 256, 4, 4), (3, 40, 512, 128, 2, 2), (2, 16, 256, 64, 1, 4), (2, 16, 512, 128, 15, 4),
+    (2, 600, 1024, 128, 4, 2)])
+def test_decode_shared_expert(L, E, H, I, k, bits):
+    """Layers with a shared expert (blob index E) added with weight sigmoid(gate . v): routing
+    of the whole stack bit-exact against the oracle stack with the same gates, and every
+    layer within the bar against the oracle layer applied to the kernel's own input to it
+    (runs of the first l layers). Across layers a token's fp32 error can be amplified by the
+    later layers' sensitivity (measured: 1e-6 after two 2-bit layers became 1.3e-5 after the
+    third, whose own error from an exact input is 2.3e-7), so the stack output is compared
+    layer by layer rather than against the fp64 trajectory. k = 15 is the most with a
+    shared slot."""
+    stack = DevStack(L, E, H, I, bits, shared=True)
+    prov = stack.provider()
+    wsb = fm.workspace_bytes(fm.OP_MOE_LAYER, 1, H, I, E, k)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    for x, ref in _stack_tokens(stack, k, 3):
+        h, idx, w = _decode(stack, x, k)
+        assert np.array_equal(idx, ref["idx"])
+        assert rel_l2(w, ref["w"]) <= TOL
+        # the shared expert contributes: its weight is strictly between 0 and 1
+        assert np.all((ref["shared_w"] > 0) & (ref["shared_w"] < 1))
+        h_in = x.astype(np.float32)
+        for l in range(L):
+            sub = fm.layers_array([stack.layers[j] for j in range(l + 1)])
+            hd = torch.empty(H, dtype=torch.float32, device="cuda")
+            fm.moe_layer(sub, to_dev(x.astype(np.float32)), hd, 1, k, 1e-6, fm.PRENORM, None, None, ws, wsb)
+            torch.cuda.synchronize()
+            h_l = hd.cpu().numpy()
+            want, i_l, _, _ = oracle.moe_layer(prov, l, stack.routers_np[l], h_in.astype(np.float64), I, k, bits,
+                                               64, 1, 1e-6, shared_gate=stack.gates_np[l])
+            assert i_l.tolist() == ref["idx"][l].tolist()
+            assert rel_l2(h_l, want) <= TOL, l
+            h_in = h_l
+        assert np.array_equal(h_in, h)  # the last run is the whole stack
+
+
+def test_decode_shared_expert_rejections():
+    """k + 1 > 16 with a shared expert, mixed layers (one with, one without a gate) and a
+    multi-token call with a shared expert are refused before any launch."""
+    stack = DevStack(2, 16, 256, 64, 4, shared=True)
+    xd = to_dev(synth.token(0, 0, 256)[None, :].astype(np.float32))
+    hd = torch.empty((1, 256), dtype=torch.float32, device="cuda")
+    wsb = fm.workspace_bytes(fm.OP_MOE_LAYER, 2, 256, 64, 16, 16)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    with pytest.raises(fm.FmoeError) as ei:
+        fm.moe_layer(stack.layers, xd, hd, 1, 16, 1e-6, fm.PRENORM, None, None, ws, wsb)
+    assert ei.value.status == fm.ERR_K
+    mixed = fm.layers_array([stack.layers[0], fm.Layer(stack.layers[1].router, stack.layers[1].experts,
+                                                       stack.stride, 16, 256, 64, 4, 64)])
+    with pytest.raises(fm.FmoeError) as ei:
+        fm.moe_layer(mixed, xd, hd, 1, 4, 1e-6, fm.PRENORM, None, None, ws, wsb)
+    assert ei.value.status == fm.ERR_SHAPE
+    x2 = to_dev(np.stack([synth.token(0, d, 256) for d in range(2)]).astype(np.float32))
+    h2 = torch.empty((2, 256), dtype=torch.float32, device="cuda")
+    with pytest.raises(fm.FmoeError) as ei:
+        fm.moe_layer(stack.layers, x2, h2, 2, 4, 1e-6, fm.PRENORM, None, None, ws, wsb)
+    assert ei.value.status == fm.ERR_SHAPE
 
 
 def test_decode_stack_full_size_top10():
