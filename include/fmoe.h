@@ -107,8 +107,8 @@ typedef struct fmoe_layer {
    * layer; "Metal Compute Shaders": a gate in the combine): an fp32 [hidden] gate vector
    * (16-byte aligned), and the expert set then holds n_experts + 1 blobs, the last (index
    * n_experts) being the shared expert, which every token runs with weight
-   * 1 / (1 + exp(-gate . v)). All layers of a call have one or none. Single-token calls
-   * only (n_tokens > 1 with a shared expert: FMOE_ERR_SHAPE); k + 1 <= 16. */
+   * 1 / (1 + exp(-gate . v)). All layers of a call have one or none; k + 1 <= 16 and
+   * n_experts + 1 <= 4096. */
   const float* shared_gate;
 } fmoe_layer;
 
@@ -226,9 +226,11 @@ int fmoe_moe_layer(const fmoe_layer* layers, int n_layers, const float* x_in, fl
 /*
  * Inspection of the batched path's SwiGLU stage (for verifying it stage by stage). After
  * an fmoe_moe_layer call with n_tokens > 1 that used workspace `ws` (same n_tokens,
- * hidden, inter, n_experts, k and bits), enqueue on `stream` a copy of the last layer's
- * bf16 SwiGLU outputs: a16_out[t][j][c] = bf16(silu(g) * u) for token t, slot j (the
- * j-th selected expert), row c, as bf16 bit patterns [n_tokens][k][inter] (device memory).
+ * hidden, inter, n_experts and bits; k = the call's slots per token: its k, or k + 1 when
+ * its layers have a shared expert), enqueue on `stream` a copy of the last layer's bf16
+ * SwiGLU outputs: a16_out[t][j][c] = bf16(silu(g) * u) for token t, slot j (the j-th
+ * selected expert; slot k of a call with a shared expert is the shared expert), row c, as
+ * bf16 bit patterns [n_tokens][slots][inter] (device memory).
  */
 int fmoe_batched_a16(const void* ws, size_t ws_bytes, int n_tokens, int hidden, int inter, int n_experts, int k,
                      int bits, uint16_t* a16_out, fmoe_stream_t stream);

@@ -66,7 +66,8 @@ DecodeWs carve_decode(void* ws, int hidden, int inter, int n_experts, int k) {
   d.h = reinterpret_cast<uint64_t*>(b + off);
   off += up256((size_t)kRep * hidden * 8);
   d.a = reinterpret_cast<uint64_t*>(b + off);
-  off += up256((size_t)kRep * (k + 1) * inter * 8);  // + the shared expert's slot
+  off += up256((size_t)kRep * 16 * inter * 8);  // the most slots (k routed + a shared one <= 16), so
+                                                 // that the regions after it do not depend on k
   d.bytes = off;
   return d;
 }
@@ -243,7 +244,7 @@ int fmoe_moe_layer(const fmoe_layer* layers, int n_layers, const float* x_in, fl
   if (k < 1 || k > 16 || k > E) return FMOE_ERR_K;
   const int hs = L0.shared_gate != nullptr;  // the layers have a shared expert
   if (hs && k + 1 > 16) return FMOE_ERR_K;
-  if (hs && n_tokens > 1) return FMOE_ERR_SHAPE;  // the multi-token path has no shared expert
+  if (hs && E + 1 > 4096) return FMOE_ERR_SHAPE;
   const size_t eb = fmoe_expert_bytes(H, I, bits, 64);
   for (int l = 0; l < n_layers; ++l) {
     const fmoe_layer& L = layers[l];
@@ -339,8 +340,9 @@ int fmoe_batched_a16(const void* ws, size_t ws_bytes, int n_tokens, int hidden, 
   if (hidden < 256 || hidden > 8192 || inter < 128 || inter > 8192 || !batched_shape_ok(hidden, inter))
     return FMOE_ERR_SHAPE;
   if (k < 1 || k > 16 || k > n_experts) return FMOE_ERR_K;
-  if (ws_bytes < fmoe_workspace_bytes(FMOE_OP_MOE_LAYER, n_tokens, hidden, inter, n_experts, k))
-    return FMOE_ERR_WORKSPACE;
+  // k: the slots of the inspected call (its k, or k + 1 with a shared expert)
+  const size_t dbytes = up256(carve_decode(nullptr, hidden, inter, n_experts, k).bytes);
+  if (ws_bytes < dbytes + batched_region_bytes(n_tokens, hidden, inter, n_experts, k)) return FMOE_ERR_WORKSPACE;
   if (!aligned(ws, 256) || !aligned(a16_out, 2)) return FMOE_ERR_ALIGN;
   if (overlaps(a16_out, (size_t)n_tokens * k * inter * 2, ws, ws_bytes)) return FMOE_ERR_OVERLAP;
   int rc = check_device();

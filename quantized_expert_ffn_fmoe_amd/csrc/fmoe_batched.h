@@ -11,6 +11,8 @@ namespace fmoe {
 
 bool batched_shape_ok(int hidden, int inter);
 size_t batched_workspace_bytes(int n_tokens, int hidden, int inter, int n_experts, int k);
+// bytes of the multi-token scratch as a call with k_slots slots per token lays it out
+size_t batched_region_bytes(int n_tokens, int hidden, int inter, int n_experts, int k_slots);
 int launch_batched_a16(const void* ws, int n_tokens, int hidden, int inter, int n_experts, int k, int bits,
                        uint16_t* out, hipStream_t s);
 int launch_batched(const fmoe_layer* layers, int n_layers, const float* x_in, float* h_out, int n_tokens, int k,

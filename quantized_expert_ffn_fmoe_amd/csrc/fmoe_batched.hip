@@ -312,11 +312,13 @@ __device__ void sort_pairs(const int32_t* __restrict__ idx, int P, int E, int32_
 // acknowledged the workgroup counts itself on a device-scope counter, and the workgroup
 // that finishes last reads all T * k selections back from the coherence point, sorts the
 // pairs by expert and resets the counter for the next call. (A device-scope fence instead
-// would write back this XCD's whole L2.)
+// would write back this XCD's whole L2.) With a shared expert (gate != null) every token has
+// ks = k + 1 slots: slot k is expert E with weight 1 / (1 + exp(-gate . v)).
 template <int BITS>
 __global__ void __launch_bounds__(kBT) route_stage_kernel(const float* __restrict__ h, int prenorm, float eps,
                                                           const float* __restrict__ part, int n_part, int T, int E,
-                                                          int H, int k, float* __restrict__ logits,
+                                                          int H, int k, const float* __restrict__ gate, int ks,
+                                                          float* __restrict__ logits,
                                                           int32_t* __restrict__ idx, float* __restrict__ w,
                                                           uint16_t* __restrict__ v16, float* __restrict__ xg,
                                                           int32_t* __restrict__ pairs, int32_t* __restrict__ act_e,
@@ -329,23 +331,38 @@ __global__ void __launch_bounds__(kBT) route_stage_kernel(const float* __restric
   __shared__ float lsel[16], wsel[16], red[kBT / 64];
   __shared__ int isel[16];
   __shared__ int is_last;
-  float inv = 1.f;
-  if (prenorm) {
-    float ss = 0.f;
+  __shared__ float gred[kBT / 64];
+  float inv = 1.f, gdot = 0.f;
+  if (prenorm || gate) {
+    float ss = 0.f, gd = 0.f;
     for (int i = threadIdx.x; i < H / 4; i += kBT) {
       const float4 q = reinterpret_cast<const float4*>(hr)[i];
       ss = fmaf(q.x, q.x, ss);
       ss = fmaf(q.y, q.y, ss);
       ss = fmaf(q.z, q.z, ss);
       ss = fmaf(q.w, q.w, ss);
+      if (gate) {
+        const float4 g4 = reinterpret_cast<const float4*>(gate)[i];
+        gd = fmaf(g4.x, q.x, gd);
+        gd = fmaf(g4.y, q.y, gd);
+        gd = fmaf(g4.z, q.z, gd);
+        gd = fmaf(g4.w, q.w, gd);
+      }
     }
     ss = wave_sum(ss);
-    if (lane == 0) red[threadIdx.x >> 6] = ss;
+    gd = wave_sum(gd);
+    if (lane == 0) {
+      red[threadIdx.x >> 6] = ss;
+      gred[threadIdx.x >> 6] = gd;
+    }
     __syncthreads();
     float tot = 0.f;
 #pragma unroll
-    for (int q = 0; q < kBT / 64; ++q) tot += red[q];
-    inv = 1.0f / sqrtf(tot / (float)H + eps);
+    for (int q = 0; q < kBT / 64; ++q) {
+      tot += red[q];
+      gdot += gred[q];
+    }
+    if (prenorm) inv = 1.0f / sqrtf(tot / (float)H + eps);
   }
   for (int e = threadIdx.x; e < E; e += kBT) {
     // all slices' loads first (clamped, unconditional), then the sum in slice order
@@ -374,8 +391,11 @@ __global__ void __launch_bounds__(kBT) route_stage_kernel(const float* __restric
   }
   __syncthreads();
   if (threadIdx.x < k) {
-    st_dev_u32(reinterpret_cast<uint32_t*>(idx) + (size_t)t * k + threadIdx.x, (uint32_t)isel[threadIdx.x]);
-    w[(size_t)t * k + threadIdx.x] = wsel[threadIdx.x];
+    st_dev_u32(reinterpret_cast<uint32_t*>(idx) + (size_t)t * ks + threadIdx.x, (uint32_t)isel[threadIdx.x]);
+    w[(size_t)t * ks + threadIdx.x] = wsel[threadIdx.x];
+  } else if (gate && (int)threadIdx.x == k) {  // the shared expert's slot (gate . v = inv * gate . h)
+    st_dev_u32(reinterpret_cast<uint32_t*>(idx) + (size_t)t * ks + k, (uint32_t)E);
+    w[(size_t)t * ks + k] = 1.0f / (1.0f + expf(-gdot * inv));
   }
   wait_vmem();  // idx acknowledged at the device coherence point (read by the last workgroup)
   __syncthreads();
@@ -383,7 +403,8 @@ __global__ void __launch_bounds__(kBT) route_stage_kernel(const float* __restric
   __syncthreads();
   if (!is_last) return;  // uniform over the workgroup
   int* cnt = reinterpret_cast<int*>(keys);
-  sort_pairs<kBT>(idx, T * k, E, pairs, act_e, act_off, act_cnt, n_act, cnt, cnt + E, sc);
+  const int EB = E + (gate ? 1 : 0);  // expert buckets of the sort
+  sort_pairs<kBT>(idx, T * ks, EB, pairs, act_e, act_off, act_cnt, n_act, cnt, cnt + EB, sc);
   if (threadIdx.x == 0) st_dev_u32(done, 0u);
 }
 
@@ -807,9 +828,10 @@ __global__ void __launch_bounds__(kBT, 2) down_kernel(BParams p) {
 // ---------------------------------------------------------------- 6. combine
 __global__ void __launch_bounds__(kBT) combine_kernel(const float* __restrict__ h, const float* __restrict__ ys,
                                                       const int32_t* __restrict__ idx, const float* __restrict__ w,
-                                                      int H, int k, float* __restrict__ h_next,
+                                                      int H, int k, int kr, float* __restrict__ h_next,
                                                       int32_t* __restrict__ idx_out, float* __restrict__ w_out,
                                                       int layer, int n_layers) {
+  // k slots per token (the kr routed ones, then the shared expert's if any)
   const int t = blockIdx.y;
   const int i4 = blockIdx.x * kBT + threadIdx.x;
   if (i4 < H / 4) {
@@ -825,8 +847,8 @@ __global__ void __launch_bounds__(kBT) combine_kernel(const float* __restrict__ 
     const float4 hv = reinterpret_cast<const float4*>(h + (size_t)t * H)[i4];
     reinterpret_cast<float4*>(h_next + (size_t)t * H)[i4] = make_float4(hv.x + s.x, hv.y + s.y, hv.z + s.z, hv.w + s.w);
   }
-  if (blockIdx.x == 0 && (int)threadIdx.x < k) {
-    const size_t o = ((size_t)t * n_layers + layer) * k + threadIdx.x;
+  if (blockIdx.x == 0 && (int)threadIdx.x < kr) {
+    const size_t o = ((size_t)t * n_layers + layer) * kr + threadIdx.x;
     if (idx_out) idx_out[o] = idx[t * k + threadIdx.x];
     if (w_out) w_out[o] = w[t * k + threadIdx.x];
   }
@@ -907,8 +929,9 @@ template <int BITS>
 int run_layers(const fmoe_layer* layers, int n_layers, const float* x_in, float* h_out, int T, int k, float eps,
                unsigned flags, int32_t* idx_out, float* w_out, const BatchedWs& ws, hipStream_t s) {
   const fmoe_layer& L0 = layers[0];
-  const int H = L0.hidden, I = L0.inter, E = L0.n_experts, P = T * k;
-  const int max_items = (int)max_units(P, E);
+  const int hs = L0.shared_gate != nullptr;
+  const int H = L0.hidden, I = L0.inter, E = L0.n_experts, ks = k + hs, P = T * ks;
+  const int max_items = (int)max_units(P, E + hs);
   const size_t sm_gu = expert_smem_bytes<BITS>(H / 64), sm_dn = expert_smem_bytes<BITS>(I / 64);
   // the stage buffers take the expert kernels past the default 64 KB of dynamic LDS
   if (hipFuncSetAttribute(reinterpret_cast<const void*>(&gate_up_kernel<BITS>),
@@ -925,7 +948,8 @@ int run_layers(const fmoe_layer* layers, int n_layers, const float* x_in, float*
                        ws.part);
     if (hipGetLastError() != hipSuccess) return FMOE_ERR_HIP;
     hipLaunchKernelGGL(route_stage_kernel<BITS>, dim3(T), dim3(kBT), 0, s, hin, (flags & FMOE_PRENORM) ? 1 : 0, eps,
-                       ws.part, n_part, T, E, H, k, ws.logits, ws.idx, ws.w, ws.v16, ws.xg, ws.pairs, ws.act_e,
+                       ws.part, n_part, T, E, H, k, L.shared_gate, ks, ws.logits, ws.idx, ws.w, ws.v16, ws.xg,
+                       ws.pairs, ws.act_e,
                        ws.act_off, ws.act_cnt, ws.n_act, ws.done);
     if (hipGetLastError() != hipSuccess) return FMOE_ERR_HIP;
     BParams bp;
@@ -933,7 +957,7 @@ int run_layers(const fmoe_layer* layers, int n_layers, const float* x_in, float*
     bp.stride = L.expert_stride;
     bp.H = H;
     bp.I = I;
-    bp.k = k;
+    bp.k = ks;
     bp.pairs = ws.pairs;
     bp.act_e = ws.act_e;
     bp.act_off = ws.act_off;
@@ -949,7 +973,7 @@ int run_layers(const fmoe_layer* layers, int n_layers, const float* x_in, float*
     hipLaunchKernelGGL(down_kernel<BITS>, dim3(H / kDnRowsWg, max_items), dim3(kBT), sm_dn, s, bp);
     if (hipGetLastError() != hipSuccess) return FMOE_ERR_HIP;
     hipLaunchKernelGGL(combine_kernel, dim3((H / 4 + kBT - 1) / kBT, T), dim3(kBT), 0, s, hin, ws.ys, ws.idx, ws.w,
-                       H, k, hnext, idx_out, w_out, l, n_layers);
+                       H, ks, k, hnext, idx_out, w_out, l, n_layers);
     if (hipGetLastError() != hipSuccess) return FMOE_ERR_HIP;
   }
   return FMOE_OK;
@@ -959,8 +983,14 @@ int run_layers(const fmoe_layer* layers, int n_layers, const float* x_in, float*
 
 bool batched_shape_ok(int hidden, int inter) { return hidden % kDnRowsWg == 0 && inter % kGuRowsWg == 0; }
 
+// The scratch is carved for n_experts + 1 sort buckets (a shared expert's) and the call's
+// slots; the size query covers k + 1 slots.
 size_t batched_workspace_bytes(int n_tokens, int hidden, int inter, int n_experts, int k) {
-  return carve(nullptr, n_tokens, hidden, inter, n_experts, k).bytes;
+  return carve(nullptr, n_tokens, hidden, inter, n_experts + 1, k + 1).bytes;
+}
+
+size_t batched_region_bytes(int n_tokens, int hidden, int inter, int n_experts, int k_slots) {
+  return carve(nullptr, n_tokens, hidden, inter, n_experts + 1, k_slots).bytes;
 }
 
 int launch_batched(const fmoe_layer* layers, int n_layers, const float* x_in, float* h_out, int n_tokens, int k,
@@ -968,7 +998,8 @@ int launch_batched(const fmoe_layer* layers, int n_layers, const float* x_in, fl
                    hipStream_t s) {
   const fmoe_layer& L0 = layers[0];
   if (!batched_shape_ok(L0.hidden, L0.inter)) return FMOE_ERR_SHAPE;
-  const BatchedWs w = carve(ws, n_tokens, L0.hidden, L0.inter, L0.n_experts, k);
+  const int ks = k + (L0.shared_gate != nullptr ? 1 : 0);
+  const BatchedWs w = carve(ws, n_tokens, L0.hidden, L0.inter, L0.n_experts + 1, ks);
   if (w.bytes > ws_bytes) return FMOE_ERR_WORKSPACE;
   if (L0.bits == 4) return run_layers<4>(layers, n_layers, x_in, h_out, n_tokens, k, eps, flags, idx_out, w_out, w, s);
   return run_layers<2>(layers, n_layers, x_in, h_out, n_tokens, k, eps, flags, idx_out, w_out, w, s);
@@ -976,7 +1007,7 @@ int launch_batched(const fmoe_layer* layers, int n_layers, const float* x_in, fl
 
 int launch_batched_a16(const void* ws, int n_tokens, int hidden, int inter, int n_experts, int k, int bits,
                        uint16_t* out, hipStream_t s) {
-  const BatchedWs w = carve(const_cast<void*>(ws), n_tokens, hidden, inter, n_experts, k);
+  const BatchedWs w = carve(const_cast<void*>(ws), n_tokens, hidden, inter, n_experts + 1, k);
   const int P = n_tokens * k;
   const size_t n = (size_t)P * inter;
   size_t blocks = (n + kBT - 1) / kBT;

@@ -227,3 +227,51 @@ def test_batched_full_size_planted():
     X, sets = planted_tokens(st.routers_np[0], 64, 4)
     r = check_layer(st, X, 4, prenorm=False, label="full size")
     print("full size:", r, "distinct experts", len(set(np.concatenate(sets).tolist())))
+
+
+@pytest.mark.parametrize("E,H,I,k,T,bits,prenorm", [
+    (64, 512, 256, 4, 37, 4, False),
+    (32, 512, 256, 2, 20, 2, True),
+    (16, 768, 384, 15, 9, 4, False),   # k + 1 = 16 slots
+])
+def test_batched_shared_expert(E, H, I, k, T, bits, prenorm):
+    """The multi-token path with a shared expert (blob index E, weight sigmoid(gate . v)):
+    routed indices bit-exact, every token's shared slot present in the a16 image (slot k)
+    within one bf16 step of the oracle's, the oracle's down stage fed the GPU's a16 (routed
+    and shared) within 1e-5, and end to end against O7 with the gate within 2^-8."""
+    st = DevStack(1, E, H, I, bits, shared=True)
+    X, _ = accepted_tokens(st.routers_np[0], T, k, prenorm=prenorm)
+    ks = k + 1
+    layers = fm.layers_array([st.layers[0]])
+    x = to_dev(X.astype(np.float32))
+    h = torch.empty_like(x)
+    idx = torch.full((T, 1, k), -1, dtype=torch.int32, device="cuda")
+    w = torch.zeros((T, 1, k), dtype=torch.float32, device="cuda")
+    wsb = fm.workspace_bytes(fm.OP_MOE_LAYER, T, H, I, E, k)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    fm.moe_layer(layers, x, h, T, k, EPS, fm.PRENORM if prenorm else 0, idx, w, ws, wsb)
+    a16 = torch.empty((T, ks, I), dtype=torch.int16, device="cuda")
+    fm.batched_a16(ws, wsb, T, H, I, E, ks, bits, a16)
+    torch.cuda.synchronize()
+    out = h.cpu().numpy().astype(np.float64)
+    a16_bits = a16.cpu().numpy().view(np.uint16)
+    prov = st.provider()
+    R, gate = st.routers_np[0], st.gates_np[0]
+    ref = oracle.layer_bf16(prov, 0, R, X, I, k, bits, 64, prenorm=prenorm, eps=EPS, shared_gate=gate)
+    assert np.array_equal(idx.cpu().numpy()[:, 0, :], ref["idx"])
+    assert np.allclose(w.cpu().numpy()[:, 0, :], ref["w"], rtol=1e-5, atol=1e-7)
+    assert np.all((ref["shared_w"] > 0) & (ref["shared_w"] < 1))
+    a_ref = np.concatenate([ref["a16"], ref["shared_a16"][:, None, :]], axis=1).astype(np.float64)
+    ref_bits = synth.bf16_bits(a_ref.astype(np.float32))
+    ulp = np.abs(_ordered(a16_bits) - _ordered(ref_bits))
+    a16_gpu = synth.bf16_to_f32(a16_bits).astype(np.float64)
+    rms = np.sqrt(np.mean(a_ref * a_ref, axis=-1, keepdims=True))
+    bad = (ulp > 1) & (np.abs(a16_gpu - a_ref) > 1e-5 * rms)
+    assert not bad.any(), f"{int(bad.sum())} a16 values off (max {ulp.max()} steps)"
+    assert float(np.mean(ulp[:, k, :] == 0)) >= 0.99  # the shared slot itself
+    forced = oracle.layer_bf16(prov, 0, R, X, I, k, bits, 64, a16_force=a16_gpu[:, :k, :], prenorm=prenorm, eps=EPS,
+                               shared_gate=gate, shared_a16_force=a16_gpu[:, k, :])
+    tf = max(rel_l2(out[t], forced["out"][t]) for t in range(T))
+    assert tf <= 1e-5, f"teacher-forced rel L2 {tf:.3e}"
+    e2e = max(rel_l2(out[t], ref["out"][t]) for t in range(T))
+    assert e2e <= 2.0 ** -8, f"end-to-end rel L2 {e2e:.3e}"
