@@ -42,9 +42,13 @@ def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
+SHARED = False  # --shared: every layer also has a shared expert and its gate
+
+
 def algorithmic_bytes_per_layer(bits: int) -> int:
     import quantized_expert_ffn_fmoe_amd as fm
-    return E_ * H_ * 4 + K_ * fm.expert_bytes(H_, I_, bits)
+    shared = (fm.expert_bytes(H_, I_, bits) + H_ * 4) if SHARED else 0  # the shared expert + its gate row
+    return E_ * H_ * 4 + K_ * fm.expert_bytes(H_, I_, bits) + shared
 
 
 def decode_source_hash() -> str:
@@ -64,19 +68,25 @@ def build_stack(bits: int, dev):
     eb = fm.expert_bytes(H_, I_, bits)
     stride = (eb + 255) // 256 * 256
     blobs, routers, layers = [], [], []
+    nb = E_ + (1 if SHARED else 0)  # a shared expert is blob index E_
     t0 = time.time()
     for l in range(L_):
-        blob = torch.empty(E_ * stride, dtype=torch.uint8, device=dev)
-        fill_experts_gpu(blob, stride, l, E_, H_, I_, bits, seed=0)
+        blob = torch.empty(nb * stride, dtype=torch.uint8, device=dev)
+        fill_experts_gpu(blob, stride, l, nb, H_, I_, bits, seed=0)
         R = to_dev(synth.router(0, l, E_, H_), dev)
         blobs.append(blob)
         routers.append(R)
-        layers.append(fm.Layer(R.data_ptr(), blob.data_ptr(), stride, E_, H_, I_, bits, 64))
+        gate = 0
+        if SHARED:  # gate N(0, 0.02) from its own generator stream
+            g = to_dev(synth.router(0, 1000 + l, 1, H_)[0], dev)
+            routers.append(g)
+            gate = g.data_ptr()
+        layers.append(fm.Layer(R.data_ptr(), blob.data_ptr(), stride, E_, H_, I_, bits, 64, gate))
         if l % 10 == 9:
             torch.cuda.synchronize()
             log(f"filled layer {l + 1}/{L_} ({time.time() - t0:.0f}s, {(l + 1) * E_ * stride / 1e9:.1f} GB)")
     torch.cuda.synchronize()
-    return blobs, routers, fm.layers_array(layers), E_ * stride * L_
+    return blobs, routers, fm.layers_array(layers), nb * stride * L_
 
 
 def cpu_baseline(bits: int, n_tokens: int = 10):
@@ -391,6 +401,8 @@ def main() -> int:
     ap.add_argument("--tokens", type=int, default=256)
     ap.add_argument("--top-k", type=int, default=4,
                     help="experts per token for the stack configs (the headline workload is top-4)")
+    ap.add_argument("--shared", action="store_true",
+                    help="stack configs: every layer also runs a shared expert with a logistic gate")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-parity", action="store_true")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -428,6 +440,8 @@ def main() -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"building {L_}-layer {bits}-bit stack on {torch.cuda.get_device_name(dev)}")
+    global SHARED
+    SHARED = bool(args.shared)
     blobs, routers, layers, resident = build_stack(bits, dev)
     T = args.tokens
     X = torch.from_numpy(np.stack([synth.token(0, d, H_) for d in range(T)])).to(dev)
@@ -469,14 +483,15 @@ def main() -> int:
     reuse = float(np.mean([len(set(ids[t, l]) & set(ids[t - 1, l])) / K_ for t in range(1, T) for l in range(L_)]))
     reuse_l0 = float(np.mean([len(set(ids[t, 0]) & set(ids[t - 1, 0])) / K_ for t in range(1, T)]))
     log(f"{tok_s:.1f} tok/s, kernel avg {avg_kernel_s * 1e6:.1f} us, {achieved:.0f} GB/s")
-    parity = None if (args.no_parity or K_ != 4) else parity_check(layers, bits, dev, ws, wsb)  # golden is top-4
+    # the stored golden results are top-4 without a shared expert
+    parity = None if (args.no_parity or K_ != 4 or SHARED) else parity_check(layers, bits, dev, ws, wsb)
     if parity is not None:
         log(f"parity: {parity}")
     cpu = None
     if not args.no_cpu_baseline:
         log("timing the CPU oracle on a sample")
         cpu = cpu_baseline(bits)
-    kernel_tag = f"decode_stack{bits}" + ("" if K_ == 4 else f"_top{K_}")
+    kernel_tag = f"decode_stack{bits}" + ("" if K_ == 4 else f"_top{K_}") + ("_shared" if SHARED else "")
     traffic = traffic_from_profiles(kernel_tag)
     out = {
         "metric": (METRIC if bits == 4 else METRIC.replace("4-bit", "2-bit")).replace(
@@ -493,7 +508,9 @@ def main() -> int:
         "dtype": "f32",
         "data": "synthetic",
         "config": {"workload": f"{L_}-layer x {E_}-expert {bits}-bit MoE expert-block decode stack"
-                               + ("" if K_ == 4 else f" (top-{K_})") + f", {T} consecutive single tokens per step",
+                               + ("" if K_ == 4 else f" (top-{K_})")
+                               + (" with a gated shared expert per layer" if SHARED else "")
+                               + f", {T} consecutive single tokens per step",
                    "layers": L_, "experts": E_, "hidden": H_, "inter": I_, "top_k": K_, "bits": bits, "group": 64,
                    "tokens_per_step": T, "resident_expert_bytes": int(resident)},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": PEAK_GBS, "unit": "GB/s",

@@ -131,7 +131,7 @@ __device__ __forceinline__ void wait_ready(const int* ready, int r) {
     __builtin_amdgcn_s_sleep(0);
 }
 
-template <int BITS, int CPL_G, int CPL_D, int HC, int IC, int EC, int KC>
+template <int BITS, int CPL_G, int CPL_D, int HC, int IC, int EC, int KC, int SH>
 __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) {
   constexpr int kBatchGU = batch_gu<CPL_G>();
   constexpr int kBatchD = batch_d<CPL_D>();
@@ -153,9 +153,10 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
   const int E = EC ? EC : p.n_experts;
   const int K = KC ? KC : p.k;  // routed experts per token
   // slots: the k routed experts, then the shared expert (index E) when the layers have one;
-  // router rows: the E experts' rows, then the shared expert's gate (generic shapes only)
-  const int KS = KC ? KC : p.k + p.has_shared;
-  const int ER = EC ? EC : p.n_experts + p.has_shared;
+  // router rows: the E experts' rows, then the shared expert's gate (SH: compiled shapes
+  // with a shared expert)
+  const int KS = KC ? KC + SH : p.k + p.has_shared;
+  const int ER = EC ? EC + SH : p.n_experts + p.has_shared;
   const int KI = KS * I;
   const int vec_len = H > KI ? H : KI;
   const int max_chunks = vec_len / CC;
@@ -816,9 +817,9 @@ int decode_grid(int* G_out) {
   return FMOE_OK;
 }
 
-template <int BITS, int CG, int CD, int HC, int IC, int EC, int KC>
+template <int BITS, int CG, int CD, int HC, int IC, int EC, int KC, int SH = 0>
 static int launch_decode_t(const DecodeParams& p, int G, size_t smem, hipStream_t s) {
-  auto fn = decode_kernel<BITS, CG, CD, HC, IC, EC, KC>;
+  auto fn = decode_kernel<BITS, CG, CD, HC, IC, EC, KC, SH>;
   // Co-residency: G is the CU count and at least one workgroup fits per CU, so the whole
   // grid is resident once the device has room for it. A plain launch is enough for that;
   // every wait inside the kernel is bounded, so a grid that cannot be made resident (other
@@ -843,7 +844,12 @@ int launch_decode(const DecodeParams& p, int G, hipStream_t s) {
   int cg = p.cpl_g, cd = p.cpl_d;
   // the decode shapes of the 512-expert stack: hidden 4096, inter 1024, top-4 (and the
   // top-10 routing of the same layer)
-  // (layers with a shared expert run the generic kernel)
+  // (and the top-4 routing with a gated shared expert; other shapes with a shared expert run
+  // the generic kernel)
+  if (p.hidden == 4096 && p.inter == 1024 && p.n_experts == 512 && p.k == 4 && p.has_shared) {
+    if (p.bits == 4) return launch_decode_t<4, 2, 1, 4096, 1024, 512, 4, 1>(p, G, smem, s);
+    return launch_decode_t<2, 1, 1, 4096, 1024, 512, 4, 1>(p, G, smem, s);
+  }
   if (p.hidden == 4096 && p.inter == 1024 && p.n_experts == 512 && p.k == 4 && !p.has_shared) {
     if (p.bits == 4) return launch_decode_t<4, 2, 1, 4096, 1024, 512, 4>(p, G, smem, s);
     return launch_decode_t<2, 1, 1, 4096, 1024, 512, 4>(p, G, smem, s);

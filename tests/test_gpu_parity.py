@@ -328,11 +328,21 @@ def test_decode_shared_expert(L, E, H, I, k, bits):
     third, whose own error from an exact input is 2.3e-7), so the stack output is compared
     layer by layer rather than against the fp64 trajectory. k = 15 is the most with a
     shared slot."""
-    stack = DevStack(L, E, H, I, bits, shared=True)
+    _check_shared_stack(DevStack(L, E, H, I, bits, shared=True), k, 3)
+
+
+def test_decode_shared_expert_full_size():
+    """The compiled decode shape with a shared expert: two pre-normed layers of 512 experts
+    plus the shared one, hidden 4096, inter 1024, top-4, 4-bit."""
+    _check_shared_stack(DevStack(2, 512, 4096, 1024, 4, gpu_fill=True, shared=True), 4, 2)
+
+
+def _check_shared_stack(stack, k, n_tokens):
+    L, E, H, I, bits = stack.L, stack.E, stack.H, stack.I, stack.bits
     prov = stack.provider()
     wsb = fm.workspace_bytes(fm.OP_MOE_LAYER, 1, H, I, E, k)
     ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
-    for x, ref in _stack_tokens(stack, k, 3):
+    for x, ref in _stack_tokens(stack, k, n_tokens):
         h, idx, w = _decode(stack, x, k)
         assert np.array_equal(idx, ref["idx"])
         assert rel_l2(w, ref["w"]) <= TOL
