@@ -505,6 +505,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
           dc_loaded = true;
         }
         if constexpr (kFastGU) {
+          static_assert(kRep == 8, "the 8 lane groups below store the 8 replicas of a");
           // one row per item (64 lanes per row): the 4 gate and 4 up sums of the batch are
           // reduced together; afterwards an even lane 8r + 2b1 + 4b2 holds the gate sum of
           // item 2b1 + b2 and its odd neighbour the up sum, and stores a to replica r.
