@@ -229,3 +229,21 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(fm, "_lib", None)
     with pytest.raises(RuntimeError, match="no non-HIP fallback"):
         fm.lib()
+
+
+def test_bench_refuses_several_gpus():
+    """bench.py runs on one GPU only: --gpus N > 1 (or a WORLD_SIZE > 1 launch) exits with
+    status 2 and a one-line JSON message, before touching a device."""
+    import json
+    import subprocess
+    import sys
+
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py"), "--gpus", "2"], capture_output=True,
+                       text=True, timeout=120)
+    assert r.returncode == 2
+    msg = json.loads(r.stdout.strip().splitlines()[-1])
+    assert msg["n_gpus"] == 2 and "one GPU" in msg["error"]
+    env = dict(os.environ, WORLD_SIZE="2")
+    r = subprocess.run([sys.executable, os.path.join(ROOT, "bench.py")], capture_output=True, text=True,
+                       timeout=120, env=env)
+    assert r.returncode == 2 and "WORLD_SIZE" in json.loads(r.stdout.strip().splitlines()[-1])["error"]
