@@ -139,9 +139,22 @@ int fmoe_pack(const uint8_t* codes_canon, const uint16_t* scale, const uint16_t*
  * pass the largest n_tokens, hidden, inter, n_experts and k that the calls will use.
  * A FMOE_OP_MOE_LAYER workspace must be zero-filled before its first use; each call
  * leaves it ready for the next one (it holds the synchronization state of the decode
- * kernel). After a call whose device-side wait gave up (outputs set to NaN), zero it
- * again. */
+ * kernel), whatever the shapes of the calls: its control words and the decode kernel's
+ * exchange region sit at fixed offsets (about 8.9 MB, the size for n_tokens == 1), the
+ * multi-token scratch after them. After a call whose device-side wait gave up (see
+ * fmoe_workspace_error), zero it again. Epochs are 32-bit: a workspace used by calls of
+ * several shapes is best zeroed again after 2^32 / 3 layer passes (24 M tokens of 60
+ * layers). */
 size_t fmoe_workspace_bytes(int op, int n_tokens, int hidden, int inter, int n_experts, int k);
+
+/* Enqueue on `stream` a copy of the workspace's error word into err_out (a device
+ * uint32): 0 when every device-side wait of the decode path on this workspace completed,
+ * non-zero once one gave up (its call wrote NaN to the rows of h_out it could not finish,
+ * and later calls on the workspace give up too until it is zero-filled again). A wait
+ * gives up when the persistent decode kernel's workgroups could not all run at once
+ * (for example when other work held compute units for seconds). ws, ws_bytes: as
+ * passed to fmoe_moe_layer (ws_bytes >= the single-token workspace size). */
+int fmoe_workspace_error(const void* ws, size_t ws_bytes, uint32_t* err_out, fmoe_stream_t stream);
 
 /*
  * y[v][r] = sum_c (q[r][c] * s[r][c/64] + b[r][c/64]) * x[v][c]  for v < n_vec.

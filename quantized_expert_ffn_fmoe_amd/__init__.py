@@ -23,7 +23,8 @@ OP_EXPERT_FFN, OP_MOE_LAYER = 1, 2
 
 EXPORTS = ("fmoe_status_string", "fmoe_version", "fmoe_codes_bytes", "fmoe_sb_bytes", "fmoe_expert_bytes",
            "fmoe_expert_view", "fmoe_pack", "fmoe_workspace_bytes", "fmoe_dequant_matvec",
-           "fmoe_dequant_matvec_multi", "fmoe_route_topk", "fmoe_expert_ffn", "fmoe_moe_layer", "fmoe_batched_a16")
+           "fmoe_dequant_matvec_multi", "fmoe_route_topk", "fmoe_expert_ffn", "fmoe_moe_layer", "fmoe_batched_a16",
+           "fmoe_workspace_error")
 
 
 class FmoeError(RuntimeError):
@@ -86,6 +87,8 @@ def lib():
         L.fmoe_moe_layer.restype = i32
         L.fmoe_moe_layer.argtypes = [ctypes.POINTER(Layer), i32, vp, vp, i32, i32, ctypes.c_float, u32, vp, vp, vp,
                                      sz, vp]
+        L.fmoe_workspace_error.restype = i32
+        L.fmoe_workspace_error.argtypes = [vp, sz, vp, vp]
         L.fmoe_batched_a16.restype = i32
         L.fmoe_batched_a16.argtypes = [vp, sz, i32, i32, i32, i32, i32, i32, vp, vp]
         _lib = L
@@ -197,3 +200,9 @@ def batched_a16(ws, ws_bytes, n_tokens, hidden, inter, n_experts, k, bits, a16_o
     """bf16 SwiGLU outputs [n_tokens][k][inter] of the last batched fmoe_moe_layer call on ws."""
     _check(lib().fmoe_batched_a16(_ptr(ws), ws_bytes, n_tokens, hidden, inter, n_experts, k, bits, _ptr(a16_out),
                                   _stream(stream)), "fmoe_batched_a16")
+
+
+def workspace_error(ws, ws_bytes, err_out, stream=None) -> None:
+    """Copy the workspace's error word (non-zero once a device-side wait gave up) into the
+    device uint32 err_out."""
+    _check(lib().fmoe_workspace_error(_ptr(ws), ws_bytes, _ptr(err_out), _stream(stream)), "fmoe_workspace_error")

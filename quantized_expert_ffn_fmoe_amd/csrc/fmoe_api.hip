@@ -42,33 +42,45 @@ int check_qmat(const fmoe_qmat* W) {
   return FMOE_OK;
 }
 
+size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
+
+// Layout of an FMOE_OP_MOE_LAYER workspace. Every offset is a constant, independent of the
+// shape of a call, so one workspace serves calls of any shape in any order:
+//   [kWsFlags, +32 KB)  the decode kernel's epoch slots [kRep][kMaxGrid] (uint32)
+//   kWsErr              the error word (non-zero after a device-side wait gave up)
+//   kWsDone             the multi-token sort's arrival counter (0 between calls)
+//   [kWsLogits, kWsDecodeEnd)  the decode kernel's tagged exchange words, sized for the
+//                       largest accepted shape (4096 + 1 router rows, hidden 8192, 16 slots
+//                       of inter 8192), so they never overlap anything else
+//   [kWsDecodeEnd, ...) the multi-token path's scratch (n_tokens > 1 only)
+// The tagged words hold only values written by the decode kernel with epochs below the
+// current one, whatever shapes earlier calls had.
+constexpr size_t kWsFlags = 0;
+constexpr size_t kWsErr = (size_t)kRep * kMaxGrid * 4;
+constexpr size_t kWsDone = kWsErr + 256;
+constexpr size_t kWsCtrlEnd = 65536;
+constexpr size_t kWsLogits = kWsCtrlEnd;
+constexpr size_t kWsH = kWsLogits + ((size_t)kRep * (4096 + 1) * 8 + 255) / 256 * 256;
+constexpr size_t kWsA = kWsH + (size_t)kRep * 8192 * 8;
+constexpr size_t kWsDecodeEnd = kWsA + (size_t)kRep * 16 * 8192 * 8;
+static_assert(kWsDone + 4 <= kWsCtrlEnd, "control block");
+
 struct DecodeWs {
   uint32_t* flags;
   uint64_t* logits;
   uint64_t* h;
   uint64_t* a;
   uint32_t* err;
-  size_t bytes;
 };
 
-size_t up256(size_t n) { return (n + 255) & ~(size_t)255; }
-
-DecodeWs carve_decode(void* ws, int hidden, int inter, int n_experts, int k) {
-  DecodeWs d;
+DecodeWs carve_decode(void* ws) {
   char* b = static_cast<char*>(ws);
-  size_t off = 0;
-  d.flags = reinterpret_cast<uint32_t*>(b + off);
-  off += up256((size_t)kRep * kMaxGrid * 4);
-  d.logits = reinterpret_cast<uint64_t*>(b + off);
-  off += up256((size_t)kRep * (n_experts + 1) * 8);  // + the shared expert's gate logit
-  d.err = reinterpret_cast<uint32_t*>(b + off);
-  off += 256;
-  d.h = reinterpret_cast<uint64_t*>(b + off);
-  off += up256((size_t)kRep * hidden * 8);
-  d.a = reinterpret_cast<uint64_t*>(b + off);
-  off += up256((size_t)kRep * 16 * inter * 8);  // the most slots (k routed + a shared one <= 16), so
-                                                 // that the regions after it do not depend on k
-  d.bytes = off;
+  DecodeWs d;
+  d.flags = reinterpret_cast<uint32_t*>(b + kWsFlags);
+  d.err = reinterpret_cast<uint32_t*>(b + kWsErr);
+  d.logits = reinterpret_cast<uint64_t*>(b + kWsLogits);
+  d.h = reinterpret_cast<uint64_t*>(b + kWsH);
+  d.a = reinterpret_cast<uint64_t*>(b + kWsA);
   return d;
 }
 
@@ -147,11 +159,10 @@ size_t fmoe_workspace_bytes(int op, int n_tokens, int hidden, int inter, int n_e
   if (n_tokens < 1 || hidden < 64 || inter < 64 || n_experts < 1 || k < 1 || k > 16) return 0;
   if (op == FMOE_OP_EXPERT_FFN) return up256((size_t)inter * 4);
   if (op == FMOE_OP_MOE_LAYER) {
-    // the decode kernel's synchronization state first, the multi-token scratch after it:
-    // a multi-token call must leave that state as the single-token calls expect it
-    size_t d = up256(carve_decode(nullptr, hidden, inter, n_experts, k).bytes);
+    // the fixed control block and decode region first (every offset independent of the
+    // shape), the multi-token scratch after them
     size_t bt = n_tokens > 1 ? batched_workspace_bytes(n_tokens, hidden, inter, n_experts, k) : 0;
-    return d + bt;
+    return kWsDecodeEnd + bt;
   }
   return 0;
 }
@@ -277,9 +288,9 @@ int fmoe_moe_layer(const fmoe_layer* layers, int n_layers, const float* x_in, fl
   hipStream_t s = (hipStream_t)stream;
 
   if (n_tokens > 1) {
-    const size_t d = up256(carve_decode(nullptr, H, I, E, k).bytes);
-    return launch_batched(layers, n_layers, x_in, h_out, n_tokens, k, eps, flags, idx_out, w_out,
-                          static_cast<char*>(ws) + d, ws_bytes - d, s);
+    char* b = static_cast<char*>(ws);
+    return launch_batched(layers, n_layers, x_in, h_out, n_tokens, k, eps, flags, idx_out, w_out, b + kWsDecodeEnd,
+                          ws_bytes - kWsDecodeEnd, reinterpret_cast<uint32_t*>(b + kWsDone), s);
   }
 
   // single-token decode: one persistent kernel per block of up to 64 layers
@@ -290,7 +301,7 @@ int fmoe_moe_layer(const fmoe_layer* layers, int n_layers, const float* x_in, fl
   if (G > kMaxGrid) G = kMaxGrid;
   const int rows_per_wg = (H + G - 1) / G;
   if (decode_smem_bytes(H, I, E + hs, k + hs, G, rows_per_wg, bits) > kDecodeMaxLds) return FMOE_ERR_SHAPE;
-  DecodeWs d = carve_decode(ws, H, I, E, k);
+  DecodeWs d = carve_decode(ws);
   DecodeParams p;
   memset(&p, 0, sizeof(p));
   p.n_experts = E;
@@ -332,6 +343,19 @@ int fmoe_moe_layer(const fmoe_layer* layers, int n_layers, const float* x_in, fl
   return FMOE_OK;
 }
 
+int fmoe_workspace_error(const void* ws, size_t ws_bytes, uint32_t* err_out, fmoe_stream_t stream) {
+  if (!ws || !err_out) return FMOE_ERR_NULL;
+  if (ws_bytes < kWsDecodeEnd) return FMOE_ERR_WORKSPACE;
+  if (!aligned(ws, 256) || !aligned(err_out, 4)) return FMOE_ERR_ALIGN;
+  if (overlaps(err_out, 4, ws, ws_bytes)) return FMOE_ERR_OVERLAP;
+  int rc = check_device();
+  if (rc) return rc;
+  const char* b = static_cast<const char*>(ws);
+  return hipMemcpyAsync(err_out, b + kWsErr, 4, hipMemcpyDeviceToDevice, (hipStream_t)stream) == hipSuccess
+             ? FMOE_OK
+             : FMOE_ERR_HIP;
+}
+
 int fmoe_batched_a16(const void* ws, size_t ws_bytes, int n_tokens, int hidden, int inter, int n_experts, int k,
                      int bits, uint16_t* a16_out, fmoe_stream_t stream) {
   if (!ws || !a16_out) return FMOE_ERR_NULL;
@@ -341,14 +365,12 @@ int fmoe_batched_a16(const void* ws, size_t ws_bytes, int n_tokens, int hidden, 
     return FMOE_ERR_SHAPE;
   if (k < 1 || k > 16 || k > n_experts) return FMOE_ERR_K;
   // k: the slots of the inspected call (its k, or k + 1 with a shared expert)
-  const size_t dbytes = up256(carve_decode(nullptr, hidden, inter, n_experts, k).bytes);
-  if (ws_bytes < dbytes + batched_region_bytes(n_tokens, hidden, inter, n_experts, k)) return FMOE_ERR_WORKSPACE;
+  if (ws_bytes < kWsDecodeEnd + batched_region_bytes(n_tokens, hidden, inter, n_experts, k)) return FMOE_ERR_WORKSPACE;
   if (!aligned(ws, 256) || !aligned(a16_out, 2)) return FMOE_ERR_ALIGN;
   if (overlaps(a16_out, (size_t)n_tokens * k * inter * 2, ws, ws_bytes)) return FMOE_ERR_OVERLAP;
   int rc = check_device();
   if (rc) return rc;
-  const size_t d = up256(carve_decode(nullptr, hidden, inter, n_experts, k).bytes);
-  return launch_batched_a16(static_cast<const char*>(ws) + d, n_tokens, hidden, inter, n_experts, k, bits, a16_out,
+  return launch_batched_a16(static_cast<const char*>(ws) + kWsDecodeEnd, n_tokens, hidden, inter, n_experts, k, bits, a16_out,
                             (hipStream_t)stream);
 }
 

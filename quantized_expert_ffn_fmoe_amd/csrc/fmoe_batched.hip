@@ -884,7 +884,7 @@ struct BatchedWs {
   int32_t* act_off;
   int32_t* act_cnt;
   int32_t* n_act;
-  uint32_t* done;  // workgroups of route_stage_kernel finished (0 between calls)
+  uint32_t* done;  // workgroups of route_stage_kernel finished (0 between calls; in the control block)
   uint16_t* a16;
   float* ag;
   float* ys;
@@ -917,7 +917,7 @@ BatchedWs carve(void* base, int T, int H, int I, int E, int k) {
   w.act_off = reinterpret_cast<int32_t*>(take(units * 4));
   w.act_cnt = reinterpret_cast<int32_t*>(take(units * 4));
   w.n_act = reinterpret_cast<int32_t*>(take(4));
-  w.done = reinterpret_cast<uint32_t*>(take(4));
+  w.done = nullptr;  // set by the caller: a fixed word of the workspace's control block
   w.a16 = reinterpret_cast<uint16_t*>(take(P * I * 2));
   w.ag = reinterpret_cast<float*>(take(P * (I / 64) * 4));
   w.ys = reinterpret_cast<float*>(take(P * H * 4));
@@ -995,12 +995,13 @@ size_t batched_region_bytes(int n_tokens, int hidden, int inter, int n_experts, 
 
 int launch_batched(const fmoe_layer* layers, int n_layers, const float* x_in, float* h_out, int n_tokens, int k,
                    float eps, unsigned flags, int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes,
-                   hipStream_t s) {
+                   uint32_t* done, hipStream_t s) {
   const fmoe_layer& L0 = layers[0];
   if (!batched_shape_ok(L0.hidden, L0.inter)) return FMOE_ERR_SHAPE;
   const int ks = k + (L0.shared_gate != nullptr ? 1 : 0);
-  const BatchedWs w = carve(ws, n_tokens, L0.hidden, L0.inter, L0.n_experts + 1, ks);
+  BatchedWs w = carve(ws, n_tokens, L0.hidden, L0.inter, L0.n_experts + 1, ks);
   if (w.bytes > ws_bytes) return FMOE_ERR_WORKSPACE;
+  w.done = done;
   if (L0.bits == 4) return run_layers<4>(layers, n_layers, x_in, h_out, n_tokens, k, eps, flags, idx_out, w_out, w, s);
   return run_layers<2>(layers, n_layers, x_in, h_out, n_tokens, k, eps, flags, idx_out, w_out, w, s);
 }

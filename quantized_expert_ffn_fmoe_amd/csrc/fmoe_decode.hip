@@ -186,7 +186,8 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
   dig_a.xsum = dig_a.step + dig_a.n_chunks;
 
   if (tid == 0) {
-    *fail = 0;
+    // a workspace whose error word is set (an earlier call gave up) fails at once
+    *fail = ld_dev_u32(p.err) != 0u;
     base[1] = 0;  // digit-builder arrivals (3 per layer)
     // Epochs: every workgroup's slot holds the same value F when a launch starts (0 in a
     // zero-filled workspace, else the last epoch of the previous launch). Layer l of this
@@ -227,6 +228,15 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
   // (a run inside the shared expert's slot needs no routing round: its expert is fixed)
   const int gu_first = blk_lo * rpwG / I, gu_lslot = gu_last / I;
   const int gu_need = blk_lo >= blk_hi ? 0 : gu_lslot < K ? gu_lslot + 1 : gu_first < K ? K : 0;
+  // What a workgroup takes part in. Router rows or gate/up items need all of v, hence the
+  // h gather. A workgroup with only down rows needs just its own rows of h, which it wrote
+  // itself in the previous layer's combine (kept in LDS): it reads no h word, so it never
+  // waits on words that faster workgroups may already have overwritten with the next
+  // layer's values (the next layer's h needs this workgroup's rows first). A workgroup
+  // with none of the three skips every exchange. (Uniform over the workgroup; at the
+  // 512-expert shapes every workgroup has all three.)
+  const bool need_v = n_ritems > 0 || blk_lo < blk_hi;
+  const int n_layers_run = (need_v || nr > 0) && !*fail ? p.n_layers : 0;
   const uint64_t* h_rep = p.h + (size_t)rep * H;
   const uint64_t* a_rep = p.a + (size_t)rep * KI;
   const uint64_t* logits_rep = p.logits + (size_t)rep * ER;
@@ -249,7 +259,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
 #pragma unroll
   for (int u = 0; u < kBatchR; ++u) router_load(0, wave + kDecodeWaves * u, u);
 
-  for (int l = 0; l < p.n_layers; ++l) {
+  for (int l = 0; l < n_layers_run; ++l) {
     const int lg = p.layer0 + l;
     const uint8_t* X = p.experts[l];
     const uint32_t ep = F + 3u * (uint32_t)l;
@@ -265,8 +275,18 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
     float ss = 0.f;
     // the first read of h waits for the router rows requested at the end of the previous
     // layer anyway (loads complete in order); issuing it after them samples h later
-    if (lg != 0) wait_vmem();
-    for (int i0 = tid; i0 < H; i0 += kDecodeThreads * kPollN) {
+    if (lg != 0 && need_v) wait_vmem();
+    if (!need_v && l == 0) {
+      // own rows only: from the input, or (a later launch of a chunked stack) from the
+      // previous launch's tagged output
+      for (int i = tid; i < nr; i += kDecodeThreads) {
+        float hv[1] = {0.f};
+        if (lg == 0) hv[0] = p.x_in[r0 + i];
+        else if (!poll_batch<1, 1>(h_rep + r0, nr, i, ep, hv, p.err)) *fail = 1;
+        hraw[i] = hv[0];
+      }
+    }
+    for (int i0 = tid; need_v && i0 < H; i0 += kDecodeThreads * kPollN) {
       float hv[kPollN];
       if (lg == 0) {
 #pragma unroll
@@ -452,7 +472,8 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
         }
       }
     } else {
-      build_digits<BITS>(dig, 0, H, [&](int i) { return vec[padded<CC>(i)]; }, kDecodeThreads - 64, tid - 64, inv);
+      if (need_v)
+        build_digits<BITS>(dig, 0, H, [&](int i) { return vec[padded<CC>(i)]; }, kDecodeThreads - 64, tid - 64, inv);
       // the digit image is complete once every builder wave has passed this point
       if (lane == 0) __hip_atomic_fetch_add(base + 1, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
       wait_ready(ready, gu_need);
@@ -759,6 +780,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
           float c = 0.f;
           for (int j = 0; j < KS; ++j) c = fmaf(wsel[j], ybuf[j * rows_wg + rl], c);
           const float hn = hraw[rl] + c;
+          hraw[rl] = hn;  // this workgroup's rows of the next layer's h (read again only without need_v)
           const uint64_t hv = tagged(hn, htag);
 #pragma unroll
           for (int rr = lane >> 4; rr < kRep; rr += 4) st_dev_u64(p.h + (size_t)rr * H + r, hv);

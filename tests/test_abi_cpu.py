@@ -70,6 +70,37 @@ def test_workspace_bytes():
     assert fm.workspace_bytes(99, 1, 4096, 1024, 512, 4) == 0
 
 
+def test_workspace_layout_is_shape_independent():
+    """The control words (epoch slots, error word, the multi-token sort counter) and the
+    decode exchange region sit at fixed offsets: the single-token size is one constant for
+    every shape, and a multi-token workspace is that constant plus the multi-token scratch,
+    which grows with n_tokens. So a call of a smaller shape after a larger one on one
+    workspace finds its control words where the earlier call left them."""
+    shapes = [(4096, 1024, 512, 4), (128, 64, 8, 1), (8192, 8192, 4096, 16), (256, 64, 16, 2),
+              (4096, 1024, 512, 10), (2048, 512, 300, 8)]
+    single = {fm.workspace_bytes(fm.OP_MOE_LAYER, 1, *sh) for sh in shapes}
+    assert len(single) == 1
+    d = single.pop()
+    # the largest exchange region: 8 replicas of 4097 logits, 8192 h words, 16 x 8192 a words
+    assert d >= 65536 + 8 * (4097 + 8192 + 16 * 8192) * 8
+    for sh in shapes:
+        b64 = fm.workspace_bytes(fm.OP_MOE_LAYER, 64, *sh)
+        b12 = fm.workspace_bytes(fm.OP_MOE_LAYER, 12, *sh)
+        assert b64 > b12 > d
+
+
+def test_workspace_error_validation():
+    ws = FAKE
+    d = fm.workspace_bytes(fm.OP_MOE_LAYER, 1, 4096, 1024, 512, 4)
+    out = FAKE + (1 << 26)
+    _raises(fm.ERR_NULL, fm.workspace_error, None, d, out, stream=0)
+    _raises(fm.ERR_NULL, fm.workspace_error, ws, d, None, stream=0)
+    _raises(fm.ERR_WORKSPACE, fm.workspace_error, ws, d - 1, out, stream=0)
+    _raises(fm.ERR_ALIGN, fm.workspace_error, ws + 16, d, out, stream=0)
+    _raises(fm.ERR_ALIGN, fm.workspace_error, ws, d, out + 2, stream=0)
+    _raises(fm.ERR_OVERLAP, fm.workspace_error, ws, d, ws + 4096, stream=0)
+
+
 def _raises(status, fn, *args, **kw):
     with pytest.raises(fm.FmoeError) as ei:
         fn(*args, **kw)
