@@ -1,0 +1,195 @@
+// measure.hip -- measurement kernels of the benchmark (not part of the fmoe library).
+//
+// 1. A read-only streaming kernel: the attainable HBM read rate of plain streaming code on
+//    this device, the bar beside the published 8 TB/s peak. Each thread keeps U 16-byte
+//    loads in flight over a grid-strided walk of the buffer; the loaded words are folded
+//    into one register that is stored only if it equals an impossible value, so the kernel
+//    writes nothing and no load can be removed.
+// 2. An exchange-latency probe: a persistent grid (one workgroup per compute unit, all
+//    resident) runs `rounds` chained exchanges of n_words tagged 64-bit words (value |
+//    round << 32): in every round each workgroup publishes its share of the words, waits
+//    for its stores, then polls all the words of its group until each carries the current
+//    round (or a later one) and stamps the 100 MHz real-time clock. Round r + 1 starts
+//    from the data of round r, so the spacing of the stamps is the latency of one exchange
+//    including the spread between workgroups. Modes:
+//      0  all workgroups, 8 replicas (replica g mod 8), device-scope accesses (the decode
+//         kernel's exchange);
+//      1  the 32 workgroups of one XCD (workgroup g is dispatched to XCD g mod 8), device-
+//         scope accesses;
+//      2  the same groups with workgroup-scope accesses (they miss the compute unit's L1
+//         and meet in the XCD's shared L2); only correct when the group shares one XCD,
+//         which the probe checks with the XCC_ID hardware register.
+//    Every wait is bounded (spin limit, then the error word).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr unsigned kSpinLimit = 1u << 22;
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <int U, bool NT>
+__global__ void __launch_bounds__(kThreads) stream_read_kernel(const u32x4* __restrict__ p, size_t n,
+                                                               uint32_t* __restrict__ sink) {
+  const size_t stride = (size_t)gridDim.x * kThreads;
+  size_t i = (size_t)blockIdx.x * kThreads + threadIdx.x;
+  uint32_t acc = 0;
+  for (; i + (U - 1) * stride < n; i += U * stride) {
+    u32x4 v[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) v[u] = NT ? __builtin_nontemporal_load(p + i + u * stride) : p[i + u * stride];
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+  }
+  for (; i < n; i += stride) {
+    const u32x4 v = p[i];
+    acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9E3779B9u && threadIdx.x == 0x3FF) sink[0] = acc;  // never true: threadIdx.x < 256
+}
+
+__device__ __forceinline__ uint32_t xcc_id() { return __builtin_amdgcn_s_getreg((3 << 11) | 20); }
+
+template <int MODE>
+__device__ __forceinline__ void put(uint64_t* p, uint64_t v) {
+  if (MODE == 2) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  else __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+template <int MODE>
+__device__ __forceinline__ uint64_t get(const uint64_t* p) {
+  if (MODE == 2) return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// buf: mode 0: [8][n_words]; modes 1-2: [8][n_words] (one region per XCD group).
+// t_end: [rounds][G] stamps; xcc: [G] XCC_ID of each workgroup; err: set when a wait gave up.
+template <int MODE>
+__global__ void __launch_bounds__(kThreads) exchange_kernel(uint64_t* buf, int n_words, int rounds, uint32_t epoch0,
+                                                            uint64_t* t_end, uint32_t* xcc, uint32_t* err) {
+  constexpr int kPoll = 16;
+  const int G = gridDim.x, g = blockIdx.x, tid = threadIdx.x;
+  const int grp = g % 8;                      // replica (mode 0) or XCD group (modes 1-2)
+  const int members = MODE == 0 ? G : G / 8;  // writers of one region
+  const int rank = MODE == 0 ? g : g / 8;
+  const int per = n_words / members;          // words owned by each writer
+  __shared__ int failed;
+  if (tid == 0) {
+    failed = 0;
+    xcc[g] = xcc_id();
+  }
+  __syncthreads();
+  for (int r = 0; r < rounds && !failed; ++r) {
+    const uint64_t tag = (uint64_t)(epoch0 + (uint32_t)r + 1u) << 32;
+    for (int i = tid; i < per; i += kThreads) {
+      const int w = rank * per + i;
+      if (MODE == 0) {
+#pragma unroll
+        for (int rr = 0; rr < 8; ++rr) put<MODE>(buf + (size_t)rr * n_words + w, tag | (uint32_t)w);
+      } else {
+        put<MODE>(buf + (size_t)grp * n_words + w, tag | (uint32_t)w);
+      }
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    const uint64_t* src = buf + (size_t)grp * n_words;
+    for (int i0 = tid; i0 < n_words; i0 += kThreads * kPoll) {
+      uint64_t v[kPoll];
+#pragma unroll
+      for (int u = 0; u < kPoll; ++u) {
+        const int i = i0 + u * kThreads;
+        v[u] = i < n_words ? get<MODE>(src + i) : tag;
+      }
+      unsigned spins = 0;
+      while (true) {
+        bool ok = true;
+#pragma unroll
+        for (int u = 0; u < kPoll; ++u) ok &= (v[u] >> 32) >= (tag >> 32);
+        if (ok) break;
+        if (++spins > kSpinLimit || ((spins & 255u) == 255u && __hip_atomic_load(err, __ATOMIC_RELAXED,
+                                                                                 __HIP_MEMORY_SCOPE_AGENT))) {
+          __hip_atomic_store(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          failed = 1;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+        for (int u = 0; u < kPoll; ++u) {
+          const int i = i0 + u * kThreads;
+          if ((v[u] >> 32) < (tag >> 32)) v[u] = get<MODE>(src + i);
+        }
+      }
+    }
+    __syncthreads();
+    if (tid == 0) t_end[(size_t)r * G + g] = __builtin_amdgcn_s_memrealtime();
+  }
+}
+
+template <typename K>
+int coresident(K fn, int G) {
+  int occ = 0, dev = 0, cus = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, fn, kThreads, 0) != hipSuccess) return -8;
+  if (hipGetDevice(&dev) != hipSuccess) return -8;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -8;
+  return (occ >= 1 && G <= cus) ? 0 : -2;
+}
+
+}  // namespace
+
+extern "C" {
+
+// Number of compute units of the current device (the exchange probe's grid).
+int measure_cus(void) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return -8;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return -8;
+  return cus;
+}
+
+// Enqueue one read of nbytes (a multiple of 16) at buf. variant: 0 plain loads, 1
+// non-temporal loads; unroll 4 or 8 loads in flight per thread; blocks: grid size.
+int measure_stream_read(const void* buf, size_t nbytes, int variant, int unroll, int blocks, uint32_t* sink,
+                        hipStream_t s) {
+  if (!buf || !sink || nbytes % 16 || blocks < 1) return -1;
+  const u32x4* p = static_cast<const u32x4*>(buf);
+  const size_t n = nbytes / 16;
+  if (variant == 0 && unroll == 4) hipLaunchKernelGGL((stream_read_kernel<4, false>), dim3(blocks), dim3(kThreads), 0, s, p, n, sink);
+  else if (variant == 0 && unroll == 8) hipLaunchKernelGGL((stream_read_kernel<8, false>), dim3(blocks), dim3(kThreads), 0, s, p, n, sink);
+  else if (variant == 1 && unroll == 4) hipLaunchKernelGGL((stream_read_kernel<4, true>), dim3(blocks), dim3(kThreads), 0, s, p, n, sink);
+  else if (variant == 1 && unroll == 8) hipLaunchKernelGGL((stream_read_kernel<8, true>), dim3(blocks), dim3(kThreads), 0, s, p, n, sink);
+  else return -2;
+  return hipGetLastError() == hipSuccess ? 0 : -8;
+}
+
+// Enqueue the exchange probe (see the file comment). buf: 8 * n_words uint64 (zero-filled
+// before the first call; epoch0 must exceed every round tag of earlier calls on buf);
+// n_words a multiple of the writers of a region (G, or G / 8); t_end: rounds * G uint64;
+// xcc: G uint32; err: one uint32 (0 before the call). G = measure_cus().
+int measure_exchange(int mode, int n_words, int rounds, uint32_t epoch0, void* buf, uint64_t* t_end, uint32_t* xcc,
+                     uint32_t* err, hipStream_t s) {
+  const int G = measure_cus();
+  if (G < 8 || G % 8) return -2;
+  if (!buf || !t_end || !xcc || !err || rounds < 1 || n_words < 1) return -1;
+  const int members = mode == 0 ? G : G / 8;
+  if (n_words % members) return -2;
+  int rc;
+  uint64_t* b = static_cast<uint64_t*>(buf);
+  switch (mode) {
+    case 0:
+      if ((rc = coresident(exchange_kernel<0>, G))) return rc;
+      hipLaunchKernelGGL(exchange_kernel<0>, dim3(G), dim3(kThreads), 0, s, b, n_words, rounds, epoch0, t_end, xcc, err);
+      break;
+    case 1:
+      if ((rc = coresident(exchange_kernel<1>, G))) return rc;
+      hipLaunchKernelGGL(exchange_kernel<1>, dim3(G), dim3(kThreads), 0, s, b, n_words, rounds, epoch0, t_end, xcc, err);
+      break;
+    case 2:
+      if ((rc = coresident(exchange_kernel<2>, G))) return rc;
+      hipLaunchKernelGGL(exchange_kernel<2>, dim3(G), dim3(kThreads), 0, s, b, n_words, rounds, epoch0, t_end, xcc, err);
+      break;
+    default:
+      return -2;
+  }
+  return hipGetLastError() == hipSuccess ? 0 : -8;
+}
+
+}  // extern "C"
