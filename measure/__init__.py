@@ -19,7 +19,9 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SO = os.path.join(_HERE, "libmeasure.so")
 MODES = {0: "all 256 workgroups, 8 replicas, device scope",
          1: "32 workgroups of one XCD, device scope",
-         2: "32 workgroups of one XCD, workgroup scope (meet in the XCD's L2)"}
+         2: "32 workgroups of one XCD, workgroup-scope atomics",
+         3: "32 workgroups of one XCD, plain stores, L1 invalidated before plain loads (meet in the XCD's L2)",
+         4: "32 workgroups of one XCD, plain stores, non-temporal loads"}
 
 
 def build() -> str:
@@ -128,7 +130,7 @@ def main(argv) -> int:
     if what == "exchange":
         G = lib().measure_cus()
         for n in (G, 512, 4096):
-            for mode in (0, 1, 2):
+            for mode in (0, 1, 2, 3, 4):
                 if n % (G if mode == 0 else G // 8):
                     continue
                 print(json.dumps(exchange(torch, mode, n)), flush=True)

@@ -16,9 +16,14 @@
 //         kernel's exchange);
 //      1  the 32 workgroups of one XCD (workgroup g is dispatched to XCD g mod 8), device-
 //         scope accesses;
-//      2  the same groups with workgroup-scope accesses (they miss the compute unit's L1
-//         and meet in the XCD's shared L2); only correct when the group shares one XCD,
-//         which the probe checks with the XCC_ID hardware register.
+//      2  the same groups with workgroup-scope accesses;
+//      3  the same groups with plain stores (written through the compute unit's L1 into
+//         the XCD's shared L2) and plain loads after an invalidation of the reader's L1
+//         (buffer_inv at workgroup scope), so both sides meet in the XCD's L2;
+//      4  the same groups with plain stores and non-temporal loads.
+//    Modes 2-4 are only correct when a group shares one XCD, which the probe checks with
+//    the XCC_ID hardware register; a mode whose loads cannot see the group's stores ends
+//    at the spin limit with the error word set.
 //    Every wait is bounded (spin limit, then the error word).
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -54,12 +59,20 @@ __device__ __forceinline__ uint32_t xcc_id() { return __builtin_amdgcn_s_getreg(
 template <int MODE>
 __device__ __forceinline__ void put(uint64_t* p, uint64_t v) {
   if (MODE == 2) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  else if (MODE >= 3) *p = v;  // plain store (kept in place by the asm wait that follows)
   else __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 template <int MODE>
 __device__ __forceinline__ uint64_t get(const uint64_t* p) {
   if (MODE == 2) return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  if (MODE == 3) return *p;  // plain load (the asm invalidation before a pass forces a reload)
+  if (MODE == 4) return __builtin_nontemporal_load(p);
   return __hip_atomic_load(const_cast<uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// Mode 3: drop the reader's L1 copies before a pass of loads.
+template <int MODE>
+__device__ __forceinline__ void before_poll() {
+  if (MODE == 3) asm volatile("buffer_inv sc0" ::: "memory");
 }
 
 // buf: mode 0: [8][n_words]; modes 1-2: [8][n_words] (one region per XCD group).
@@ -94,6 +107,7 @@ __global__ void __launch_bounds__(kThreads) exchange_kernel(uint64_t* buf, int n
     const uint64_t* src = buf + (size_t)grp * n_words;
     for (int i0 = tid; i0 < n_words; i0 += kThreads * kPoll) {
       uint64_t v[kPoll];
+      before_poll<MODE>();
 #pragma unroll
       for (int u = 0; u < kPoll; ++u) {
         const int i = i0 + u * kThreads;
@@ -112,6 +126,7 @@ __global__ void __launch_bounds__(kThreads) exchange_kernel(uint64_t* buf, int n
           break;
         }
         __builtin_amdgcn_s_sleep(1);
+        before_poll<MODE>();
 #pragma unroll
         for (int u = 0; u < kPoll; ++u) {
           const int i = i0 + u * kThreads;
@@ -185,6 +200,14 @@ int measure_exchange(int mode, int n_words, int rounds, uint32_t epoch0, void* b
     case 2:
       if ((rc = coresident(exchange_kernel<2>, G))) return rc;
       hipLaunchKernelGGL(exchange_kernel<2>, dim3(G), dim3(kThreads), 0, s, b, n_words, rounds, epoch0, t_end, xcc, err);
+      break;
+    case 3:
+      if ((rc = coresident(exchange_kernel<3>, G))) return rc;
+      hipLaunchKernelGGL(exchange_kernel<3>, dim3(G), dim3(kThreads), 0, s, b, n_words, rounds, epoch0, t_end, xcc, err);
+      break;
+    case 4:
+      if ((rc = coresident(exchange_kernel<4>, G))) return rc;
+      hipLaunchKernelGGL(exchange_kernel<4>, dim3(G), dim3(kThreads), 0, s, b, n_words, rounds, epoch0, t_end, xcc, err);
       break;
     default:
       return -2;
