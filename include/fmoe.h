@@ -79,11 +79,13 @@ enum fmoe_status {
   FMOE_ERR_HIP = -8,       /* a HIP call or kernel launch failed */
   FMOE_ERR_INTERNAL = -9,  /* unexpected internal condition */
   FMOE_ERR_DEVICE = -10,   /* the current device is not gfx950 */
-  FMOE_ERR_OVERLAP = -11   /* an output buffer overlaps an input buffer */
+  FMOE_ERR_OVERLAP = -11,  /* an output buffer overlaps an input buffer */
+  FMOE_ERR_SCRATCH = -12   /* fmoe_moe_layer_noalloc: the call needs more than the static scratch */
 };
 
 /* Flags of fmoe_moe_layer. */
 #define FMOE_PRENORM 1u /* v = rmsnorm(h) feeds router and experts (between layers) */
+#define FMOE_RESET_SCRATCH 2u /* fmoe_moe_layer_noalloc: zero the scratch's synchronization state first */
 
 /* Operation ids of fmoe_workspace_bytes. */
 enum fmoe_op { FMOE_OP_EXPERT_FFN = 1, FMOE_OP_MOE_LAYER = 2 };
@@ -235,6 +237,25 @@ int fmoe_expert_ffn(const fmoe_expert* e, const float* x, float* y, void* ws, si
 int fmoe_moe_layer(const fmoe_layer* layers, int n_layers, const float* x_in, float* h_out, int n_tokens, int k,
                    float eps, unsigned flags, int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes,
                    fmoe_stream_t stream);
+
+/*
+ * fmoe_moe_layer without a caller workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid allocation).
+ * Same operation, arguments, limits and errors as fmoe_moe_layer; the workspace is the
+ * library's own static scratch of 32 MiB per GPU (a file-scope device array that each GPU
+ * the library runs on holds until the process ends). Nothing is allocated or freed.
+ *  - A call whose fmoe_workspace_bytes(FMOE_OP_MOE_LAYER, n_tokens, hidden, inter,
+ *    n_experts, k) exceeds 32 MiB returns FMOE_ERR_SCRATCH before enqueuing anything (the
+ *    single-token path always fits; at hidden 4096, inter 1024, 512 experts, top-4 the
+ *    multi-token path fits up to 150 tokens).
+ *  - Every call on a GPU shares that GPU's scratch, which keeps the state of the last call:
+ *    the first call on a GPU, and any call with FMOE_RESET_SCRATCH in flags, first
+ *    zero-fills its synchronization state on `stream` (needed again after a call whose
+ *    device-side wait gave up, visible as NaN rows of h_out). Calls that overlap on one GPU
+ *    (other streams, other threads) race on the scratch and give undefined results.
+ */
+int fmoe_moe_layer_noalloc(const fmoe_layer* layers, int n_layers, const float* x_in, float* h_out, int n_tokens,
+                           int k, float eps, unsigned flags, int32_t* idx_out, float* w_out, fmoe_stream_t stream);
 
 /*
  * Inspection of the batched path's SwiGLU stage (for verifying it stage by stage). After

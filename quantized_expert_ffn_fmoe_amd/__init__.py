@@ -17,14 +17,15 @@ SO_PATH = os.path.join(_HERE, "libfmoe.so")
 
 OK = 0
 ERR_NULL, ERR_SHAPE, ERR_BITS, ERR_GROUP, ERR_K, ERR_ALIGN = -1, -2, -3, -4, -5, -6
-ERR_WORKSPACE, ERR_HIP, ERR_INTERNAL, ERR_DEVICE, ERR_OVERLAP = -7, -8, -9, -10, -11
+ERR_WORKSPACE, ERR_HIP, ERR_INTERNAL, ERR_DEVICE, ERR_OVERLAP, ERR_SCRATCH = -7, -8, -9, -10, -11, -12
 PRENORM = 1
+RESET_SCRATCH = 2
 OP_EXPERT_FFN, OP_MOE_LAYER = 1, 2
 
 EXPORTS = ("fmoe_status_string", "fmoe_version", "fmoe_codes_bytes", "fmoe_sb_bytes", "fmoe_expert_bytes",
            "fmoe_expert_view", "fmoe_pack", "fmoe_workspace_bytes", "fmoe_dequant_matvec",
            "fmoe_dequant_matvec_multi", "fmoe_route_topk", "fmoe_expert_ffn", "fmoe_moe_layer", "fmoe_batched_a16",
-           "fmoe_workspace_error")
+           "fmoe_workspace_error", "fmoe_moe_layer_noalloc")
 
 
 class FmoeError(RuntimeError):
@@ -87,6 +88,9 @@ def lib():
         L.fmoe_moe_layer.restype = i32
         L.fmoe_moe_layer.argtypes = [ctypes.POINTER(Layer), i32, vp, vp, i32, i32, ctypes.c_float, u32, vp, vp, vp,
                                      sz, vp]
+        L.fmoe_moe_layer_noalloc.restype = i32
+        L.fmoe_moe_layer_noalloc.argtypes = [ctypes.POINTER(Layer), i32, vp, vp, i32, i32, ctypes.c_float, u32, vp,
+                                             vp, vp]
         L.fmoe_workspace_error.restype = i32
         L.fmoe_workspace_error.argtypes = [vp, sz, vp, vp]
         L.fmoe_batched_a16.restype = i32
@@ -194,6 +198,14 @@ def moe_layer(layers, x_in, h_out, n_tokens, k, eps, flags, idx_out, w_out, ws, 
         layers = layers_array(layers)
     _check(lib().fmoe_moe_layer(layers, len(layers), _ptr(x_in), _ptr(h_out), n_tokens, k, eps, flags, _ptr(idx_out),
                                 _ptr(w_out), _ptr(ws), ws_bytes, _stream(stream)), "fmoe_moe_layer")
+
+
+def moe_layer_noalloc(layers, x_in, h_out, n_tokens, k, eps, flags, idx_out, w_out, stream=None) -> None:
+    """fmoe_moe_layer on the library's static scratch (no workspace argument)."""
+    if not isinstance(layers, ctypes.Array):
+        layers = layers_array(layers)
+    _check(lib().fmoe_moe_layer_noalloc(layers, len(layers), _ptr(x_in), _ptr(h_out), n_tokens, k, eps, flags,
+                                        _ptr(idx_out), _ptr(w_out), _stream(stream)), "fmoe_moe_layer_noalloc")
 
 
 def batched_a16(ws, ws_bytes, n_tokens, hidden, inter, n_experts, k, bits, a16_out, stream=None) -> None:

@@ -2,6 +2,8 @@
 // dispatch to the kernels. Every check runs before anything is enqueued.
 #include <string.h>
 
+#include <mutex>
+
 #include "fmoe_batched.h"
 #include "fmoe_decode.h"
 #include "fmoe_internal.h"
@@ -84,6 +86,63 @@ DecodeWs carve_decode(void* ws) {
   return d;
 }
 
+int moe_layer_impl(const fmoe_layer* layers, int n_layers, const float* x_in, float* h_out, int n_tokens, int k,
+                   float eps, unsigned flags, int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes,
+                   hipStream_t s, bool zero_sync_region);
+
+__global__ void zero_fill_kernel(uint4* p, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (size_t)gridDim.x * blockDim.x)
+    p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+// Zero `bytes` (a multiple of 16) at a 16-byte aligned device address, on stream s (a
+// kernel rather than a memset node, so that it replays correctly when captured).
+int zero_fill(void* p, size_t bytes, hipStream_t s) {
+  const size_t n = bytes / 16;
+  hipLaunchKernelGGL(zero_fill_kernel, dim3(1024), dim3(256), 0, s, static_cast<uint4*>(p), n);
+  return hipGetLastError() == hipSuccess ? FMOE_OK : FMOE_ERR_HIP;
+}
+
+// ---- the allocation-free variant's scratch
+// The library's own workspace for fmoe_moe_layer_noalloc: one file-scope device array,
+// of which every GPU the library runs on holds its own copy (zero at load) until the
+// process ends. Host code never passes the array's name to a kernel (on the host it only
+// stands for the symbol): the device address of each GPU's copy is looked up once per
+// device with hipGetSymbolAddress and kept below.
+constexpr size_t kScratchBytes = (size_t)32 << 20;
+static_assert(kWsDecodeEnd <= kScratchBytes, "the scratch holds at least the single-token workspace");
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];  // device address of `scratch` on device d (null until looked up)
+bool g_scratch_zeroed[kMaxDevices];  // a zero-fill of its synchronization region was enqueued
+
+// The current device's scratch address (looked up on the device's first call, with the
+// device current), the device, and whether its synchronization region was zero-filled by
+// a call already.
+int scratch_of_current_device(void** out, int* dev_out, bool* zeroed) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FMOE_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return FMOE_ERR_DEVICE;
+  int rc = check_device();
+  if (rc) return rc;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return FMOE_ERR_HIP;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  *dev_out = dev;
+  *zeroed = g_scratch_zeroed[dev];
+  return FMOE_OK;
+}
+
+void scratch_zero_enqueued(int dev) {
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  g_scratch_zeroed[dev] = true;
+}
+
 }  // namespace
 
 extern "C" {
@@ -102,6 +161,7 @@ const char* fmoe_status_string(int status) {
     case FMOE_ERR_INTERNAL: return "internal error";
     case FMOE_ERR_DEVICE: return "current device is not gfx950";
     case FMOE_ERR_OVERLAP: return "an output buffer overlaps an input buffer";
+    case FMOE_ERR_SCRATCH: return "the call needs more than the library's static scratch (fmoe_moe_layer_noalloc)";
     default: return "unknown status";
   }
 }
@@ -244,6 +304,35 @@ int fmoe_expert_ffn(const fmoe_expert* e, const float* x, float* y, void* ws, si
 int fmoe_moe_layer(const fmoe_layer* layers, int n_layers, const float* x_in, float* h_out, int n_tokens, int k,
                    float eps, unsigned flags, int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes,
                    fmoe_stream_t stream) {
+  return moe_layer_impl(layers, n_layers, x_in, h_out, n_tokens, k, eps, flags, idx_out, w_out, ws, ws_bytes,
+                        (hipStream_t)stream, false);
+}
+
+int fmoe_moe_layer_noalloc(const fmoe_layer* layers, int n_layers, const float* x_in, float* h_out, int n_tokens,
+                           int k, float eps, unsigned flags, int32_t* idx_out, float* w_out, fmoe_stream_t stream) {
+  if (!layers) return FMOE_ERR_NULL;
+  const size_t need = fmoe_workspace_bytes(FMOE_OP_MOE_LAYER, n_tokens, layers[0].hidden, layers[0].inter,
+                                           layers[0].n_experts, k);
+  if (need > kScratchBytes) return FMOE_ERR_SCRATCH;  // (need == 0: the shape error is reported below)
+  void* ptr = nullptr;
+  int dev = 0;
+  bool zeroed = false;
+  int rc = scratch_of_current_device(&ptr, &dev, &zeroed);
+  if (rc) return rc;
+  const bool fill = !zeroed || (flags & FMOE_RESET_SCRATCH);
+  rc = moe_layer_impl(layers, n_layers, x_in, h_out, n_tokens, k, eps, flags, idx_out, w_out, ptr, kScratchBytes,
+                      (hipStream_t)stream, fill);
+  if (rc == FMOE_OK && fill) scratch_zero_enqueued(dev);
+  return rc;
+}
+
+}  // extern "C"
+
+namespace {
+
+int moe_layer_impl(const fmoe_layer* layers, int n_layers, const float* x_in, float* h_out, int n_tokens, int k,
+                   float eps, unsigned flags, int32_t* idx_out, float* w_out, void* ws, size_t ws_bytes,
+                   hipStream_t s, bool zero_sync_region) {
   if (!layers || !x_in || !h_out) return FMOE_ERR_NULL;
   if (n_layers < 1 || n_layers > 4096 || n_tokens < 1 || n_tokens > 4096) return FMOE_ERR_SHAPE;
   const fmoe_layer& L0 = layers[0];
@@ -285,7 +374,8 @@ int fmoe_moe_layer(const fmoe_layer* layers, int n_layers, const float* x_in, fl
   if (n_tokens > 1 && !batched_shape_ok(H, I)) return FMOE_ERR_SHAPE;
   int rc = check_device();
   if (rc) return rc;
-  hipStream_t s = (hipStream_t)stream;
+  // every check has passed: from here on work is enqueued
+  if (zero_sync_region && (rc = zero_fill(ws, kWsDecodeEnd, s))) return rc;
 
   if (n_tokens > 1) {
     char* b = static_cast<char*>(ws);
@@ -342,6 +432,10 @@ int fmoe_moe_layer(const fmoe_layer* layers, int n_layers, const float* x_in, fl
   }
   return FMOE_OK;
 }
+
+}  // namespace
+
+extern "C" {
 
 int fmoe_workspace_error(const void* ws, size_t ws_bytes, uint32_t* err_out, fmoe_stream_t stream) {
   if (!ws || !err_out) return FMOE_ERR_NULL;

@@ -28,7 +28,7 @@ def test_exports_every_declared_function():
 
 
 def test_status_strings_and_version():
-    for code in range(0, -12, -1):
+    for code in range(0, -13, -1):
         assert fm.status_string(code) and fm.status_string(code) != "unknown status"
     assert fm.status_string(-99) == "unknown status"
     assert "gfx950" in fm.version()
