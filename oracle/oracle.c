@@ -15,6 +15,13 @@ int oracle_code(const uint8_t* codes, int cols, int bits, int r, int c) {
     uint8_t byte = row[c / 2];
     return (c % 2 == 0) ? (byte & 0x0f) : (byte >> 4);
   }
+  if (bits == 3) {
+    /* 8 columns per 3 bytes: column 8j+t is bits 3t..3t+2 of the little-endian 24-bit
+     * word of bytes 3j..3j+2 */
+    const uint8_t* p = row + 3 * (size_t)(c / 8);
+    uint32_t w = (uint32_t)p[0] | ((uint32_t)p[1] << 8) | ((uint32_t)p[2] << 16);
+    return (int)((w >> (3 * (c % 8))) & 0x07u);
+  }
   /* bits == 2 */
   uint8_t byte = row[c / 4];
   return (byte >> (2 * (c % 4))) & 0x03;

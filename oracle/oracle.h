@@ -33,8 +33,11 @@ extern "C" {
 typedef int (*oracle_provider_fn)(void* ctx, int layer, int expert, const uint8_t** codes,
                                   const uint16_t** scale, const uint16_t** bias);
 
-/* Code q[r][c] from the canonical layout (4-bit: element 2c low nibble; 2-bit: element
- * 4c+t in bits 2t..2t+1). */
+/* Code q[r][c] from the canonical layout: each row is a little-endian bit stream in which
+ * column c occupies bits bits*c .. bits*c + bits - 1. 4-bit: element 2c low nibble; 2-bit:
+ * element 4c+t in bits 2t..2t+1; 3-bit (openclawradar.com "Optimisations efficaces": 3-bit
+ * experts, 23% smaller than 4-bit): 8 columns per 3 bytes, column 8j+t in bits 3t..3t+2 of
+ * the little-endian 24-bit word of bytes 3j..3j+2. */
 int oracle_code(const uint8_t* codes, int cols, int bits, int r, int c);
 
 /* bf16 bit pattern -> value (exact widening). */

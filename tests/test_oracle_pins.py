@@ -34,6 +34,10 @@ def dense_decode(codes, scale, bias, rows, cols, bits, group):
         q = np.empty((rows, cols), dtype=np.int64)
         q[:, 0::2] = codes & 0x0F
         q[:, 1::2] = codes >> 4
+    elif bits == 3:
+        # a row is a little-endian bit stream, column c at bits 3c .. 3c + 2
+        stream = np.unpackbits(codes, axis=1, bitorder="little").reshape(rows, cols, 3).astype(np.int64)
+        q = stream[:, :, 0] + 2 * stream[:, :, 1] + 4 * stream[:, :, 2]
     else:
         q = np.empty((rows, cols), dtype=np.int64)
         for t in range(4):
@@ -52,6 +56,12 @@ def random_matrix(rng, rows, cols, bits, group=64):
 
 def bf16_of(values):
     return synth.bf16_bits(np.asarray(values, dtype=np.float32))
+
+
+def code_of(row_bytes, c, bits):
+    """Code of column c: bits bits*c .. bits*c + bits - 1 of the row read as one
+    little-endian integer (Python ints, independent of oracle.c)."""
+    return (int.from_bytes(bytes(row_bytes), "little") >> (bits * c)) & ((1 << bits) - 1)
 
 
 # ------------------------------------------------------------------ O1/O2 dequant matvec
@@ -75,21 +85,37 @@ def test_golden_dequant_tiny(golden_dir):
             assert y.tolist() == xc["y"], (case["name"], xc["x"])
 
 
-@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("bits", [4, 3, 2])
 def test_code_layout_bruteforce(bits):
     """oracle_code reads element (r, c) exactly where the canonical layout puts it."""
     rng = np.random.default_rng(1)
     rows, cols = 3, 128
     codes = rng.integers(0, 256, size=(rows, cols * bits // 8), dtype=np.uint8)
-    per = 8 // bits
     for r in range(rows):
         for c in range(cols):
-            byte = int(codes[r, c // per])
-            want = (byte >> (bits * (c % per))) & ((1 << bits) - 1)
+            want = code_of(codes[r], c, bits)
+            if bits != 3:  # the byte-and-shift form of the 4-bit and 2-bit layouts
+                per = 8 // bits
+                assert want == (int(codes[r, c // per]) >> (bits * (c % per))) & ((1 << bits) - 1)
             assert oracle.code(codes, cols, bits, r, c) == want
 
 
-@pytest.mark.parametrize("bits", [4, 2])
+def test_code_layout_3bit_words():
+    """3 bits: column 8j + t in bits 3t..3t+2 of the little-endian word of bytes 3j..3j+2
+    (every column of a 64-column row set one at a time to each value 0..7)."""
+    cols = 64
+    for c in range(cols):
+        for q in range(8):
+            stream = q << (3 * c)
+            row = np.frombuffer(stream.to_bytes(cols * 3 // 8, "little"), dtype=np.uint8)[None, :]
+            j, t = divmod(c, 8)
+            word = int(row[0, 3 * j]) | (int(row[0, 3 * j + 1]) << 8) | (int(row[0, 3 * j + 2]) << 16)
+            assert (word >> (3 * t)) & 7 == q
+            for c2 in range(cols):
+                assert oracle.code(row, cols, 3, 0, c2) == (q if c2 == c else 0)
+
+
+@pytest.mark.parametrize("bits", [4, 3, 2])
 def test_integer_exact_and_fma_identity(bits):
     """Integer-valued s, b, x: oracle == exact integer sum; == per-group factorisation;
     == the FMA rewrite sum fma(n, s*x, b*x), in fp32 and fp64 (all exact on such data)."""
@@ -100,7 +126,6 @@ def test_integer_exact_and_fma_identity(bits):
     b_int = rng.integers(-8, 9, size=(rows, cols // group))
     x_int = rng.integers(-5, 6, size=cols)
     y = oracle.matvec(codes, bf16_of(s_int), bf16_of(b_int), rows, cols, bits, group, x_int.astype(np.float64))
-    per = 8 // bits
     for r in range(rows):
         exact = 0
         fact = 0
@@ -108,7 +133,7 @@ def test_integer_exact_and_fma_identity(bits):
             sum_nx = 0
             sum_x = 0
             for c in range(g * group, (g + 1) * group):
-                n = (int(codes[r, c // per]) >> (bits * (c % per))) & ((1 << bits) - 1)
+                n = code_of(codes[r], c, bits)
                 exact += (n * int(s_int[r, g]) + int(b_int[r, g])) * int(x_int[c])
                 sum_nx += n * int(x_int[c])
                 sum_x += int(x_int[c])
@@ -120,14 +145,14 @@ def test_integer_exact_and_fma_identity(bits):
             acc_fma = dt(0)
             for c in range(cols):
                 g = c // group
-                n = dt((int(codes[r, c // per]) >> (bits * (c % per))) & ((1 << bits) - 1))
+                n = dt(code_of(codes[r], c, bits))
                 s, b, x = dt(s_int[r, g]), dt(b_int[r, g]), dt(x_int[c])
                 acc_plain = dt(acc_plain + (n * s + b) * x)
                 acc_fma = dt(acc_fma + (n * (s * x) + (b * x)))
             assert acc_plain == acc_fma == dt(exact)
 
 
-@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("bits", [4, 3, 2])
 def test_onehot_returns_dequantized_column(bits):
     rng = np.random.default_rng(3)
     rows, cols, group = 5, 128, 64
@@ -157,7 +182,7 @@ def test_zero_codes_and_zero_affine():
     assert np.all(oracle.matvec(codes, zeros, zeros, rows, cols, 4, group, x) == 0.0)
 
 
-@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("bits", [4, 3, 2])
 def test_dense_matmul_and_linearity(bits):
     rng = np.random.default_rng(5)
     rows, cols, group = 96, 320, 64
@@ -278,7 +303,7 @@ def _expert(rng, H, I, bits):
     return [random_matrix(rng, I, H, bits), random_matrix(rng, I, H, bits), random_matrix(rng, H, I, bits)]
 
 
-@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("bits", [4, 3, 2])
 def test_expert_ffn_dense(bits):
     rng = np.random.default_rng(11)
     H, I = 256, 128

@@ -62,3 +62,15 @@ def test_two_bit_codes_uniform():
     vals = np.concatenate([(codes >> (2 * t)) & 3 for t in range(4)]).ravel()
     counts = np.bincount(vals, minlength=4)
     assert counts.min() > 0.98 * counts.mean()
+
+
+def test_three_bit_codes_uniform():
+    """3-bit matrices take rows * cols * 3 / 8 bytes of the hash stream, so every code 0..7
+    is equally likely (decoded here as a little-endian bit stream, 3 bits per column)."""
+    rows, cols = 256, 512
+    codes, scale, bias = synth.matrix(0, 0, 0, synth.GATE, rows, cols, 3)
+    assert codes.shape == (rows, cols * 3 // 8) and scale.shape == (rows, cols // 64)
+    bits = np.unpackbits(codes, axis=1, bitorder="little").reshape(rows, cols, 3).astype(np.int64)
+    q = bits[:, :, 0] + 2 * bits[:, :, 1] + 4 * bits[:, :, 2]
+    freq = np.bincount(q.ravel(), minlength=8) / q.size
+    assert np.all(np.abs(freq - 0.125) < 0.005)
