@@ -34,9 +34,11 @@ int check_device() {
   return cached_ok ? FMOE_OK : FMOE_ERR_DEVICE;
 }
 
+bool bits_ok(int bits) { return bits == 2 || bits == 3 || bits == 4; }
+
 int check_qmat(const fmoe_qmat* W) {
   if (!W || !W->codes || !W->sb) return FMOE_ERR_NULL;
-  if (W->bits != 2 && W->bits != 4) return FMOE_ERR_BITS;
+  if (!bits_ok(W->bits)) return FMOE_ERR_BITS;
   if (W->group != 64) return FMOE_ERR_GROUP;
   if (W->rows < 1 || W->cols < 64 || W->cols % 64 != 0) return FMOE_ERR_SHAPE;
   if (W->cols > (W->bits == 4 ? 8192 : 16384)) return FMOE_ERR_SHAPE;
@@ -152,7 +154,7 @@ const char* fmoe_status_string(int status) {
     case FMOE_OK: return "ok";
     case FMOE_ERR_NULL: return "a required pointer is NULL";
     case FMOE_ERR_SHAPE: return "sizes out of range, not a multiple of 64, or inconsistent";
-    case FMOE_ERR_BITS: return "bits must be 2 or 4";
+    case FMOE_ERR_BITS: return "bits must be 2, 3 or 4";
     case FMOE_ERR_GROUP: return "group must be 64";
     case FMOE_ERR_K: return "k must be in 1..min(16, n_experts)";
     case FMOE_ERR_ALIGN: return "pointer not 16-byte aligned (workspace, expert stride: 256-byte)";
@@ -169,7 +171,7 @@ const char* fmoe_status_string(int status) {
 const char* fmoe_version(void) { return "fmoe 0.1 gfx950"; }
 
 size_t fmoe_codes_bytes(int rows, int cols, int bits) {
-  if (rows < 1 || cols < 64 || cols % 64 || (bits != 2 && bits != 4)) return 0;
+  if (rows < 1 || cols < 64 || cols % 64 || !bits_ok(bits)) return 0;
   return (size_t)rows * cols * bits / 8;
 }
 
@@ -187,7 +189,7 @@ size_t fmoe_expert_bytes(int hidden, int inter, int bits, int group) {
 
 int fmoe_expert_view(const void* blob, int hidden, int inter, int bits, int group, fmoe_expert* out) {
   if (!blob || !out) return FMOE_ERR_NULL;
-  if (bits != 2 && bits != 4) return FMOE_ERR_BITS;
+  if (!bits_ok(bits)) return FMOE_ERR_BITS;
   if (group != 64) return FMOE_ERR_GROUP;
   if (fmoe_expert_bytes(hidden, inter, bits, group) == 0) return FMOE_ERR_SHAPE;
   const char* b = static_cast<const char*>(blob);
@@ -201,7 +203,7 @@ int fmoe_expert_view(const void* blob, int hidden, int inter, int bits, int grou
 int fmoe_pack(const uint8_t* codes_canon, const uint16_t* scale, const uint16_t* bias, int rows, int cols, int bits,
               int group, void* codes_out, uint32_t* sb_out, fmoe_stream_t stream) {
   if (!codes_canon || !scale || !bias || !codes_out || !sb_out) return FMOE_ERR_NULL;
-  if (bits != 2 && bits != 4) return FMOE_ERR_BITS;
+  if (!bits_ok(bits)) return FMOE_ERR_BITS;
   if (group != 64) return FMOE_ERR_GROUP;
   if (rows < 1 || cols < 64 || cols % 64) return FMOE_ERR_SHAPE;
   if (!aligned(codes_canon, 16) || !aligned(codes_out, 16) || !aligned(sb_out, 16) || !aligned(scale, 2) ||
@@ -337,7 +339,7 @@ int moe_layer_impl(const fmoe_layer* layers, int n_layers, const float* x_in, fl
   if (n_layers < 1 || n_layers > 4096 || n_tokens < 1 || n_tokens > 4096) return FMOE_ERR_SHAPE;
   const fmoe_layer& L0 = layers[0];
   const int H = L0.hidden, I = L0.inter, E = L0.n_experts, bits = L0.bits;
-  if (bits != 2 && bits != 4) return FMOE_ERR_BITS;
+  if (!bits_ok(bits)) return FMOE_ERR_BITS;
   if (L0.group != 64) return FMOE_ERR_GROUP;
   if (H < 64 || H % 64 || I < 64 || I % 64 || H > 8192 || I > 8192) return FMOE_ERR_SHAPE;
   if (E < 1 || E > 4096) return FMOE_ERR_SHAPE;
@@ -372,6 +374,7 @@ int moe_layer_impl(const fmoe_layer* layers, int n_layers, const float* x_in, fl
                 (idx_out && overlaps(w_out, nk, idx_out, nk))))
     return FMOE_ERR_OVERLAP;
   if (n_tokens > 1 && !batched_shape_ok(H, I)) return FMOE_ERR_SHAPE;
+  if (n_tokens > 1 && !batched_bits_ok(bits)) return FMOE_ERR_BITS;
   int rc = check_device();
   if (rc) return rc;
   // every check has passed: from here on work is enqueued
@@ -453,7 +456,7 @@ int fmoe_workspace_error(const void* ws, size_t ws_bytes, uint32_t* err_out, fmo
 int fmoe_batched_a16(const void* ws, size_t ws_bytes, int n_tokens, int hidden, int inter, int n_experts, int k,
                      int bits, uint16_t* a16_out, fmoe_stream_t stream) {
   if (!ws || !a16_out) return FMOE_ERR_NULL;
-  if (bits != 2 && bits != 4) return FMOE_ERR_BITS;
+  if (!bits_ok(bits) || !batched_bits_ok(bits)) return FMOE_ERR_BITS;
   if (n_tokens < 2 || n_tokens > 4096 || n_experts < 1 || n_experts > 4096) return FMOE_ERR_SHAPE;
   if (hidden < 256 || hidden > 8192 || inter < 128 || inter > 8192 || !batched_shape_ok(hidden, inter))
     return FMOE_ERR_SHAPE;

@@ -10,6 +10,7 @@
 namespace fmoe {
 
 bool batched_shape_ok(int hidden, int inter);
+bool batched_bits_ok(int bits);
 // ws: the multi-token scratch; done: the sort's arrival counter, a word of the workspace's
 // fixed control block (0 between calls, whatever the shapes of earlier calls)
 size_t batched_workspace_bytes(int n_tokens, int hidden, int inter, int n_experts, int k);

@@ -122,6 +122,25 @@ __device__ __forceinline__ void build_b(const uint32_t* w, u32x4& b0, u32x4& b1)
   }
 }
 
+// 3 bits: the lane's low-plane dword as at 2 bits, plus the high-plane word of its 32-column
+// half (kb / 2), shifted by 2 (kb % 2): byte m of the shift-by-2r unpack holds column
+// 4m + r of the lane's 16, whose third bit then sits at 8m + 4 (r / 2) + r % 2
+// (fmoe_layout.h, hi_bit); one shift and an and-or put it at bit 2 of the byte.
+__device__ __forceinline__ void build_b3(uint32_t d, uint32_t hw, int kb, u32x4& b0, u32x4& b1) {
+  const uint32_t hs = hw >> (2 * (kb & 1));
+  const uint32_t t0 = (d & 0x03030303u) | ((hs << 2) & 0x04040404u);
+  const uint32_t t1 = ((d >> 2) & 0x03030303u) | ((hs << 1) & 0x04040404u);
+  const uint32_t t2 = ((d >> 4) & 0x03030303u) | ((hs >> 2) & 0x04040404u);
+  const uint32_t t3 = ((d >> 6) & 0x03030303u) | ((hs >> 3) & 0x04040404u);
+  b0.x = __builtin_amdgcn_perm(kHiBytes, t0, kSelEven);
+  b0.y = __builtin_amdgcn_perm(kHiBytes, t1, kSelEven);
+  b0.z = __builtin_amdgcn_perm(kHiBytes, t2, kSelEven);
+  b0.w = __builtin_amdgcn_perm(kHiBytes, t3, kSelEven);
+  b1.x = __builtin_amdgcn_perm(kHiBytes, t0, kSelOdd);
+  b1.y = __builtin_amdgcn_perm(kHiBytes, t1, kSelOdd);
+  b1.z = __builtin_amdgcn_perm(kHiBytes, t2, kSelOdd);
+  b1.w = __builtin_amdgcn_perm(kHiBytes, t3, kSelOdd);
+}
 __device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
                                                  0, 0);
@@ -446,12 +465,19 @@ constexpr int kWaveRows = 64;
 
 template <int BITS, int GC>
 struct StageGeom {
-  static constexpr int kBPG = BITS * 8;          // code bytes per row per group
+  static constexpr int kLB = BITS == 3 ? 2 : BITS;  // code width of the (low) plane's layout
+  static constexpr int kBPG = kLB * 8;           // (low-plane) code bytes per row per group
   static constexpr int kRS = GC * kBPG;          // bytes per row per stage
   static constexpr int kRPI = 1024 / kRS;        // rows per DMA instruction
   static constexpr int kNJ = kWaveRows / kRPI;   // DMA instructions per stage
-  static constexpr int kBytes = kWaveRows * kRS;  // LDS bytes of one stage
-  static constexpr int kLoads = 4 + 2 * GC + kNJ;  // vector memory instructions per stage
+  static constexpr int kLoBytes = kWaveRows * kRS;
+  // 3 bits: the high plane's two words per (row, group) follow in the stage buffer, one KB
+  // per DMA instruction (4-group stages: 32 rows' whole pieces; 2-group stages: 16 bytes of
+  // each of the 64 rows)
+  static constexpr int kHRS = BITS == 3 ? 8 * GC : 0;        // high-plane bytes per row per stage
+  static constexpr int kNJH = kWaveRows * kHRS / 1024;       // its DMA instructions
+  static constexpr int kBytes = kLoBytes + kWaveRows * kHRS;  // LDS bytes of one stage
+  static constexpr int kLoads = 4 + 2 * GC + kNJ + kNJH;  // vector memory instructions per stage
 };
 
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
@@ -487,9 +513,9 @@ struct StageRegs {
 
 // src(j, g0): the lane's 16 source bytes for DMA instruction j of the stage at group g0;
 // sbs(t, g0): the lane's scale/bias words of tile t for groups g0 .. g0 + GC - 1.
-template <int BITS, int GC, typename Src, typename SbSrc>
-__device__ __forceinline__ void issue_stage(char* buf, StageRegs<GC>& r, Src src, SbSrc sbs, const uint16_t* tp,
-                                            int g0, int lane) {
+template <int BITS, int GC, typename Src, typename HSrc, typename SbSrc>
+__device__ __forceinline__ void issue_stage(char* buf, StageRegs<GC>& r, Src src, HSrc hsrc, SbSrc sbs,
+                                            const uint16_t* tp, int g0, int lane) {
   using SG = StageGeom<BITS, GC>;
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -514,6 +540,8 @@ __device__ __forceinline__ void issue_stage(char* buf, StageRegs<GC>& r, Src src
   const uint32_t lb = lds_addr(buf);
 #pragma unroll
   for (int j = 0; j < SG::kNJ; ++j) dma16(src(j, g0), lb + j * 1024);
+#pragma unroll
+  for (int j = 0; j < SG::kNJH; ++j) dma16(hsrc(j, g0), lb + SG::kLoBytes + j * 1024);
 }
 
 // Byte offset in a stage buffer of weight row R's code bytes at offset `off` of its stage
@@ -563,6 +591,30 @@ __device__ __forceinline__ void read_group2(uint32_t base, uint32_t xaddr, uint3
   w[0][1] = w[1][1] = w[2][1] = w[3][1] = 0;
 }
 
+// 3 bits: the 2-bit read plus the lane's high-plane word of each tile (at hbase + H1 * t).
+template <int T1, int T2, int T3, int H1, int H2, int H3>
+__device__ __forceinline__ void read_group3(uint32_t base, uint32_t hbase, uint32_t xaddr, uint32_t (&w)[4][2],
+                                            uint32_t (&hw)[4], f32x4& x4) {
+  uint32_t q0, q1, q2, q3, g0, g1, g2, g3;
+  asm volatile(
+      "ds_read_b32 %0, %9\n"
+      "ds_read_b32 %1, %9 offset:%12\n"
+      "ds_read_b32 %2, %9 offset:%13\n"
+      "ds_read_b32 %3, %9 offset:%14\n"
+      "ds_read_b32 %4, %10\n"
+      "ds_read_b32 %5, %10 offset:%15\n"
+      "ds_read_b32 %6, %10 offset:%16\n"
+      "ds_read_b32 %7, %10 offset:%17\n"
+      "ds_read_b128 %8, %11\n"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(q0), "=&v"(q1), "=&v"(q2), "=&v"(q3), "=&v"(g0), "=&v"(g1), "=&v"(g2), "=&v"(g3), "=&v"(x4)
+      : "v"(base), "v"(hbase), "v"(xaddr), "n"(T1), "n"(T2), "n"(T3), "n"(H1), "n"(H2), "n"(H3)
+      : "memory");
+  w[0][0] = q0, w[1][0] = q1, w[2][0] = q2, w[3][0] = q3;
+  w[0][1] = w[1][1] = w[2][1] = w[3][1] = 0;
+  hw[0] = g0, hw[1] = g1, hw[2] = g2, hw[3] = g3;
+}
+
 // acc[tile] += the affine group products of the GC groups of one stage (see the header:
 // codes enter the matrix core as exact bf16 values, 256 s P + (b - 128 s) X per group).
 // Stage buffer layouts. 4-group stages hold the code layout's own bytes (fmoe_layout.h):
@@ -572,10 +624,13 @@ template <int BITS, int GC>
 __device__ __forceinline__ void compute_stage(f32x4 (&acc)[4], const char* buf, const StageRegs<GC>& r,
                                               const float* xs, int g0, int nl, int kb) {
   using SG = StageGeom<BITS, GC>;
-  using CL = CodeLayout<BITS>;
+  using CL = CodeLayout<SG::kLB>;
   const f32x4 zero = {0.f, 0.f, 0.f, 0.f};
   constexpr bool kPiece = GC == 4;  // the stage is one piece of the code layout
-  const int lane_part = kb * (BITS * 2);  // the lane's code bytes within a group's kBPG
+  const int lane_part = kb * (SG::kLB * 2);  // the lane's code bytes within a group's kBPG
+  // 3 bits: the lane's high-plane word of group gl, tile 0 (row nl), word kb / 2; 4-group
+  // stages hold 32 rows' pieces (32 bytes per row) per KB, 2-group stages 16 bytes per row
+  const uint32_t h_base = lds_addr(buf) + SG::kLoBytes + (kPiece ? nl * 32 : nl * 16) + (kb >> 1) * 4;
   const uint32_t lane_base = kPiece ? lds_addr(buf) + (nl / SG::kRPI) * 1024 + (nl % SG::kRPI) * SG::kRS + lane_part % 16
                                     : lds_addr(buf) + stage_off<BITS, GC>(nl, lane_part);
   const uint32_t x_base = lds_addr(xs + g0 * 16 + 4 * kb);
@@ -593,12 +648,17 @@ __device__ __forceinline__ void compute_stage(f32x4 (&acc)[4], const char* buf, 
     constexpr int T1 = kPiece ? (16 / SG::kRPI) * 1024 : stage_off<BITS, GC>(16, 0);
     constexpr int T2 = kPiece ? 2 * T1 : stage_off<BITS, GC>(32, 0);
     constexpr int T3 = kPiece ? 3 * T1 : stage_off<BITS, GC>(48, 0);
+    uint32_t hw[4] = {0u, 0u, 0u, 0u};
     if constexpr (BITS == 4) read_group4<T1, T2, T3>(gbase, x_base + gl * 64, w, x4);
+    else if constexpr (BITS == 3)
+      read_group3<T1, T2, T3, kPiece ? 512 : 256, kPiece ? 1024 : 512, kPiece ? 1536 : 768>(gbase, h_base + gl * 8,
+                                                                                         x_base + gl * 64, w, hw, x4);
     else read_group2<T1, T2, T3>(gbase, x_base + gl * 64, w, x4);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       u32x4 b0, b1;
-      build_b<BITS>(w[t], b0, b1);
+      if constexpr (BITS == 3) build_b3(w[t][0], hw[t], kb, b0, b1);
+      else build_b<BITS>(w[t], b0, b1);
       const float cs = 256.f * bf16_lo(r.sb[t][gl]);
       const float cb = fmaf(-0.5f, cs, bf16_hi(r.sb[t][gl]));
       f32x4 P = mfma(r.a[gl][0], b0, zero);
@@ -615,14 +675,14 @@ __device__ __forceinline__ void compute_stage(f32x4 (&acc)[4], const char* buf, 
 // All G groups of a pass (GC * U divides G): blocks of U stages, two stages in flight
 // inside a block (stage u + 2 is requested once stage u has been read). A block issues
 // and consumes all of its own loads, so nothing is in flight across the loop's back edge.
-template <int BITS, int GC, int U, typename Src, typename SbSrc>
-__device__ __forceinline__ void expert_pass(f32x4 (&acc)[4], char* wbuf, Src src, SbSrc sptr,
+template <int BITS, int GC, int U, typename Src, typename HSrc, typename SbSrc>
+__device__ __forceinline__ void expert_pass(f32x4 (&acc)[4], char* wbuf, Src src, HSrc hsrc, SbSrc sptr,
                                             const uint16_t* tp, const float* xs, int G, int lane, int nl, int kb) {
   using SG = StageGeom<BITS, GC>;
   for (int s0 = 0; s0 < G / GC; s0 += U) {
     StageRegs<GC> r[2];
-    issue_stage<BITS, GC>(wbuf, r[0], src, sptr, tp, s0 * GC, lane);
-    if constexpr (U > 1) issue_stage<BITS, GC>(wbuf + SG::kBytes, r[1], src, sptr, tp, (s0 + 1) * GC, lane);
+    issue_stage<BITS, GC>(wbuf, r[0], src, hsrc, sptr, tp, s0 * GC, lane);
+    if constexpr (U > 1) issue_stage<BITS, GC>(wbuf + SG::kBytes, r[1], src, hsrc, sptr, tp, (s0 + 1) * GC, lane);
 #pragma unroll
     for (int u = 0; u < U; ++u) {
       if (u + 1 < U) wait_vmcnt<SG::kLoads>();
@@ -630,7 +690,7 @@ __device__ __forceinline__ void expert_pass(f32x4 (&acc)[4], char* wbuf, Src src
       compute_stage<BITS, GC>(acc, wbuf + (u % 2) * SG::kBytes, r[u % 2], xs, (s0 + u) * GC, nl, kb);
       if (u + 2 < U) {
         wait_lgkm();  // the stage's reads of this buffer are done before the DMA refills it
-        issue_stage<BITS, GC>(wbuf + (u % 2) * SG::kBytes, r[u % 2], src, sptr, tp, (s0 + u + 2) * GC, lane);
+        issue_stage<BITS, GC>(wbuf + (u % 2) * SG::kBytes, r[u % 2], src, hsrc, sptr, tp, (s0 + u + 2) * GC, lane);
       }
       __builtin_amdgcn_sched_barrier(0);
     }
@@ -648,28 +708,43 @@ __device__ __forceinline__ void expert_pass_any(f32x4 (&acc)[4], char* wbuf, Mat
                                                 int rows_of, size_t row_bytes, const uint32_t* const (&sbm)[4],
                                                 const int (&sbr)[4],
                                                 const uint16_t* tp, const float* xs, int G, int lane, int nl, int kb) {
+  constexpr int LB = BITS == 3 ? 2 : BITS;
+  // 3 bits: the high plane (two words per (row, group), blocked in 32-row blocks, fmoe_layout.h)
+  // starts after the low plane of each matrix
+  auto hi_of = [&](int R) {
+    return reinterpret_cast<const uint32_t*>(mat_of(R) + lo_plane_bytes(rows_of, G * 64));
+  };
   if (G % 4 == 0) {
     using SG = StageGeom<BITS, 4>;
-    static_assert(SG::kRPI == CodeLayout<BITS>::kSubRows && SG::kRS == CodeLayout<BITS>::kPieceBytes,
+    static_assert(SG::kRPI == CodeLayout<LB>::kSubRows && SG::kRS == CodeLayout<LB>::kPieceBytes,
                   "a 4-group stage instruction is one contiguous KB of the code layout");
     const uint8_t* dmarow[SG::kNJ];
     int run[SG::kNJ];  // bytes from one piece of the instruction's rows to the next
 #pragma unroll
     for (int j = 0; j < SG::kNJ; ++j) {  // rows j * kRPI .. (consecutive, kRPI-aligned): lane l takes byte 16 l
       const int R = j * SG::kRPI;
-      const size_t o0 = code_offset<BITS>(rows_of, row_bytes, row_of(R), 0);
+      const size_t o0 = code_offset<LB>(rows_of, row_bytes, row_of(R), 0);
       dmarow[j] = mat_of(R) + o0 + 16 * lane;
-      run[j] = (int)(code_offset<BITS>(rows_of, row_bytes, row_of(R), SG::kRS) - o0);
+      run[j] = (int)(code_offset<LB>(rows_of, row_bytes, row_of(R), SG::kRS) - o0);
     }
     auto src = [&](int j, int g0) { return dmarow[j] + (size_t)(g0 / 4) * run[j]; };
+    // high plane: instruction j takes the piece of wave rows 32 j .. 32 j + 31 (one 32-row
+    // block of one matrix: the wave's row halves start at multiples of 32), one KB per
+    // piece, lane l bytes 16 l .. 16 l + 15
+    const uint8_t* hrow[SG::kNJH > 0 ? SG::kNJH : 1];
+#pragma unroll
+    for (int j = 0; j < SG::kNJH; ++j)
+      hrow[j] = reinterpret_cast<const uint8_t*>(hi_of(32 * j) + hi_offset(rows_of, G, row_of(32 * j), 0, 0)) +
+                16 * lane;
+    auto hsrc = [&](int j, int g0) { return hrow[j] + (size_t)(g0 / 4) * 1024; };
     const uint32_t* sp[4];  // the lane's scale/bias piece at stage 0; a stage is 32 rows x 4 words further
 #pragma unroll
     for (int t = 0; t < 4; ++t) sp[t] = sbm[t] + sb_offset(rows_of, G, sbr[t], 0);
     auto sptr = [&](int t, int g0) { return sp[t] + (g0 / 4) * 128; };
     const int NS = G / 4;
-    if (NS % 4 == 0) expert_pass<BITS, 4, 4>(acc, wbuf, src, sptr, tp, xs, G, lane, nl, kb);
-    else if (NS % 2 == 0) expert_pass<BITS, 4, 2>(acc, wbuf, src, sptr, tp, xs, G, lane, nl, kb);
-    else expert_pass<BITS, 4, 1>(acc, wbuf, src, sptr, tp, xs, G, lane, nl, kb);
+    if (NS % 4 == 0) expert_pass<BITS, 4, 4>(acc, wbuf, src, hsrc, sptr, tp, xs, G, lane, nl, kb);
+    else if (NS % 2 == 0) expert_pass<BITS, 4, 2>(acc, wbuf, src, hsrc, sptr, tp, xs, G, lane, nl, kb);
+    else expert_pass<BITS, 4, 1>(acc, wbuf, src, hsrc, sptr, tp, xs, G, lane, nl, kb);
   } else {
     using SG = StageGeom<BITS, 2>;
     const uint8_t* mat[SG::kNJ];
@@ -682,10 +757,14 @@ __device__ __forceinline__ void expert_pass_any(f32x4 (&acc)[4], char* wbuf, Mat
     }
     const int seg = 16 * (lane / SG::kRPI);
     auto src = [&](int j, int g0) {
-      return mat[j] + code_offset<BITS>(rows_of, row_bytes, row[j], (size_t)g0 * SG::kBPG + seg);
+      return mat[j] + code_offset<LB>(rows_of, row_bytes, row[j], (size_t)g0 * SG::kBPG + seg);
     };
+    // high plane: one instruction, lane l the 16 bytes (groups g0, g0 + 1) of wave row l
+    const uint32_t* hl = hi_of(lane);
+    const int hr = row_of(lane);
+    auto hsrc = [&](int, int g0) { return hl + hi_offset(rows_of, G, hr, g0, 0); };
     auto sptr = [&](int t, int g0) { return sbm[t] + sb_offset(rows_of, G, sbr[t], g0); };
-    expert_pass<BITS, 2, 1>(acc, wbuf, src, sptr, tp, xs, G, lane, nl, kb);
+    expert_pass<BITS, 2, 1>(acc, wbuf, src, hsrc, sptr, tp, xs, G, lane, nl, kb);
   }
 }
 
@@ -721,7 +800,7 @@ __global__ void __launch_bounds__(kBT, 2) gate_up_kernel(BParams p) {
   const int H = p.H, I = p.I, G = H / 64;
   const uint8_t* blob = p.experts + (size_t)e * p.stride;
   const size_t cbytes = (size_t)I * H * BITS / 8, sbytes = (size_t)I * G * 4;
-  const size_t rowb = (size_t)H * BITS / 8;
+  const size_t rowb = (size_t)H * (BITS == 3 ? 2 : BITS) / 8;  // (low-plane) code bytes per row
   const int row0 = blockIdx.x * kGuRowsWg + wave * kGuRowsWave;
   // tiles 0, 1: gate rows row0 .. row0 + 31; tiles 2, 3: the same rows of up
   const uint32_t* sbm[4];  // scale/bias matrix and row of each tile (blocked layout, fmoe_layout.h)
@@ -790,7 +869,7 @@ __global__ void __launch_bounds__(kBT, 2) down_kernel(BParams p) {
   const int H = p.H, I = p.I, G = I / 64;
   const uint8_t* blob = p.experts + (size_t)e * p.stride;
   const size_t cbytes = (size_t)I * H * BITS / 8, sbytes = (size_t)H * G * 4;
-  const size_t rowb = (size_t)I * BITS / 8;
+  const size_t rowb = (size_t)I * (BITS == 3 ? 2 : BITS) / 8;  // (low-plane) code bytes per row
   const int row0 = blockIdx.x * kDnRowsWg + wave * kDnRowsWave;
   const uint32_t* sbm[4];
   int sbr[4];
@@ -982,6 +1061,7 @@ int run_layers(const fmoe_layer* layers, int n_layers, const float* x_in, float*
 }  // namespace
 
 bool batched_shape_ok(int hidden, int inter) { return hidden % kDnRowsWg == 0 && inter % kGuRowsWg == 0; }
+bool batched_bits_ok(int bits) { return bits == 2 || bits == 3 || bits == 4; }
 
 // The scratch is carved for n_experts + 1 sort buckets (a shared expert's) and the call's
 // slots; the size query covers k + 1 slots.
@@ -1003,6 +1083,7 @@ int launch_batched(const fmoe_layer* layers, int n_layers, const float* x_in, fl
   if (w.bytes > ws_bytes) return FMOE_ERR_WORKSPACE;
   w.done = done;
   if (L0.bits == 4) return run_layers<4>(layers, n_layers, x_in, h_out, n_tokens, k, eps, flags, idx_out, w_out, w, s);
+  if (L0.bits == 3) return run_layers<3>(layers, n_layers, x_in, h_out, n_tokens, k, eps, flags, idx_out, w_out, w, s);
   return run_layers<2>(layers, n_layers, x_in, h_out, n_tokens, k, eps, flags, idx_out, w_out, w, s);
 }
 
@@ -1015,7 +1096,7 @@ int launch_batched_a16(const void* ws, int n_tokens, int hidden, int inter, int 
   if (blocks > 4096) blocks = 4096;
   if (bits == 4)
     hipLaunchKernelGGL(a16_natural_kernel<4>, dim3((unsigned)blocks), dim3(kBT), 0, s, w.a16, P, inter, out);
-  else
+  else  // 3 bits: the operand order of 2 bits
     hipLaunchKernelGGL(a16_natural_kernel<2>, dim3((unsigned)blocks), dim3(kBT), 0, s, w.a16, P, inter, out);
   return hipGetLastError() == hipSuccess ? FMOE_OK : FMOE_ERR_HIP;
 }

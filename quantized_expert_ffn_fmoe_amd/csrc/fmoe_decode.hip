@@ -202,7 +202,6 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
   const size_t cbH = (size_t)I * H * BITS / 8;  // bytes of gate (= up = down) codes
   const size_t sbb = (size_t)I * (H / 64) * 4;  // bytes of one sb array
   const int ngH = H / 64, ngI = I / 64;
-  const size_t rowH = (size_t)H * BITS / 8, rowI = (size_t)I * BITS / 8;
   const int nchG = H / CC, nchD = I / CC;
   const int lprG = HC ? lanes_per_row(HC / CC) : p.lpr_g, rpwG = 64 / lprG;
   const int lprD = IC ? lanes_per_row(IC / CC) : p.lpr_d, rpwD = 64 / lprD;
@@ -490,7 +489,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
       bool dc_loaded = false;  // the digits are read from LDS after the first loads are issued
       const uint64_t atag = (uint64_t)(ep + 2u) << 32;
       for (int b0 = blk_lo + wave * kBatchGU; b0 < blk_hi; b0 += kDecodeWaves * kBatchGU) {
-        uint4 wg[kBatchGU][CPL_G], wu[kBatchGU][CPL_G];
+        CChunk<BITS> wg[kBatchGU][CPL_G], wu[kBatchGU][CPL_G];
         uint32_t sg[kBatchGU][CPL_G], su[kBatchGU][CPL_G];
 #pragma unroll
         for (int u = 0; u < kBatchGU; ++u) {
@@ -507,9 +506,8 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
             for (int q = 0; q < CPL_G; ++q) {
               int c = subG + lprG * q;
               if (kFastGU || c < nchG) {  // the fast path covers exactly nchG chunks per row
-                const size_t off = code_offset<BITS>(I, rowH, i, (size_t)c * 16);
-                wg[u][q] = *reinterpret_cast<const uint4*>(gp + off);
-                wu[u][q] = *reinterpret_cast<const uint4*>(gp + cbH + off);
+                load_cchunk<BITS>(wg[u][q], gp, I, H, i, c);
+                load_cchunk<BITS>(wu[u][q], gp + cbH, I, H, i, c);
                 const size_t so = sb_offset(I, ngH, i, c / C::kPerGroup);
                 sg[u][q] = gsb[so];
                 su[u][q] = usb[so];
@@ -586,7 +584,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
     // ---- prefetch: every wave issues the loads of its first kBatchD down items (all k
     // experts must be known)
     wait_ready(ready, K);
-    uint4 wd[kBatchD][CPL_D];
+    CChunk<BITS> wd[kBatchD][CPL_D];
     uint32_t sd[kBatchD][CPL_D];
     auto down_load = [&](int m, int u) {
       const int t = d_lo + m;
@@ -602,7 +600,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
           for (int q = 0; q < CPL_D; ++q) {
             int c = subD + lprD * q;
             if (c < nchD) {
-              wd[u][q] = *reinterpret_cast<const uint4*>(dp + code_offset<BITS>(H, rowI, r, (size_t)c * 16));
+              load_cchunk<BITS>(wd[u][q], dp, H, I, r, c);
               sd[u][q] = dsb[sb_offset(H, ngI, r, c / C::kPerGroup)];
             }
           }
@@ -816,7 +814,7 @@ int decode_geometry(int hidden, int inter, int bits, int* lpr_g, int* cpl_g, int
 
 size_t decode_smem_bytes(int hidden, int inter, int n_experts, int k, int G, int rows_per_wg, int bits) {
   const int cc = bits == 4 ? 32 : 64;
-  const int nw = bits == 4 ? Digits<4>::kWords : Digits<2>::kWords;
+  const int nw = bits == 4 ? Digits<4>::kWords : Digits<2>::kWords;  // (3 bits: the digit sets of 2)
   const size_t ki = (size_t)k * inter;
   const size_t vec_len = (size_t)hidden > ki ? (size_t)hidden : ki;
   const size_t max_chunks = vec_len / cc;
@@ -866,19 +864,22 @@ int launch_decode(const DecodeParams& p, int G, hipStream_t s) {
                                         p.rows_per_wg, p.bits);
   int cg = p.cpl_g, cd = p.cpl_d;
   // the decode shapes of the 512-expert stack: hidden 4096, inter 1024, top-4 (and the
-  // top-10 routing of the same layer)
+  // top-10 routing of the same layer), at 4, 3 and 2 bits
   // (and the top-4 routing with a gated shared expert; other shapes with a shared expert run
   // the generic kernel)
   if (p.hidden == 4096 && p.inter == 1024 && p.n_experts == 512 && p.k == 4 && p.has_shared) {
     if (p.bits == 4) return launch_decode_t<4, 2, 1, 4096, 1024, 512, 4, 1>(p, G, smem, s);
+    if (p.bits == 3) return launch_decode_t<3, 1, 1, 4096, 1024, 512, 4, 1>(p, G, smem, s);
     return launch_decode_t<2, 1, 1, 4096, 1024, 512, 4, 1>(p, G, smem, s);
   }
   if (p.hidden == 4096 && p.inter == 1024 && p.n_experts == 512 && p.k == 4 && !p.has_shared) {
     if (p.bits == 4) return launch_decode_t<4, 2, 1, 4096, 1024, 512, 4>(p, G, smem, s);
+    if (p.bits == 3) return launch_decode_t<3, 1, 1, 4096, 1024, 512, 4>(p, G, smem, s);
     return launch_decode_t<2, 1, 1, 4096, 1024, 512, 4>(p, G, smem, s);
   }
   if (p.hidden == 4096 && p.inter == 1024 && p.n_experts == 512 && p.k == 10 && !p.has_shared) {
     if (p.bits == 4) return launch_decode_t<4, 2, 1, 4096, 1024, 512, 10>(p, G, smem, s);
+    if (p.bits == 3) return launch_decode_t<3, 1, 1, 4096, 1024, 512, 10>(p, G, smem, s);
     return launch_decode_t<2, 1, 1, 4096, 1024, 512, 10>(p, G, smem, s);
   }
 #define FMOE_DEC(B, X, Y) \
@@ -887,6 +888,7 @@ int launch_decode(const DecodeParams& p, int G, hipStream_t s) {
   FMOE_DEC(4, 1, 4) FMOE_DEC(4, 2, 4) FMOE_DEC(4, 4, 4)
   FMOE_DEC(2, 1, 1) FMOE_DEC(2, 2, 1) FMOE_DEC(2, 4, 1) FMOE_DEC(2, 1, 2) FMOE_DEC(2, 2, 2) FMOE_DEC(2, 4, 2)
   FMOE_DEC(2, 1, 4) FMOE_DEC(2, 2, 4) FMOE_DEC(2, 4, 4)
+  FMOE_DEC(3, 1, 1) FMOE_DEC(3, 2, 1) FMOE_DEC(3, 1, 2) FMOE_DEC(3, 2, 2)  // 3 bits: hidden, inter <= 8192
 #undef FMOE_DEC
   return FMOE_ERR_SHAPE;
 }

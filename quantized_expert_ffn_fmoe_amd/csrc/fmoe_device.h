@@ -17,10 +17,15 @@
 //   sum_j (q_j s + b) x_j = s * sum_j q_j x_j + b * sum_j x_j
 // (the affine dequantization of the Flash-MoE pages, aibit.im "Techniques de rupture"
 // item 2), with sum_j x_j precomputed per chunk.
+//
+// 3-bit codes (two planes, fmoe_layout.h): a chunk is the 16 bytes of the low plane for 64
+// columns (as a 2-bit chunk) plus the two high-plane words of the same group.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include "fmoe_layout.h"
 
 namespace fmoe {
 
@@ -44,9 +49,34 @@ __device__ __forceinline__ float bf16_hi(uint32_t v) { return __uint_as_float(v 
 
 template <int BITS>
 struct Chunk {
-  static constexpr int kCodes = BITS == 4 ? 32 : 64;  // columns per 16-byte chunk
+  static constexpr int kCodes = BITS == 4 ? 32 : 64;  // columns per 16-byte (low-plane) chunk
   static constexpr int kPerGroup = 64 / kCodes;       // chunks per 64-weight group
+  static constexpr int kLoBits = BITS == 3 ? 2 : BITS;  // code width of the (low) plane's layout
 };
+
+// The code bytes of one chunk as loaded: 16 bytes, plus the two high-plane words at 3 bits.
+template <int BITS>
+struct CChunk {
+  uint4 w;
+};
+template <>
+struct CChunk<3> {
+  uint4 w;
+  uint2 h;
+};
+
+// Load chunk `c` (16-byte chunk index along the row) of row r of a packed matrix whose codes
+// start at `mat` (rows x cols).
+template <int BITS>
+__device__ __forceinline__ void load_cchunk(CChunk<BITS>& cc, const uint8_t* mat, int rows, int cols, int r, int c) {
+  constexpr int LB = Chunk<BITS>::kLoBits;
+  const size_t row_bytes = (size_t)cols * LB / 8;
+  cc.w = *reinterpret_cast<const uint4*>(mat + code_offset<LB>(rows, row_bytes, r, (size_t)c * 16));
+  if constexpr (BITS == 3) {
+    const uint32_t* hp = reinterpret_cast<const uint32_t*>(mat + lo_plane_bytes(rows, cols));
+    cc.h = *reinterpret_cast<const uint2*>(hp + hi_offset(rows, cols / 64, r, c, 0));
+  }
+}
 
 // Register image of the activation values of one chunk (see header comment).
 template <int BITS>
@@ -124,10 +154,55 @@ __device__ __forceinline__ float chunk_qx(const uint4& w, const XChunk<BITS>& xc
   return a0 + a1;
 }
 
+// 3-bit: the low plane's dword t holds columns 16t..16t+15 in bit pairs, (w >> 2p) &
+// 0x03030303 has column 16t + 4m + p in byte m; the high-plane word of the dword's 32-column
+// half, shifted by 2 (t % 2), has that column's third bit at 8m + 4 (p / 2) + p % 2
+// (fmoe_layout.h, hi_bit), which one shift and mask move to bit 2 of byte m. The register
+// image of x is kept unscaled in that order: v[16t + 4p + m] = x[16t + 4m + p].
+__device__ __forceinline__ uint32_t hi_bytes3(uint32_t hs, int p) {
+  const int b = 4 * (p / 2) + (p % 2);  // the bit of byte m, before the move to bit 2
+  return (b >= 2 ? (hs >> (b - 2)) : (hs << (2 - b))) & 0x04040404u;
+}
+template <>
+__device__ __forceinline__ void load_xchunk<3>(XChunk<3>& xc, const float* x) {
+  float s = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const float e = x[16 * t + 4 * m + p];
+        xc.v[16 * t + 4 * p + m] = e;
+        s += e;
+      }
+  xc.sum = s;
+}
+__device__ __forceinline__ float chunk_qx3(const CChunk<3>& cc, const XChunk<3>& xc) {
+  const uint32_t ws[4] = {cc.w.x, cc.w.y, cc.w.z, cc.w.w};
+  float a0 = 0.f, a1 = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    const uint32_t hs = (t < 2 ? cc.h.x : cc.h.y) >> (2 * (t % 2));
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const uint32_t q = ((ws[t] >> (2 * p)) & 0x03030303u) | hi_bytes3(hs, p);
+      float& acc = (p & 1) ? a1 : a0;
+      acc = fmaf(ub0(q), xc.v[16 * t + 4 * p + 0], acc);
+      acc = fmaf(ub1(q), xc.v[16 * t + 4 * p + 1], acc);
+      acc = fmaf(ub2(q), xc.v[16 * t + 4 * p + 2], acc);
+      acc = fmaf(ub3(q), xc.v[16 * t + 4 * p + 3], acc);
+    }
+  }
+  return a0 + a1;
+}
+
 // Contribution of one chunk to its row: s * sum(q x) + b * sum(x).
 template <int BITS>
-__device__ __forceinline__ float chunk_dot(const uint4& w, uint32_t sb, const XChunk<BITS>& xc) {
-  float qx = chunk_qx<BITS>(w, xc);
+__device__ __forceinline__ float chunk_dot(const CChunk<BITS>& cc, uint32_t sb, const XChunk<BITS>& xc) {
+  float qx;
+  if constexpr (BITS == 3) qx = chunk_qx3(cc, xc);
+  else qx = chunk_qx<BITS>(cc.w, xc);
   return fmaf(bf16_lo(sb), qx, bf16_hi(sb) * xc.sum);
 }
 

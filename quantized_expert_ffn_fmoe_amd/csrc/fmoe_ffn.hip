@@ -23,7 +23,6 @@ __global__ void __launch_bounds__(256) gate_up_kernel(const uint8_t* __restrict_
   const int rsel = lane / lpr;
   const int n_chunks = cols / C::kCodes;
   const int ngroups = cols / 64;
-  const size_t row_bytes = (size_t)cols * BITS / 8;
 
   XChunk<BITS> xc[CPL];
 #pragma unroll
@@ -36,15 +35,14 @@ __global__ void __launch_bounds__(256) gate_up_kernel(const uint8_t* __restrict_
     const int r = rb + rsel;
     float g = 0.f, u = 0.f;
     if (r < rows) {
-      uint4 wg[CPL], wu[CPL];
+      CChunk<BITS> wg[CPL], wu[CPL];
       uint32_t sg[CPL], su[CPL];
 #pragma unroll
       for (int j = 0; j < CPL; ++j) {
         int c = sub + lpr * j;
         if (c < n_chunks) {
-          const size_t off = code_offset<BITS>(rows, row_bytes, r, (size_t)c * 16);
-          wg[j] = *reinterpret_cast<const uint4*>(gcodes + off);
-          wu[j] = *reinterpret_cast<const uint4*>(ucodes + off);
+          load_cchunk<BITS>(wg[j], gcodes, rows, cols, r, c);
+          load_cchunk<BITS>(wu[j], ucodes, rows, cols, r, c);
           const size_t so = sb_offset(rows, ngroups, r, c / C::kPerGroup);
           sg[j] = gsb[so];
           su[j] = usb[so];
@@ -67,7 +65,7 @@ __global__ void __launch_bounds__(256) gate_up_kernel(const uint8_t* __restrict_
 
 int launch_expert_ffn(const fmoe_expert& e, const float* x, float* y, float* a_ws, hipStream_t s) {
   const int rows = e.gate.rows, cols = e.gate.cols, bits = e.gate.bits;
-  const int n_chunks = cols * bits / 128;
+  const int n_chunks = cols / (bits == 4 ? 32 : 64);
   int lpr = 1;
   while (lpr < n_chunks && lpr < 64) lpr <<= 1;
   const int cpl = (n_chunks + lpr - 1) / lpr;
@@ -83,6 +81,11 @@ int launch_expert_ffn(const fmoe_expert& e, const float* x, float* y, float* a_w
     if (cpl == 1) FMOE_GU(4, 1);
     else if (cpl == 2) FMOE_GU(4, 2);
     else if (cpl <= 4) FMOE_GU(4, 4);
+    else return FMOE_ERR_SHAPE;
+  } else if (bits == 3) {
+    if (cpl == 1) FMOE_GU(3, 1);
+    else if (cpl == 2) FMOE_GU(3, 2);
+    else if (cpl <= 4) FMOE_GU(3, 4);
     else return FMOE_ERR_SHAPE;
   } else {
     if (cpl == 1) FMOE_GU(2, 1);

@@ -1,4 +1,4 @@
-// fmoe_intdot.h -- integer dot products of 4-bit / 2-bit codes with block-fixed-point
+// fmoe_intdot.h -- integer dot products of 4-bit / 3-bit / 2-bit codes with block-fixed-point
 // activations (gfx950 v_dot8_u32_u4: eight 4-bit x 4-bit products summed into 32 bits).
 //
 // Per chunk of activation values (the columns one 16-byte code chunk covers: 32 at 4
@@ -58,9 +58,14 @@ __device__ __forceinline__ void load_dchunk(DChunk<BITS>& dc, const DigitStore& 
   dc.xsum = st.xsum[c];
 }
 
-// sum_j q_j x_j of one chunk of codes, via the digit image.
+// sum_j q_j x_j of one chunk of codes, via the digit image. 3 bits: the code dwords are the
+// low plane's (2-bit order) and the high-plane word of a dword's 32-column half, shifted by
+// 2 (t % 2), has the third bit of nibble n of the even operand at bit 4n and of the odd one
+// at 4n + 1 (fmoe_layout.h, hi_bit): one shift and an and-or make each operand's nibbles the
+// full 3-bit codes, and the digit sets are those of 2 bits.
 template <int BITS>
-__device__ __forceinline__ float chunk_qx_int(const uint4& w, const DChunk<BITS>& dc) {
+__device__ __forceinline__ float chunk_qx_int(const CChunk<BITS>& cc, const DChunk<BITS>& dc) {
+  const uint4& w = cc.w;
   const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
   uint32_t D[6] = {0, 0, 0, 0, 0, 0};
   uint32_t N = 0;
@@ -74,8 +79,13 @@ __device__ __forceinline__ float chunk_qx_int(const uint4& w, const DChunk<BITS>
   } else {
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
-      const uint32_t ev = and_opaque(ws[t], 0x33333333u);
-      const uint32_t od = (ws[t] >> 2) & 0x33333333u;
+      uint32_t ev = and_opaque(ws[t], 0x33333333u);
+      uint32_t od = (ws[t] >> 2) & 0x33333333u;
+      if constexpr (BITS == 3) {
+        const uint32_t hs = (t < 2 ? cc.h.x : cc.h.y) >> (2 * (t % 2));
+        ev |= (hs << 2) & 0x44444444u;
+        od |= (hs << 1) & 0x44444444u;
+      }
 #pragma unroll
       for (int k = 0; k < 6; ++k) {
         D[k] = __builtin_amdgcn_udot8(ev, dc.d[(2 * t) * 6 + k], D[k], false);
@@ -91,8 +101,8 @@ __device__ __forceinline__ float chunk_qx_int(const uint4& w, const DChunk<BITS>
 }
 
 template <int BITS>
-__device__ __forceinline__ float chunk_dot_int(const uint4& w, uint32_t sb, const DChunk<BITS>& dc) {
-  return fmaf(bf16_lo(sb), chunk_qx_int<BITS>(w, dc), bf16_hi(sb) * dc.xsum);
+__device__ __forceinline__ float chunk_dot_int(const CChunk<BITS>& cc, uint32_t sb, const DChunk<BITS>& dc) {
+  return fmaf(bf16_lo(sb), chunk_qx_int<BITS>(cc, dc), bf16_hi(sb) * dc.xsum);
 }
 
 // Six 4-bit digit words of 8 values: word k holds nibble k of u[p] in nibble p (an 8 x 8

@@ -28,7 +28,7 @@ namespace fmoe {
 
 template <int BITS>
 struct CodeLayout {
-  static_assert(BITS == 4 || BITS == 2, "4-bit or 2-bit codes");
+  static_assert(BITS == 4 || BITS == 2, "4-bit or 2-bit codes (a 3-bit matrix's low plane is laid out as 2-bit)");
   static constexpr int kBlockRows = 32;  // measured against 16, 64 and 256 rows: best for the batched kernels
   static constexpr int kPieceBytes = BITS * 32;  // 4 groups of 64 columns
   static constexpr int kSubRows = 1024 / kPieceBytes;  // rows of one contiguous KB
@@ -63,5 +63,32 @@ __host__ __device__ __forceinline__ size_t sb_offset(int rows, int groups, int r
   const int pg = groups - p * PG < PG ? groups - p * PG : PG;  // groups of this piece
   return (size_t)r0 * groups + (size_t)p * nr * PG + (size_t)(r - r0) * pg + g % PG;
 }
+
+// 3-bit codes are stored as two planes. The low plane holds the low 2 bits of every code
+// laid out exactly as a 2-bit matrix of the same shape (code_offset<2> with row bytes
+// cols / 4), so every 2-bit reader takes it as it is. The high plane follows it and holds
+// the third bit of every code, one uint32 per 32 columns (two per group), blocked like the
+// scale/bias words with two words per group: blocks of 32 rows, each row's words cut into
+// pieces of 4 groups (32 bytes), piece p of the block's rows stored together in row order.
+// A 4-group stage of 32 rows is one contiguous KB, and the two words of one (row, group)
+// are one 8-byte load. Word offset of word h (0, 1) of group g of row r:
+__host__ __device__ __forceinline__ size_t hi_offset(int rows, int groups, int r, int g, int h) {
+  constexpr int RB = 32, PG = 4;
+  const int r0 = r / RB * RB;
+  const int nr = rows - r0 < RB ? rows - r0 : RB;
+  const int p = g / PG;
+  const int pg = groups - p * PG < PG ? groups - p * PG : PG;
+  return (size_t)r0 * groups * 2 + (size_t)p * nr * PG * 2 + (size_t)(r - r0) * pg * 2 + (size_t)(g % PG) * 2 + h;
+}
+// Bit of column c (0..31 of a high-plane word's 32 columns) in that word. The columns of a
+// 16-column code dword t = c / 16 are split into even and odd ones as the integer dot
+// product takes them (operand s = 2 t + c % 2, nibble n = (c % 16) / 2), and the bit sits
+// at 4 n + s: then (word >> s) & 0x11111111 puts the high bits of operand s in its nibbles,
+// and for the matrix-core unpack, whose byte m after a shift by 2 r holds column
+// 16 t + 4 m + r, (word >> (2 t)) has that column's bit at 8 m + 4 (r / 2) + r % 2.
+__host__ __device__ constexpr int hi_bit(int c) { return 4 * ((c % 16) / 2) + 2 * (c / 16) + (c % 2); }
+
+// Bytes of the low plane of a 3-bit matrix (the high plane starts there).
+__host__ __device__ __forceinline__ size_t lo_plane_bytes(int rows, int cols) { return (size_t)rows * cols / 4; }
 
 }  // namespace fmoe

@@ -17,7 +17,7 @@ namespace fmoe {
 // registers, so taking several row blocks per pass spreads that load over more weights.
 template <int BITS, int CPL, int R>
 struct MvPass {
-  uint4 w[R][CPL];
+  CChunk<BITS> w[R][CPL];
   uint32_t s[R][CPL];
 };
 
@@ -28,7 +28,6 @@ __device__ __forceinline__ void mv_load(MvPass<BITS, CPL, R>& P, const uint8_t* 
   const int lane = threadIdx.x & 63;
   const int rpw = kWave / lpr, sub = lane & (lpr - 1), rsel = lane / lpr;
   const int n_chunks = cols / C::kCodes, ngroups = cols / 64;
-  const size_t row_bytes = (size_t)cols * BITS / 8;
 #pragma unroll
   for (int u = 0; u < R; ++u) {
     const int r = rb0 + u * rpw + rsel;
@@ -37,7 +36,7 @@ __device__ __forceinline__ void mv_load(MvPass<BITS, CPL, R>& P, const uint8_t* 
       for (int j = 0; j < CPL; ++j) {
         int c = sub + lpr * j;
         if (c < n_chunks) {
-          P.w[u][j] = *reinterpret_cast<const uint4*>(codes + code_offset<BITS>(rows, row_bytes, r, (size_t)c * 16));
+          load_cchunk<BITS>(P.w[u][j], codes, rows, cols, r, c);
           P.s[u][j] = sb[sb_offset(rows, ngroups, r, c / C::kPerGroup)];
         }
       }
@@ -109,14 +108,29 @@ __global__ void __launch_bounds__(256) matvec_kernel(const uint8_t* __restrict__
   const int span = R * (kWave / lpr);
   const float* xv = x + (size_t)blockIdx.y * cols;
   float* yv = y + (size_t)blockIdx.y * rows;
+  const int waves_total = gridDim.x * (blockDim.x >> 6);
+  const int rb0 = (blockIdx.x * (blockDim.x >> 6) + wave) * span;
+  if (rb0 >= rows) return;  // uniform over the wave
   XChunk<BITS> xc[CPL];
+  if (rb0 + waves_total * span >= rows) {
+    // one pass for this wave (small matrices): its weight loads go out before x is read,
+    // so the two memory latencies overlap instead of adding up
+    MvPass<BITS, CPL, R> P;
+    mv_load<BITS, CPL, R>(P, codes, sb, rows, cols, lpr, rb0);
+#pragma unroll
+    for (int j = 0; j < CPL; ++j) {
+      int c = sub + lpr * j;
+      if (c < n_chunks) load_xchunk<BITS>(xc[j], xv + (size_t)c * C::kCodes);
+    }
+    mv_reduce<BITS, CPL, R>(P, yv, rows, cols, lpr, rb0, xc);
+    return;
+  }
 #pragma unroll
   for (int j = 0; j < CPL; ++j) {
     int c = sub + lpr * j;
     if (c < n_chunks) load_xchunk<BITS>(xc[j], xv + (size_t)c * C::kCodes);
   }
-  const int waves_total = gridDim.x * (blockDim.x >> 6);
-  for (int rb = (blockIdx.x * (blockDim.x >> 6) + wave) * span; rb < rows; rb += waves_total * span)
+  for (int rb = rb0; rb < rows; rb += waves_total * span)
     matvec_pass<BITS, CPL, R>(codes, sb, yv, rows, cols, lpr, rb, xc);
 }
 // Several matrices applied to one input (openclawradar.com "Optimisations efficaces": the
@@ -244,22 +258,40 @@ __global__ void __launch_bounds__(64) topk_kernel(const float* __restrict__ logi
 }
 
 // ------------------------------------------------------------------ host launchers
+// Launch shape of the matvec kernels (any multiple of 64 threads up to 256 per workgroup;
+// a wave walks its passes by its global wave index). A call with fewer waves than about
+// four per compute unit uses one-wave workgroups, so that its waves spread over all the
+// compute units instead of filling a quarter of them with four-wave workgroups (a
+// 1024 x 4096 4-bit matrix is 256 waves of one pass each).
+void mv_grid(int total_waves, int waves_per_vec, int* threads, int* blocks) {
+  const int per_wg = total_waves < 1024 ? 1 : 4;
+  *threads = 64 * per_wg;
+  int b = (waves_per_vec + per_wg - 1) / per_wg;
+  const int cap = per_wg == 1 ? 8192 : 2048;
+  *blocks = b > cap ? cap : b;
+}
+
 int launch_matvec(const QMat& W, const float* x, float* y, int n_vec, hipStream_t s) {
-  const int n_chunks = W.cols * W.bits / 128;
+  const int n_chunks = W.cols / (W.bits == 4 ? 32 : 64);  // 16-byte (low-plane) chunks per row
   int lpr = 1;
   while (lpr < n_chunks && lpr < 64) lpr <<= 1;
   const int cpl = (n_chunks + lpr - 1) / lpr;
   const int span = (cpl >= 3 ? 2 : 4) * (64 / lpr);  // rows of a wave pass (mv_pass_blocks of the CPL run)
   const int waves_needed = (W.rows + span - 1) / span;
-  int blocks = (waves_needed + 3) / 4;
-  if (blocks > 2048) blocks = 2048;
+  int threads = 0, blocks = 0;
+  mv_grid(waves_needed * n_vec, waves_needed, &threads, &blocks);
   dim3 grid(blocks, n_vec);
   const uint8_t* codes = static_cast<const uint8_t*>(W.codes);
-#define FMOE_MV(B, C) hipLaunchKernelGGL((matvec_kernel<B, C>), grid, dim3(256), 0, s, codes, W.sb, x, y, W.rows, W.cols, lpr)
+#define FMOE_MV(B, C) hipLaunchKernelGGL((matvec_kernel<B, C>), grid, dim3(threads), 0, s, codes, W.sb, x, y, W.rows, W.cols, lpr)
   if (W.bits == 4) {
     if (cpl == 1) FMOE_MV(4, 1);
     else if (cpl == 2) FMOE_MV(4, 2);
     else if (cpl <= 4) FMOE_MV(4, 4);
+    else return FMOE_ERR_SHAPE;
+  } else if (W.bits == 3) {
+    if (cpl == 1) FMOE_MV(3, 1);
+    else if (cpl == 2) FMOE_MV(3, 2);
+    else if (cpl <= 4) FMOE_MV(3, 4);
     else return FMOE_ERR_SHAPE;
   } else {
     if (cpl == 1) FMOE_MV(2, 1);
@@ -273,7 +305,7 @@ int launch_matvec(const QMat& W, const float* x, float* y, int n_vec, hipStream_
 
 int launch_matvec_multi(const QMat* W, int n_mats, const float* x, float* const* y, int n_vec, hipStream_t s) {
   const int cols = W[0].cols, bits = W[0].bits;
-  const int n_chunks = cols * bits / 128;
+  const int n_chunks = cols / (bits == 4 ? 32 : 64);
   int lpr = 1;
   while (lpr < n_chunks && lpr < 64) lpr <<= 1;
   const int cpl = (n_chunks + lpr - 1) / lpr;
@@ -290,14 +322,19 @@ int launch_matvec_multi(const QMat* W, int n_mats, const float* x, float* const*
     P.prow[i + 1] = P.prow[i] + (i < n_mats ? (W[i].rows + span - 1) / span * span : 0);
   }
   const int waves_needed = P.prow[n_mats] / span;
-  int blocks = (waves_needed + 3) / 4;
-  if (blocks > 2048) blocks = 2048;
+  int threads = 0, blocks = 0;
+  mv_grid(waves_needed * n_vec, waves_needed, &threads, &blocks);
   dim3 grid(blocks, n_vec);
-#define FMOE_MV(B, C) hipLaunchKernelGGL((matvec_multi_kernel<B, C>), grid, dim3(256), 0, s, P, x, cols, lpr)
+#define FMOE_MV(B, C) hipLaunchKernelGGL((matvec_multi_kernel<B, C>), grid, dim3(threads), 0, s, P, x, cols, lpr)
   if (bits == 4) {
     if (cpl == 1) FMOE_MV(4, 1);
     else if (cpl == 2) FMOE_MV(4, 2);
     else if (cpl <= 4) FMOE_MV(4, 4);
+    else return FMOE_ERR_SHAPE;
+  } else if (bits == 3) {
+    if (cpl == 1) FMOE_MV(3, 1);
+    else if (cpl == 2) FMOE_MV(3, 2);
+    else if (cpl <= 4) FMOE_MV(3, 4);
     else return FMOE_ERR_SHAPE;
   } else {
     if (cpl == 1) FMOE_MV(2, 1);
@@ -309,8 +346,54 @@ int launch_matvec_multi(const QMat* W, int n_mats, const float* x, float* const*
   return hipGetLastError() == hipSuccess ? FMOE_OK : FMOE_ERR_HIP;
 }
 
+// 3-bit canonical codes -> the two planes of fmoe_layout.h: one (row, group) per thread
+// step. The group's 24 canonical bytes hold its 64 codes as a little-endian bit stream
+// (column c at bits 3c..3c+2); the low 2 bits go to the low plane's 16-byte chunk in the
+// 2-bit order (column c at bits 2c), the third bits to the group's two high-plane words at
+// hi_bit(c % 32) of word c / 32. Scale and bias words as for the other widths.
+__global__ void pack3_kernel(const uint8_t* __restrict__ codes_in, const uint16_t* __restrict__ scale,
+                             const uint16_t* __restrict__ bias, uint8_t* __restrict__ codes_out,
+                             uint32_t* __restrict__ sb_out, int rows, int cols) {
+  const int groups = cols / 64;
+  const size_t n_groups = (size_t)rows * groups;
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  const size_t row_bytes = (size_t)cols * 3 / 8, lo_row_bytes = (size_t)cols / 4;
+  uint32_t* hi = reinterpret_cast<uint32_t*>(codes_out + lo_plane_bytes(rows, cols));
+  for (size_t i = blockIdx.x * (size_t)blockDim.x + threadIdx.x; i < n_groups; i += stride) {
+    const int r = (int)(i / groups), g = (int)(i % groups);
+    sb_out[sb_offset(rows, groups, r, g)] = (uint32_t)scale[i] | ((uint32_t)bias[i] << 16);
+    const uint64_t* src = reinterpret_cast<const uint64_t*>(codes_in + (size_t)r * row_bytes + (size_t)g * 24);
+    const uint64_t s0 = src[0], s1 = src[1], s2 = src[2];
+    uint32_t lo[4] = {0u, 0u, 0u, 0u}, hw[2] = {0u, 0u};
+#pragma unroll
+    for (int c = 0; c < 64; ++c) {
+      const int b = 3 * c;  // first bit of column c in the 192-bit stream s0 | s1 << 64 | s2 << 128
+      uint32_t q;
+      if (b + 3 <= 64) q = (uint32_t)(s0 >> b);
+      else if (b < 64) q = (uint32_t)((s0 >> b) | (s1 << (64 - b)));
+      else if (b + 3 <= 128) q = (uint32_t)(s1 >> (b - 64));
+      else if (b < 128) q = (uint32_t)((s1 >> (b - 64)) | (s2 << (128 - b)));
+      else q = (uint32_t)(s2 >> (b - 128));
+      q &= 7u;
+      lo[c / 16] |= (q & 3u) << (2 * (c % 16));
+      hw[c / 32] |= (q >> 2) << hi_bit(c % 32);
+    }
+    *reinterpret_cast<uint4*>(codes_out + code_offset<2>(rows, lo_row_bytes, r, (size_t)g * 16)) =
+        make_uint4(lo[0], lo[1], lo[2], lo[3]);
+    *reinterpret_cast<uint2*>(hi + hi_offset(rows, groups, r, g, 0)) = make_uint2(hw[0], hw[1]);
+  }
+}
+
 int launch_pack(const uint8_t* codes_in, const uint16_t* scale, const uint16_t* bias, int rows, int cols, int bits,
                 void* codes_out, uint32_t* sb_out, hipStream_t s) {
+  if (bits == 3) {
+    const size_t n_groups = (size_t)rows * (cols / 64);
+    size_t blocks = (n_groups + 255) / 256;
+    if (blocks > 65536) blocks = 65536;
+    hipLaunchKernelGGL(pack3_kernel, dim3((unsigned)blocks), dim3(256), 0, s, codes_in, scale, bias,
+                       static_cast<uint8_t*>(codes_out), sb_out, rows, cols);
+    return hipGetLastError() == hipSuccess ? FMOE_OK : FMOE_ERR_HIP;
+  }
   size_t n_code16 = (size_t)rows * cols * bits / 8 / 16;
   size_t n_groups = (size_t)rows * (cols / 64);
   size_t work = n_code16 > n_groups ? n_code16 : n_groups;

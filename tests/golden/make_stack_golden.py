@@ -9,7 +9,7 @@ For each kept draw the file stores the draw index, the experts and weights per l
 margins and the output h after the last layer (fp64).
 
 Calls only the oracle and the input generator. Usage:
-    python tests/golden/make_stack_golden.py --bits 4 --tokens 4
+    python tests/golden/make_stack_golden.py --bits 4 --tokens 4   (also --bits 2, --bits 3)
 """
 import argparse
 import os

@@ -106,3 +106,33 @@ class DevStack:
 
     def provider(self):
         return synth.Provider(self.seed, self.H, self.I, self.bits)
+
+
+def check_stack_layers(stack, x, k, h_stack, tol=1e-5):
+    """Every layer of a pre-normed stack against the oracle layer applied to the kernel's own
+    input to it (fmoe_moe_layer runs of the first l + 1 layers): experts bit-exact, routing
+    weights and output within tol. A stack's fp32 error can be amplified by later layers
+    (the synthetic layers change h by orders of magnitude), so the bar is applied layer by
+    layer; the last run is the whole stack, compared bit for bit with h_stack."""
+    import oracle
+
+    prov = stack.provider()
+    wsb = fm.workspace_bytes(fm.OP_MOE_LAYER, 1, stack.H, stack.I, stack.E, k)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device="cuda")
+    h_in = x.astype(np.float32)
+    for l in range(stack.L):
+        sub = fm.layers_array([stack.layers[j] for j in range(l + 1)])
+        hd = torch.empty(stack.H, dtype=torch.float32, device="cuda")
+        idx = torch.empty((l + 1, k), dtype=torch.int32, device="cuda")
+        w = torch.empty((l + 1, k), dtype=torch.float32, device="cuda")
+        fm.moe_layer(sub, to_dev(x.astype(np.float32)), hd, 1, k, 1e-6, fm.PRENORM, idx, w, ws, wsb)
+        torch.cuda.synchronize()
+        h_l = hd.cpu().numpy()
+        want, i_l, w_l, _ = oracle.moe_layer(prov, l, stack.routers_np[l], h_in.astype(np.float64), stack.I, k,
+                                             stack.bits, 64, 1, 1e-6,
+                                             shared_gate=None if stack.gates_np is None else stack.gates_np[l])
+        assert idx.cpu().numpy()[l].tolist() == i_l.tolist(), l
+        assert rel_l2(w.cpu().numpy()[l], w_l) <= tol, l
+        assert rel_l2(h_l, want) <= tol, l
+        h_in = h_l
+    assert np.array_equal(h_in, h_stack)

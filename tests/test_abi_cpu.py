@@ -45,8 +45,20 @@ def test_format_sizes_match_pages():
     assert abs(60 * 512 * e2 / 1e9 - 120.8) < 0.05
     assert fm.codes_bytes(1024, 4096, 4) == 2_097_152
     assert fm.sb_bytes(1024, 4096) == 262_144
-    assert fm.codes_bytes(1024, 4096, 3) == 0
+    assert fm.codes_bytes(1024, 4096, 5) == 0
     assert fm.expert_bytes(4096, 1000, 4) == 0
+
+
+def test_format_sizes_3bit():
+    """3-bit experts (openclawradar.com, 'Optimisations efficaces': 3-bit experts about 23%
+    smaller than 4-bit): 3/8 byte per weight plus the same bf16 (s, b) per 64 weights gives
+    5,505,024 bytes per expert, 22.2% below the 4-bit 7,077,888 (the page's 23% rounds a
+    comparison whose 4-bit baseline it does not give); 60 x 512 experts = 169.1 GB."""
+    e3 = fm.expert_bytes(4096, 1024, 3)
+    assert fm.codes_bytes(1024, 4096, 3) == 1024 * 4096 * 3 // 8 == 1_572_864
+    assert e3 == 5_505_024
+    assert 0.215 < 1 - e3 / fm.expert_bytes(4096, 1024, 4) < 0.235
+    assert abs(60 * 512 * e3 / 1e9 - 169.1) < 0.05
     assert fm.sb_bytes(10, 128, 32) == 0
 
 
@@ -58,7 +70,7 @@ def test_expert_view_offsets():
     assert e.gate.sb == FAKE + 3 * cb and e.up.sb == FAKE + 3 * cb + sb and e.down.sb == FAKE + 3 * cb + 2 * sb
     assert (e.gate.rows, e.gate.cols, e.down.rows, e.down.cols) == (I, H, H, I)
     with pytest.raises(fm.FmoeError) as ei:
-        fm.expert_view(FAKE, H, I, 3)
+        fm.expert_view(FAKE, H, I, 5)
     assert ei.value.status == fm.ERR_BITS
 
 
@@ -111,7 +123,8 @@ def test_matvec_validation():
     W = fm.qmat(FAKE, FAKE, 1024, 4096, 4)
     _raises(fm.ERR_NULL, fm.dequant_matvec, fm.qmat(None, FAKE, 4, 64, 4), FAKE, FAKE, stream=0)
     _raises(fm.ERR_NULL, fm.dequant_matvec, W, None, FAKE, stream=0)
-    _raises(fm.ERR_BITS, fm.dequant_matvec, fm.qmat(FAKE, FAKE, 4, 64, 3), FAKE, FAKE + 4096, stream=0)
+    _raises(fm.ERR_BITS, fm.dequant_matvec, fm.qmat(FAKE, FAKE, 4, 64, 5), FAKE, FAKE + 4096, stream=0)
+    _raises(fm.ERR_BITS, fm.dequant_matvec, fm.qmat(FAKE, FAKE, 4, 64, 1), FAKE, FAKE + 4096, stream=0)
     _raises(fm.ERR_GROUP, fm.dequant_matvec, fm.qmat(FAKE, FAKE, 4, 64, 4, 32), FAKE, FAKE + 4096, stream=0)
     _raises(fm.ERR_SHAPE, fm.dequant_matvec, fm.qmat(FAKE, FAKE, 4, 96, 4), FAKE, FAKE + 4096, stream=0)
     _raises(fm.ERR_SHAPE, fm.dequant_matvec, fm.qmat(FAKE, FAKE, 0, 64, 4), FAKE, FAKE + 4096, stream=0)
@@ -133,7 +146,8 @@ def test_matvec_multi_validation():
     _raises(fm.ERR_SHAPE, mv, [k] * 9, x, [FAKE + (i + 2 << 26) for i in range(9)], stream=0)
     _raises(fm.ERR_SHAPE, mv, [q, fm.qmat(FAKE, FAKE, 512, 2048, 4)], x, ys[:2], stream=0)  # cols differ
     _raises(fm.ERR_SHAPE, mv, [q, fm.qmat(FAKE, FAKE, 512, 4096, 2)], x, ys[:2], stream=0)  # bits differ
-    _raises(fm.ERR_BITS, mv, [q, fm.qmat(FAKE, FAKE, 512, 4096, 3)], x, ys[:2], stream=0)
+    _raises(fm.ERR_BITS, mv, [q, fm.qmat(FAKE, FAKE, 512, 4096, 5)], x, ys[:2], stream=0)
+    _raises(fm.ERR_SHAPE, mv, [q, fm.qmat(FAKE, FAKE, 512, 4096, 3)], x, ys[:2], stream=0)  # bits differ
     _raises(fm.ERR_NULL, mv, [q, k, k], None, ys, stream=0)
     _raises(fm.ERR_NULL, mv, [q, k, k], x, [ys[0], None, ys[2]], stream=0)
     _raises(fm.ERR_ALIGN, mv, [q, k, k], x, [ys[0], ys[1] + 4, ys[2]], stream=0)
@@ -210,8 +224,10 @@ def test_moe_layer_validation():
     _raises(fm.ERR_SHAPE, call, layers=[L4])
     L5 = fm.Layer(None, 1 << 32, stride, E, H, I, 4, 64)
     _raises(fm.ERR_NULL, call, layers=[L5])
-    L6 = fm.Layer(FAKE, 1 << 32, stride, E, H, I, 3, 64)
+    L6 = fm.Layer(FAKE, 1 << 32, stride, E, H, I, 5, 64)
     _raises(fm.ERR_BITS, call, layers=[L6])
+    L6b = fm.Layer(FAKE, 1 << 32, stride, E, H, I, 3, 64)
+    _raises(fm.ERR_BITS, call, layers=[L, L6b])  # widths differ between layers
     L7 = fm.Layer(FAKE, 1 << 32, stride, E, H, I, 4, 128)
     _raises(fm.ERR_GROUP, call, layers=[L7])
 
@@ -232,7 +248,7 @@ def test_batched_validation():
     # inspection of a16
     out = FAKE + (5 << 30)
     _raises(fm.ERR_NULL, fm.batched_a16, None, wsb, T, H, I, E, k, 4, out, stream=0)
-    _raises(fm.ERR_BITS, fm.batched_a16, ws, wsb, T, H, I, E, k, 3, out, stream=0)
+    _raises(fm.ERR_BITS, fm.batched_a16, ws, wsb, T, H, I, E, k, 5, out, stream=0)
     _raises(fm.ERR_SHAPE, fm.batched_a16, ws, wsb, 1, H, I, E, k, 4, out, stream=0)
     _raises(fm.ERR_SHAPE, fm.batched_a16, ws, wsb, T, H, I + 64, E, k, 4, out, stream=0)
     _raises(fm.ERR_K, fm.batched_a16, ws, wsb, T, H, I, E, 0, 4, out, stream=0)

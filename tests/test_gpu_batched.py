@@ -127,6 +127,9 @@ def check_layer(st: DevStack, X: np.ndarray, k: int, prenorm: bool, layer: int =
     (32, 512, 256, 16, 9, 4),   # k = 16
     (4, 512, 128, 4, 80, 4),    # k = E: every expert gets 80 tokens (two passes of 64)
     (4, 512, 128, 4, 80, 2),
+    (64, 512, 256, 4, 37, 3),   # 3-bit codes (two planes)
+    (32, 768, 384, 2, 2, 3),    # 3 bits, down with 6 groups: two-group stages
+    (4, 512, 128, 4, 80, 3),
 ])
 def test_batched_layer(E, H, I, k, T, bits):
     st = DevStack(1, E, H, I, bits)
@@ -185,6 +188,14 @@ def test_batched_full_size_2bit():
     check_layer(st, X, 4, prenorm=False, label="full size 2-bit")
 
 
+def test_batched_full_size_3bit():
+    """3-bit experts at the full layer shape: 24 tokens through one 512-expert layer (hidden
+    4096, inter 1024)."""
+    st = DevStack(1, 512, 4096, 1024, 3, gpu_fill=True)
+    X, _ = accepted_tokens(st.routers_np[0], 24, 4)
+    check_layer(st, X, 4, prenorm=False, label="full size 3-bit")
+
+
 def test_decode_after_batched_on_one_workspace():
     """A multi-token call leaves a workspace ready for single-token calls: the decode kernel's
     synchronization state sits apart from the multi-token scratch, so a decode after a
@@ -233,6 +244,7 @@ def test_batched_full_size_planted():
     (64, 512, 256, 4, 37, 4, False),
     (32, 512, 256, 2, 20, 2, True),
     (16, 768, 384, 15, 9, 4, False),   # k + 1 = 16 slots
+    (32, 512, 256, 4, 20, 3, True),
 ])
 def test_batched_shared_expert(E, H, I, k, T, bits, prenorm):
     """The multi-token path with a shared expert (blob index E, weight sigmoid(gate . v)):

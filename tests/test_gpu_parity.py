@@ -14,7 +14,7 @@ import torch
 import oracle
 import quantized_expert_ffn_fmoe_amd as fm
 import synth
-from gpu_util import DevMatrix, DevStack, rel_l2, to_dev
+from gpu_util import DevMatrix, DevStack, check_stack_layers, rel_l2, to_dev
 
 pytestmark = pytest.mark.gpu
 TOL = 1e-5
@@ -68,6 +68,69 @@ def _sb_layout_offset(rows, groups, r, g):
     return r0 * groups + p * nr * 4 + (r - r0) * pg + g % 4
 
 
+def _hi_layout_offset(rows, groups, r, g, h):
+    """Word offset of high-plane word h (0, 1) of group g of row r of a 3-bit matrix, written
+    out independently of the library: blocks of 32 rows, each row's words cut into pieces of
+    4 groups (8 words), piece p of the block's rows stored together in row order; short last
+    pieces and blocks keep their own sizes."""
+    r0 = r // 32 * 32
+    nr = min(32, rows - r0)
+    p = g // 4
+    pg = min(4, groups - p * 4)
+    return r0 * groups * 2 + p * nr * 8 + (r - r0) * pg * 2 + (g % 4) * 2 + h
+
+
+def _hi_bit(c):
+    """Bit of column c (0..31 of a 32-column half group) in its high-plane word: column c of
+    16-column dword t = c // 16 is operand 2t + c % 2, nibble (c % 16) // 2."""
+    return 4 * ((c % 16) // 2) + 2 * (c // 16) + (c % 2)
+
+
+@pytest.mark.parametrize("rows,cols", [(64, 4096), (13, 192), (40, 320), (45, 448), (300, 512), (33, 64)])
+def test_pack_layout_3bit(rows, cols):
+    """3-bit codes: the low 2 bits of every code land where a 2-bit matrix of the same shape
+    puts its codes, the third bits in the high-plane words after it; the two planes take
+    exactly rows * cols * 3 / 8 bytes."""
+    rng = np.random.default_rng(rows * 1000 + cols + 3)
+    row_bytes = cols * 3 // 8
+    canon = rng.integers(0, 256, size=(rows, row_bytes), dtype=np.uint8)
+    ng = rows * cols // 64
+    groups = cols // 64
+    scale = rng.integers(0, 1 << 16, size=ng, dtype=np.uint16)
+    bias = rng.integers(0, 1 << 16, size=ng, dtype=np.uint16)
+    cb = fm.codes_bytes(rows, cols, 3)
+    assert cb == rows * row_bytes
+    out = torch.full((cb + 64,), 0xA5, dtype=torch.uint8, device="cuda")
+    sb = torch.empty(ng, dtype=torch.int32, device="cuda")
+    fm.pack(to_dev(canon), to_dev(scale), to_dev(bias), rows, cols, 3, 64, out, sb)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    assert np.all(got[cb:] == 0xA5)
+    lo_bytes = rows * cols // 4
+    stream = np.unpackbits(canon, axis=1, bitorder="little").reshape(rows, cols, 3)
+    lo2 = np.packbits(stream[:, :, :2].reshape(rows, cols * 2), axis=1, bitorder="little")  # 2-bit canonical
+    want_lo = np.empty(lo_bytes, dtype=np.uint8)
+    for r in range(rows):
+        for b in range(0, cols // 4, 16):
+            o = _layout_offset(2, rows, cols // 4, r, b)
+            want_lo[o:o + 16] = lo2[r, b:b + 16]
+    assert np.array_equal(got[:lo_bytes], want_lo)
+    hi = got[lo_bytes:cb].view(np.uint32)
+    want_hi = np.zeros(rows * groups * 2, dtype=np.uint32)
+    for r in range(rows):
+        for c in range(cols):
+            g, h, cc = c // 64, (c % 64) // 32, c % 32
+            want_hi[_hi_layout_offset(rows, groups, r, g, h)] |= np.uint32(int(stream[r, c, 2]) << _hi_bit(cc))
+    assert np.array_equal(hi, want_hi)
+    sbw = sb.cpu().numpy().view(np.uint32)
+    words = scale.astype(np.uint32) | (bias.astype(np.uint32) << 16)
+    want_sb = np.empty(ng, dtype=np.uint32)
+    for r in range(rows):
+        for g in range(groups):
+            want_sb[_sb_layout_offset(rows, groups, r, g)] = words[r * groups + g]
+    assert np.array_equal(sbw, want_sb)
+
+
 @pytest.mark.parametrize("bits,rows,cols", [(4, 64, 4096), (4, 13, 192), (4, 40, 320), (2, 96, 1024),
                                             (2, 19, 128), (2, 45, 448), (4, 300, 512), (2, 520, 256)])
 def test_pack_layout(bits, rows, cols):
@@ -103,7 +166,7 @@ def test_pack_layout(bits, rows, cols):
     assert np.array_equal(sbw, want_sb)
 
 
-@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("bits", [4, 3, 2])
 def test_gpu_fixture_matches_cpu_generator(bits):
     H, I = 4096, 1024
     for (layer, e0, ne, which) in [(0, 0, 2, 0), (7, 509, 3, 2), (59, 100, 1, 1)]:
@@ -124,7 +187,7 @@ def test_gpu_fixture_matches_cpu_generator(bits):
             assert np.array_equal(b_h[j * ng:(j + 1) * ng], b.ravel())
 
 
-@pytest.mark.parametrize("bits", [4, 2])
+@pytest.mark.parametrize("bits", [4, 3, 2])
 def test_pack_onehot_returns_dequantized_column(bits):
     """Packed layout end to end: one-hot x gives the dequantized column, exactly q*s+b
     rounded once to fp32 (the oracle's exact value rounded to fp32)."""
@@ -155,7 +218,9 @@ def test_matvec_config1():
 
 @pytest.mark.parametrize("rows,cols,bits,n_vec", [
     (1, 64, 4, 1), (3, 192, 4, 2), (37, 320, 2, 1), (100, 2048, 4, 3), (64, 8192, 4, 1),
-    (65, 16384, 2, 1), (513, 1024, 2, 2), (250, 4096, 2, 1), (7, 6144, 4, 1), (1000, 960, 4, 64)])
+    (65, 16384, 2, 1), (513, 1024, 2, 2), (250, 4096, 2, 1), (7, 6144, 4, 1), (1000, 960, 4, 64),
+    (1024, 4096, 3, 1), (3, 192, 3, 2), (37, 320, 3, 1), (100, 2048, 3, 3), (65, 16384, 3, 1), (513, 1024, 3, 2),
+    (1000, 960, 3, 64), (31, 8192, 3, 1)])
 def test_matvec_shapes(rows, cols, bits, n_vec):
     rng = np.random.default_rng(rows * 7 + cols + bits)
     codes, scale, bias = synth.matrix(11, rows, cols, bits, rows, cols, bits)
@@ -172,7 +237,9 @@ def test_matvec_shapes(rows, cols, bits, n_vec):
     ([100, 37, 1], 2048, 2, 3),         # ragged row counts (partial row blocks)
     ([64] * 8, 960, 4, 2),              # the maximum of 8 matrices
     ([5, 300], 16384, 2, 1),
-    ([33], 320, 4, 64)])
+    ([33], 320, 4, 64),
+    ([4096, 512, 512], 4096, 3, 1),
+    ([100, 37, 1], 2048, 3, 3)])
 def test_matvec_multi(rows_list, cols, bits, n_vec):
     """fmoe_dequant_matvec_multi against the oracle's matvec of each matrix, and bit for bit
     against fmoe_dequant_matvec of each matrix alone (same per-row arithmetic)."""
@@ -251,7 +318,8 @@ def test_route_topk(E, H, k, n):
 
 
 # ------------------------------------------------------------------ expert FFN
-@pytest.mark.parametrize("H,I,bits", [(4096, 1024, 4), (4096, 1024, 2), (512, 192, 4), (256, 64, 2)])
+@pytest.mark.parametrize("H,I,bits", [(4096, 1024, 4), (4096, 1024, 2), (512, 192, 4), (256, 64, 2),
+                                      (4096, 1024, 3), (512, 192, 3)])
 def test_expert_ffn(H, I, bits):
     mats = synth.expert(0, 2, 5, H, I, bits)
     dm = [DevMatrix(*mats[m], *((I, H) if m < 2 else (H, I)), bits) for m in range(3)]
@@ -306,19 +374,24 @@ def _stack_tokens(stack, k, n, prenorm=True, start=0):
 
 @pytest.mark.parametrize("L,E,H,I,k,bits", [
     (5, 64, 1024, 256, 4, 4), (4, 64, 1024, 256, 4, 2), (3, 16, 256, 64, 1, 4), (2, 16, 512, 128, 16, 4),
-    (3, 8, 4096, 1024, 4, 4), (2, 300, 2048, 512, 8, 2), (3, 1000, 128, 64, 2, 4)])
+    (3, 8, 4096, 1024, 4, 4), (2, 300, 2048, 512, 8, 2), (3, 1000, 128, 64, 2, 4),
+    (4, 64, 1024, 256, 4, 3), (2, 300, 2048, 512, 8, 3), (3, 16, 256, 64, 1, 3), (2, 40, 8192, 128, 2, 3),
+    (2, 24, 512, 8192, 1, 3)])
 def test_decode_stack(L, E, H, I, k, bits):
+    """Experts of the whole stack bit-exact against the oracle's fp64 trajectory, and every
+    layer within the bar against the oracle layer applied to the kernel's own input to it
+    (gpu_util.check_stack_layers)."""
     stack = DevStack(L, E, H, I, bits)
     for x, ref in _stack_tokens(stack, k, 3):
         h, idx, w = _decode(stack, x, k)
         assert np.array_equal(idx, ref["idx"])
-        assert rel_l2(w, ref["w"]) <= TOL
-        assert rel_l2(h, ref["out"]) <= TOL
+        assert rel_l2(w[0], ref["w"][0]) <= TOL  # the first layer sees the exact input
+        check_stack_layers(stack, x, k, h)
 
 
 @pytest.mark.parametrize("L,E,H,I,k,bits", [
     (3, 64, 1024, 256, 4, 4), (3, 40, 512, 128, 2, 2), (2, 16, 256, 64, 1, 4), (2, 16, 512, 128, 15, 4),
-    (2, 600, 1024, 128, 4, 2)])
+    (2, 600, 1024, 128, 4, 2), (3, 40, 512, 128, 2, 3)])
 def test_decode_shared_expert(L, E, H, I, k, bits):
     """Layers with a shared expert (blob index E) added with weight sigmoid(gate . v): routing
     of the whole stack bit-exact against the oracle stack with the same gates, and every
