@@ -14,7 +14,8 @@ spot check of the full-size stack against stored oracle results, the measured in
 expert reuse, and the CPU oracle's throughput on a small sample (cpu_baseline).
 
 Usage: python bench.py [--gpus 1] [--steps 5] [--warmup 1]
-       [--config stack4|stack2|layer|matvec|batch64|batch64_2bit|qkv4|qkv2] [--top-k K] [--shared]
+       [--config stack4|stack3|stack2|layer|matvec|batch64|batch64_3bit|batch64_2bit|qkv4|qkv2]
+       [--top-k K] [--shared]
 (layer: one MoE layer per call over the 60 distinct layers, us per layer-token; matvec: one
 1024 x 4096 4-bit dequant matvec over a pool of 512 matrices, us per call; batch64: 64 tokens
 through one layer on the grouped path; qkv4 / qkv2: the fused multi-output projection,
@@ -195,12 +196,15 @@ def shared_gates_np():
     return [synth.router(0, 1000 + l, 1, H_)[0] for l in range(L_)] if SHARED else None
 
 
-def live_parity(layers, bits, dev, ws, wsb, n_tokens: int = 2, max_draws: int = 64):
+def live_parity(layers, bits, dev, ws, wsb, n_tokens: int = 2):
     """Parity against the live oracle for workloads without stored results (top-k != 4, a
-    shared expert): the first n_tokens draws whose oracle top-k margin is >= 1e-3 at every
-    layer. Experts of every layer bit-exact; the whole stack within 1e-5 of the oracle's
-    fp64 trajectory, or else (a stack's fp32 error can be amplified by later layers) every
-    layer within 1e-5 of the oracle layer applied to the kernel's own input to it."""
+    shared expert), layer by layer on the kernel's own input: tokens are draws 0..n_tokens-1;
+    for each layer l the kernel's h after layers 0..l is compared with the oracle layer
+    applied to the kernel's h after layers 0..l-1 (experts bit-exact, output within 1e-5)
+    wherever the oracle's top-k margin there is >= 1e-3 (elsewhere the selection is decided
+    by rounding and either choice is right). With top-10 routing few tokens keep that margin
+    through all 60 layers, so the layer is the unit; at least 90% of the layers must be
+    checked."""
     import torch
 
     import oracle
@@ -210,37 +214,33 @@ def live_parity(layers, bits, dev, ws, wsb, n_tokens: int = 2, max_draws: int = 
     routers = [synth.router(0, l, E_, H_) for l in range(L_)]
     gates = shared_gates_np()
     prov = synth.Provider(0, H_, I_, bits)
-    exact, worst_stack, worst_layer, draws = True, 0.0, 0.0, []
-    for d in range(max_draws):
-        if len(draws) == n_tokens:
-            break
+    exact, worst, checked = True, 0.0, 0
+    for d in range(n_tokens):
         x = synth.token(0, d, H_)
-        ref = oracle.stack(prov, routers, x, I_, K_, bits, 64, EPS, stop_margin=1e-3, keep_all=False,
-                           shared_gates=gates)
-        if ref["layers_done"] != L_ or np.min(ref["margins"]) < 1e-3:
-            continue
-        draws.append(d)
         xd = torch.from_numpy(x).to(dev)
-        hs = []
-        for l in range(L_):  # the kernel's h after layers 0..l
+        hs, ids = [], []
+        for l in range(L_):  # the kernel's h and experts after layers 0..l
             h = torch.empty(H_, dtype=torch.float32, device=dev)
             idx = torch.empty((l + 1, K_), dtype=torch.int32, device=dev)
             sub = fm.layers_array([layers[j] for j in range(l + 1)])
             fm.moe_layer(sub, xd, h, 1, K_, EPS, fm.PRENORM, idx, None, ws, wsb)
             torch.cuda.synchronize()
-            hs.append(h.cpu().numpy())
-        exact &= bool(np.array_equal(idx.cpu().numpy(), ref["idx"]))
-        out = hs[-1].astype(np.float64)
-        worst_stack = max(worst_stack, float(np.linalg.norm(out - ref["out"]) / np.linalg.norm(ref["out"])))
+            hs.append(h.cpu().numpy().astype(np.float64))
+            ids.append(idx.cpu().numpy()[l])
         h_in = x.astype(np.float64)
         for l in range(L_):
-            want, _, _, _ = oracle.moe_layer(prov, l, routers[l], h_in, I_, K_, bits, 64, 1, EPS,
-                                             shared_gate=None if gates is None else gates[l])
-            worst_layer = max(worst_layer, float(np.linalg.norm(hs[l] - want) / np.linalg.norm(want)))
-            h_in = hs[l].astype(np.float64)
-    ok = len(draws) == n_tokens and exact and (worst_stack <= 1e-5 or worst_layer <= 1e-5)
-    return {"tokens": len(draws), "draws": draws, "experts_bit_exact": exact, "max_rel_l2": worst_stack,
-            "max_rel_l2_per_layer": worst_layer, "tolerance": 1e-5, "reference": "live oracle", "pass": bool(ok)}
+            want, i_ref, _, m = oracle.moe_layer(prov, l, routers[l], h_in, I_, K_, bits, 64, 1, EPS,
+                                                 shared_gate=None if gates is None else gates[l])
+            if m >= 1e-3:
+                checked += 1
+                exact &= bool(np.array_equal(ids[l], i_ref))
+                worst = max(worst, float(np.linalg.norm(hs[l] - want) / np.linalg.norm(want)))
+            h_in = hs[l]
+    ok = exact and worst <= 1e-5 and checked >= 0.9 * L_ * n_tokens
+    return {"tokens": n_tokens, "draws": list(range(n_tokens)), "layers_checked": checked,
+            "layers_total": L_ * n_tokens, "experts_bit_exact": exact, "max_rel_l2_per_layer": worst,
+            "tolerance": 1e-5, "reference": "live oracle, layer by layer on the kernel's own input",
+            "pass": bool(ok)}
 
 
 def traffic_from_profiles(kernel_tag: str):
@@ -735,8 +735,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=5)
     ap.add_argument("--warmup", type=int, default=1)
-    ap.add_argument("--config", choices=["stack4", "stack2", "layer", "matvec", "batch64", "batch64_2bit", "qkv4",
-                                         "qkv2"], default="stack4")
+    ap.add_argument("--config", choices=["stack4", "stack3", "stack2", "layer", "matvec", "batch64", "batch64_3bit",
+                                         "batch64_2bit", "qkv4", "qkv2"], default="stack4")
     ap.add_argument("--tokens", type=int, default=256)
     ap.add_argument("--top-k", type=int, default=4,
                     help="experts per token for the stack configs (the headline workload is top-4)")
@@ -762,8 +762,8 @@ def main() -> int:
     if args.calibrate_copy:
         return calibrate_copy(torch)
 
-    if args.config in ("batch64", "batch64_2bit"):
-        return run_batch64(args, torch, 4 if args.config == "batch64" else 2)
+    if args.config in ("batch64", "batch64_3bit", "batch64_2bit"):
+        return run_batch64(args, torch, {"batch64": 4, "batch64_3bit": 3, "batch64_2bit": 2}[args.config])
     if args.config in ("qkv4", "qkv2"):
         return run_qkv(args, torch, 4 if args.config == "qkv4" else 2)
     if args.config == "matvec":
@@ -779,7 +779,7 @@ def main() -> int:
     import quantized_expert_ffn_fmoe_amd as fm
     import synth
 
-    bits = 4 if args.config == "stack4" else 2
+    bits = {"stack4": 4, "stack3": 3, "stack2": 2}[args.config]
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     log(f"building {L_}-layer {bits}-bit stack on {torch.cuda.get_device_name(dev)}")
@@ -855,8 +855,7 @@ def main() -> int:
     probe = stream_read_probe(torch)
     log(f"stream-read probe: {probe['gbs']:.0f} GB/s")
     out = {
-        "metric": (METRIC if bits == 4 else METRIC.replace("4-bit", "2-bit")).replace(
-            "4-bit)", f"4-bit, top-{K_})" if K_ != 4 else "4-bit)"),
+        "metric": METRIC.replace("4-bit)", f"{bits}-bit" + (f", top-{K_})" if K_ != 4 else ")")),
         "value": round(tok_s, 2),
         "unit": "tokens/s",
         "n_gpus": 1,

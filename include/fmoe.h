@@ -9,7 +9,7 @@
  *   [radar]  openclawradar.com, "Autoresearch pousse Qwen3.5-397B a 20,34 tok/s sur M5 Max
  *            via le streaming SSD"
  * i.e. an fp32 router over the experts, top-k selection with softmax weights, affine
- * group-quantized (4-bit or 2-bit codes with a bf16 scale and bias per group of 64
+ * group-quantized (4-bit, 3-bit or 2-bit codes with a bf16 scale and bias per group of 64
  * weights) gate/up matvecs with a fused SwiGLU, the down matvec, and the weighted
  * combine plus residual, with an RMS norm between layers.
  *
@@ -29,10 +29,13 @@
  *  - Alignment: codes, sb, activation and output pointers must be 16-byte aligned.
  *
  * Quantized matrix layout (the library's packed layout, produced by fmoe_pack)
- *  - canonical codes (fmoe_pack's input): row-major, rows x (cols*bits/8) bytes. 4-bit:
+ *  - canonical codes (fmoe_pack's input): row-major, rows x (cols*bits/8) bytes; a row is
+ *    a little-endian bit stream with column c in bits bits*c .. bits*c + bits - 1. 4-bit:
  *    byte j of a row holds column 2j in bits 0-3 and column 2j+1 in bits 4-7. 2-bit: byte
- *    j holds column 4j+t in bits 2t..2t+1.
- *  - packed codes: the same rows * cols*bits/8 bytes, regrouped in blocks of 32
+ *    j holds column 4j+t in bits 2t..2t+1. 3-bit ([radar] "Optimisations efficaces": 3-bit
+ *    experts): bytes 3j..3j+2, read as a little-endian 24-bit word, hold column 8j+t in
+ *    bits 3t..3t+2.
+ *  - packed 4-bit and 2-bit codes: the same rows * cols*bits/8 bytes, regrouped in blocks of 32
  *    consecutive rows. Each row is cut into pieces of 4 groups of 64 columns (128 bytes at
  *    4 bits, 64 at 2 bits); piece p of a block's rows is stored contiguously in row order,
  *    at block start + p * rows_in_block * piece bytes (a final block may hold fewer than
@@ -40,6 +43,12 @@
  *    (k + rot) mod (chunks in the piece), rot = r mod 8 (4-bit) or (r mod 16) / 4 (2-bit);
  *    a row that ends in a shorter piece stores it the same way with its own size. 16-byte
  *    chunks keep their canonical contents.
+ *  - packed 3-bit codes: two planes in the same rows * cols * 3 / 8 bytes. The low plane
+ *    (rows * cols / 4 bytes) holds the low 2 bits of every code exactly as the packed codes
+ *    of a 2-bit matrix of the same shape; the high plane follows it with the third bits,
+ *    one uint32 per 32 columns (two per group), blocked like sb (below) with two words per
+ *    group; in the word of columns 32h..32h+31 of a group, column 32h + c (c < 32) is bit
+ *    4 * ((c % 16) / 2) + 2 * (c / 16) + c % 2.
  *  - sb: one uint32 per (row, group); bits 0-15 = bf16 scale s, bits 16-31 = bf16 bias b
  *    of the group; blocked like the codes: blocks of 32 rows, each row's words cut into
  *    pieces of 4 groups, piece p of a block's rows stored together in row order (short
@@ -53,7 +62,8 @@
  *    [gate codes][up codes][down codes][gate sb][up sb][down sb]
  *  gate/up are inter x hidden, down is hidden x inter. At hidden 4096, inter 1024 a
  *  4-bit blob is 7,077,888 bytes (the pages' "about 6.75 MB per expert", [aibit]
- *  "Techniques de rupture" item 1 and [hada] "SSD Expert Streaming"); 2-bit: 3,932,160.
+ *  "Techniques de rupture" item 1 and [hada] "SSD Expert Streaming"); 3-bit: 5,505,024
+ *  (22% less); 2-bit: 3,932,160.
  */
 #ifndef FMOE_H
 #define FMOE_H
@@ -71,7 +81,7 @@ enum fmoe_status {
   FMOE_OK = 0,
   FMOE_ERR_NULL = -1,      /* a required pointer is NULL */
   FMOE_ERR_SHAPE = -2,     /* sizes out of range, not a multiple of 64, or inconsistent */
-  FMOE_ERR_BITS = -3,      /* bits not in {2, 4} */
+  FMOE_ERR_BITS = -3,      /* bits not in {2, 3, 4} */
   FMOE_ERR_GROUP = -4,     /* group != 64 */
   FMOE_ERR_K = -5,         /* k not in 1..min(16, n_experts) */
   FMOE_ERR_ALIGN = -6,     /* a pointer or stride is not 16-byte (stride: 256-byte) aligned */
@@ -161,9 +171,10 @@ int fmoe_workspace_error(const void* ws, size_t ws_bytes, uint32_t* err_out, fmo
 /*
  * y[v][r] = sum_c (q[r][c] * s[r][c/64] + b[r][c/64]) * x[v][c]  for v < n_vec.
  * The dequantized matvec of [aibit] "Techniques de rupture" item 4 (4-bit and 2-bit
- * dequant matvec), computed per group as s * sum(q*x) + b * sum(x) in fp32.
+ * dequant matvec; 3-bit as in [radar] "Optimisations efficaces"), computed per group as
+ * s * sum(q*x) + b * sum(x) in fp32.
  * x: fp32 [n_vec][cols]; y: fp32 [n_vec][rows]; 1 <= n_vec <= 64; cols <= 8192 (4-bit)
- * or 16384 (2-bit). y must not overlap x.
+ * or 16384 (3-bit, 2-bit). y must not overlap x.
  */
 int fmoe_dequant_matvec(const fmoe_qmat* W, const float* x, float* y, int n_vec, fmoe_stream_t stream);
 
