@@ -4,6 +4,7 @@ not part of the fmoe library; bench.py and the profile summaries use them.
 
     python -m measure stream      # JSON line: best read rate over 4 GiB
     python -m measure exchange    # JSON lines: exchange latency per mode and word count
+    python -m measure replicas    # JSON lines: device-wide exchange per replica count / ack wait
 """
 from __future__ import annotations
 
@@ -47,7 +48,7 @@ def lib():
         L.measure_stream_read.restype = i32
         L.measure_stream_read.argtypes = [vp, sz, i32, i32, i32, vp, vp]
         L.measure_exchange.restype = i32
-        L.measure_exchange.argtypes = [i32, i32, i32, u32, vp, vp, vp, vp, vp]
+        L.measure_exchange.argtypes = [i32, i32, i32, u32, vp, vp, vp, vp, i32, i32, vp]
         _lib = L
     return _lib
 
@@ -91,7 +92,8 @@ def stream_read(torch, gib: int = 4, reps: int = 5) -> dict:
             "gbs": round(best, 1), "variants": table}
 
 
-def exchange(torch, mode: int, n_words: int, rounds: int = 200, epoch0: int = 0, buf=None) -> dict:
+def exchange(torch, mode: int, n_words: int, rounds: int = 200, epoch0: int = 0, buf=None, reps: int = 8,
+             no_ack: bool = False) -> dict:
     """Latency of one exchange round (µs): median and 90th percentile over rounds 10.. of the
     spacing between the last workgroup's completion stamps of consecutive rounds, plus the
     spread of completion stamps inside a round and the XCC_ID check of the placement."""
@@ -99,12 +101,12 @@ def exchange(torch, mode: int, n_words: int, rounds: int = 200, epoch0: int = 0,
     G = lib().measure_cus()
     own = buf is None
     if own:
-        buf = torch.zeros(8 * n_words, dtype=torch.int64, device=dev)
+        buf = torch.zeros(max(reps, 8) * n_words, dtype=torch.int64, device=dev)
     t_end = torch.zeros(rounds * G, dtype=torch.int64, device=dev)
     xcc = torch.zeros(G, dtype=torch.int32, device=dev)
     err = torch.zeros(1, dtype=torch.int32, device=dev)
     rc = lib().measure_exchange(mode, n_words, rounds, epoch0, buf.data_ptr(), t_end.data_ptr(), xcc.data_ptr(),
-                                err.data_ptr(), torch.cuda.current_stream(dev).cuda_stream)
+                                err.data_ptr(), reps, int(no_ack), torch.cuda.current_stream(dev).cuda_stream)
     if rc != 0:
         raise RuntimeError(f"measure_exchange: {rc}")
     torch.cuda.synchronize()
@@ -113,7 +115,9 @@ def exchange(torch, mode: int, n_words: int, rounds: int = 200, epoch0: int = 0,
     last = t.max(axis=1)
     per = np.diff(last)[10:]
     spread = (t.max(axis=1) - t.min(axis=1))[10:]
-    return {"mode": mode, "what": MODES[mode], "words": n_words, "rounds": rounds,
+    what = MODES[mode].replace("8 replicas", f"{reps} replicas") + (", polls before its stores are acknowledged"
+                                                                     if no_ack else "")
+    return {"mode": mode, "what": what, "words": n_words, "rounds": rounds, "replicas": reps if mode == 0 else None,
             "round_us_median": round(float(np.median(per)), 3), "round_us_p90": round(float(np.percentile(per, 90)), 3),
             "spread_us_median": round(float(np.median(spread)), 3),
             "xcc_is_g_mod_8": bool(np.all(xc == np.arange(G) % 8)), "gave_up": bool(err.item() != 0)}
@@ -134,6 +138,12 @@ def main(argv) -> int:
                 if n % (G if mode == 0 else G // 8):
                     continue
                 print(json.dumps(exchange(torch, mode, n)), flush=True)
+        return 0
+    if what == "replicas":  # the device-wide exchange's replica count and ack wait
+        for n in (512, 4096):
+            for reps in (1, 2, 4, 8, 16):
+                for no_ack in (False, True):
+                    print(json.dumps(exchange(torch, 0, n, reps=reps, no_ack=no_ack)), flush=True)
         return 0
     print(f"unknown probe {what}", file=sys.stderr)
     return 2

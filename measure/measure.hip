@@ -12,8 +12,8 @@
 //    round (or a later one) and stamps the 100 MHz real-time clock. Round r + 1 starts
 //    from the data of round r, so the spacing of the stamps is the latency of one exchange
 //    including the spread between workgroups. Modes:
-//      0  all workgroups, 8 replicas (replica g mod 8), device-scope accesses (the decode
-//         kernel's exchange);
+//      0  all workgroups, R replicas (replica g mod R), device-scope accesses (the decode
+//         kernel's exchange uses R = 8);
 //      1  the 32 workgroups of one XCD (workgroup g is dispatched to XCD g mod 8), device-
 //         scope accesses;
 //      2  the same groups with workgroup-scope accesses;
@@ -75,14 +75,15 @@ __device__ __forceinline__ void before_poll() {
   if (MODE == 3) asm volatile("buffer_inv sc0" ::: "memory");
 }
 
-// buf: mode 0: [8][n_words]; modes 1-2: [8][n_words] (one region per XCD group).
+// buf: mode 0: [reps][n_words]; modes 1-4: [8][n_words] (one region per XCD group).
 // t_end: [rounds][G] stamps; xcc: [G] XCC_ID of each workgroup; err: set when a wait gave up.
 template <int MODE>
 __global__ void __launch_bounds__(kThreads) exchange_kernel(uint64_t* buf, int n_words, int rounds, uint32_t epoch0,
-                                                            uint64_t* t_end, uint32_t* xcc, uint32_t* err) {
+                                                            uint64_t* t_end, uint32_t* xcc, uint32_t* err, int reps,
+                                                            int no_ack) {
   constexpr int kPoll = 16;
   const int G = gridDim.x, g = blockIdx.x, tid = threadIdx.x;
-  const int grp = g % 8;                      // replica (mode 0) or XCD group (modes 1-2)
+  const int grp = MODE == 0 ? g % reps : g % 8;  // replica (mode 0) or XCD group (modes 1-4)
   const int members = MODE == 0 ? G : G / 8;  // writers of one region
   const int rank = MODE == 0 ? g : g / 8;
   const int per = n_words / members;          // words owned by each writer
@@ -97,13 +98,12 @@ __global__ void __launch_bounds__(kThreads) exchange_kernel(uint64_t* buf, int n
     for (int i = tid; i < per; i += kThreads) {
       const int w = rank * per + i;
       if (MODE == 0) {
-#pragma unroll
-        for (int rr = 0; rr < 8; ++rr) put<MODE>(buf + (size_t)rr * n_words + w, tag | (uint32_t)w);
+        for (int rr = 0; rr < reps; ++rr) put<MODE>(buf + (size_t)rr * n_words + w, tag | (uint32_t)w);
       } else {
         put<MODE>(buf + (size_t)grp * n_words + w, tag | (uint32_t)w);
       }
     }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    if (!no_ack) asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     const uint64_t* src = buf + (size_t)grp * n_words;
     for (int i0 = tid; i0 < n_words; i0 += kThreads * kPoll) {
       uint64_t v[kPoll];
@@ -175,12 +175,15 @@ int measure_stream_read(const void* buf, size_t nbytes, int variant, int unroll,
   return hipGetLastError() == hipSuccess ? 0 : -8;
 }
 
-// Enqueue the exchange probe (see the file comment). buf: 8 * n_words uint64 (zero-filled
+// Enqueue the exchange probe (see the file comment). reps: replicas of mode 0 (1..16; the
+// XCD modes use 8 regions); no_ack: poll without first waiting for the own stores.
+// buf: max(reps, 8) * n_words uint64 (zero-filled
 // before the first call; epoch0 must exceed every round tag of earlier calls on buf);
 // n_words a multiple of the writers of a region (G, or G / 8); t_end: rounds * G uint64;
 // xcc: G uint32; err: one uint32 (0 before the call). G = measure_cus().
 int measure_exchange(int mode, int n_words, int rounds, uint32_t epoch0, void* buf, uint64_t* t_end, uint32_t* xcc,
-                     uint32_t* err, hipStream_t s) {
+                     uint32_t* err, int reps, int no_ack, hipStream_t s) {
+  if (reps < 1 || reps > 16) return -2;
   const int G = measure_cus();
   if (G < 8 || G % 8) return -2;
   if (!buf || !t_end || !xcc || !err || rounds < 1 || n_words < 1) return -1;
@@ -191,23 +194,28 @@ int measure_exchange(int mode, int n_words, int rounds, uint32_t epoch0, void* b
   switch (mode) {
     case 0:
       if ((rc = coresident(exchange_kernel<0>, G))) return rc;
-      hipLaunchKernelGGL(exchange_kernel<0>, dim3(G), dim3(kThreads), 0, s, b, n_words, rounds, epoch0, t_end, xcc, err);
+      hipLaunchKernelGGL(exchange_kernel<0>, dim3(G), dim3(kThreads), 0, s, b, n_words, rounds, epoch0, t_end, xcc, err,
+                         reps, no_ack);
       break;
     case 1:
       if ((rc = coresident(exchange_kernel<1>, G))) return rc;
-      hipLaunchKernelGGL(exchange_kernel<1>, dim3(G), dim3(kThreads), 0, s, b, n_words, rounds, epoch0, t_end, xcc, err);
+      hipLaunchKernelGGL(exchange_kernel<1>, dim3(G), dim3(kThreads), 0, s, b, n_words, rounds, epoch0, t_end, xcc, err,
+                         8, no_ack);
       break;
     case 2:
       if ((rc = coresident(exchange_kernel<2>, G))) return rc;
-      hipLaunchKernelGGL(exchange_kernel<2>, dim3(G), dim3(kThreads), 0, s, b, n_words, rounds, epoch0, t_end, xcc, err);
+      hipLaunchKernelGGL(exchange_kernel<2>, dim3(G), dim3(kThreads), 0, s, b, n_words, rounds, epoch0, t_end, xcc, err,
+                         8, no_ack);
       break;
     case 3:
       if ((rc = coresident(exchange_kernel<3>, G))) return rc;
-      hipLaunchKernelGGL(exchange_kernel<3>, dim3(G), dim3(kThreads), 0, s, b, n_words, rounds, epoch0, t_end, xcc, err);
+      hipLaunchKernelGGL(exchange_kernel<3>, dim3(G), dim3(kThreads), 0, s, b, n_words, rounds, epoch0, t_end, xcc, err,
+                         8, no_ack);
       break;
     case 4:
       if ((rc = coresident(exchange_kernel<4>, G))) return rc;
-      hipLaunchKernelGGL(exchange_kernel<4>, dim3(G), dim3(kThreads), 0, s, b, n_words, rounds, epoch0, t_end, xcc, err);
+      hipLaunchKernelGGL(exchange_kernel<4>, dim3(G), dim3(kThreads), 0, s, b, n_words, rounds, epoch0, t_end, xcc, err,
+                         8, no_ack);
       break;
     default:
       return -2;
