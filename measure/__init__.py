@@ -53,7 +53,7 @@ def lib():
     return _lib
 
 
-def stream_read(torch, gib: int = 4, reps: int = 5) -> dict:
+def stream_read(torch, gib: int = 4, reps: int = 5, variants=(0, 1)) -> dict:
     """Best read rate (GB/s, 1e9 B/s) of the streaming kernel over a gib-GiB buffer, HIP
     events on the launch stream around each pass; plain and non-temporal loads, 4 or 8
     loads in flight per thread, 2 grid sizes; best of `reps` passes per variant after one
@@ -67,7 +67,7 @@ def stream_read(torch, gib: int = 4, reps: int = 5) -> dict:
     stream = torch.cuda.current_stream(dev)
     cus = lib().measure_cus()
     best, table = 0.0, []
-    for variant in (0, 1):
+    for variant in variants:
         for unroll in (4, 8):
             for blocks in (cus * 8, cus * 32):
                 rc = lib().measure_stream_read(buf.data_ptr(), nbytes, variant, unroll, blocks, sink.data_ptr(),
@@ -83,7 +83,8 @@ def stream_read(torch, gib: int = 4, reps: int = 5) -> dict:
                     e1.record(stream)
                     torch.cuda.synchronize()
                     gbs = max(gbs, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
-                table.append({"loads": "non-temporal" if variant else "plain", "in_flight": unroll,
+                table.append({"loads": ("plain", "non-temporal", "LDS-DMA", "non-temporal LDS-DMA")[variant],
+                              "in_flight": unroll,
                               "blocks": blocks, "gbs": round(gbs, 1)})
                 best = max(best, gbs)
     del buf
@@ -130,6 +131,9 @@ def main(argv) -> int:
     what = argv[1] if len(argv) > 1 else "exchange"
     if what == "stream":
         print(json.dumps(stream_read(torch)), flush=True)
+        return 0
+    if what == "stream_lds":  # plain, non-temporal and LDS-DMA reads
+        print(json.dumps(stream_read(torch, variants=(0, 1, 2, 3))), flush=True)
         return 0
     if what == "exchange":
         G = lib().measure_cus()

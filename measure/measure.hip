@@ -1,7 +1,8 @@
 // measure.hip -- measurement kernels of the benchmark (not part of the fmoe library).
 //
 // 1. A read-only streaming kernel: the attainable HBM read rate of plain streaming code on
-//    this device, the bar beside the published 8 TB/s peak. Each thread keeps U 16-byte
+//    this device, the bar beside the published 8 TB/s peak (plain, non-temporal, and
+//    LDS-DMA loads). Each thread keeps U 16-byte
 //    loads in flight over a grid-strided walk of the buffer; the loaded words are folded
 //    into one register that is stored only if it equals an impossible value, so the kernel
 //    writes nothing and no load can be removed.
@@ -50,6 +51,46 @@ __global__ void __launch_bounds__(kThreads) stream_read_kernel(const u32x4* __re
   for (; i < n; i += stride) {
     const u32x4 v = p[i];
     acc ^= v.x ^ v.y ^ v.z ^ v.w;
+  }
+  if (acc == 0x9E3779B9u && threadIdx.x == 0x3FF) sink[0] = acc;  // never true: threadIdx.x < 256
+}
+
+// The same read through LDS-DMA (global_load_lds_dwordx4, 16 bytes per lane into LDS, one KB
+// per wave instruction): each wave streams its grid-strided KB-sized pieces into a private
+// ring of U KB in LDS, keeping U instructions in flight, and folds one dword of each landed
+// KB into a register (read back from LDS after the data has arrived).
+template <int U, bool NT>
+__global__ void __launch_bounds__(kThreads) stream_read_lds_kernel(const u32x4* __restrict__ p, size_t n,
+                                                                   uint32_t* __restrict__ sink) {
+  __shared__ uint32_t ring[kThreads / 64][U][256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const size_t n_kb = n / 64;  // KB pieces (64 lanes x 16 bytes)
+  const size_t stride = (size_t)gridDim.x * (kThreads / 64);
+  size_t kb = (size_t)blockIdx.x * (kThreads / 64) + wave;
+  uint32_t acc = 0;
+  for (; kb + (U - 1) * stride < n_kb; kb += U * stride) {
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const u32x4* src = p + (kb + u * stride) * 64 + lane;
+      const uint32_t lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&ring[wave][u][0];
+      if (NT)
+        asm volatile(
+            "s_mov_b32 m0, %1\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %0, off nt" ::"v"(src),
+            "s"(__builtin_amdgcn_readfirstlane(lds))
+            : "memory", "m0");
+      else
+        asm volatile(
+            "s_mov_b32 m0, %1\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %0, off" ::"v"(src),
+            "s"(__builtin_amdgcn_readfirstlane(lds))
+            : "memory", "m0");
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+#pragma unroll
+    for (int u = 0; u < U; ++u) acc ^= ring[wave][u][lane * 4];
   }
   if (acc == 0x9E3779B9u && threadIdx.x == 0x3FF) sink[0] = acc;  // never true: threadIdx.x < 256
 }
@@ -160,8 +201,9 @@ int measure_cus(void) {
   return cus;
 }
 
-// Enqueue one read of nbytes (a multiple of 16) at buf. variant: 0 plain loads, 1
-// non-temporal loads; unroll 4 or 8 loads in flight per thread; blocks: grid size.
+// Enqueue one read of nbytes (a multiple of 16; LDS-DMA: of 1024) at buf. variant: 0 plain
+// loads, 1 non-temporal loads, 2 LDS-DMA, 3 non-temporal LDS-DMA; unroll 4 or 8 loads in flight per thread (LDS-DMA:
+// KB pieces per wave); blocks: grid size.
 int measure_stream_read(const void* buf, size_t nbytes, int variant, int unroll, int blocks, uint32_t* sink,
                         hipStream_t s) {
   if (!buf || !sink || nbytes % 16 || blocks < 1) return -1;
@@ -171,6 +213,10 @@ int measure_stream_read(const void* buf, size_t nbytes, int variant, int unroll,
   else if (variant == 0 && unroll == 8) hipLaunchKernelGGL((stream_read_kernel<8, false>), dim3(blocks), dim3(kThreads), 0, s, p, n, sink);
   else if (variant == 1 && unroll == 4) hipLaunchKernelGGL((stream_read_kernel<4, true>), dim3(blocks), dim3(kThreads), 0, s, p, n, sink);
   else if (variant == 1 && unroll == 8) hipLaunchKernelGGL((stream_read_kernel<8, true>), dim3(blocks), dim3(kThreads), 0, s, p, n, sink);
+  else if (variant == 2 && unroll == 4) hipLaunchKernelGGL((stream_read_lds_kernel<4, false>), dim3(blocks), dim3(kThreads), 0, s, p, n, sink);
+  else if (variant == 2 && unroll == 8) hipLaunchKernelGGL((stream_read_lds_kernel<8, false>), dim3(blocks), dim3(kThreads), 0, s, p, n, sink);
+  else if (variant == 3 && unroll == 4) hipLaunchKernelGGL((stream_read_lds_kernel<4, true>), dim3(blocks), dim3(kThreads), 0, s, p, n, sink);
+  else if (variant == 3 && unroll == 8) hipLaunchKernelGGL((stream_read_lds_kernel<8, true>), dim3(blocks), dim3(kThreads), 0, s, p, n, sink);
   else return -2;
   return hipGetLastError() == hipSuccess ? 0 : -8;
 }
