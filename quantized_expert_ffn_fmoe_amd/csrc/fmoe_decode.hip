@@ -143,6 +143,13 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
   constexpr int kLprD = IC ? lanes_per_row(IC / CC) : 0;
   constexpr bool kFastGU = kLprG == 64 && kBatchGU == 4;
   constexpr bool kFastD = kLprD >= 16 && kBatchD >= 2 && kBatchD <= 8;
+  // Compiled shapes with a gated shared expert: its expert is fixed, so its gate/up rows run
+  // while wave 0 waits for the logits and ranks them (waves 1-3, right after v's digit
+  // image), its SwiGLU outputs are exchanged during the routed gate/up, and every
+  // workgroup forms the gate logit itself from the gathered h (no router row, no logits
+  // word for it).
+  constexpr bool kSharedEarly = SH == 1;
+  static_assert(!kSharedEarly || (HC && IC && EC && KC && kFastGU), "early shared expert: compiled shapes only");
   constexpr int NW = Digits<BITS>::kWords;
   extern __shared__ float smem_raw[];
   const int tid = threadIdx.x, lane = tid & 63;
@@ -156,7 +163,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
   // router rows: the E experts' rows, then the shared expert's gate (SH: compiled shapes
   // with a shared expert)
   const int KS = KC ? KC + SH : p.k + p.has_shared;
-  const int ER = EC ? EC + SH : p.n_experts + p.has_shared;
+  const int ER = EC ? EC + (kSharedEarly ? 0 : SH) : p.n_experts + p.has_shared;
   const int KI = KS * I;
   const int vec_len = H > KI ? H : KI;
   const int max_chunks = vec_len / CC;
@@ -172,8 +179,8 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
   float* part = dig.xsum + max_chunks;  // [router items]
   float* ybuf = part + p.router_items;  // [k][rows per workgroup]
   float* hraw = ybuf + KS * p.rows_per_wg;  // [rows per workgroup] this workgroup's rows of h
-  float* red = hraw + p.rows_per_wg;
-  float* wsel = red + kDecodeWaves;
+  float* red = hraw + p.rows_per_wg;  // per wave: sum of squares of h, then the shared gate's dot with h
+  float* wsel = red + 2 * kDecodeWaves;
   float* lsel = wsel + 16;
   int* isel = reinterpret_cast<int*>(lsel + 16);
   int* fail = isel + 16;
@@ -211,19 +218,30 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
   const int r0 = g * rows_wg;
   const int nr = max(0, min(H - r0, rows_wg));
   const int n_rb = (nr + rpwD - 1) / rpwD;  // down row blocks per slot
-  // down items (j, rb) of this workgroup, a contiguous run per wave
-  const int d_items = KS * n_rb;
+  // down items (j, rb) of this workgroup, a contiguous run per wave. With the early shared
+  // expert, when every wave's run of the routed slots is one batch of one slot (sep_sh), the
+  // shared slot's row blocks are dealt apart, at most two per wave, and computed first (their
+  // a is exchanged before the routed a).
+  const int dper_r = (K * n_rb + kDecodeWaves - 1) / kDecodeWaves;
+  const int sd_per = (n_rb + kDecodeWaves - 1) / kDecodeWaves;
+  const bool sep_sh = kSharedEarly && kFastD && dper_r > 0 && dper_r <= kBatchD && n_rb % dper_r == 0 && sd_per <= 2;
+  const int sd_lo = min(n_rb, wave * sd_per), sd_hi = min(n_rb, sd_lo + sd_per);
+  const int d_items = (sep_sh ? K : KS) * n_rb;
   const int d_per = (d_items + kDecodeWaves - 1) / kDecodeWaves;
   const int d_lo = wave * d_per, d_hi = min(d_items, d_lo + d_per);
   const int S = (H + 1023) / 1024;  // router slices per row
   const int my_experts = (ER - g + G - 1) / G;
   const int n_ritems = my_experts * S;
   // gate/up: a contiguous run of blocks (rpwG consecutive items each) per workgroup; the
-  // last slot it touches is the top-k round the workgroup has to wait for
-  const int n_blocks = (KI + rpwG - 1) / rpwG;
+  // last slot it touches is the top-k round the workgroup has to wait for. The early shared
+  // expert's rows are dealt apart: rows sh_lo .. sh_hi - 1 (items K * I + row) per workgroup.
+  const int KG = kSharedEarly ? K * I : KI;
+  const int n_blocks = (KG + rpwG - 1) / rpwG;
   const int per_wg = (n_blocks + G - 1) / G;
   const int blk_lo = g * per_wg, blk_hi = min(n_blocks, blk_lo + per_wg);
-  const int gu_last = min(blk_hi * rpwG, KI) - 1;
+  const int gu_last = min(blk_hi * rpwG, KG) - 1;
+  const int sh_per = (I + G - 1) / G;
+  const int sh_lo = kSharedEarly ? min(I, g * sh_per) : 0, sh_hi = kSharedEarly ? min(I, sh_lo + sh_per) : 0;
   // (a run inside the shared expert's slot needs no routing round: its expert is fixed)
   const int gu_first = blk_lo * rpwG / I, gu_lslot = gu_last / I;
   const int gu_need = blk_lo >= blk_hi ? 0 : gu_lslot < K ? gu_lslot + 1 : gu_first < K ? K : 0;
@@ -234,7 +252,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
   // layer's values (the next layer's h needs this workgroup's rows first). A workgroup
   // with none of the three skips every exchange. (Uniform over the workgroup; at the
   // 512-expert shapes every workgroup has all three.)
-  const bool need_v = n_ritems > 0 || blk_lo < blk_hi;
+  const bool need_v = n_ritems > 0 || blk_lo < blk_hi || sh_lo < sh_hi;
   const int n_layers_run = (need_v || nr > 0) && !*fail ? p.n_layers : 0;
   const uint64_t* h_rep = p.h + (size_t)rep * H;
   const uint64_t* a_rep = p.a + (size_t)rep * KI;
@@ -285,8 +303,13 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
         hraw[i] = hv[0];
       }
     }
+    float gd = 0.f;  // early shared expert: this thread's part of the gate's dot with h
     for (int i0 = tid; need_v && i0 < H; i0 += kDecodeThreads * kPollN) {
-      float hv[kPollN];
+      float hv[kPollN], gv[kPollN];
+      if constexpr (kSharedEarly) {
+#pragma unroll
+        for (int u = 0; u < kPollN; ++u) gv[u] = p.shared_gate[l][min(i0 + u * kDecodeThreads, H - 1)];
+      }
       if (lg == 0) {
 #pragma unroll
         for (int u = 0; u < kPollN; ++u) {
@@ -303,11 +326,16 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
           vec[padded<CC>(i)] = hv[u];
           if (i >= r0 && i < r0 + nr) hraw[i - r0] = hv[u];
           ss = fmaf(hv[u], hv[u], ss);
+          if constexpr (kSharedEarly) gd = fmaf(gv[u], hv[u], gd);
         }
       }
     }
     ss = wave_sum(ss);
     if (lane == 0) red[wave] = ss;
+    if constexpr (kSharedEarly) {
+      gd = wave_sum(gd);
+      if (lane == 0) red[kDecodeWaves + wave] = gd;
+    }
     if (tid == 0) *ready = 0;
     __syncthreads();
     if (*fail) break;
@@ -318,6 +346,14 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
       float tot = 0.f;
       for (int w2 = 0; w2 < kDecodeWaves; ++w2) tot += red[w2];
       inv = 1.0f / sqrtf(tot / (float)H + p.eps);
+    }
+    if constexpr (kSharedEarly) {
+      // the shared expert's weight: the logistic function of gate . v = inv * (gate . h)
+      if (tid == 0) {
+        float gdot = 0.f;
+        for (int w2 = 0; w2 < kDecodeWaves; ++w2) gdot += red[kDecodeWaves + w2];
+        wsel[K] = 1.0f / (1.0f + expf(-gdot * inv));
+      }
     }
 
     // ---- 2. router: dot the loaded slices with v (the first two of a wave reduced together)
@@ -370,133 +406,21 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
     __syncthreads();
     const uint64_t tag = (uint64_t)(ep + 1u) << 32;
 
-    // ---- 3. publish this workgroup's logits and gather all of them (wave 0), then the
-    // top-k, released round by round; the other waves build the digit image of v
-    if (wave == 0) {
-      for (int t = lane; t < my_experts * kRep; t += 64) {
-        const int el = t / kRep, rr = t % kRep;
-        float lsum = 0.f;
-        for (int s = 0; s < S; ++s) lsum += part[el * S + s];
-        st_dev_u64(p.logits + (size_t)rr * ER + g + el * G, tag | __float_as_uint(lsum));
-      }
-      // poll only once the own logits are acknowledged: a first read issued right behind
-      // the stores samples memory too early (its result waits for the stores anyway) and
-      // costs one more round trip
-      wait_vmem();
-      unsigned spins = 0;
-      bool failed = false;
-      uint64_t kr[kKeysInRegs];  // E <= 64 * kKeysInRegs: keys stay in registers
-      float gate_logit = 0.f;
-      if (E <= 64 * kKeysInRegs) {
-        // one poll batch in flight; words that arrived are kept, only stale ones are read
-        // again
-        uint64_t t[kKeysInRegs];
-        uint32_t got = 0, want = 0;
-        // the shared expert's gate logit (lane 0; others never wait for it)
-        uint64_t tg = (KS > K && lane == 0) ? ld_dev_u64(logits_rep + E) : tag;
-#pragma unroll
-        for (int j = 0; j < kKeysInRegs; ++j) {
-          const int e = lane + 64 * j;
-          kr[j] = 0;
-          if (e < E) {
-            want |= 1u << j;
-            t[j] = ld_dev_u64(logits_rep + e);
-          }
-        }
-        while (true) {
-#pragma unroll
-          for (int j = 0; j < kKeysInRegs; ++j) {
-            const int e = lane + 64 * j;
-            if (((want & ~got) >> j) & 1u) {
-              if ((t[j] & 0xffffffff00000000ull) == tag) {
-                kr[j] = rank_key(__uint_as_float((uint32_t)t[j]), e);
-                got |= 1u << j;
-              }
-            }
-          }
-          const bool gok = (tg & 0xffffffff00000000ull) == tag;
-          if (__all(got == want && gok)) break;
-          if (spin_failed(++spins, p.err)) {
-            failed = true;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-#pragma unroll
-          for (int j = 0; j < kKeysInRegs; ++j)
-            if (((want & ~got) >> j) & 1u) t[j] = ld_dev_u64(logits_rep + lane + 64 * j);
-          if (!gok) tg = ld_dev_u64(logits_rep + E);
-        }
-        if (KS > K && lane == 0) gate_logit = __uint_as_float((uint32_t)tg);
-      } else {
-        while (true) {
-          bool ok = true;
-          for (int e = lane; e < E; e += 64) {
-            const uint64_t t = ld_dev_u64(logits_rep + e);
-            ok &= (t & 0xffffffff00000000ull) == tag;
-            key[e] = rank_key(__uint_as_float((uint32_t)t), e);
-          }
-          if (KS > K && lane == 0) {
-            const uint64_t t = ld_dev_u64(logits_rep + E);
-            ok &= (t & 0xffffffff00000000ull) == tag;
-            gate_logit = __uint_as_float((uint32_t)t);
-          }
-          if (__all(ok)) break;
-          if (spin_failed(++spins, p.err)) {
-            failed = true;
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-        }
-      }
-      if (failed) {
-        if (lane == 0) {
-          st_dev_u32(p.err, 1u);
-          *fail = 1;
-        }
-        if (lane < KS) {
-          isel[lane] = lane < K ? 0 : E;
-          wsel[lane] = 0.f;
-        }
-        topk_progress(ready, K + 1);
-      } else {
-        // the shared expert's weight: the logistic function of its gate logit (written
-        // before the top-k releases its last round)
-        if (KS > K && lane == 0) wsel[K] = 1.0f / (1.0f + expf(-gate_logit));
-        if (E <= 64 * kKeysInRegs) wave_topk_regs<kKeysInRegs>(kr, K, isel, lsel, wsel, ready);
-        else wave_topk_keys(key, E, K, isel, lsel, wsel, ready);
-        if (g == 0 && lane < K) {
-          size_t o = ((size_t)lg) * K + lane;
-          if (p.idx_out) p.idx_out[o] = isel[lane];
-          if (p.w_out) p.w_out[o] = wsel[lane];
-        }
-      }
-    } else {
-      if (need_v)
-        build_digits<BITS>(dig, 0, H, [&](int i) { return vec[padded<CC>(i)]; }, kDecodeThreads - 64, tid - 64, inv);
-      // the digit image is complete once every builder wave has passed this point
-      if (lane == 0) __hip_atomic_fetch_add(base + 1, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
-      wait_ready(ready, gu_need);
-    }
-    // every wave (wave 0 included) waits for the three builder waves of this layer
-    while (__hip_atomic_load(base + 1, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < 3u * (uint32_t)(l + 1))
-      __builtin_amdgcn_s_sleep(0);
-    if (*fail) break;  // set by wave 0 before it released the waiters
-
-    // ---- 4. gate/up + SwiGLU over this workgroup's run of blocks, dealt to its waves in
-    // runs of kBatchGU blocks whose loads are issued together; a is published tagged
-    {
-      DChunk<BITS> dc[CPL_G];
-      bool dc_loaded = false;  // the digits are read from LDS after the first loads are issued
-      const uint64_t atag = (uint64_t)(ep + 2u) << 32;
-      for (int b0 = blk_lo + wave * kBatchGU; b0 < blk_hi; b0 += kDecodeWaves * kBatchGU) {
+    // gate/up state (step 4); the early shared expert's rows run before the routing is known
+    DChunk<BITS> dc[CPL_G];
+    bool dc_loaded = false;  // the digits are read from LDS after the first loads are issued
+    const uint64_t atag = (uint64_t)(ep + 2u) << 32;
+    // items b0 .. b0 + kBatchGU - 1 (rows for rpwG > 1: blocks) for b0 = b_first, + b_step, ... < b_hi
+    auto gu_run = [&](int b_first, int b_hi, int b_step) {
+      for (int b0 = b_first; b0 < b_hi; b0 += b_step) {
         CChunk<BITS> wg[kBatchGU][CPL_G], wu[kBatchGU][CPL_G];
         uint32_t sg[kBatchGU][CPL_G], su[kBatchGU][CPL_G];
 #pragma unroll
         for (int u = 0; u < kBatchGU; ++u) {
           // fast path: unconditional loads (an item past the run reads the run's last row,
           // whose result is not stored), so that each item waits only for its own loads
-          const int item = kFastGU ? min(b0 + u, blk_hi - 1) : (b0 + u) * rpwG + rselG;
-          if (kFastGU || (b0 + u < blk_hi && item < KI)) {
+          const int item = kFastGU ? min(b0 + u, b_hi - 1) : (b0 + u) * rpwG + rselG;
+          if (kFastGU || (b0 + u < b_hi && item < KI)) {
             const int j = item / I, i = item % I;
             const uint8_t* bp = X + (size_t)isel[j] * p.expert_stride;
             const uint8_t* gp = bp;  // gate codes; up codes follow at cbH
@@ -550,13 +474,13 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
           const float sum = reduce_transposed<8, 64>(vals);
           const float up_sum = xlane<1>(sum);
           const int u = 2 * ((lane >> 1) & 1) + ((lane >> 2) & 1);
-          if (!(lane & 1) && b0 + u < blk_hi)
+          if (!(lane & 1) && b0 + u < b_hi)
             st_dev_u64(p.a + (size_t)(lane >> 3) * KI + (b0 + u), atag | __float_as_uint(swiglu(sum, up_sum)));
           continue;
         }
 #pragma unroll
         for (int u = 0; u < kBatchGU; ++u) {
-          if (b0 + u >= blk_hi) break;  // uniform over the wave
+          if (b0 + u >= b_hi) break;  // uniform over the wave
           const int item = (b0 + u) * rpwG + rselG;
           const bool valid = item < KI;
           float gs = 0.f, us = 0.f;
@@ -579,7 +503,133 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
           }
         }
       }
+    };
+
+
+    // ---- 3. publish this workgroup's logits and gather all of them (wave 0), then the
+    // top-k, released round by round; the other waves build the digit image of v
+    if (wave == 0) {
+      for (int t = lane; t < my_experts * kRep; t += 64) {
+        const int el = t / kRep, rr = t % kRep;
+        float lsum = 0.f;
+        for (int s = 0; s < S; ++s) lsum += part[el * S + s];
+        st_dev_u64(p.logits + (size_t)rr * ER + g + el * G, tag | __float_as_uint(lsum));
+      }
+      // poll only once the own logits are acknowledged: a first read issued right behind
+      // the stores samples memory too early (its result waits for the stores anyway) and
+      // costs one more round trip
+      wait_vmem();
+      unsigned spins = 0;
+      bool failed = false;
+      const bool kGateWord = KS > K && !kSharedEarly;  // the gate logit comes with the others
+      uint64_t kr[kKeysInRegs];  // E <= 64 * kKeysInRegs: keys stay in registers
+      float gate_logit = 0.f;
+      if (E <= 64 * kKeysInRegs) {
+        // one poll batch in flight; words that arrived are kept, only stale ones are read
+        // again
+        uint64_t t[kKeysInRegs];
+        uint32_t got = 0, want = 0;
+        // the shared expert's gate logit (lane 0; others never wait for it)
+        uint64_t tg = (kGateWord && lane == 0) ? ld_dev_u64(logits_rep + E) : tag;
+#pragma unroll
+        for (int j = 0; j < kKeysInRegs; ++j) {
+          const int e = lane + 64 * j;
+          kr[j] = 0;
+          if (e < E) {
+            want |= 1u << j;
+            t[j] = ld_dev_u64(logits_rep + e);
+          }
+        }
+        while (true) {
+#pragma unroll
+          for (int j = 0; j < kKeysInRegs; ++j) {
+            const int e = lane + 64 * j;
+            if (((want & ~got) >> j) & 1u) {
+              if ((t[j] & 0xffffffff00000000ull) == tag) {
+                kr[j] = rank_key(__uint_as_float((uint32_t)t[j]), e);
+                got |= 1u << j;
+              }
+            }
+          }
+          const bool gok = (tg & 0xffffffff00000000ull) == tag;
+          if (__all(got == want && gok)) break;
+          if (spin_failed(++spins, p.err)) {
+            failed = true;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+#pragma unroll
+          for (int j = 0; j < kKeysInRegs; ++j)
+            if (((want & ~got) >> j) & 1u) t[j] = ld_dev_u64(logits_rep + lane + 64 * j);
+          if (!gok) tg = ld_dev_u64(logits_rep + E);
+        }
+        if (kGateWord && lane == 0) gate_logit = __uint_as_float((uint32_t)tg);
+      } else {
+        while (true) {
+          bool ok = true;
+          for (int e = lane; e < E; e += 64) {
+            const uint64_t t = ld_dev_u64(logits_rep + e);
+            ok &= (t & 0xffffffff00000000ull) == tag;
+            key[e] = rank_key(__uint_as_float((uint32_t)t), e);
+          }
+          if (kGateWord && lane == 0) {
+            const uint64_t t = ld_dev_u64(logits_rep + E);
+            ok &= (t & 0xffffffff00000000ull) == tag;
+            gate_logit = __uint_as_float((uint32_t)t);
+          }
+          if (__all(ok)) break;
+          if (spin_failed(++spins, p.err)) {
+            failed = true;
+            break;
+          }
+          __builtin_amdgcn_s_sleep(1);
+        }
+      }
+      if (failed) {
+        if (lane == 0) {
+          st_dev_u32(p.err, 1u);
+          *fail = 1;
+        }
+        if (lane < KS) {
+          isel[lane] = lane < K ? 0 : E;
+          wsel[lane] = 0.f;
+        }
+        topk_progress(ready, K + 1);
+      } else {
+        // the shared expert's weight: the logistic function of its gate logit (written
+        // before the top-k releases its last round)
+        if (kGateWord && lane == 0) wsel[K] = 1.0f / (1.0f + expf(-gate_logit));
+        if (E <= 64 * kKeysInRegs) wave_topk_regs<kKeysInRegs>(kr, K, isel, lsel, wsel, ready);
+        else wave_topk_keys(key, E, K, isel, lsel, wsel, ready);
+        if (g == 0 && lane < K) {
+          size_t o = ((size_t)lg) * K + lane;
+          if (p.idx_out) p.idx_out[o] = isel[lane];
+          if (p.w_out) p.w_out[o] = wsel[lane];
+        }
+      }
+    } else {
+      if (need_v)
+        build_digits<BITS>(dig, 0, H, [&](int i) { return vec[padded<CC>(i)]; }, kDecodeThreads - 64, tid - 64, inv);
+      // the digit image is complete once every builder wave has passed this point
+      if (lane == 0) __hip_atomic_fetch_add(base + 1, 1, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_WORKGROUP);
+      if constexpr (kSharedEarly) {
+        // the shared expert's rows of this workgroup, once v's digit image is complete
+        if (sh_lo + (wave - 1) * kBatchGU < sh_hi) {  // uniform over the wave
+          while (__hip_atomic_load(base + 1, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < 3u * (uint32_t)(l + 1))
+            __builtin_amdgcn_s_sleep(0);
+          gu_run(K * I + sh_lo + (wave - 1) * kBatchGU, K * I + sh_hi, (kDecodeWaves - 1) * kBatchGU);
+        }
+      }
+      wait_ready(ready, gu_need);
     }
+    // every wave (wave 0 included) waits for the three builder waves of this layer
+    while (__hip_atomic_load(base + 1, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < 3u * (uint32_t)(l + 1))
+      __builtin_amdgcn_s_sleep(0);
+    if (*fail) break;  // set by wave 0 before it released the waiters
+
+    // ---- 4. gate/up + SwiGLU over this workgroup's run of blocks, dealt to its waves in
+    // runs of kBatchGU blocks whose loads are issued together; a is published tagged
+    gu_run(blk_lo + wave * kBatchGU, blk_hi, kDecodeWaves * kBatchGU);
 
     // ---- prefetch: every wave issues the loads of its first kBatchD down items (all k
     // experts must be known)
@@ -609,6 +659,68 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
     };
 #pragma unroll
     for (int u = 0; u < kBatchD; ++u) down_load(u, u);
+    // the shared slot's row blocks of this wave (sep_sh; a run of at most two, loaded
+    // unconditionally: a block past the run repeats the run's last one, not stored)
+    CChunk<BITS> wsh[2][CPL_D];
+    uint32_t ssh[2][CPL_D];
+    if (sep_sh && sd_lo < sd_hi) {
+      const uint8_t* bp = X + (size_t)E * p.expert_stride;
+      const uint8_t* dp = bp + 2 * cbH;
+      const uint32_t* dsb = reinterpret_cast<const uint32_t*>(bp + 3 * cbH + 2 * sbb);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int r = r0 + min((min(sd_lo + u, sd_hi - 1)) * rpwD + rselD, nr - 1);
+#pragma unroll
+        for (int q = 0; q < CPL_D; ++q) {
+          const int c = min(subD + lprD * q, nchD - 1);
+          load_cchunk<BITS>(wsh[u][q], dp, H, I, r, c);
+          ssh[u][q] = dsb[sb_offset(H, ngI, r, c / C::kPerGroup)];
+        }
+      }
+    }
+
+    // ---- 5a. the shared slot's down rows (sep_sh): its a was published while the routed
+    // experts were being selected, so it is gathered and used while the routed a arrives
+    if constexpr (kSharedEarly && kFastD) {
+      if (sep_sh && sd_lo < sd_hi) {
+        const uint64_t* a_s = a_rep + (size_t)K * I;
+        wait_vmem();
+        for (int i0 = lane; i0 < I; i0 += 64 * kPollA) {
+          float av[kPollA];
+          if (!poll_batch<kPollA, 64>(a_s, I, i0, ep + 2u, av, p.err)) *fail = 1;
+#pragma unroll
+          for (int u = 0; u < kPollA; ++u) {
+            const int i = i0 + 64 * u;
+            if (i < I) vec[padded<CC>(K * I + i)] = av[u];
+          }
+        }
+        __builtin_amdgcn_wave_barrier();
+        // every wave builds the same image of the shared slot's a (identical values)
+        build_digits<BITS>(dig_a, K * nchD, I, [&](int i) { return vec[padded<CC>(i)]; }, 64, lane);
+        __builtin_amdgcn_wave_barrier();
+        DChunk<BITS> dcs[CPL_D];
+#pragma unroll
+        for (int q = 0; q < CPL_D; ++q) {
+          int c = subD + kLprD * q;
+          if (c < nchD) load_dchunk<BITS>(dcs[q], dig_a, K * nchD + c);
+        }
+        float acc[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          float a_ = 0.f;
+#pragma unroll
+          for (int q = 0; q < CPL_D; ++q) {
+            int c = subD + kLprD * q;
+            if (c < nchD) a_ += chunk_dot_int<BITS>(wsh[u][q], ssh[u][q], dcs[q]);
+          }
+          acc[u] = a_;
+        }
+        const float sum = reduce_transposed<2, kLprD>(acc);
+        const int u = transposed_index<2>(lane);
+        const int rl = (sd_lo + u) * rpwD + rselD;
+        if (subD < 2 && sd_lo + u < sd_hi && rl < nr) ybuf[K * rows_wg + rl] = sum;
+      }
+    }
 
     // ---- 5./6. a, then down. When every wave's down items belong to one slot and fit one
     // batch (the compiled decode shapes), each wave gathers only its slot's a (written by
@@ -824,7 +936,7 @@ size_t decode_smem_bytes(int hidden, int inter, int n_experts, int k, int G, int
   // after the padded vector and v's digit store: router partials, ybuf, hraw, red, wsel,
   // lsel, isel (16 each), fail, ready, base[4], then a's digit store
   size_t words = vec_len + vec_len / cc + (size_t)nw * max_chunks + 2 * max_chunks + (size_t)my_experts * S +
-                 (size_t)k * rows_per_wg + rows_per_wg + kDecodeWaves + 16 + 16 + 16 + 6 + (size_t)nw * a_chunks +
+                 (size_t)k * rows_per_wg + rows_per_wg + 2 * kDecodeWaves + 16 + 16 + 16 + 6 + (size_t)nw * a_chunks +
                  2 * a_chunks;
   return (size_t)n_experts * 8 + words * 4;  // rank keys first
 }
