@@ -21,15 +21,20 @@
 //
 // Matrix-core form of the affine dequantization. A weight is q*s + b with (s, b) per
 // group of 64 columns of a row (the nibble*scale+bias form of aibit.im "Techniques de
-// rupture" item 2). The codes enter the bf16 matrix core as the exact values
-// c = (1 + q/128) / 2, whose bf16 bits are 0x3F00 | q (q in the low mantissa bits, for
-// both code widths): one AND isolates a dword's codes byte-wise and one byte permute pairs
-// two of them with the 0x3F high bytes, per bf16 pair. For one group, with X = sum of the
-// group's bf16 activations and P = sum x*c from the matrix core,
-//   sum x (q s + b) = 256 s P + (b - 128 s) X,
-// applied once per group to the fp32 partial product (the per-group factorisation
-// s*sum(q x) + b*sum(x)). No weight is rounded; only v and a are (to bf16).
-//
+// rupture" item 2). The codes enter the bf16 matrix core as the exact values c = o + u*q:
+// q sits in the top mantissa bits of a bf16 whose exponent is fixed and even (4 bits:
+// bits 0x4200 | q << 3, c = 32 + 2q; 3 and 2 bits: 0x4100 | q << 4, c = 8 + q), so a
+// shift and an AND place a dword's codes byte-wise and one byte permute pairs two of them
+// with the fixed high bytes, per bf16 pair. For one group, with X = sum of the group's
+// bf16 activations and P = sum x*c from the matrix core,
+//   u * sum x (q s + b) = s P + (u b - o s) X
+// (the per-group factorisation s*sum(q x) + b*sum(x)), and the factor u (a power of two) is
+// divided out once at the end. The first term is applied once per group to the fp32
+// partial product; the second, summed over the groups of a stage, is itself a small
+// product (tokens x groups times groups x rows), done as one fp32 matrix-core product per
+// tile and stage (v_mfma_f32_16x16x4f32, operands in fp32). The offset cancels between the
+// two terms, so the partial sums hold up to ~o/u times the magnitude of sum x q; o/u is
+// kept at 16 or below. No weight is rounded; only v and a are (to bf16).
 // Operand order. For 16x16x32 bf16 products lane l holds, for the A operand, row l % 16
 // and the 8 consecutive K indices 8*(l/16)..+7; the same for B with column l % 16; the
 // result holds D[4*(l/16) + i][l % 16] in element i. Tokens are the rows (A), weight rows
@@ -85,61 +90,65 @@ __device__ __forceinline__ uint32_t shift(uint32_t w) {
 }
 
 // The two 8-element B operands of one group from this lane's code bytes (see header).
-// v_perm_b32 byte selectors: 0-3 take bytes of the second operand, 4 the 0x3F byte.
-constexpr uint32_t kHiBytes = 0x3F3F3F3Fu;
-constexpr uint32_t kSelEven = 0x04020400u;  // [x.b0, 3F, x.b2, 3F]
-constexpr uint32_t kSelOdd = 0x04030401u;   // [x.b1, 3F, x.b3, 3F]
+// v_perm_b32 byte selectors: 0-3 take bytes of the second operand, 4 the fixed high byte.
+template <int BITS>
+constexpr uint32_t kHiBytes = BITS == 4 ? 0x42424242u : 0x41414141u;
+template <int BITS>
+constexpr float kCodeOffset = BITS == 4 ? 32.f : 8.f;  // o
+template <int BITS>
+constexpr float kCodeUnit = BITS == 4 ? 2.f : 1.f;  // u
+constexpr uint32_t kSelEven = 0x04020400u;  // [x.b0, hi, x.b2, hi]
+constexpr uint32_t kSelOdd = 0x04030401u;   // [x.b1, hi, x.b3, hi]
 template <int BITS>
 __device__ __forceinline__ void build_b(const uint32_t* w, u32x4& b0, u32x4& b1) {
   if constexpr (BITS == 4) {
     // w[h] holds columns 8h..8h+7 of the lane's 16, nibble p = column 8h + p; pair j of
-    // half h is (8h + j, 8h + j + 4): the even nibbles sit in the bytes of w & 0x0F0F0F0F,
-    // the odd ones in those of (w >> 4) & 0x0F0F0F0F
+    // half h is (8h + j, 8h + j + 4): the even nibbles go to bits 3-6 of the bytes of ev,
+    // the odd ones to those of od
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
-      const uint32_t ev = w[h] & 0x0F0F0F0Fu, od = (w[h] >> 4) & 0x0F0F0F0Fu;
+      const uint32_t ev = (w[h] << 3) & 0x78787878u, od = (w[h] >> 1) & 0x78787878u;
       u32x4& b = h ? b1 : b0;
-      b.x = __builtin_amdgcn_perm(kHiBytes, ev, kSelEven);
-      b.y = __builtin_amdgcn_perm(kHiBytes, od, kSelEven);
-      b.z = __builtin_amdgcn_perm(kHiBytes, ev, kSelOdd);
-      b.w = __builtin_amdgcn_perm(kHiBytes, od, kSelOdd);
+      b.x = __builtin_amdgcn_perm(kHiBytes<4>, ev, kSelEven);
+      b.y = __builtin_amdgcn_perm(kHiBytes<4>, od, kSelEven);
+      b.z = __builtin_amdgcn_perm(kHiBytes<4>, ev, kSelOdd);
+      b.w = __builtin_amdgcn_perm(kHiBytes<4>, od, kSelOdd);
     }
   } else {
-    // w[0] holds the lane's 16 columns, column i in bits 2i; byte m of
-    // (w >> 2 r) & 0x03030303 holds column 4m + r, and half h, pair r takes columns
-    // 4h + r and 4h + r + 8
+    // w[0] holds the lane's 16 columns, column i in bits 2i; byte m of t_r holds column
+    // 4m + r in bits 4-5, and half h, pair r takes columns 4h + r and 4h + r + 8
     const uint32_t d = w[0];
-    const uint32_t t0 = d & 0x03030303u, t1 = (d >> 2) & 0x03030303u;
-    const uint32_t t2 = (d >> 4) & 0x03030303u, t3 = (d >> 6) & 0x03030303u;
-    b0.x = __builtin_amdgcn_perm(kHiBytes, t0, kSelEven);
-    b0.y = __builtin_amdgcn_perm(kHiBytes, t1, kSelEven);
-    b0.z = __builtin_amdgcn_perm(kHiBytes, t2, kSelEven);
-    b0.w = __builtin_amdgcn_perm(kHiBytes, t3, kSelEven);
-    b1.x = __builtin_amdgcn_perm(kHiBytes, t0, kSelOdd);
-    b1.y = __builtin_amdgcn_perm(kHiBytes, t1, kSelOdd);
-    b1.z = __builtin_amdgcn_perm(kHiBytes, t2, kSelOdd);
-    b1.w = __builtin_amdgcn_perm(kHiBytes, t3, kSelOdd);
+    const uint32_t t0 = (d << 4) & 0x30303030u, t1 = (d << 2) & 0x30303030u;
+    const uint32_t t2 = d & 0x30303030u, t3 = (d >> 2) & 0x30303030u;
+    b0.x = __builtin_amdgcn_perm(kHiBytes<2>, t0, kSelEven);
+    b0.y = __builtin_amdgcn_perm(kHiBytes<2>, t1, kSelEven);
+    b0.z = __builtin_amdgcn_perm(kHiBytes<2>, t2, kSelEven);
+    b0.w = __builtin_amdgcn_perm(kHiBytes<2>, t3, kSelEven);
+    b1.x = __builtin_amdgcn_perm(kHiBytes<2>, t0, kSelOdd);
+    b1.y = __builtin_amdgcn_perm(kHiBytes<2>, t1, kSelOdd);
+    b1.z = __builtin_amdgcn_perm(kHiBytes<2>, t2, kSelOdd);
+    b1.w = __builtin_amdgcn_perm(kHiBytes<2>, t3, kSelOdd);
   }
 }
 
 // 3 bits: the lane's low-plane dword as at 2 bits, plus the high-plane word of its 32-column
-// half (kb / 2), shifted by 2 (kb % 2): byte m of the shift-by-2r unpack holds column
-// 4m + r of the lane's 16, whose third bit then sits at 8m + 4 (r / 2) + r % 2
-// (fmoe_layout.h, hi_bit); one shift and an and-or put it at bit 2 of the byte.
+// half (kb / 2), shifted by 2 (kb % 2): the low bits of column 4m + r sit at bits 8m + 2r,
+// + 1 of the dword and its third bit at 8m + 4 (r / 2) + r % 2 of the shifted word
+// (fmoe_layout.h, hi_bit); byte m of t_r gets the code in bits 4-6.
 __device__ __forceinline__ void build_b3(uint32_t d, uint32_t hw, int kb, u32x4& b0, u32x4& b1) {
   const uint32_t hs = hw >> (2 * (kb & 1));
-  const uint32_t t0 = (d & 0x03030303u) | ((hs << 2) & 0x04040404u);
-  const uint32_t t1 = ((d >> 2) & 0x03030303u) | ((hs << 1) & 0x04040404u);
-  const uint32_t t2 = ((d >> 4) & 0x03030303u) | ((hs >> 2) & 0x04040404u);
-  const uint32_t t3 = ((d >> 6) & 0x03030303u) | ((hs >> 3) & 0x04040404u);
-  b0.x = __builtin_amdgcn_perm(kHiBytes, t0, kSelEven);
-  b0.y = __builtin_amdgcn_perm(kHiBytes, t1, kSelEven);
-  b0.z = __builtin_amdgcn_perm(kHiBytes, t2, kSelEven);
-  b0.w = __builtin_amdgcn_perm(kHiBytes, t3, kSelEven);
-  b1.x = __builtin_amdgcn_perm(kHiBytes, t0, kSelOdd);
-  b1.y = __builtin_amdgcn_perm(kHiBytes, t1, kSelOdd);
-  b1.z = __builtin_amdgcn_perm(kHiBytes, t2, kSelOdd);
-  b1.w = __builtin_amdgcn_perm(kHiBytes, t3, kSelOdd);
+  const uint32_t t0 = ((d << 4) & 0x30303030u) | ((hs << 6) & 0x40404040u);
+  const uint32_t t1 = ((d << 2) & 0x30303030u) | ((hs << 5) & 0x40404040u);
+  const uint32_t t2 = (d & 0x30303030u) | ((hs << 2) & 0x40404040u);
+  const uint32_t t3 = ((d >> 2) & 0x30303030u) | ((hs << 1) & 0x40404040u);
+  b0.x = __builtin_amdgcn_perm(kHiBytes<3>, t0, kSelEven);
+  b0.y = __builtin_amdgcn_perm(kHiBytes<3>, t1, kSelEven);
+  b0.z = __builtin_amdgcn_perm(kHiBytes<3>, t2, kSelEven);
+  b0.w = __builtin_amdgcn_perm(kHiBytes<3>, t3, kSelEven);
+  b1.x = __builtin_amdgcn_perm(kHiBytes<3>, t0, kSelOdd);
+  b1.y = __builtin_amdgcn_perm(kHiBytes<3>, t1, kSelOdd);
+  b1.z = __builtin_amdgcn_perm(kHiBytes<3>, t2, kSelOdd);
+  b1.w = __builtin_amdgcn_perm(kHiBytes<3>, t3, kSelOdd);
 }
 __device__ __forceinline__ f32x4 mfma(const u32x4& a, const u32x4& b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), __builtin_bit_cast(bf16x8, b), c, 0,
@@ -480,6 +489,15 @@ struct StageGeom {
   static constexpr int kLoads = 4 + 2 * GC + kNJ + kNJH;  // vector memory instructions per stage
 };
 
+// b in the lanes of `lanes` (a constant lane mask), a elsewhere: one v_cndmask with the mask
+// in scalar registers (written as asm so that a chain of them over one register array is not
+// turned into a dynamically indexed copy of the array in scratch memory).
+__device__ __forceinline__ uint32_t lane_pick(uint32_t a, uint32_t b, uint64_t lanes) {
+  uint32_t r;
+  asm("v_cndmask_b32_e64 %0, %1, %2, %3" : "=v"(r) : "v"(a), "v"(b), "s"(lanes));
+  return r;
+}
+
 __device__ __forceinline__ uint32_t lds_addr(const void* p) {
   return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
 }
@@ -555,70 +573,113 @@ __host__ __device__ constexpr int stage_off(int R, int off) {
   return (R / SG::kRPI) * 1024 + ((off / 16) * SG::kRPI + R % SG::kRPI) * 16 + off % 16;
 }
 
-// One group's LDS operands: the lane's code bytes of the 4 tiles (at base + T1 * t) and its
-// 4 group sums (at xaddr), read in one asm block that also waits for them. The reads are
-// written in asm because the compiler, unable to tell them apart from the stage buffers
-// that LDS-DMA is still filling, would otherwise wait for every load in flight before them.
-template <int T1, int T2, int T3>
-__device__ __forceinline__ void read_group4(uint32_t base, uint32_t xaddr, uint32_t (&w)[4][2], f32x4& x4) {
+// One group's LDS operands: the lane's code bytes of the 4 tiles (at base + T1 * t) and,
+// with WX (the stage's first group), the lane's activation group sum X[token nl][g0 + kb]
+// for the stage's bias product (at xaddr), read in one asm block that also waits for them.
+// The reads are written in asm because the compiler, unable to tell them apart from the
+// stage buffers that LDS-DMA is still filling, would otherwise wait for every load in flight
+// before them.
+template <bool WX, int T1, int T2, int T3>
+__device__ __forceinline__ void read_group4(uint32_t base, uint32_t xaddr, uint32_t (&w)[4][2], float& xa) {
   typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
   u32x2 q0, q1, q2, q3;
-  asm volatile(
-      "ds_read_b64 %0, %5\n"
-      "ds_read_b64 %1, %5 offset:%7\n"
-      "ds_read_b64 %2, %5 offset:%8\n"
-      "ds_read_b64 %3, %5 offset:%9\n"
-      "ds_read_b128 %4, %6\n"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(q0), "=&v"(q1), "=&v"(q2), "=&v"(q3), "=&v"(x4)
-      : "v"(base), "v"(xaddr), "n"(T1), "n"(T2), "n"(T3)
-      : "memory");
+  if constexpr (WX) {
+    asm volatile(
+        "ds_read_b64 %0, %5\n"
+        "ds_read_b64 %1, %5 offset:%7\n"
+        "ds_read_b64 %2, %5 offset:%8\n"
+        "ds_read_b64 %3, %5 offset:%9\n"
+        "ds_read_b32 %4, %6\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(q0), "=&v"(q1), "=&v"(q2), "=&v"(q3), "=&v"(xa)
+        : "v"(base), "v"(xaddr), "n"(T1), "n"(T2), "n"(T3)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b64 %0, %4\n"
+        "ds_read_b64 %1, %4 offset:%5\n"
+        "ds_read_b64 %2, %4 offset:%6\n"
+        "ds_read_b64 %3, %4 offset:%7\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(q0), "=&v"(q1), "=&v"(q2), "=&v"(q3)
+        : "v"(base), "n"(T1), "n"(T2), "n"(T3)
+        : "memory");
+  }
   w[0][0] = q0.x, w[0][1] = q0.y, w[1][0] = q1.x, w[1][1] = q1.y;
   w[2][0] = q2.x, w[2][1] = q2.y, w[3][0] = q3.x, w[3][1] = q3.y;
 }
-template <int T1, int T2, int T3>
-__device__ __forceinline__ void read_group2(uint32_t base, uint32_t xaddr, uint32_t (&w)[4][2], f32x4& x4) {
+template <bool WX, int T1, int T2, int T3>
+__device__ __forceinline__ void read_group2(uint32_t base, uint32_t xaddr, uint32_t (&w)[4][2], float& xa) {
   uint32_t q0, q1, q2, q3;
-  asm volatile(
-      "ds_read_b32 %0, %5\n"
-      "ds_read_b32 %1, %5 offset:%7\n"
-      "ds_read_b32 %2, %5 offset:%8\n"
-      "ds_read_b32 %3, %5 offset:%9\n"
-      "ds_read_b128 %4, %6\n"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(q0), "=&v"(q1), "=&v"(q2), "=&v"(q3), "=&v"(x4)
-      : "v"(base), "v"(xaddr), "n"(T1), "n"(T2), "n"(T3)
-      : "memory");
+  if constexpr (WX) {
+    asm volatile(
+        "ds_read_b32 %0, %5\n"
+        "ds_read_b32 %1, %5 offset:%7\n"
+        "ds_read_b32 %2, %5 offset:%8\n"
+        "ds_read_b32 %3, %5 offset:%9\n"
+        "ds_read_b32 %4, %6\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(q0), "=&v"(q1), "=&v"(q2), "=&v"(q3), "=&v"(xa)
+        : "v"(base), "v"(xaddr), "n"(T1), "n"(T2), "n"(T3)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b32 %0, %4\n"
+        "ds_read_b32 %1, %4 offset:%5\n"
+        "ds_read_b32 %2, %4 offset:%6\n"
+        "ds_read_b32 %3, %4 offset:%7\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(q0), "=&v"(q1), "=&v"(q2), "=&v"(q3)
+        : "v"(base), "n"(T1), "n"(T2), "n"(T3)
+        : "memory");
+  }
   w[0][0] = q0, w[1][0] = q1, w[2][0] = q2, w[3][0] = q3;
   w[0][1] = w[1][1] = w[2][1] = w[3][1] = 0;
 }
 
 // 3 bits: the 2-bit read plus the lane's high-plane word of each tile (at hbase + H1 * t).
-template <int T1, int T2, int T3, int H1, int H2, int H3>
+template <bool WX, int T1, int T2, int T3, int H1, int H2, int H3>
 __device__ __forceinline__ void read_group3(uint32_t base, uint32_t hbase, uint32_t xaddr, uint32_t (&w)[4][2],
-                                            uint32_t (&hw)[4], f32x4& x4) {
+                                            uint32_t (&hw)[4], float& xa) {
   uint32_t q0, q1, q2, q3, g0, g1, g2, g3;
-  asm volatile(
-      "ds_read_b32 %0, %9\n"
-      "ds_read_b32 %1, %9 offset:%12\n"
-      "ds_read_b32 %2, %9 offset:%13\n"
-      "ds_read_b32 %3, %9 offset:%14\n"
-      "ds_read_b32 %4, %10\n"
-      "ds_read_b32 %5, %10 offset:%15\n"
-      "ds_read_b32 %6, %10 offset:%16\n"
-      "ds_read_b32 %7, %10 offset:%17\n"
-      "ds_read_b128 %8, %11\n"
-      "s_waitcnt lgkmcnt(0)"
-      : "=&v"(q0), "=&v"(q1), "=&v"(q2), "=&v"(q3), "=&v"(g0), "=&v"(g1), "=&v"(g2), "=&v"(g3), "=&v"(x4)
-      : "v"(base), "v"(hbase), "v"(xaddr), "n"(T1), "n"(T2), "n"(T3), "n"(H1), "n"(H2), "n"(H3)
-      : "memory");
+  if constexpr (WX) {
+    asm volatile(
+        "ds_read_b32 %0, %9\n"
+        "ds_read_b32 %1, %9 offset:%12\n"
+        "ds_read_b32 %2, %9 offset:%13\n"
+        "ds_read_b32 %3, %9 offset:%14\n"
+        "ds_read_b32 %4, %10\n"
+        "ds_read_b32 %5, %10 offset:%15\n"
+        "ds_read_b32 %6, %10 offset:%16\n"
+        "ds_read_b32 %7, %10 offset:%17\n"
+        "ds_read_b32 %8, %11\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(q0), "=&v"(q1), "=&v"(q2), "=&v"(q3), "=&v"(g0), "=&v"(g1), "=&v"(g2), "=&v"(g3), "=&v"(xa)
+        : "v"(base), "v"(hbase), "v"(xaddr), "n"(T1), "n"(T2), "n"(T3), "n"(H1), "n"(H2), "n"(H3)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b32 %0, %8\n"
+        "ds_read_b32 %1, %8 offset:%10\n"
+        "ds_read_b32 %2, %8 offset:%11\n"
+        "ds_read_b32 %3, %8 offset:%12\n"
+        "ds_read_b32 %4, %9\n"
+        "ds_read_b32 %5, %9 offset:%13\n"
+        "ds_read_b32 %6, %9 offset:%14\n"
+        "ds_read_b32 %7, %9 offset:%15\n"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(q0), "=&v"(q1), "=&v"(q2), "=&v"(q3), "=&v"(g0), "=&v"(g1), "=&v"(g2), "=&v"(g3)
+        : "v"(base), "v"(hbase), "n"(T1), "n"(T2), "n"(T3), "n"(H1), "n"(H2), "n"(H3)
+        : "memory");
+  }
   w[0][0] = q0, w[1][0] = q1, w[2][0] = q2, w[3][0] = q3;
   w[0][1] = w[1][1] = w[2][1] = w[3][1] = 0;
   hw[0] = g0, hw[1] = g1, hw[2] = g2, hw[3] = g3;
 }
 
-// acc[tile] += the affine group products of the GC groups of one stage (see the header:
-// codes enter the matrix core as exact bf16 values, 256 s P + (b - 128 s) X per group).
+// acc[tile] += u times the affine group products of the GC groups of one stage (see the
+// header: codes enter the matrix core as the exact bf16 values o + u q; per group s P, and
+// per stage one fp32 product of the group sums X with u b - o s).
 // Stage buffer layouts. 4-group stages hold the code layout's own bytes (fmoe_layout.h):
 // instruction j's KB holds rows j * kRPI .. + kRPI - 1, each row's piece contiguous with
 // its 16-byte chunks rotated by rot(row). 2-group stages use the layout of stage_off.
@@ -635,11 +696,13 @@ __device__ __forceinline__ void compute_stage(f32x4 (&acc)[4], const char* buf, 
   const uint32_t h_base = lds_addr(buf) + SG::kLoBytes + (kPiece ? nl * 32 : nl * 16) + (kb >> 1) * 4;
   const uint32_t lane_base = kPiece ? lds_addr(buf) + (nl / SG::kRPI) * 1024 + (nl % SG::kRPI) * SG::kRS + lane_part % 16
                                     : lds_addr(buf) + stage_off<BITS, GC>(nl, lane_part);
-  const uint32_t x_base = lds_addr(xs + g0 * 16 + 4 * kb);
+  // A operand of the bias product: X[token nl][group g0 + kb] (zero for kb >= GC; the read
+  // stays inside the LDS: xs is followed by the stage buffers)
+  const uint32_t x_addr = lds_addr(xs + (g0 + kb) * 16 + nl);
+  float xa = 0.f;
 #pragma unroll
   for (int gl = 0; gl < GC; ++gl) {
     uint32_t w[4][2];
-    f32x4 x4;
     uint32_t gbase;
     if constexpr (kPiece) {
       const int k = (gl * SG::kBPG + lane_part) / 16;  // the lane's chunk of the row's piece
@@ -651,26 +714,47 @@ __device__ __forceinline__ void compute_stage(f32x4 (&acc)[4], const char* buf, 
     constexpr int T2 = kPiece ? 2 * T1 : stage_off<BITS, GC>(32, 0);
     constexpr int T3 = kPiece ? 3 * T1 : stage_off<BITS, GC>(48, 0);
     uint32_t hw[4] = {0u, 0u, 0u, 0u};
-    if constexpr (BITS == 4) read_group4<T1, T2, T3>(gbase, x_base + gl * 64, w, x4);
-    else if constexpr (BITS == 3)
-      read_group3<T1, T2, T3, kPiece ? 512 : 256, kPiece ? 1024 : 512, kPiece ? 1536 : 768>(gbase, h_base + gl * 8,
-                                                                                         x_base + gl * 64, w, hw, x4);
-    else read_group2<T1, T2, T3>(gbase, x_base + gl * 64, w, x4);
+    if (gl == 0) {
+      if constexpr (BITS == 4) read_group4<true, T1, T2, T3>(gbase, x_addr, w, xa);
+      else if constexpr (BITS == 3)
+        read_group3<true, T1, T2, T3, kPiece ? 512 : 256, kPiece ? 1024 : 512, kPiece ? 1536 : 768>(gbase, h_base,
+                                                                                               x_addr, w, hw, xa);
+      else read_group2<true, T1, T2, T3>(gbase, x_addr, w, xa);
+      if (kb >= GC) xa = 0.f;
+    } else {
+      if constexpr (BITS == 4) read_group4<false, T1, T2, T3>(gbase, 0u, w, xa);
+      else if constexpr (BITS == 3)
+        read_group3<false, T1, T2, T3, kPiece ? 512 : 256, kPiece ? 1024 : 512, kPiece ? 1536 : 768>(
+            gbase, h_base + gl * 8, 0u, w, hw, xa);
+      else read_group2<false, T1, T2, T3>(gbase, 0u, w, xa);
+    }
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       u32x4 b0, b1;
       if constexpr (BITS == 3) build_b3(w[t][0], hw[t], kb, b0, b1);
       else build_b<BITS>(w[t], b0, b1);
-      const float cs = 256.f * bf16_lo(r.sb[t][gl]);
-      const float cb = fmaf(-0.5f, cs, bf16_hi(r.sb[t][gl]));
+      const float cs = bf16_lo(r.sb[t][gl]);
       f32x4 P = mfma(r.a[gl][0], b0, zero);
       P = mfma(r.a[gl][1], b1, P);
-      acc[t][0] = fmaf(cb, x4[0], fmaf(cs, P[0], acc[t][0]));
-      acc[t][1] = fmaf(cb, x4[1], fmaf(cs, P[1], acc[t][1]));
-      acc[t][2] = fmaf(cb, x4[2], fmaf(cs, P[2], acc[t][2]));
-      acc[t][3] = fmaf(cb, x4[3], fmaf(cs, P[3], acc[t][3]));
+      acc[t][0] = fmaf(cs, P[0], acc[t][0]);
+      acc[t][1] = fmaf(cs, P[1], acc[t][1]);
+      acc[t][2] = fmaf(cs, P[2], acc[t][2]);
+      acc[t][3] = fmaf(cs, P[3], acc[t][3]);
     }
     __builtin_amdgcn_sched_barrier(0);  // one group at a time: bounds the live fragments
+  }
+  // the stage's bias term: tile t += X (tokens x groups) times (u b - o s) (groups x rows);
+  // last in the stage, so that its latency passes while the next stage's first group is
+  // read and unpacked
+#pragma unroll
+  for (int t = 0; t < 4; ++t) {
+    // the lane's own group's word (group g0 + kb; the X operand is zero for kb >= GC)
+    uint32_t wk = lane_pick(r.sb[t][0], r.sb[t][1], 0x00000000FFFF0000ull);
+    if constexpr (GC == 4) {
+      wk = lane_pick(wk, r.sb[t][2], 0x0000FFFF00000000ull);
+      wk = lane_pick(wk, r.sb[t][3], 0xFFFF000000000000ull);
+    }
+    acc[t] = mfma4(xa, fmaf(-kCodeOffset<BITS>, bf16_lo(wk), kCodeUnit<BITS> * bf16_hi(wk)), acc[t]);
   }
 }
 
@@ -853,7 +937,7 @@ __global__ void __launch_bounds__(kBT, 2) gate_up_kernel(BParams p) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int r = m0 + 4 * kb + i;
-        const uint32_t b = bf16_rne(swiglu(acc[t][i], acc[t + 2][i]));
+        const uint32_t b = bf16_rne(swiglu(acc[t][i] / kCodeUnit<BITS>, acc[t + 2][i] / kCodeUnit<BITS>));
         if (r < cnt) {
           p.a16[(size_t)p.pairs[off + r] * I + col] = (uint16_t)b;
           part[i] += bf16_val(b);
@@ -914,7 +998,7 @@ __global__ void __launch_bounds__(kBT, 2) down_kernel(BParams p) {
       if (r < cnt) {
         float* y = p.ys + (size_t)p.pairs[off + r] * H + row0 + nl;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) y[16 * t] = acc[t][i];
+        for (int t = 0; t < 4; ++t) y[16 * t] = acc[t][i] / kCodeUnit<BITS>;
       }
     }
   }
