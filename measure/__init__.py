@@ -5,6 +5,11 @@ not part of the fmoe library; bench.py and the profile summaries use them.
     python -m measure stream      # JSON line: best read rate over 4 GiB
     python -m measure exchange    # JSON lines: exchange latency per mode and word count
     python -m measure replicas    # JSON lines: device-wide exchange per replica count / ack wait
+    python -m measure trace       # phase trace of the decode kernel on the 60-layer 4-bit stack
+
+The phase trace runs a copy of the fmoe library compiled with its trace hooks
+(-DFMOE_TRACE, libfmoe_trace.so here, built by build_trace()); the library itself is built
+without them.
 """
 from __future__ import annotations
 
@@ -31,6 +36,18 @@ def build() -> str:
            os.path.join(_HERE, "measure.hip"), "-o", _SO]
     subprocess.run(cmd, check=True, stderr=subprocess.DEVNULL)
     return _SO
+
+
+TRACE_SO = os.path.join(_HERE, "libfmoe_trace.so")
+TRACE_PHASES = 18  # phase stamps per layer and workgroup (fmoe_decode.hip, FMOE_TRACE)
+MAX_GRID = 1024
+
+
+def build_trace() -> str:
+    """The fmoe library compiled with its phase-trace hooks, as libfmoe_trace.so next to this file."""
+    from quantized_expert_ffn_fmoe_amd import _build
+
+    return _build.build(so=TRACE_SO, extra=["-DFMOE_TRACE"])
 
 
 _lib = None
@@ -124,6 +141,114 @@ def exchange(torch, mode: int, n_words: int, rounds: int = 200, epoch0: int = 0,
             "xcc_is_g_mod_8": bool(np.all(xc == np.arange(G) % 8)), "gave_up": bool(err.item() != 0)}
 
 
+def _q(x, axis=None):
+    """Median and 90th percentile (µs, rounded)."""
+    return [round(float(np.median(x, axis=axis)), 3), round(float(np.percentile(x, 90, axis=axis)), 3)]
+
+
+def phase_trace(torch, n_tokens: int = 16, warmup: int = 4) -> dict:
+    """Phase stamps of the decode kernel (traced build) on the 60-layer x 512-expert 4-bit
+    top-4 stack with the pre-norm, one launch per token (tokens = synthetic draws). Per layer
+    1..59 and workgroup: phase durations; per exchange, the time from the last workgroup's
+    publish to each reader's completion, and the spread of the publishes. Medians and 90th
+    percentiles over layers, tokens and workgroups. The tokens run back to back as in the
+    benchmark (the stamp buffer is switched by a kernel on the stream); per-token launch times
+    with the trace on and off (HIP events) give the hooks' own cost."""
+    import bench
+    import quantized_expert_ffn_fmoe_amd as fm
+    import synth
+
+    dev = torch.device("cuda:0")
+    L = fm.load(TRACE_SO)
+    L.fmoe_trace_set.restype = ctypes.c_int
+    L.fmoe_trace_set.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+    fm.use(L)
+    bits, H, I, E, K, NL = 4, bench.H_, bench.I_, bench.E_, bench.K_, bench.L_
+    blobs, routers, layers, _ = bench.build_stack(bits, dev)
+    G = lib().measure_cus()
+    per = NL * TRACE_PHASES * MAX_GRID
+    stamps = torch.zeros(n_tokens * per, dtype=torch.int64, device=dev)
+    wsb = fm.workspace_bytes(fm.OP_MOE_LAYER, 1, H, I, E, K)
+    ws = torch.zeros(wsb, dtype=torch.uint8, device=dev)
+    n_all = warmup + 2 * n_tokens
+    xs = torch.from_numpy(np.stack([synth.token(0, t, H) for t in range(n_all)])).to(dev)
+    h = torch.empty(H, dtype=torch.float32, device=dev)
+    idx = torch.empty((NL, K), dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    sp = stream.cuda_stream
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n_all)]
+
+    def run(t, buf):
+        if L.fmoe_trace_set(buf, sp) != 0:
+            raise RuntimeError("fmoe_trace_set failed")
+        ev[t][0].record(stream)
+        fm.moe_layer(layers, xs[t], h, 1, K, bench.EPS, fm.PRENORM, idx, None, ws, wsb, stream)
+        ev[t][1].record(stream)
+
+    # warm-up, then n_tokens back to back with the trace off, then n_tokens traced, each into
+    # its own slice of the stamp buffer; no host synchronisation in between
+    for t in range(warmup):
+        run(t, None)
+    for t in range(warmup, warmup + n_tokens):
+        run(t, None)
+    for i, t in enumerate(range(warmup + n_tokens, n_all)):
+        run(t, stamps.data_ptr() + i * per * 8)
+    L.fmoe_trace_set(None, sp)
+    torch.cuda.synchronize()
+    launch_us = {"off": [ev[t][0].elapsed_time(ev[t][1]) * 1e3 for t in range(warmup, warmup + n_tokens)],
+                 "on": [ev[t][0].elapsed_time(ev[t][1]) * 1e3 for t in range(warmup + n_tokens, n_all)]}
+    allst = stamps.cpu().numpy().reshape(n_tokens, NL, TRACE_PHASES, MAX_GRID)[:, :, :, :G]
+    per_token = [allst[i].astype(np.float64) * 0.01 for i in range(n_tokens)]
+    S = np.stack(per_token)  # [token][layer][phase][workgroup], µs
+    ls = slice(1, NL)  # layers with an h exchange
+    layer_us = np.diff(S[:, :, 0, :], axis=1)  # start-to-start per workgroup
+    out = {"workload": "60-layer x 512-expert 4-bit top-4 decode stack with pre-norm, one token per launch",
+           "tokens_traced": len(per_token), "workgroups": G, "clock": "s_memrealtime, 100 MHz",
+           "launch_us_trace_on": _q(launch_us["on"]), "launch_us_trace_off": _q(launch_us["off"]),
+           "layer_us": _q(layer_us)}
+    d = lambda a, b: S[:, ls, a, :] - S[:, ls, b, :]
+    ph = {"h gathered (from layer start)": d(1, 0),
+          "router + logits published": d(2, 1),
+          "logits gathered (after own publish)": d(3, 2),
+          "top-k (all rounds, softmax)": d(4, 3)}
+    for w in range(4):
+        ph[f"gate/up done, wave {w} (from h gathered)"] = d(5 + w, 1)
+    for w in range(4):
+        ph[f"a gathered, wave {w} (from its gate/up done)"] = d(9 + w, 5 + w)
+        ph[f"down done, wave {w} (from its a gathered)"] = d(13 + w, 9 + w)
+    ph["h published (from layer start)"] = d(17, 0)
+    out["phases_us"] = {k: _q(v) for k, v in ph.items()}
+    # exchanges: time from the last publish (over workgroups) to each reader's completion
+    last_h = S[:, 0:NL - 1, 17, :].max(axis=2)[:, :, None]  # layer l-1's h
+    last_lg = S[:, ls, 2, :].max(axis=2)[:, :, None]
+    ex = {"h": S[:, ls, 1, :] - last_h, "logits": S[:, ls, 3, :] - last_lg}
+    for j in range(4):  # slot j: produced by wave (j + 1) % 4 everywhere, read by wave j
+        last_a = S[:, ls, 5 + (j + 1) % 4, :].max(axis=2)[:, :, None]
+        ex[f"a slot {j}"] = S[:, ls, 9 + j, :] - last_a
+    out["exchange_after_last_publish_us"] = {k: _q(v) for k, v in ex.items()}
+    spread = {"layer start": S[:, ls, 0, :], "logits published": S[:, ls, 2, :], "h published": S[:, ls, 17, :]}
+    for w in range(4):
+        spread[f"gate/up done, wave {w}"] = S[:, ls, 5 + w, :]
+    out["spread_over_workgroups_us"] = {k: _q(v.max(axis=2) - v.min(axis=2)) for k, v in spread.items()}
+    del blobs, routers, layers, ws, stamps
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def trace_markdown(r: dict) -> str:
+    lines = [f"Workload: {r['workload']}; {r['tokens_traced']} traced tokens, {r['workgroups']} workgroups; "
+             f"clock {r['clock']}. Launch (µs, median / p90): trace on {r['launch_us_trace_on']}, "
+             f"off {r['launch_us_trace_off']}; layer start-to-start {r['layer_us']}.", "",
+             "| phase (per workgroup, layers 1-59) | median µs | p90 µs |", "|---|---:|---:|"]
+    lines += [f"| {k} | {v[0]} | {v[1]} |" for k, v in r["phases_us"].items()]
+    lines += ["", "| exchange: reader's completion after the last publish | median µs | p90 µs |", "|---|---:|---:|"]
+    lines += [f"| {k} | {v[0]} | {v[1]} |" for k, v in r["exchange_after_last_publish_us"].items()]
+    lines += ["", "| spread over workgroups (max - min) of | median µs | p90 µs |", "|---|---:|---:|"]
+    lines += [f"| {k} | {v[0]} | {v[1]} |" for k, v in r["spread_over_workgroups_us"].items()]
+    return "\n".join(lines)
+
+
 def main(argv) -> int:
     import torch
 
@@ -148,6 +273,11 @@ def main(argv) -> int:
             for reps in (1, 2, 4, 8, 16):
                 for no_ack in (False, True):
                     print(json.dumps(exchange(torch, 0, n, reps=reps, no_ack=no_ack)), flush=True)
+        return 0
+    if what == "trace":  # phase trace of the decode kernel (traced build)
+        r = phase_trace(torch)
+        print(json.dumps(r), flush=True)
+        print(trace_markdown(r), flush=True)
         return 0
     print(f"unknown probe {what}", file=sys.stderr)
     return 2

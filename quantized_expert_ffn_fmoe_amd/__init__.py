@@ -56,47 +56,59 @@ def lib():
     """The loaded libfmoe.so (raises if it was not built)."""
     global _lib
     if _lib is None:
-        if not os.path.exists(SO_PATH):
-            raise RuntimeError(f"{SO_PATH} is missing: build it with __graft_entry__.build() "
-                               "(hipcc --offload-arch=gfx950); there is no non-HIP fallback")
-        L = ctypes.CDLL(SO_PATH)
-        vp, i32, sz, u32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_uint
-        L.fmoe_status_string.restype = ctypes.c_char_p
-        L.fmoe_status_string.argtypes = [i32]
-        L.fmoe_version.restype = ctypes.c_char_p
-        L.fmoe_version.argtypes = []
-        L.fmoe_codes_bytes.restype = sz
-        L.fmoe_codes_bytes.argtypes = [i32, i32, i32]
-        L.fmoe_sb_bytes.restype = sz
-        L.fmoe_sb_bytes.argtypes = [i32, i32, i32]
-        L.fmoe_expert_bytes.restype = sz
-        L.fmoe_expert_bytes.argtypes = [i32, i32, i32, i32]
-        L.fmoe_expert_view.restype = i32
-        L.fmoe_expert_view.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(Expert)]
-        L.fmoe_pack.restype = i32
-        L.fmoe_pack.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
-        L.fmoe_workspace_bytes.restype = sz
-        L.fmoe_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
-        L.fmoe_dequant_matvec.restype = i32
-        L.fmoe_dequant_matvec.argtypes = [ctypes.POINTER(QMat), vp, vp, i32, vp]
-        L.fmoe_dequant_matvec_multi.restype = i32
-        L.fmoe_dequant_matvec_multi.argtypes = [ctypes.POINTER(QMat), i32, vp, ctypes.POINTER(vp), i32, vp]
-        L.fmoe_route_topk.restype = i32
-        L.fmoe_route_topk.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp]
-        L.fmoe_expert_ffn.restype = i32
-        L.fmoe_expert_ffn.argtypes = [ctypes.POINTER(Expert), vp, vp, vp, sz, vp]
-        L.fmoe_moe_layer.restype = i32
-        L.fmoe_moe_layer.argtypes = [ctypes.POINTER(Layer), i32, vp, vp, i32, i32, ctypes.c_float, u32, vp, vp, vp,
-                                     sz, vp]
-        L.fmoe_moe_layer_noalloc.restype = i32
-        L.fmoe_moe_layer_noalloc.argtypes = [ctypes.POINTER(Layer), i32, vp, vp, i32, i32, ctypes.c_float, u32, vp,
-                                             vp, vp]
-        L.fmoe_workspace_error.restype = i32
-        L.fmoe_workspace_error.argtypes = [vp, sz, vp, vp]
-        L.fmoe_batched_a16.restype = i32
-        L.fmoe_batched_a16.argtypes = [vp, sz, i32, i32, i32, i32, i32, i32, vp, vp]
-        _lib = L
+        _lib = load(SO_PATH)
     return _lib
+
+
+def use(library) -> None:
+    """Route this module's calls to another build of the library (the same C-ABI), e.g. the
+    phase-traced build that the measurement package makes; ``load`` gives such a handle."""
+    global _lib
+    _lib = library
+
+
+def load(path: str):
+    """ctypes handle of a build of the library at `path`, with every export's signature."""
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with __graft_entry__.build() "
+                           "(hipcc --offload-arch=gfx950); there is no non-HIP fallback")
+    L = ctypes.CDLL(path)
+    vp, i32, sz, u32 = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_uint
+    L.fmoe_status_string.restype = ctypes.c_char_p
+    L.fmoe_status_string.argtypes = [i32]
+    L.fmoe_version.restype = ctypes.c_char_p
+    L.fmoe_version.argtypes = []
+    L.fmoe_codes_bytes.restype = sz
+    L.fmoe_codes_bytes.argtypes = [i32, i32, i32]
+    L.fmoe_sb_bytes.restype = sz
+    L.fmoe_sb_bytes.argtypes = [i32, i32, i32]
+    L.fmoe_expert_bytes.restype = sz
+    L.fmoe_expert_bytes.argtypes = [i32, i32, i32, i32]
+    L.fmoe_expert_view.restype = i32
+    L.fmoe_expert_view.argtypes = [vp, i32, i32, i32, i32, ctypes.POINTER(Expert)]
+    L.fmoe_pack.restype = i32
+    L.fmoe_pack.argtypes = [vp, vp, vp, i32, i32, i32, i32, vp, vp, vp]
+    L.fmoe_workspace_bytes.restype = sz
+    L.fmoe_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32]
+    L.fmoe_dequant_matvec.restype = i32
+    L.fmoe_dequant_matvec.argtypes = [ctypes.POINTER(QMat), vp, vp, i32, vp]
+    L.fmoe_dequant_matvec_multi.restype = i32
+    L.fmoe_dequant_matvec_multi.argtypes = [ctypes.POINTER(QMat), i32, vp, ctypes.POINTER(vp), i32, vp]
+    L.fmoe_route_topk.restype = i32
+    L.fmoe_route_topk.argtypes = [vp, vp, i32, i32, i32, i32, vp, vp, vp, vp]
+    L.fmoe_expert_ffn.restype = i32
+    L.fmoe_expert_ffn.argtypes = [ctypes.POINTER(Expert), vp, vp, vp, sz, vp]
+    L.fmoe_moe_layer.restype = i32
+    L.fmoe_moe_layer.argtypes = [ctypes.POINTER(Layer), i32, vp, vp, i32, i32, ctypes.c_float, u32, vp, vp, vp,
+                                 sz, vp]
+    L.fmoe_moe_layer_noalloc.restype = i32
+    L.fmoe_moe_layer_noalloc.argtypes = [ctypes.POINTER(Layer), i32, vp, vp, i32, i32, ctypes.c_float, u32, vp,
+                                         vp, vp]
+    L.fmoe_workspace_error.restype = i32
+    L.fmoe_workspace_error.argtypes = [vp, sz, vp, vp]
+    L.fmoe_batched_a16.restype = i32
+    L.fmoe_batched_a16.argtypes = [vp, sz, i32, i32, i32, i32, i32, i32, vp, vp]
+    return L
 
 
 def _ptr(t) -> int | None:

@@ -57,6 +57,26 @@ constexpr int kPollA = 16;      // tagged a words of one slot polled together pe
 constexpr int kBatchR = 2;      // router slices per wave loaded ahead
 constexpr int kKeysInRegs = 8;  // top-k from registers when n_experts <= 512
 
+#ifdef FMOE_TRACE
+// Phase trace (measurement builds only, compiled with -DFMOE_TRACE): lane 0 of the named wave
+// of every workgroup stamps the device's constant-rate clock (s_memrealtime, 100 MHz) at each
+// phase boundary of every layer into trace_stamps[(layer * kTracePhases + phase) * kMaxGrid +
+// workgroup] (plain vector stores; set with fmoe_trace_set, null = off). Phases: 0 layer
+// start, 1 h gathered, 2 logits published, 3 logits gathered, 4 top-k done (wave 0); 5 + w
+// gate/up done, 9 + w a gathered, 13 + w down done (wave w); 17 h published (wave 0).
+constexpr int kTracePhases = 18;
+__device__ uint64_t* trace_stamps;
+#define FMOE_STAMP(ph, who)                                                                     \
+  do {                                                                                          \
+    if ((who) && lane == 0 && tstamps != nullptr)                                               \
+      tstamps[((size_t)lg * kTracePhases + (ph)) * kMaxGrid + g] = __builtin_amdgcn_s_memrealtime(); \
+  } while (0)
+#else
+#define FMOE_STAMP(ph, who) \
+  do {                      \
+  } while (0)
+#endif
+
 // gate/up items and down row blocks whose loads are issued together (fewer when every
 // lane holds more chunks per row, to stay within the register file)
 template <int CPL> constexpr int batch_gu() { return CPL >= 4 ? 1 : 4; }
@@ -192,6 +212,9 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
   dig_a.step = reinterpret_cast<float*>(dig_a.words + (size_t)NW * dig_a.n_chunks);
   dig_a.xsum = dig_a.step + dig_a.n_chunks;
 
+#ifdef FMOE_TRACE
+  uint64_t* const tstamps = trace_stamps;  // read once: the stamp sites then test a register
+#endif
   if (tid == 0) {
     // a workspace whose error word is set (an earlier call gave up) fails at once
     *fail = ld_dev_u32(p.err) != 0u;
@@ -292,6 +315,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
     const int lg = p.layer0 + l;
     const uint8_t* X = p.experts[l];
     const uint32_t ep = F + 3u * (uint32_t)l;
+    FMOE_STAMP(0, wave == 0);
     {
       const int ln = opaque_lane(lane);
       subG = ln & (lprG - 1);
@@ -351,6 +375,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
     if (tid == 0) *ready = 0;
     __syncthreads();
     if (*fail) break;
+    FMOE_STAMP(1, wave == 0);
     // v = inv * h is never formed: the router sums are scaled by inv, and so are the
     // steps and sums of v's digit image
     float inv = 1.f;
@@ -531,6 +556,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
       // the stores samples memory too early (its result waits for the stores anyway) and
       // costs one more round trip
       wait_vmem();
+      FMOE_STAMP(2, true);
       unsigned spins = 0;
       bool failed = false;
       const bool kGateWord = KS > K && !kSharedEarly;  // the gate logit comes with the others
@@ -608,11 +634,13 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
         }
         topk_progress(ready, K + 1);
       } else {
+        FMOE_STAMP(3, true);
         // the shared expert's weight: the logistic function of its gate logit (written
         // before the top-k releases its last round)
         if (kGateWord && lane == 0) wsel[K] = 1.0f / (1.0f + expf(-gate_logit));
         if (E <= 64 * kKeysInRegs) wave_topk_regs<kKeysInRegs>(kr, K, isel, lsel, wsel, ready);
         else wave_topk_keys(key, E, K, isel, lsel, wsel, ready);
+        FMOE_STAMP(4, true);
         if (g == 0 && lane < K) {
           size_t o = ((size_t)lg) * K + lane;
           if (p.idx_out) p.idx_out[o] = isel[lane];
@@ -650,6 +678,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
     } else {
       gu_run(blk_lo + wave * kBatchGU, blk_hi, kDecodeWaves * kBatchGU);
     }
+    FMOE_STAMP(5 + wave, true);
 
     // ---- prefetch: every wave issues the loads of its first kBatchD down items (all k
     // experts must be known)
@@ -765,6 +794,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
               if (i < I) vec[padded<CC>(j_lo * I + i)] = av[u];
             }
           }
+          FMOE_STAMP(9 + wave, true);
           __builtin_amdgcn_wave_barrier();
           build_digits<BITS>(dig_a, j_lo * nchD, I, [&](int i) { return vec[padded<CC>(i)]; }, 64, lane);
           __builtin_amdgcn_wave_barrier();
@@ -790,6 +820,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
           const int u = transposed_index<kBatchD>(lane);
           const int rl = (d_lo - j_lo * n_rb + u) * rpwD + rselD;
           if (subD < kBatchD && d_lo + u < d_hi && rl < nr) ybuf[j_lo * rows_wg + rl] = sum;
+          FMOE_STAMP(13 + wave, true);
         }
       }
     } else if (kFastD) {
@@ -917,6 +948,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
           if (last && lane < 16) p.h_out[r] = hn;
         }
       }
+      FMOE_STAMP(17, true);
     }
   }
   __syncthreads();
@@ -1026,3 +1058,16 @@ int launch_decode(const DecodeParams& p, int G, hipStream_t s) {
 }
 
 }  // namespace fmoe
+
+#ifdef FMOE_TRACE
+// Measurement builds only: where the decode kernels launched after this call on stream s
+// write their phase stamps (null = off). Set by a one-thread kernel on the stream, so that
+// traced launches can follow each other without a host synchronisation.
+namespace fmoe {
+__global__ void trace_set_kernel(uint64_t* stamps) { trace_stamps = stamps; }
+}  // namespace fmoe
+extern "C" int fmoe_trace_set(uint64_t* stamps, hipStream_t s) {
+  hipLaunchKernelGGL(fmoe::trace_set_kernel, dim3(1), dim3(1), 0, s, stamps);
+  return hipGetLastError() == hipSuccess ? 0 : -1;
+}
+#endif
