@@ -278,6 +278,11 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
   const int rs = I / G;
   const bool gu_il =
       kFastGU && !kSharedEarly && kDecodeWaves == 4 && I % G == 0 && rs > 0 && rs % kBatchGU == 0;
+  // the workgroup's row group: consecutive groups go to workgroups of one XCD (workgroup g
+  // runs on XCD g mod 8), so that the 128-byte lines of blocked scale/bias words that two
+  // 4-row groups share are fetched once into that XCD's L2 (with row group g they were
+  // fetched by two XCDs: 1.097 against 1.041 bytes per algorithmic byte)
+  const int gu_row0 = (G % 8 == 0 ? (g % 8) * (G / 8) + g / 8 : g) * rs;
   const int gu_need =
       gu_il ? 0 : blk_lo >= blk_hi ? 0 : gu_lslot < K ? gu_lslot + 1 : gu_first < K ? K : 0;
   // What a workgroup takes part in. Router rows or gate/up items need all of v, hence the
@@ -673,7 +678,7 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
     if (gu_il) {
       for (int j = (wave + 3) % kDecodeWaves; j < K; j += kDecodeWaves) {
         wait_ready(ready, j + 1);
-        gu_run(j * I + g * rs, j * I + g * rs + rs, kBatchGU);
+        gu_run(j * I + gu_row0, j * I + gu_row0 + rs, kBatchGU);
       }
     } else {
       gu_run(blk_lo + wave * kBatchGU, blk_hi, kDecodeWaves * kBatchGU);
