@@ -1010,20 +1010,33 @@ __global__ void __launch_bounds__(kBT) combine_kernel(const float* __restrict__ 
                                                       int H, int k, int kr, float* __restrict__ h_next,
                                                       int32_t* __restrict__ idx_out, float* __restrict__ w_out,
                                                       int layer, int n_layers) {
-  // k slots per token (the kr routed ones, then the shared expert's if any)
+  // k slots per token (the kr routed ones, then the shared expert's if any). The loads of h
+  // and of up to 4 slots' rows are issued together (one memory round trip per 4 slots, not
+  // one per slot); the sum still runs in slot order.
   const int t = blockIdx.y;
   const int i4 = blockIdx.x * kBT + threadIdx.x;
   if (i4 < H / 4) {
-    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    for (int j = 0; j < k; ++j) {
-      const float wj = w[t * k + j];
-      const float4 y = reinterpret_cast<const float4*>(ys + ((size_t)t * k + j) * H)[i4];
-      s.x = fmaf(wj, y.x, s.x);
-      s.y = fmaf(wj, y.y, s.y);
-      s.z = fmaf(wj, y.z, s.z);
-      s.w = fmaf(wj, y.w, s.w);
-    }
     const float4 hv = reinterpret_cast<const float4*>(h + (size_t)t * H)[i4];
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int j0 = 0; j0 < k; j0 += 4) {
+      float4 y[4];
+      float wj[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int j = min(j0 + u, k - 1);  // past the last slot: a repeated row, weight 0
+        y[u] = reinterpret_cast<const float4*>(ys + ((size_t)t * k + j) * H)[i4];
+        wj[u] = j0 + u < k ? w[t * k + j] : 0.f;
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        if (j0 + u < k) {
+          s.x = fmaf(wj[u], y[u].x, s.x);
+          s.y = fmaf(wj[u], y[u].y, s.y);
+          s.z = fmaf(wj[u], y[u].z, s.z);
+          s.w = fmaf(wj[u], y[u].w, s.w);
+        }
+      }
+    }
     reinterpret_cast<float4*>(h_next + (size_t)t * H)[i4] = make_float4(hv.x + s.x, hv.y + s.y, hv.z + s.z, hv.w + s.w);
   }
   if (blockIdx.x == 0 && (int)threadIdx.x < kr) {
