@@ -43,11 +43,11 @@ TRACE_PHASES = 18  # phase stamps per layer and workgroup (fmoe_decode.hip, FMOE
 MAX_GRID = 1024
 
 
-def build_trace() -> str:
+def build_trace(jobs: int = 4) -> str:
     """The fmoe library compiled with its phase-trace hooks, as libfmoe_trace.so next to this file."""
     from quantized_expert_ffn_fmoe_amd import _build
 
-    return _build.build(so=TRACE_SO, extra=["-DFMOE_TRACE"])
+    return _build.build(jobs=jobs, so=TRACE_SO, extra=["-DFMOE_TRACE"])
 
 
 _lib = None
