@@ -210,76 +210,91 @@ __device__ __forceinline__ void stage_token(const float* __restrict__ hr, int H,
 // ---------------------------------------------------------------- 2. route
 // Router logits as an fp32 matrix-core product on the raw h (the pre-norm's 1 / rms is a
 // per-token factor, applied to the summed logits by route_stage_kernel), with
-// v_mfma_f32_16x16x4f32 (lane l holds
-// A[l % 16][l / 16], B[l / 16][l % 16], result as above). Workgroup (e-tile, slice):
-// 16 experts x one 512-column slice of K, wave w taking 128 columns of it; the four
-// waves' tiles are added in LDS in wave order and written as the slice's partial
-// logits part[slice][t][e]. A lane loads 4 consecutive columns of its token / expert row
-// and feeds them to 4 products, so each group of 4 products covers 16 columns.
+// v_mfma_f32_16x16x4f32 (lane l holds A[l % 16][l / 16], B[l / 16][l % 16], result as above).
+// Workgroup (e-tile, slice): 16 experts x one 512-column slice of K, for up to 64 tokens at a
+// time, wave w taking the 16-token tile w; its partial logits part[slice][t][e] are written
+// directly. The operands go through LDS in 128-column chunks: the global loads are in lane
+// order (consecutive threads read consecutive 16-byte pieces of one row, so every lane quad
+// reads one piece of a cache line; loaded in matrix-core order instead, a quad would span 4
+// rows), and each row's 32 pieces sit in LDS as 8 blocks of 4 pieces plus one pad piece per
+// row, so the 16-byte operand reads (16 rows, same block) fall on distinct banks. The next
+// chunk's loads are in flight while the current one is multiplied.
 constexpr int kRtSlice = 512;
-constexpr int kRtWaveCols = kRtSlice / (kBT / 64);
-constexpr int kRtSteps = kRtWaveCols / 16;
+constexpr int kRtChunk = 128;                     // columns per LDS chunk
+constexpr int kRtBlocks = kRtChunk / 16;          // 16-column blocks per chunk
+constexpr int kRtPad = 5;                         // 16-byte pieces per row and block slot (4 + pad)
+constexpr int kRtTok = 64;                        // tokens per pass (4 waves x 16)
+constexpr int kRtLoadsA = kRtTok * kRtChunk / 4 / kBT;  // float4 loads per thread per chunk
+constexpr int kRtLoadsB = 16 * kRtChunk / 4 / kBT;
 constexpr int kRtMaxParts = 16;  // slices of a hidden size up to 8192
+static_assert(kRtLoadsA * kBT * 4 == kRtTok * kRtChunk && kRtLoadsB * kBT * 4 == 16 * kRtChunk, "chunk loads");
 
 __device__ __forceinline__ f32x4 mfma4(float a, float b, const f32x4& c) {
   return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
 }
 
+// Lane-order loads of one chunk (columns k0 .. k0 + 127): item i = tid + kBT * u is the
+// 16-byte piece i % 32 of row i / 32 (token rows past T and expert rows past E repeat the
+// last one; their products are not stored).
+__device__ __forceinline__ void rt_load_chunk(f32x4 (&ra)[kRtLoadsA], f32x4 (&rb)[kRtLoadsB],
+                                              const float* __restrict__ R, const float* __restrict__ v, int tid,
+                                              int t0, int T, int e0, int E, int H, int k0) {
+#pragma unroll
+  for (int u = 0; u < kRtLoadsA; ++u) {
+    const int i = tid + kBT * u, t = min(t0 + i / 32, T - 1);
+    ra[u] = reinterpret_cast<const f32x4*>(v + (size_t)t * H + k0)[i % 32];
+  }
+#pragma unroll
+  for (int u = 0; u < kRtLoadsB; ++u) {
+    const int i = tid + kBT * u, e = min(e0 + i / 32, E - 1);
+    rb[u] = reinterpret_cast<const f32x4*>(R + (size_t)e * H + k0)[i % 32];
+  }
+}
+
 __global__ void __launch_bounds__(kBT) router_kernel_mfma(const float* __restrict__ R, const float* __restrict__ v,
                                                           int T, int E, int H, float* __restrict__ part) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nl = lane & 15, kb = lane >> 4;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nl = lane & 15, kb = lane >> 4;
   const int e0 = blockIdx.x * 16, ks = blockIdx.y;
-  const int k_lo = ks * kRtSlice + wave * kRtWaveCols;
-  const bool e_ok = e0 + nl < E;
-  const float* rrow = R + (size_t)(e_ok ? e0 + nl : 0) * H;
-  __shared__ float red[kBT / 64][4][256];  // [wave][m-tile][16 tokens x 16 experts]
-  for (int t0 = 0; t0 < T; t0 += 64) {
-    const int nmt = min(4, (T - t0 + 15) / 16);
-    f32x4 acc[4];
+  const int k_lo = ks * kRtSlice, k_hi = min(H, k_lo + kRtSlice);
+  const int n_chunks = (k_hi - k_lo) / kRtChunk;  // H % 128 == 0 (batched shapes)
+  __shared__ f32x4 sA[kRtBlocks][kRtTok][kRtPad];  // [block][token][piece]
+  __shared__ f32x4 sB[kRtBlocks][16][kRtPad];      // [block][expert][piece]
+  for (int t0 = 0; t0 < T; t0 += kRtTok) {
+    f32x4 ra[kRtLoadsA], rb[kRtLoadsB];
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    rt_load_chunk(ra, rb, R, v, tid, t0, T, e0, E, H, k_lo);
+    for (int c = 0; c < n_chunks; ++c) {
+      __syncthreads();  // the previous chunk's operand reads are done
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt) acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    // A wave's 128 columns are 8 steps of 16; all of a step's loads are issued before the
-    // first product so that one memory round trip covers the whole slice. The loads are
-    // unconditional: rows past the token count read the last token and rows past the
-    // expert count the first expert's row, and their products only reach sums that are
-    // never stored. A wave past the end of K (H % 512 == 256) has no columns.
-    if (k_lo < H) {  // uniform
-      const float* brow = rrow + k_lo + 4 * kb;
-      float4 b[kRtSteps], a[4][kRtSteps];
-#pragma unroll
-      for (int j = 0; j < kRtSteps; ++j) b[j] = *reinterpret_cast<const float4*>(brow + 16 * j);
-#pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        const float* arow = v + (size_t)min(t0 + mt * 16 + nl, T - 1) * H + k_lo + 4 * kb;
-#pragma unroll
-        for (int j = 0; j < kRtSteps; ++j) a[mt][j] = *reinterpret_cast<const float4*>(arow + 16 * j);
+      for (int u = 0; u < kRtLoadsA; ++u) {
+        const int i = tid + kBT * u;
+        sA[(i % 32) / 4][i / 32][i % 4] = ra[u];
       }
 #pragma unroll
-      for (int mt = 0; mt < 4; ++mt) {
-        if (mt < nmt) {  // uniform
+      for (int u = 0; u < kRtLoadsB; ++u) {
+        const int i = tid + kBT * u;
+        sB[(i % 32) / 4][i / 32][i % 4] = rb[u];
+      }
+      __syncthreads();
+      // the next chunk (unconditional: after the last one, the last again, unused)
+      rt_load_chunk(ra, rb, R, v, tid, t0, T, e0, E, H, k_lo + min(c + 1, n_chunks - 1) * kRtChunk);
+      // tile of wave w: tokens t0 + 16 w + nl; block j's columns 16 j + 4 kb + (0..3)
 #pragma unroll
-          for (int j = 0; j < kRtSteps; ++j) {
-            acc[mt] = mfma4(a[mt][j].x, b[j].x, acc[mt]);
-            acc[mt] = mfma4(a[mt][j].y, b[j].y, acc[mt]);
-            acc[mt] = mfma4(a[mt][j].z, b[j].z, acc[mt]);
-            acc[mt] = mfma4(a[mt][j].w, b[j].w, acc[mt]);
-          }
-        }
+      for (int j = 0; j < kRtBlocks; ++j) {
+        const f32x4 a = sA[j][16 * wave + nl][kb];
+        const f32x4 b = sB[j][nl][kb];
+        acc = mfma4(a[0], b[0], acc);
+        acc = mfma4(a[1], b[1], acc);
+        acc = mfma4(a[2], b[2], acc);
+        acc = mfma4(a[3], b[3], acc);
       }
     }
+    // lane holds tokens t0 + 16 w + 4 kb + i, expert e0 + nl
 #pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) red[wave][mt][(4 * kb + i) * 16 + nl] = acc[mt][i];
-    __syncthreads();
-    for (int i = threadIdx.x; i < nmt * 256; i += kBT) {
-      const int mt = i >> 8, m = (i >> 4) & 15, n = i & 15;
-      const int tok = t0 + mt * 16 + m, e = e0 + n;
-      const float s = ((red[0][mt][m * 16 + n] + red[1][mt][m * 16 + n]) + red[2][mt][m * 16 + n]) +
-                      red[3][mt][m * 16 + n];
-      if (tok < T && e < E) part[((size_t)ks * T + tok) * E + e] = s;
+    for (int i = 0; i < 4; ++i) {
+      const int tok = t0 + 16 * wave + 4 * kb + i, e = e0 + nl;
+      if (tok < T && e < E) part[((size_t)ks * T + tok) * E + e] = acc[i];
     }
-    __syncthreads();
   }
 }
 
