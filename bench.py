@@ -93,10 +93,35 @@ def workspace_error_word(torch, ws, wsb) -> int:
     return int(err.item())
 
 
+def _code_only(text: str) -> str:
+    """C++ source without its comments and blank lines (string literals kept as they are)."""
+    out, i, n = [], 0, len(text)
+    while i < n:
+        c = text[i]
+        if c == '"':  # string literal
+            j = i + 1
+            while j < n and text[j] != '"':
+                j += 2 if text[j] == "\\" else 1
+            out.append(text[i:j + 1])
+            i = j + 1
+        elif text.startswith("//", i):
+            while i < n and text[i] != "\n":
+                i += 1
+        elif text.startswith("/*", i):
+            j = text.find("*/", i + 2)
+            i = n if j < 0 else j + 2
+        else:
+            out.append(c)
+            i += 1
+    return "\n".join(ln.rstrip() for ln in "".join(out).splitlines() if ln.strip())
+
+
 def decode_source_hash() -> str:
+    """Hash of the decode kernel's sources with comments removed: the committed HBM-traffic
+    counters (profiles/) stay attached to the kernel as long as its code is unchanged."""
     h = hashlib.sha256()
     for f in ("fmoe_decode.hip", "fmoe_device.h", "fmoe_decode.h", "fmoe_intdot.h", "fmoe_layout.h"):
-        h.update(open(os.path.join(ROOT, "quantized_expert_ffn_fmoe_amd", "csrc", f), "rb").read())
+        h.update(_code_only(open(os.path.join(ROOT, "quantized_expert_ffn_fmoe_amd", "csrc", f)).read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -13,9 +13,11 @@
 //   3. every workgroup gathers the logits; wave 0 selects the top-k and the softmax
 //      weights (no extra round trip) and releases the slots one by one, while the other
 //      waves build the digit image of v (see fmoe_intdot.h);
-//   4. gate/up: workgroup g owns a contiguous run of (slot j, row i) items (consecutive
-//      rows of one expert); each item reads gate row i and up row i of expert idx[j] and
-//      publishes a[j][i] = silu(g)*u; every wave then issues the loads of its down rows;
+//   4. gate/up: every workgroup takes 4 consecutive rows of every routed slot, slot j on
+//      wave (j + 1) mod 4 once that slot's top-k round is out (compiled shapes; otherwise a
+//      contiguous run of (slot, row) items per workgroup); each item reads gate row i and up
+//      row i of expert idx[j] and publishes a[j][i] = silu(g)*u; every wave then issues the
+//      loads of its down rows;
 //   5. a: each wave gathers the a values of the slot(s) its down rows belong to and
 //      builds their digit image;
 //   6. down + combine + residual: workgroup g owns a contiguous block of h rows and
