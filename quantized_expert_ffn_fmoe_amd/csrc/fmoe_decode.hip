@@ -147,6 +147,51 @@ __device__ __forceinline__ int opaque_lane(int v) {
   return v;
 }
 
+// Spread gate/up schedule (compiled top-4 shapes at 2 and 3 bits): a workgroup's 4 rows of each
+// of the 4 slots go to its 4 waves so that no wave computes more than one row of the slot
+// released last. Wave 1 + d (d < 3) takes rows 0 and 1 of slot d and one row of each other slot
+// j < 3 (row 2 on wave 1 + (j + 1) % 3, row 3 on wave 1 + (j + 2) % 3); row w of slot 3 goes to
+// wave w, so that wave 0, busy with the top-k, takes a single row. Item m of wave 1 + D
+// (D = -1: wave 0) is row sp_row(m) of slot sp_slot(m), items in slot order.
+template <int D>
+constexpr int sp_items() {
+  return D < 0 ? 1 : 5;
+}
+template <int D>
+constexpr int sp_slot(int m) {
+  if (D < 0) return 3;
+  int first = 0;
+  for (int j = 0; j < 3; ++j) {
+    const int n = j == D ? 2 : 1;
+    if (m < first + n) return j;
+    first += n;
+  }
+  return 3;
+}
+template <int D>
+constexpr int sp_row(int m) {
+  if (D < 0) return 0;
+  int first = 0;
+  for (int j = 0; j < 3; ++j) {
+    const int n = j == D ? 2 : 1;
+    if (m < first + n) return j == D ? m - first : (D == (j + 1) % 3 ? 2 : 3);
+    first += n;
+  }
+  return 1 + D;
+}
+template <int D>
+constexpr int sp_first(int j) {  // the first item of slot j
+  int m = 0;
+  while (m < sp_items<D>() && sp_slot<D>(m) != j) ++m;
+  return m;
+}
+template <int D>
+constexpr int sp_count(int j) {  // items of slot j
+  int n = 0;
+  for (int m = 0; m < sp_items<D>(); ++m) n += sp_slot<D>(m) == j ? 1 : 0;
+  return n;
+}
+
 // Wait until wave 0's top-k progress word (LDS) reached r.
 __device__ __forceinline__ void wait_ready(const int* ready, int r) {
   while (__hip_atomic_load(const_cast<int*>(ready), __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP) < r)
@@ -285,6 +330,12 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
   // 4-row groups share are fetched once into that XCD's L2 (with row group g they were
   // fetched by two XCDs: 1.097 against 1.041 bytes per algorithmic byte)
   const int gu_row0 = (G % 8 == 0 ? (g % 8) * (G / 8) + g / 8 : g) * rs;
+  // The spread schedule above, at 2 and 3 bits: there each slot's rows arrive about a fixed
+  // latency after its release, so the products of the slot released last set the end of the
+  // gate/up phase. (At 4 bits the gate/up window streams near the HBM rate, so spreading the
+  // products gains nothing, and the fifth row in flight on waves 1-3 costs registers.)
+  constexpr bool kSpreadGU = kFastGU && !kSharedEarly && KC == 4 && kDecodeWaves == 4 && BITS != 4;
+  const bool gu_sp = kSpreadGU && gu_il && rs == 4;
   const int gu_need =
       gu_il ? 0 : blk_lo >= blk_hi ? 0 : gu_lslot < K ? gu_lslot + 1 : gu_first < K ? K : 0;
   // What a workgroup takes part in. Router rows or gate/up items need all of v, hence the
@@ -677,7 +728,81 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
 
     // ---- 4. gate/up + SwiGLU over this workgroup's run of blocks, dealt to its waves in
     // runs of kBatchGU blocks whose loads are issued together; a is published tagged
-    if (gu_il) {
+    if (gu_sp) {
+      if constexpr (kSpreadGU) {
+        // the wave's items (sp_slot): loads issued slot by slot as the top-k releases them,
+        // then the products slot by slot in arrival order, each slot's items reduced together
+        // and their a published
+        auto run_spread = [&](auto DS) {
+          constexpr int D = decltype(DS)::value;
+          constexpr int NI = sp_items<D>();
+          CChunk<BITS> wg[NI][CPL_G], wu[NI][CPL_G];
+          uint32_t sg[NI][CPL_G], su[NI][CPL_G];
+#pragma unroll
+          for (int m = 0; m < NI; ++m) {
+            const int j = sp_slot<D>(m);
+            if (m == 0 || j != sp_slot<D>(m - 1)) wait_ready(ready, j + 1);
+            const int i = gu_row0 + sp_row<D>(m);
+            const uint8_t* bp = X + (size_t)isel[j] * p.expert_stride;
+            const uint32_t* gsb = reinterpret_cast<const uint32_t*>(bp + 3 * cbH);  // blocked, fmoe_layout.h
+            const uint32_t* usb = reinterpret_cast<const uint32_t*>(bp + 3 * cbH + sbb);
+#pragma unroll
+            for (int q = 0; q < CPL_G; ++q) {
+              const int c = lane + 64 * q;  // kFastGU: 64 lanes per row
+              load_cchunk<BITS>(wg[m][q], bp, I, H, i, c);
+              load_cchunk<BITS>(wu[m][q], bp + cbH, I, H, i, c);
+              const size_t so = sb_offset(I, ngH, i, c / C::kPerGroup);
+              sg[m][q] = gsb[so];
+              su[m][q] = usb[so];
+            }
+            if (m == 0) {
+#pragma unroll
+              for (int q = 0; q < CPL_G; ++q) load_dchunk<BITS>(dc[q], dig, lane + 64 * q);
+            }
+          }
+          static_assert(kRep == 8, "the lane groups below store the 8 replicas of a");
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int n = sp_count<D>(j), m0 = sp_first<D>(j);
+            if (n == 0) continue;
+            float gsum[2] = {0.f, 0.f}, usum[2] = {0.f, 0.f};
+#pragma unroll
+            for (int b = 0; b < 2; ++b) {
+              if (b < n) {
+#pragma unroll
+                for (int q = 0; q < CPL_G; ++q) {
+                  gsum[b] += chunk_dot_int<BITS>(wg[m0 + b][q], sg[m0 + b][q], dc[q]);
+                  usum[b] += chunk_dot_int<BITS>(wu[m0 + b][q], su[m0 + b][q], dc[q]);
+                }
+              }
+            }
+            const size_t a0 = (size_t)j * I + gu_row0 + sp_row<D>(m0);
+            if (n == 1) {
+              // even lanes hold the gate sum, odd lanes the up sum; even lane 2 r stores replica r
+              const float vals[2] = {gsum[0], usum[0]};
+              const float sum = reduce_transposed<2, 64>(vals);
+              const float up_sum = xlane<1>(sum);
+              if (!(lane & 1) && (lane >> 1) < kRep)
+                st_dev_u64(p.a + (size_t)(lane >> 1) * KI + a0, atag | __float_as_uint(swiglu(sum, up_sum)));
+            } else {
+              // lane 4 r + 2 b holds the gate sum of item b (rows 0, 1), its odd neighbour the
+              // up sum; it stores replica r
+              const float vals[4] = {gsum[0], gsum[1], usum[0], usum[1]};
+              const float sum = reduce_transposed<4, 64>(vals);
+              const float up_sum = xlane<1>(sum);
+              if (!(lane & 1) && (lane >> 2) < kRep)
+                st_dev_u64(p.a + (size_t)(lane >> 2) * KI + a0 + ((lane >> 1) & 1),
+                           atag | __float_as_uint(swiglu(sum, up_sum)));
+            }
+            __builtin_amdgcn_sched_barrier(0);  // slots in arrival order
+          }
+        };
+        if (wave == 0) run_spread(std::integral_constant<int, -1>{});
+        else if (wave == 1) run_spread(std::integral_constant<int, 0>{});
+        else if (wave == 2) run_spread(std::integral_constant<int, 1>{});
+        else run_spread(std::integral_constant<int, 2>{});
+      }
+    } else if (gu_il) {
       for (int j = (wave + 3) % kDecodeWaves; j < K; j += kDecodeWaves) {
         wait_ready(ready, j + 1);
         gu_run(j * I + gu_row0, j * I + gu_row0 + rs, kBatchGU);
