@@ -95,12 +95,12 @@ __device__ __forceinline__ void matvec_pass(const uint8_t* __restrict__ codes, c
   mv_load<BITS, CPL, R>(P, codes, sb, rows, cols, lpr, rb0);
   mv_reduce<BITS, CPL, R>(P, yv, rows, cols, lpr, rb0, xc);
 }
-template <int BITS, int CPL>
+template <int BITS, int CPL, int RB = 0>
 __global__ void __launch_bounds__(256) matvec_kernel(const uint8_t* __restrict__ codes,
                                                      const uint32_t* __restrict__ sb, const float* __restrict__ x,
                                                      float* __restrict__ y, int rows, int cols, int lpr) {
   using C = Chunk<BITS>;
-  constexpr int R = mv_pass_blocks<CPL>();
+  constexpr int R = RB ? RB : mv_pass_blocks<CPL>();
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int sub = lane & (lpr - 1);
@@ -276,13 +276,30 @@ int launch_matvec(const QMat& W, const float* x, float* y, int n_vec, hipStream_
   int lpr = 1;
   while (lpr < n_chunks && lpr < 64) lpr <<= 1;
   const int cpl = (n_chunks + lpr - 1) / lpr;
-  const int span = (cpl >= 3 ? 2 : 4) * (64 / lpr);  // rows of a wave pass (mv_pass_blocks of the CPL run)
+  // A matrix of at most 4096 row blocks (of 64 / lpr rows) gets one row block per wave, in
+  // four-wave workgroups, so that every SIMD of every compute unit takes part; larger ones
+  // take mv_pass_blocks row blocks per wave pass.
+  const int one = (W.rows + 64 / lpr - 1) / (64 / lpr);
+  const bool single = one * n_vec <= 4096;
+  const int span = single ? 64 / lpr : (cpl >= 3 ? 2 : 4) * (64 / lpr);  // rows of a wave pass
   const int waves_needed = (W.rows + span - 1) / span;
   int threads = 0, blocks = 0;
-  mv_grid(waves_needed * n_vec, waves_needed, &threads, &blocks);
+  if (single) {
+    threads = 256;
+    blocks = (waves_needed + 3) / 4;
+  } else {
+    mv_grid(waves_needed * n_vec, waves_needed, &threads, &blocks);
+  }
   dim3 grid(blocks, n_vec);
   const uint8_t* codes = static_cast<const uint8_t*>(W.codes);
-#define FMOE_MV(B, C) hipLaunchKernelGGL((matvec_kernel<B, C>), grid, dim3(threads), 0, s, codes, W.sb, x, y, W.rows, W.cols, lpr)
+#define FMOE_MV(B, C)                                                                                         \
+  do {                                                                                                        \
+    if (single)                                                                                               \
+      hipLaunchKernelGGL((matvec_kernel<B, C, 1>), grid, dim3(threads), 0, s, codes, W.sb, x, y, W.rows, W.cols, \
+                         lpr);                                                                                \
+    else                                                                                                      \
+      hipLaunchKernelGGL((matvec_kernel<B, C>), grid, dim3(threads), 0, s, codes, W.sb, x, y, W.rows, W.cols, lpr); \
+  } while (0)
   if (W.bits == 4) {
     if (cpl == 1) FMOE_MV(4, 1);
     else if (cpl == 2) FMOE_MV(4, 2);
