@@ -191,6 +191,27 @@ constexpr int sp_count(int j) {  // items of slot j
   for (int m = 0; m < sp_items<D>(); ++m) n += sp_slot<D>(m) == j ? 1 : 0;
   return n;
 }
+template <int D>
+constexpr void sp_mark(int (&seen)[4][4]) {
+  for (int m = 0; m < sp_items<D>(); ++m) ++seen[sp_slot<D>(m)][sp_row<D>(m)];
+}
+// every (slot, row) of the workgroup's 16 goes to exactly one wave, and each wave's items are in
+// slot order
+constexpr bool sp_schedule_ok() {
+  int seen[4][4] = {};
+  sp_mark<-1>(seen);
+  sp_mark<0>(seen);
+  sp_mark<1>(seen);
+  sp_mark<2>(seen);
+  for (int j = 0; j < 4; ++j)
+    for (int r = 0; r < 4; ++r)
+      if (seen[j][r] != 1) return false;
+  for (int m = 1; m < 5; ++m)
+    if (sp_slot<0>(m) < sp_slot<0>(m - 1) || sp_slot<1>(m) < sp_slot<1>(m - 1) || sp_slot<2>(m) < sp_slot<2>(m - 1))
+      return false;
+  return true;
+}
+static_assert(sp_schedule_ok(), "the spread gate/up schedule covers each row of each slot once");
 
 // Wait until wave 0's top-k progress word (LDS) reached r.
 __device__ __forceinline__ void wait_ready(const int* ready, int r) {
