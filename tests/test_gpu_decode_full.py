@@ -134,6 +134,7 @@ def _plant(R, z, experts, gammas):
     (512, 4096, 1024, 4, 4, (37, 300), []),               # compiled shape: the tied pair ranks first
     (512, 4096, 1024, 4, 4, (37, 300), [5, 411, 128]),    # ... and at the cut: only 37 is selected
     (512, 4096, 1024, 4, 2, (300, 301), [7]),              # 2-bit compiled shape, neighbours in one lane row
+    (512, 4096, 1024, 4, 3, (37, 300), [5, 411, 128]),     # 3-bit compiled shape, the pair at the cut
     (64, 1024, 256, 4, 4, (3, 50), [60]),                  # generic kernel, keys in registers
     (1000, 128, 64, 2, 4, (900, 901), [2]),                # more than 512 experts: keys in LDS
 ])
