@@ -64,6 +64,8 @@ def lib():
         L.measure_cus.argtypes = []
         L.measure_stream_read.restype = i32
         L.measure_stream_read.argtypes = [vp, sz, i32, i32, i32, vp, vp]
+        L.measure_row_stages.restype = i32
+        L.measure_row_stages.argtypes = [vp, sz, i32, i32, i32, vp, vp]
         L.measure_exchange.restype = i32
         L.measure_exchange.argtypes = [i32, i32, i32, u32, vp, vp, vp, vp, i32, i32, vp]
         _lib = L
@@ -108,6 +110,47 @@ def stream_read(torch, gib: int = 4, reps: int = 5, variants=(0, 1)) -> dict:
     torch.cuda.empty_cache()
     return {"kind": f"read-only streaming kernel (measure.hip) over {gib} GiB, best of {reps} passes per variant",
             "gbs": round(best, 1), "variants": table}
+
+
+def row_stages(torch, gib: int = 4, reps: int = 5) -> dict:
+    """Read rate (GB/s) of the row-stage kernel (measure.hip item 3) over a gib-GiB buffer for
+    rows of 2048 bytes (a 4-bit gate/up row at hidden 4096) and 512 bytes (a 4-bit down row at
+    intermediate 1024), every stage piece P and 2 or 4 stages in flight; best of `reps` passes
+    after one untimed pass, HIP events on the launch stream."""
+    dev = torch.device("cuda:0")
+    nbytes = gib << 30
+    buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
+    buf.fill_(1)
+    sink = torch.zeros(4, dtype=torch.int32, device=dev)
+    stream = torch.cuda.current_stream(dev)
+    table = []
+    for row_bytes in (2048, 512):
+        for depth in (2, 4):
+            for piece in (128, 256, 512, 1024, 2048):
+                if row_bytes % piece:
+                    continue
+
+                def once():
+                    rc = lib().measure_row_stages(buf.data_ptr(), nbytes, row_bytes, piece, depth, sink.data_ptr(),
+                                                  stream.cuda_stream)
+                    if rc != 0:
+                        raise RuntimeError(f"measure_row_stages: {rc}")
+
+                once()
+                gbs = 0.0
+                for _ in range(reps):
+                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                    e0.record(stream)
+                    once()
+                    e1.record(stream)
+                    torch.cuda.synchronize()
+                    gbs = max(gbs, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+                table.append({"row_bytes": row_bytes, "piece": piece, "rows_per_stage": 8192 // piece,
+                              "stages_in_flight": depth, "gbs": round(gbs, 1)})
+                print(json.dumps(table[-1]), flush=True)
+    del buf
+    torch.cuda.empty_cache()
+    return {"kind": f"row-stage LDS-DMA read (measure.hip) over {gib} GiB, best of {reps} passes", "rows": table}
 
 
 def exchange(torch, mode: int, n_words: int, rounds: int = 200, epoch0: int = 0, buf=None, reps: int = 8,
@@ -259,6 +302,9 @@ def main(argv) -> int:
         return 0
     if what == "stream_lds":  # plain, non-temporal and LDS-DMA reads
         print(json.dumps(stream_read(torch, variants=(0, 1, 2, 3))), flush=True)
+        return 0
+    if what == "rows":  # the batched expert kernels' stage pattern against whole rows
+        print(json.dumps(row_stages(torch)), flush=True)
         return 0
     if what == "exchange":
         G = lib().measure_cus()

@@ -26,6 +26,12 @@
 //    the XCC_ID hardware register; a mode whose loads cannot see the group's stores ends
 //    at the spin limit with the error word set.
 //    Every wait is bounded (spin limit, then the error word).
+// 3. A row-stage read: the access pattern of the batched expert kernels' weight stages. Each
+//    wave owns a block of 64 rows of row_bytes bytes and reads it through D 8-KB LDS stage
+//    buffers with LDS-DMA (eight 1-KB instructions per stage, D stages in flight); a stage
+//    covers 8192 / P rows x P bytes (P = 128: 128 bytes of each of the 64 rows, the batched
+//    kernels' 4-group stages; P = row_bytes: whole consecutive rows, a contiguous 8 KB). Same
+//    bytes, instructions and depth for every P, so the rates differ only by the pattern.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -91,6 +97,48 @@ __global__ void __launch_bounds__(kThreads) stream_read_lds_kernel(const u32x4* 
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 #pragma unroll
     for (int u = 0; u < U; ++u) acc ^= ring[wave][u][lane * 4];
+  }
+  if (acc == 0x9E3779B9u && threadIdx.x == 0x3FF) sink[0] = acc;  // never true: threadIdx.x < 256
+}
+
+// Row-stage read (item 3 above). Stage s of a wave's block covers rows rg * Rs .. + Rs - 1
+// (Rs = 8192 / P, rg = s / (row_bytes / P)) at bytes c * P .. + P - 1 of each (c = s mod
+// row_bytes / P); byte e of the stage (e = 1024 j + 16 lane for instruction j) is byte e mod P
+// of its row e / P. Requires row_bytes % P == 0 and P | 8192 (checked by the caller).
+template <int P, int D>
+__global__ void __launch_bounds__(kThreads) row_stage_kernel(const uint8_t* __restrict__ p, int row_bytes,
+                                                             uint32_t* __restrict__ sink) {
+  __shared__ uint32_t ring[kThreads / 64][D][2048];
+  constexpr int Rs = 8192 / P;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint8_t* blk = p + ((size_t)blockIdx.x * (kThreads / 64) + wave) * 64 * (size_t)row_bytes;
+  const int n_c = row_bytes / P, stages = row_bytes / 128;
+  auto issue = [&](int s) {
+    const int rg = s / n_c, c = s - rg * n_c;
+    const uint8_t* base = blk + (size_t)rg * Rs * row_bytes + (size_t)c * P;
+    const uint32_t lds = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)&ring[wave][s % D][0];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int e = j * 1024 + 16 * lane;
+      const uint8_t* src = base + (size_t)(e / P) * row_bytes + (e % P);
+      asm volatile(
+          "s_mov_b32 m0, %1\n\t"
+          "s_nop 0\n\t"
+          "global_load_lds_dwordx4 %0, off nt" ::"v"(src),
+          "s"(__builtin_amdgcn_readfirstlane(lds + j * 1024))
+          : "memory", "m0");
+    }
+  };
+  for (int s = 0; s < D && s < stages; ++s) issue(s);
+  uint32_t acc = 0;
+  for (int s = 0; s < stages; ++s) {
+    if (s + D - 1 < stages)
+      asm volatile("s_waitcnt vmcnt(%0)" ::"n"(8 * (D - 1)) : "memory");
+    else
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    acc ^= ring[wave][s % D][lane * 32];
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (s + D < stages) issue(s + D);
   }
   if (acc == 0x9E3779B9u && threadIdx.x == 0x3FF) sink[0] = acc;  // never true: threadIdx.x < 256
 }
@@ -219,6 +267,28 @@ int measure_stream_read(const void* buf, size_t nbytes, int variant, int unroll,
   else if (variant == 3 && unroll == 8) hipLaunchKernelGGL((stream_read_lds_kernel<8, true>), dim3(blocks), dim3(kThreads), 0, s, p, n, sink);
   else return -2;
   return hipGetLastError() == hipSuccess ? 0 : -8;
+}
+
+// Enqueue one row-stage read (item 3 of the file comment) of nbytes at buf: nbytes a multiple
+// of 256 * row_bytes (one workgroup per 4 blocks of 64 rows), row_bytes a multiple of 128 and
+// of piece, piece (P) one of 128, 256, 512, 1024, 2048, depth (D) 2 or 4 stages in flight.
+int measure_row_stages(const void* buf, size_t nbytes, int row_bytes, int piece, int depth, uint32_t* sink,
+                       hipStream_t s) {
+  if (!buf || !sink || row_bytes < 128 || row_bytes % 128 || piece < 128 || row_bytes % piece) return -1;
+  if (nbytes % ((size_t)256 * row_bytes)) return -1;
+  const size_t blocks = nbytes / ((size_t)256 * row_bytes);
+  if (blocks < 1 || blocks > 0x7FFFFFFF) return -1;
+  const uint8_t* p = static_cast<const uint8_t*>(buf);
+  const dim3 g((unsigned)blocks), b(kThreads);
+#define ROW_STAGES(P_, D_)                                                                   \
+  if (piece == P_ && depth == D_) {                                                          \
+    hipLaunchKernelGGL((row_stage_kernel<P_, D_>), g, b, 0, s, p, row_bytes, sink);         \
+    return hipGetLastError() == hipSuccess ? 0 : -8;                                         \
+  }
+  ROW_STAGES(128, 2) ROW_STAGES(256, 2) ROW_STAGES(512, 2) ROW_STAGES(1024, 2) ROW_STAGES(2048, 2)
+  ROW_STAGES(128, 4) ROW_STAGES(256, 4) ROW_STAGES(512, 4) ROW_STAGES(1024, 4) ROW_STAGES(2048, 4)
+#undef ROW_STAGES
+  return -2;
 }
 
 // Enqueue the exchange probe (see the file comment). reps: replicas of mode 0 (1..16; the
