@@ -57,11 +57,18 @@ def algorithmic_bytes_per_layer(bits: int) -> int:
 
 
 def stream_read_probe(torch) -> dict:
-    """The attainable read rate of plain streaming code here: the read-only HIP streaming
-    kernel of measure/measure.hip over 4 GiB (best variant, HIP events on its stream)."""
+    """The attainable read rate of plain streaming code here: the better of measure/measure.hip's
+    read-only streaming kernel (best variant) and its row-stage LDS-DMA read (128-byte pieces of
+    64 rows per 8-KB stage, rows of 2048 and 512 bytes, and 512-byte pieces of 2-KB rows with 4
+    stages in flight), each over 4 GiB, HIP events on the launch stream."""
     import measure
 
-    return measure.stream_read(torch)
+    s = measure.stream_read(torch)
+    r = measure.row_stages(torch, configs=((2048, 2, 128), (2048, 4, 512), (512, 2, 128)), verbose=False)
+    return {"kind": "best of the read-only streaming kernel and the row-stage LDS-DMA read (measure.hip), "
+                    "4 GiB each, best of 5 passes per variant",
+            "gbs": max(s["gbs"], r["gbs"]), "stream_gbs": s["gbs"], "row_stage_gbs": r["gbs"],
+            "variants": s["variants"], "row_stage_variants": r["rows"]}
 
 
 def cpu_model() -> str:

@@ -112,11 +112,16 @@ def stream_read(torch, gib: int = 4, reps: int = 5, variants=(0, 1)) -> dict:
             "gbs": round(best, 1), "variants": table}
 
 
-def row_stages(torch, gib: int = 4, reps: int = 5) -> dict:
+ROW_STAGE_SWEEP = tuple((rb, d, p) for rb in (2048, 512) for d in (2, 4) for p in (128, 256, 512, 1024, 2048)
+                        if rb % p == 0)
+
+
+def row_stages(torch, gib: int = 4, reps: int = 5, configs=ROW_STAGE_SWEEP, verbose: bool = True) -> dict:
     """Read rate (GB/s) of the row-stage kernel (measure.hip item 3) over a gib-GiB buffer for
-    rows of 2048 bytes (a 4-bit gate/up row at hidden 4096) and 512 bytes (a 4-bit down row at
-    intermediate 1024), every stage piece P and 2 or 4 stages in flight; best of `reps` passes
-    after one untimed pass, HIP events on the launch stream."""
+    each (row bytes, stages in flight, piece P) of `configs`; the default sweep covers rows of
+    2048 bytes (a 4-bit gate/up row at hidden 4096) and 512 bytes (a 4-bit down row at
+    intermediate 1024), every piece and 2 or 4 stages in flight. Best of `reps` passes after
+    one untimed pass, HIP events on the launch stream."""
     dev = torch.device("cuda:0")
     nbytes = gib << 30
     buf = torch.empty(nbytes, dtype=torch.uint8, device=dev)
@@ -124,33 +129,31 @@ def row_stages(torch, gib: int = 4, reps: int = 5) -> dict:
     sink = torch.zeros(4, dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream(dev)
     table = []
-    for row_bytes in (2048, 512):
-        for depth in (2, 4):
-            for piece in (128, 256, 512, 1024, 2048):
-                if row_bytes % piece:
-                    continue
+    for row_bytes, depth, piece in configs:
 
-                def once():
-                    rc = lib().measure_row_stages(buf.data_ptr(), nbytes, row_bytes, piece, depth, sink.data_ptr(),
-                                                  stream.cuda_stream)
-                    if rc != 0:
-                        raise RuntimeError(f"measure_row_stages: {rc}")
+        def once():
+            rc = lib().measure_row_stages(buf.data_ptr(), nbytes, row_bytes, piece, depth, sink.data_ptr(),
+                                          stream.cuda_stream)
+            if rc != 0:
+                raise RuntimeError(f"measure_row_stages: {rc}")
 
-                once()
-                gbs = 0.0
-                for _ in range(reps):
-                    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-                    e0.record(stream)
-                    once()
-                    e1.record(stream)
-                    torch.cuda.synchronize()
-                    gbs = max(gbs, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
-                table.append({"row_bytes": row_bytes, "piece": piece, "rows_per_stage": 8192 // piece,
-                              "stages_in_flight": depth, "gbs": round(gbs, 1)})
-                print(json.dumps(table[-1]), flush=True)
+        once()
+        gbs = 0.0
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            once()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            gbs = max(gbs, nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+        table.append({"row_bytes": row_bytes, "piece": piece, "rows_per_stage": 8192 // piece,
+                      "stages_in_flight": depth, "gbs": round(gbs, 1)})
+        if verbose:
+            print(json.dumps(table[-1]), flush=True)
     del buf
     torch.cuda.empty_cache()
-    return {"kind": f"row-stage LDS-DMA read (measure.hip) over {gib} GiB, best of {reps} passes", "rows": table}
+    return {"kind": f"row-stage LDS-DMA read (measure.hip) over {gib} GiB, best of {reps} passes",
+            "gbs": max(r["gbs"] for r in table), "rows": table}
 
 
 def exchange(torch, mode: int, n_words: int, rounds: int = 200, epoch0: int = 0, buf=None, reps: int = 8,
