@@ -192,9 +192,10 @@ def _q(x, axis=None):
     return [round(float(np.median(x, axis=axis)), 3), round(float(np.percentile(x, 90, axis=axis)), 3)]
 
 
-def phase_trace(torch, n_tokens: int = 16, warmup: int = 4) -> dict:
-    """Phase stamps of the decode kernel (traced build) on the 60-layer x 512-expert 4-bit
-    top-4 stack with the pre-norm, one launch per token (tokens = synthetic draws). Per layer
+def phase_trace(torch, n_tokens: int = 16, warmup: int = 4, bits: int = 4) -> dict:
+    """Phase stamps of the decode kernel (traced build) on the 60-layer x 512-expert top-4
+    stack (4-, 3- or 2-bit experts) with the pre-norm, one launch per token (tokens =
+    synthetic draws). Per layer
     1..59 and workgroup: phase durations; per exchange, the time from the last workgroup's
     publish to each reader's completion, and the spread of the publishes. Medians and 90th
     percentiles over layers, tokens and workgroups. The tokens run back to back as in the
@@ -209,7 +210,7 @@ def phase_trace(torch, n_tokens: int = 16, warmup: int = 4) -> dict:
     L.fmoe_trace_set.restype = ctypes.c_int
     L.fmoe_trace_set.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
     fm.use(L)
-    bits, H, I, E, K, NL = 4, bench.H_, bench.I_, bench.E_, bench.K_, bench.L_
+    H, I, E, K, NL = bench.H_, bench.I_, bench.E_, bench.K_, bench.L_
     blobs, routers, layers, _ = bench.build_stack(bits, dev)
     G = lib().measure_cus()
     per = NL * TRACE_PHASES * MAX_GRID
@@ -248,7 +249,7 @@ def phase_trace(torch, n_tokens: int = 16, warmup: int = 4) -> dict:
     S = np.stack(per_token)  # [token][layer][phase][workgroup], µs
     ls = slice(1, NL)  # layers with an h exchange
     layer_us = np.diff(S[:, :, 0, :], axis=1)  # start-to-start per workgroup
-    out = {"workload": "60-layer x 512-expert 4-bit top-4 decode stack with pre-norm, one token per launch",
+    out = {"workload": f"60-layer x 512-expert {bits}-bit top-4 decode stack with pre-norm, one token per launch",
            "tokens_traced": len(per_token), "workgroups": G, "clock": "s_memrealtime, 100 MHz",
            "launch_us_trace_on": _q(launch_us["on"]), "launch_us_trace_off": _q(launch_us["off"]),
            "layer_us": _q(layer_us)}
@@ -268,9 +269,13 @@ def phase_trace(torch, n_tokens: int = 16, warmup: int = 4) -> dict:
     last_h = S[:, 0:NL - 1, 17, :].max(axis=2)[:, :, None]  # layer l-1's h
     last_lg = S[:, ls, 2, :].max(axis=2)[:, :, None]
     ex = {"h": S[:, ls, 1, :] - last_h, "logits": S[:, ls, 3, :] - last_lg}
-    for j in range(4):  # slot j: produced by wave (j + 1) % 4 everywhere, read by wave j
-        last_a = S[:, ls, 5 + (j + 1) % 4, :].max(axis=2)[:, :, None]
-        ex[f"a slot {j}"] = S[:, ls, 9 + j, :] - last_a
+    for j in range(4):
+        if bits == 4:  # slot j: produced by wave (j + 1) % 4 everywhere, read by wave j
+            last_a = S[:, ls, 5 + (j + 1) % 4, :].max(axis=2)[:, :, None]
+            ex[f"a slot {j}"] = S[:, ls, 9 + j, :] - last_a
+        else:  # spread schedule: a slot's rows come from several waves; the last gate/up of any wave
+            last_a = S[:, ls, 5:9, :].max(axis=(2, 3))[:, :, None]
+            ex[f"a slot {j} (after the last gate/up of any wave)"] = S[:, ls, 9 + j, :] - last_a
     out["exchange_after_last_publish_us"] = {k: _q(v) for k, v in ex.items()}
     spread = {"layer start": S[:, ls, 0, :], "logits published": S[:, ls, 2, :], "h published": S[:, ls, 17, :]}
     for w in range(4):
@@ -323,8 +328,8 @@ def main(argv) -> int:
                 for no_ack in (False, True):
                     print(json.dumps(exchange(torch, 0, n, reps=reps, no_ack=no_ack)), flush=True)
         return 0
-    if what == "trace":  # phase trace of the decode kernel (traced build)
-        r = phase_trace(torch)
+    if what == "trace":  # phase trace of the decode kernel (traced build); optional code width
+        r = phase_trace(torch, bits=int(argv[2]) if len(argv) > 2 else 4)
         print(json.dumps(r), flush=True)
         print(trace_markdown(r), flush=True)
         return 0

@@ -222,13 +222,19 @@ __device__ __forceinline__ void wait_ready(const int* ready, int r) {
 template <int BITS, int CPL_G, int CPL_D, int HC, int IC, int EC, int KC, int SH>
 __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) {
   constexpr int kBatchGU = batch_gu<CPL_G>();
-  constexpr int kBatchD = batch_d<CPL_D>();
   using C = Chunk<BITS>;
   constexpr int CC = C::kCodes;
   // With the shape fixed at compile time, a wave reduces all of its gate/up or down items
   // in one transposed pass (reduce_transposed) instead of one cross-lane reduction each.
   constexpr int kLprG = HC ? lanes_per_row(HC / CC) : 0;
   constexpr int kLprD = IC ? lanes_per_row(IC / CC) : 0;
+  // Down items per batch. The compiled shapes give each workgroup 16 rows of every slot (hidden
+  // 4096 over 256 workgroups), i.e. kLprD / 4 items of 64 / kLprD rows: 8 at 4 bits, 4 at 2
+  // and 3 bits (64 columns per chunk, so a wave pass covers 4 rows). The batch is sized to
+  // that, since the unrolled item loop computes every item of a batch, present or not.
+  constexpr int kBatchD =
+      (HC && IC) ? (kLprD / 4 < 2 ? 2 : (kLprD / 4 > batch_d<CPL_D>() ? batch_d<CPL_D>() : kLprD / 4))
+                 : batch_d<CPL_D>();
   constexpr bool kFastGU = kLprG == 64 && kBatchGU == 4;
   constexpr bool kFastD = kLprD >= 16 && kBatchD >= 2 && kBatchD <= 8;
   // Compiled shapes with a gated shared expert: its expert is fixed, so its gate/up rows run
