@@ -1018,15 +1018,21 @@ __global__ void __launch_bounds__(kDecodeThreads) decode_kernel(DecodeParams p) 
 #pragma unroll
             for (int u = 0; u < kBatchD; ++u) {
               float a_ = 0.f;
+              // Items past the slot's end are skipped (a wave-uniform branch) in the top-4
+              // shapes, which take this path only on grids other than 256 workgroups. With
+              // top-10 routing every wave takes it, and there the branch measured slower than
+              // reducing the empty items.
+              if (KC != 4 || t0 + u < t_hi) {
 #pragma unroll
-              for (int q = 0; q < CPL_D; ++q) {
-                int c = subD + kLprD * q;
-                if (c < nchD) a_ += chunk_dot_int<BITS>(wd[u][q], sd[u][q], dc[q]);
+                for (int q = 0; q < CPL_D; ++q) {
+                  int c = subD + kLprD * q;
+                  if (c < nchD) a_ += chunk_dot_int<BITS>(wd[u][q], sd[u][q], dc[q]);
+                }
               }
               acc[u] = a_;
             }
-            // items past t_hi (another slot's or none) are reduced too; their sums are
-            // not stored
+            // items past t_hi (another slot's or none) are reduced as zeros; their sums
+            // are not stored
             const float sum = reduce_transposed<kBatchD, kLprD>(acc);
             const int u = transposed_index<kBatchD>(lane);
             const int t = t0 + u;
